@@ -1,0 +1,216 @@
+/*
+ * slora.h - C ABI of the paged, heterogeneous-batch LoRA delta on MI355X.
+ *
+ * The operation (S-LoRA pages): with the base forward h = xW, LoRA adds the
+ * product of two thin factors, A (d_in x r) and B (r x d_out), and a server of
+ * many adapters keeps that delta separate, computing x A B on the fly for each
+ * request's own adapter (summary page "S-LoRA: Serving Thousands of
+ * Concurrent LoRA Adapters", sections "What this paper explains", "The
+ * mechanism" and "How to read the paper" item 2).  Every token t of a batch
+ * names an adapter a with rank r_a and scale s_a and receives
+ *
+ *     y[t, :] += s_a * (x[t, :] A_a) B_a                      (fp32 accumulate)
+ *
+ * (blog page "Multiplexing Thousands of Fine-Tuned Adapters", section 2
+ * pseudocode: the per-token delta times a scaling factor added to the base
+ * output).  A_a and B_a live as non-contiguous pages of one pool shared with
+ * KV blocks and found through a block table (summary page, "Unified Paging";
+ * blog page section 2; catalog page, mechanism paragraph).  A page here is one
+ * row: an adapter of rank r holds, per projection, r pages with the rows of
+ * A^T (row j is column j of A) and r pages with the rows of B.
+ *
+ * Conventions shared by every entry point:
+ *  - Every call returns an slora_status; no C++ exception crosses the ABI.
+ *    On failure nothing changes (all-or-nothing) and slora_last_error()
+ *    returns a message for the calling thread.
+ *  - Device memory is owned by the caller: pool classes, x, y, the metadata
+ *    buffer and the workspace.  The library never frees it and a pool must not
+ *    outlive it.  Host arrays are only borrowed for the duration of a call.
+ *    Opaque objects belong to the library and are released by *_destroy.
+ *  - Streams are hipStream_t values passed as void* (NULL = default stream).
+ *    The library uses the device that is current when the pool is created and
+ *    makes it current again for its own HIP calls.
+ *  - A pool and its segments are not thread-safe; callers serialise.
+ *  - Page offsets are 64-bit: page_id * page_bytes may exceed 4 GiB.
+ */
+#ifndef SLORA_H
+#define SLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct slora_pool slora_pool;
+typedef struct slora_segments slora_segments;
+
+typedef enum {
+  SLORA_OK = 0,
+  SLORA_E_INVAL = -1,  /* bad argument (NULL pointer, size, rank, dtype, layout) */
+  SLORA_E_NOMEM = -2,  /* not enough free pages, or a host/device buffer too small */
+  SLORA_E_EXIST = -3,  /* adapter id already loaded */
+  SLORA_E_NOENT = -4,  /* adapter id not loaded */
+  SLORA_E_STALE = -5,  /* segments built against an adapter since unloaded/reloaded */
+  SLORA_E_HIP = -6     /* a HIP runtime call failed; the message names it */
+} slora_status;
+
+typedef enum { SLORA_F32 = 0, SLORA_F16 = 1 } slora_dtype;
+
+/* Pool description.  With n_classes == 1 every page (A^T rows, B rows and KV
+ * blocks) holds h_in elements and h_in must equal h_out.  With n_classes == 2,
+ * class 0 pages hold h_in elements (A^T rows, KV) and class 1 pages hold h_out
+ * elements (B rows, KV).  class_base[c] is caller-owned device memory of
+ * n_pages[c] * page_elems * sizeof(dtype) bytes, 16-byte aligned.
+ * free_order[c] (host, borrowed) is the order in which the free list hands out
+ * pages: a permutation of [0, n_pages[c]); NULL means ascending ids.
+ * h_in and h_out must be multiples of 8; max_rank is at most 256. */
+typedef struct {
+  int32_t dtype;        /* slora_dtype of pages, x and y */
+  int32_t h_in;         /* d_in: elements of x rows and of A^T rows */
+  int32_t h_out;        /* d_out: elements of y rows and of B rows */
+  int32_t n_proj;       /* projections per adapter sharing one token->adapter map (1..8) */
+  int32_t max_adapters; /* adapter ids are 0 .. max_adapters-1 */
+  int32_t max_rank;     /* largest rank accepted by slora_load_adapter */
+  int32_t n_classes;    /* 1 or 2, see above */
+  int32_t reserved0;    /* must be 0 */
+  int64_t n_pages[2];
+  void* class_base[2];
+  const int32_t* free_order[2];
+} slora_pool_desc;
+
+/* Create a pool over caller-owned page memory.  Host-only: no device memory is
+ * touched until the first adapter load with data. */
+slora_status slora_pool_create(const slora_pool_desc* desc, slora_pool** out);
+void slora_pool_destroy(slora_pool* pool);
+
+/* Tuning knobs of the tile builder (applied by later slora_build_segments):
+ *  SLORA_TUNE_MFMA_MIN_TOKENS  - fp16 segments with at least this many tokens
+ *                                use the matrix-core (MFMA) tiles; default 16.
+ *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
+ *                                expand tile; default 32768.
+ *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
+ *                                of 256; default 512.
+ * They change how the work is cut, never what is computed. */
+typedef enum {
+  SLORA_TUNE_MFMA_MIN_TOKENS = 0,
+  SLORA_TUNE_GEMV_EXPAND_ELEMS = 1,
+  SLORA_TUNE_MFMA_EXPAND_COLS = 2
+} slora_tune_key;
+slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
+
+/* Take n pages of class cls from the head of the free list for KV blocks
+ * (summary page, walkthrough step 4: KV growth and adapters share one
+ * allocator).  Writes the ids to out_ids (host, n entries). */
+slora_status slora_alloc_pages(slora_pool* pool, int32_t cls, int64_t n, int32_t* out_ids);
+/* Return KV pages to the tail of the free list, in the order given.  Only
+ * pages handed out by slora_alloc_pages and not yet freed are accepted. */
+slora_status slora_free_pages(slora_pool* pool, int32_t cls, int64_t n, const int32_t* ids);
+/* Free pages of class cls, or -1 on a bad argument. */
+int64_t slora_free_count(const slora_pool* pool, int32_t cls);
+
+/* Make adapter `id` resident (summary page, "Host-resident adapter store" and
+ * walkthrough step 2: adapters live in host memory and are fetched on demand).
+ * Takes from the head of the free list, for each projection p in order, rank
+ * pages for the A^T rows j = 0..rank-1 and then rank pages for the B rows (B
+ * rows come from class 1 when the pool has two classes).  A and B are host
+ * arrays of n_proj pointers: A[p] is h_in x rank row-major, B[p] is
+ * rank x h_out row-major, both of the pool dtype.  The rows are copied to the
+ * pages through pinned staging on `stream`, and the call returns after the
+ * copy has completed, so A and B may be freed at once.  A == NULL and
+ * B == NULL together reserve the pages and block-table entry without writing
+ * them (the pages keep their previous content).  1 <= rank <= max_rank; scale
+ * must be finite. */
+slora_status slora_load_adapter(slora_pool* pool, int32_t id, int32_t rank, float scale,
+                                const void* const* A, const void* const* B, void* stream);
+/* Drop adapter `id` from the pool (summary page, walkthrough step 4: unused
+ * adapters leave GPU memory).  Its pages go to the tail of the free list in the
+ * order they were taken.  Segments built against it become stale. */
+slora_status slora_unload_adapter(slora_pool* pool, int32_t id);
+/* Page ids of adapter `id`, projection `proj`: rank A^T pages to a_ids and
+ * rank B pages to b_ids (host arrays; either may be NULL).  *rank_out
+ * (may be NULL) receives the rank. */
+slora_status slora_adapter_pages(const slora_pool* pool, int32_t id, int32_t proj,
+                                 int32_t* a_ids, int32_t* b_ids, int32_t* rank_out);
+
+/* Group a batch by adapter (host only).  ids[t] (host, n_tokens entries) is
+ * token t's adapter; a negative id means "no adapter" and leaves y[t]
+ * untouched.  Tokens are stably sorted by adapter id into segments in
+ * ascending id order, each with its rank, scale, rank prefix offset and page
+ * lists, and the work is cut into tiles for the shrink (x A) and expand
+ * (. B, scale, accumulate) kernels.  Every named adapter must be loaded. */
+slora_status slora_build_segments(slora_pool* pool, int32_t n_tokens, const int32_t* ids,
+                                  slora_segments** out);
+void slora_segments_destroy(slora_segments* seg);
+
+typedef struct {
+  int32_t n_tokens;       /* batch size given to slora_build_segments */
+  int32_t n_routed;       /* tokens with an adapter */
+  int32_t n_segments;     /* distinct adapters in the batch */
+  int32_t n_proj;
+  int64_t sum_rank;       /* sum over segments of rank: page-list length per projection */
+  int64_t sum_rank_tokens;/* sum over routed tokens of their adapter's rank */
+  int32_t n_shrink_tiles;
+  int32_t n_expand_tiles;
+  int32_t n_mfma_segments;/* segments routed to the matrix-core (MFMA) tiles */
+  int32_t reserved0;
+  size_t meta_bytes;      /* device metadata size for slora_segments_upload */
+  size_t workspace_bytes; /* device workspace size for slora_lora_delta */
+} slora_segments_info;
+
+slora_status slora_segments_get_info(const slora_segments* seg, slora_segments_info* info);
+
+/* Host copies of the segment metadata; any pointer may be NULL.  Sizes:
+ * perm[n_routed] (batch index of the i-th sorted token), seg_start[S+1],
+ * seg_adapter[S], seg_rank[S], seg_scale[S], seg_page_off[S+1] (prefix sum of
+ * ranks), a_pages[n_proj*sum_rank] and b_pages[n_proj*sum_rank] (entry
+ * p*sum_rank + seg_page_off[s] + j is row j of segment s, projection p). */
+slora_status slora_segments_export(const slora_segments* seg, int32_t* perm, int32_t* seg_start,
+                                   int32_t* seg_adapter, int32_t* seg_rank, float* seg_scale,
+                                   int32_t* seg_page_off, int32_t* a_pages, int32_t* b_pages);
+
+/* Introspection of the work split (host copies): layout[8] receives
+ * {n_shrink_tiles, shrink_stride, shrink_tokcap, shrink_pagecap,
+ *  n_expand_tiles, expand_stride, expand_tokcap, expand_pagecap} and, when
+ * records is not NULL and holds at least meta_bytes / 4 words, the tile
+ * records: n_shrink_tiles records of shrink_stride int32 words, then the
+ * expand records.  Record words: 0 kind (0 vector ALU, 1 MFMA), 1 token count,
+ * 2 segment rank, 3 first rank row (shrink) or first column (expand), 4 rows
+ * or columns covered, 5 workspace offset of the first token's v row, 6 scale
+ * (float bits), 7 expand thread-map width; then tokcap batch indices of the
+ * tokens, then per projection pagecap page ids (shrink: the rows covered;
+ * expand: all rank B rows).  For tests and tools; the layout may change. */
+slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, int32_t* records,
+                                  size_t records_words);
+
+/* Copy the tile metadata to caller-owned device memory dev_meta (at least
+ * meta_bytes, 16-byte aligned) on `stream` and remember that address for
+ * later deltas.  The copy is asynchronous; dev_meta must stay untouched while
+ * deltas that use it are in flight. */
+slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t dev_meta_bytes,
+                                   void* stream);
+
+/* The hot path: y[t] += s_a * (x[t] A_a) B_a for every routed token, for
+ * projection `proj` (0 <= proj < n_proj).  x is device memory of
+ * n_tokens x h_in and y of n_tokens x h_out, both row-major in batch order
+ * and of the pool dtype; y is updated in place with one rounding of
+ * fp32(y) + s * d per element, where d is accumulated in fp32.  workspace is
+ * device memory of at least workspace_bytes (fp32 x A products), 16-byte
+ * aligned.  Launches the shrink and expand kernels on `stream` and returns
+ * without waiting; launch errors return SLORA_E_HIP, device faults surface at
+ * the caller's next synchronisation.  Requires a prior slora_segments_upload.
+ * Returns SLORA_E_STALE if an adapter of the batch was unloaded since the
+ * segments were built.  With no routed tokens it launches nothing. */
+slora_status slora_lora_delta(slora_pool* pool, const slora_segments* seg, int32_t proj,
+                              const void* x, void* y, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* slora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLORA_H */

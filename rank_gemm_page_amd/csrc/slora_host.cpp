@@ -1,0 +1,810 @@
+// Host runtime of the paged LoRA delta: unified page pool with FIFO free lists
+// and a block table, the adapter loader, the segment builder and tile lists,
+// and the C ABI declared in include/slora.h.
+//
+// S-LoRA pages this follows:
+//  * one pool hands out pages to KV blocks and to LoRA factors of varying
+//    rank, and a block table maps logical tensors to physical pages (summary
+//    page "S-LoRA: Serving Thousands of Concurrent LoRA Adapters", "Unified
+//    Paging"; blog page section 2: adapter weights in non-contiguous blocks);
+//  * adapters stay in host memory and only those a batch needs are copied to
+//    the device; unused ones leave it (summary page, "Host-resident adapter
+//    store" and walkthrough steps 2 and 4);
+//  * a batch mixes adapters and ranks and is computed by kernels that gather
+//    non-contiguous pages (summary page, "Heterogeneous batching kernels";
+//    blog page section 3: the kernel matches each request's hidden state to
+//    its adapter's pages in the paging table).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "slora.h"
+#include "slora_internal.h"
+
+using namespace slora;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+slora_status fail(slora_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+slora_status hip_fail(hipError_t e, const char* what) {
+  return fail(SLORA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int elem_bytes(int32_t dtype) { return dtype == SLORA_F16 ? 2 : 4; }
+
+// FIFO free list of one page class as a ring over [0, capacity).
+struct FreeRing {
+  std::vector<int32_t> buf;
+  int64_t head = 0, count = 0;
+  int64_t cap() const { return (int64_t)buf.size(); }
+  int32_t pop_front() {
+    const int32_t v = buf[head];
+    head = (head + 1 == cap()) ? 0 : head + 1;
+    --count;
+    return v;
+  }
+  void push_back(int32_t v) {
+    int64_t pos = head + count;
+    if (pos >= cap()) pos -= cap();
+    buf[pos] = v;
+    ++count;
+  }
+  void push_front(int32_t v) {
+    head = (head == 0) ? cap() - 1 : head - 1;
+    buf[head] = v;
+    ++count;
+  }
+};
+
+enum : uint8_t { PAGE_FREE = 0, PAGE_KV = 1, PAGE_ADAPTER = 2 };
+
+struct AdapterRec {
+  bool loaded = false;
+  int32_t rank = 0;
+  float scale = 0.f;
+  uint64_t gen = 0;
+  std::vector<int32_t> a_pages;  // [n_proj][rank]
+  std::vector<int32_t> b_pages;  // [n_proj][rank]
+};
+
+struct Tuning {
+  int64_t mfma_min_tokens = 16;
+  int64_t gemv_expand_elems = 32768;
+  int64_t mfma_expand_cols = 512;
+};
+
+// GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
+// two (the kernel instantiates 1, 2, 4, 8), and the rank rows per tile.
+int shrink_nck(int32_t dtype, int32_t h_in) {
+  const int vec = dtype == SLORA_F16 ? 8 : 4;
+  const int per = (h_in / vec + kThreads - 1) / kThreads;
+  int nck = 1;
+  while (nck < per) nck *= 2;
+  return nck;
+}
+
+}  // namespace
+
+struct slora_pool {
+  slora_pool_desc d{};
+  int elem = 2;
+  int64_t page_elems[2] = {0, 0};
+  int64_t page_bytes[2] = {0, 0};
+  FreeRing free_list[2];
+  std::vector<uint8_t> state[2];
+  std::vector<AdapterRec> adapters;
+  uint64_t gen_counter = 0;
+  Tuning tune;
+  // load staging (lazily allocated on the first load with data)
+  int device = -1;
+  char* h_stage = nullptr;
+  char* d_stage = nullptr;
+  size_t stage_bytes = 0;
+  int32_t* h_pages = nullptr;
+  int32_t* d_pages = nullptr;
+  // metadata upload arena (pinned, two slots used in turn)
+  char* h_meta[2] = {nullptr, nullptr};
+  size_t h_meta_bytes[2] = {0, 0};
+  hipEvent_t meta_done[2] = {nullptr, nullptr};
+  int meta_slot = 0;
+  // counting-sort scratch, all zero between builds
+  std::vector<int32_t> count_scratch;
+
+  int n_classes() const { return d.n_classes; }
+  int b_class() const { return d.n_classes == 2 ? 1 : 0; }
+};
+
+struct slora_segments {
+  slora_pool* pool = nullptr;
+  int32_t n_tokens = 0;
+  int32_t n_proj = 1;
+  std::vector<int32_t> perm, seg_start, seg_adapter, seg_rank, seg_page_off, a_pages, b_pages;
+  std::vector<float> seg_scale;
+  std::vector<uint64_t> seg_gen;
+  std::vector<int64_t> seg_v_off;
+  int64_t sum_r = 0, sum_rt = 0;
+  int32_t n_mfma_segments = 0;
+  // tile records: shrink records, then expand records
+  std::vector<int32_t> blob;
+  int32_t n_shrink = 0, n_expand = 0;
+  int32_t shrink_stride = 0, shrink_tokcap = 0, shrink_pagecap = 0;
+  int32_t expand_stride = 0, expand_tokcap = 0, expand_pagecap = 0;
+  int64_t expand_off_words = 0;
+  int32_t gemv_rows = 0;
+  const int32_t* dev_meta = nullptr;
+};
+
+namespace {
+
+slora_status set_device(slora_pool* p) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (p->device < 0) p->device = cur;
+  if (cur != p->device) {
+    e = hipSetDevice(p->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  }
+  return SLORA_OK;
+}
+
+slora_status ensure_stage(slora_pool* p) {
+  if (p->h_stage) return SLORA_OK;
+  slora_status st = set_device(p);
+  if (st != SLORA_OK) return st;
+  const size_t rows = (size_t)p->d.n_proj * (size_t)p->d.max_rank;
+  const size_t bytes = rows * (size_t)(p->d.h_in + p->d.h_out) * (size_t)p->elem;
+  const size_t pbytes = 2 * rows * sizeof(int32_t);
+  hipError_t e = hipHostMalloc((void**)&p->h_stage, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) { p->h_stage = nullptr; return hip_fail(e, "hipHostMalloc(load staging)"); }
+  e = hipHostMalloc((void**)&p->h_pages, pbytes, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipMalloc((void**)&p->d_stage, bytes);
+  if (e == hipSuccess) e = hipMalloc((void**)&p->d_pages, pbytes);
+  if (e != hipSuccess) {
+    if (p->d_stage) (void)hipFree(p->d_stage);
+    if (p->h_pages) (void)hipHostFree(p->h_pages);
+    (void)hipHostFree(p->h_stage);
+    p->h_stage = nullptr; p->d_stage = nullptr; p->h_pages = nullptr; p->d_pages = nullptr;
+    return hip_fail(e, "load staging allocation");
+  }
+  p->stage_bytes = bytes;
+  return SLORA_OK;
+}
+
+// Put pages taken for a failed load back at the head, newest first, so the
+// free list is exactly as before.
+void rollback_pages(slora_pool* p, const AdapterRec& rec) {
+  for (int pr = p->d.n_proj - 1; pr >= 0; --pr) {
+    for (int j = rec.rank - 1; j >= 0; --j) {
+      const int32_t b = rec.b_pages[(size_t)pr * rec.rank + j];
+      p->state[p->b_class()][b] = PAGE_FREE;
+      p->free_list[p->b_class()].push_front(b);
+    }
+    for (int j = rec.rank - 1; j >= 0; --j) {
+      const int32_t a = rec.a_pages[(size_t)pr * rec.rank + j];
+      p->state[0][a] = PAGE_FREE;
+      p->free_list[0].push_front(a);
+    }
+  }
+}
+
+slora_status upload_adapter(slora_pool* p, const AdapterRec& rec, const void* const* A,
+                            const void* const* B, hipStream_t stream) {
+  slora_status st = ensure_stage(p);
+  if (st != SLORA_OK) return st;
+  const int r = rec.rank, np = p->d.n_proj, e = p->elem;
+  const int64_t hin = p->d.h_in, hout = p->d.h_out;
+  char* a_rows = p->h_stage;
+  char* b_rows = p->h_stage + (size_t)np * r * hin * e;
+  for (int pr = 0; pr < np; ++pr) {
+    const char* Ap = static_cast<const char*>(A[pr]);
+    const char* Bp = static_cast<const char*>(B[pr]);
+    if (!Ap || !Bp) return fail(SLORA_E_INVAL, "slora_load_adapter: NULL A[p] or B[p]");
+    // A^T row j is column j of the h_in x r row-major A.
+    char* dst = a_rows + (size_t)pr * r * hin * e;
+    for (int64_t k = 0; k < hin; ++k)
+      for (int j = 0; j < r; ++j)
+        std::memcpy(dst + ((size_t)j * hin + k) * e, Ap + ((size_t)k * r + j) * e, e);
+    std::memcpy(b_rows + (size_t)pr * r * hout * e, Bp, (size_t)r * hout * e);
+    std::memcpy(p->h_pages + (size_t)pr * r, rec.a_pages.data() + (size_t)pr * r, r * sizeof(int32_t));
+    std::memcpy(p->h_pages + (size_t)(np + pr) * r, rec.b_pages.data() + (size_t)pr * r,
+                r * sizeof(int32_t));
+  }
+  const size_t bytes = (size_t)np * r * (hin + hout) * e;
+  hipError_t he = hipMemcpyAsync(p->d_stage, p->h_stage, bytes, hipMemcpyHostToDevice, stream);
+  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(adapter rows)");
+  he = hipMemcpyAsync(p->d_pages, p->h_pages, (size_t)2 * np * r * sizeof(int32_t),
+                      hipMemcpyHostToDevice, stream);
+  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(page ids)");
+  he = launch_scatter_rows(p->d_stage, np * r, hin * e, p->d_pages,
+                           static_cast<char*>(p->d.class_base[0]), p->page_bytes[0], stream);
+  if (he != hipSuccess) return hip_fail(he, "scatter A^T rows");
+  he = launch_scatter_rows(p->d_stage + (size_t)np * r * hin * e, np * r, hout * e,
+                           p->d_pages + (size_t)np * r,
+                           static_cast<char*>(p->d.class_base[p->b_class()]),
+                           p->page_bytes[p->b_class()], stream);
+  if (he != hipSuccess) return hip_fail(he, "scatter B rows");
+  he = hipStreamSynchronize(stream);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize(adapter load)");
+  return SLORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Tiles.  Each segment's tokens are cut into token blocks; the shrink work of
+// a block into rank-row blocks, the expand work into column blocks.
+
+struct TileSpec {
+  int32_t kind, seg, i0, ntok, pos, len, aux;
+};
+
+void split_tokens(int32_t c, int32_t cap, std::vector<std::pair<int32_t, int32_t>>& out) {
+  // ceil(c / cap) blocks of near-equal size
+  out.clear();
+  const int32_t nb = (c + cap - 1) / cap;
+  int32_t start = 0;
+  for (int32_t b = 0; b < nb; ++b) {
+    const int32_t len = (c - start) / (nb - b);
+    out.emplace_back(start, len);
+    start += len;
+  }
+}
+
+void build_tiles(slora_segments* s) {
+  const slora_pool* p = s->pool;
+  const int32_t S = (int32_t)s->seg_adapter.size();
+  const int32_t hin = p->d.h_in, hout = p->d.h_out;
+  const bool f16 = p->d.dtype == SLORA_F16;
+  const int vec = f16 ? 8 : 4;
+  const int nck = shrink_nck(p->d.dtype, hin);
+  const int gemv_rows = kShrinkRowBudget / nck;
+  s->gemv_rows = gemv_rows;
+
+  std::vector<TileSpec> sh, ex;
+  std::vector<std::pair<int32_t, int32_t>> blocks;
+  int32_t max_rank = 1;
+  s->n_mfma_segments = 0;
+  for (int32_t g = 0; g < S; ++g) {
+    const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
+    const int32_t r = s->seg_rank[g];
+    max_rank = std::max(max_rank, r);
+    const bool mfma = f16 && c >= p->tune.mfma_min_tokens && hin % 32 == 0;
+    if (mfma) {
+      ++s->n_mfma_segments;
+      split_tokens(c, kMfmaTok, blocks);
+      for (auto& tb : blocks) {
+        for (int32_t j0 = 0; j0 < r; j0 += kMfmaMaxRows)
+          sh.push_back({KIND_MFMA, g, tb.first, tb.second, j0, std::min(kMfmaMaxRows, r - j0), 0});
+        const int32_t cols = (int32_t)p->tune.mfma_expand_cols;
+        for (int32_t o0 = 0; o0 < hout; o0 += cols)
+          ex.push_back({KIND_MFMA, g, tb.first, tb.second, o0, std::min(cols, hout - o0), 0});
+      }
+    } else {
+      split_tokens(c, kGemvMaxTok, blocks);
+      // expand width: largest of vec*{256,128,64,32} with rank x width within budget
+      int32_t width = vec * 256;
+      while (width > vec * 32 && (int64_t)r * width > p->tune.gemv_expand_elems) width /= 2;
+      for (auto& tb : blocks) {
+        for (int32_t j0 = 0; j0 < r; j0 += gemv_rows)
+          sh.push_back({KIND_GEMV, g, tb.first, tb.second, j0, std::min(gemv_rows, r - j0), 0});
+        for (int32_t o0 = 0; o0 < hout; o0 += width)
+          ex.push_back({KIND_GEMV, g, tb.first, tb.second, o0, std::min(width, hout - o0), width});
+      }
+    }
+  }
+  // Heavier (MFMA) tiles first so they start early; stable otherwise.
+  auto heavier_first = [](const TileSpec& a, const TileSpec& b) { return a.kind > b.kind; };
+  std::stable_sort(sh.begin(), sh.end(), heavier_first);
+  std::stable_sort(ex.begin(), ex.end(), heavier_first);
+
+  const int np = s->n_proj;
+  s->shrink_tokcap = std::max(kGemvMaxTok, kMfmaTok);
+  s->shrink_pagecap = std::max(gemv_rows, kMfmaMaxRows);
+  s->shrink_stride = (REC_HDR + s->shrink_tokcap + np * s->shrink_pagecap + 3) & ~3;
+  s->expand_tokcap = std::max(kGemvMaxTok, kMfmaTok);
+  s->expand_pagecap = (max_rank + 3) & ~3;
+  s->expand_stride = (REC_HDR + s->expand_tokcap + np * s->expand_pagecap + 3) & ~3;
+  s->n_shrink = (int32_t)sh.size();
+  s->n_expand = (int32_t)ex.size();
+  s->expand_off_words = (int64_t)s->n_shrink * s->shrink_stride;
+  s->blob.assign((size_t)s->expand_off_words + (size_t)s->n_expand * s->expand_stride, 0);
+
+  auto fill = [&](int32_t* rec, const TileSpec& t, int32_t tokcap, int32_t pagecap, bool shrink) {
+    const int32_t g = t.seg;
+    const int32_t r = s->seg_rank[g];
+    rec[REC_KIND] = t.kind;
+    rec[REC_NTOK] = t.ntok;
+    rec[REC_RANK] = r;
+    rec[REC_POS] = t.pos;
+    rec[REC_LEN] = t.len;
+    rec[REC_V0] = (int32_t)(s->seg_v_off[g] + (int64_t)t.i0 * r);
+    float sc = s->seg_scale[g];
+    std::memcpy(&rec[REC_SCALE], &sc, 4);
+    rec[REC_AUX] = t.aux;
+    const int32_t first = s->seg_start[g] + t.i0;
+    for (int32_t k = 0; k < t.ntok; ++k) rec[REC_HDR + k] = s->perm[first + k];
+    for (int pr = 0; pr < np; ++pr) {
+      int32_t* pg = rec + REC_HDR + tokcap + pr * pagecap;
+      const int32_t* src = (shrink ? s->a_pages.data() : s->b_pages.data()) +
+                           (size_t)pr * s->sum_r + s->seg_page_off[g];
+      if (shrink)
+        for (int32_t j = 0; j < t.len; ++j) pg[j] = src[t.pos + j];
+      else
+        for (int32_t j = 0; j < r; ++j) pg[j] = src[j];
+    }
+  };
+  for (int32_t i = 0; i < s->n_shrink; ++i)
+    fill(s->blob.data() + (size_t)i * s->shrink_stride, sh[i], s->shrink_tokcap, s->shrink_pagecap, true);
+  for (int32_t i = 0; i < s->n_expand; ++i)
+    fill(s->blob.data() + (size_t)s->expand_off_words + (size_t)i * s->expand_stride, ex[i],
+         s->expand_tokcap, s->expand_pagecap, false);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+const char* slora_last_error(void) { return g_last_error.c_str(); }
+
+slora_status slora_pool_create(const slora_pool_desc* desc, slora_pool** out) {
+  if (!desc || !out) return fail(SLORA_E_INVAL, "slora_pool_create: NULL argument");
+  const slora_pool_desc& d = *desc;
+  if (d.dtype != SLORA_F32 && d.dtype != SLORA_F16)
+    return fail(SLORA_E_INVAL, "slora_pool_create: dtype must be SLORA_F32 or SLORA_F16");
+  if (d.h_in <= 0 || d.h_out <= 0 || d.h_in % 8 || d.h_out % 8 || d.h_in > 65536 || d.h_out > 65536)
+    return fail(SLORA_E_INVAL, "slora_pool_create: h_in and h_out must be positive multiples of 8, at most 65536");
+  const int vec = d.dtype == SLORA_F16 ? 8 : 4;
+  if ((d.h_in / vec + kThreads - 1) / kThreads > 8)
+    return fail(SLORA_E_INVAL, "slora_pool_create: h_in too large for the shrink kernel (max 16384 fp16, 8192 fp32)");
+  if (d.n_proj < 1 || d.n_proj > 8) return fail(SLORA_E_INVAL, "slora_pool_create: n_proj must be 1..8");
+  if (d.max_adapters < 1) return fail(SLORA_E_INVAL, "slora_pool_create: max_adapters must be >= 1");
+  if (d.max_rank < 1 || d.max_rank > 256) return fail(SLORA_E_INVAL, "slora_pool_create: max_rank must be 1..256");
+  if (d.n_classes != 1 && d.n_classes != 2) return fail(SLORA_E_INVAL, "slora_pool_create: n_classes must be 1 or 2");
+  if (d.n_classes == 1 && d.h_in != d.h_out)
+    return fail(SLORA_E_INVAL, "slora_pool_create: one page class needs h_in == h_out");
+  if (d.reserved0 != 0) return fail(SLORA_E_INVAL, "slora_pool_create: reserved0 must be 0");
+  for (int c = 0; c < d.n_classes; ++c) {
+    if (d.n_pages[c] < 1 || d.n_pages[c] > INT32_MAX)
+      return fail(SLORA_E_INVAL, "slora_pool_create: n_pages must be 1..2^31-1");
+    if (!d.class_base[c] || (reinterpret_cast<uintptr_t>(d.class_base[c]) & 15))
+      return fail(SLORA_E_INVAL, "slora_pool_create: class_base must be non-NULL and 16-byte aligned");
+  }
+  slora_pool* p = new (std::nothrow) slora_pool();
+  if (!p) return fail(SLORA_E_NOMEM, "slora_pool_create: out of host memory");
+  try {
+    p->d = d;
+    p->elem = elem_bytes(d.dtype);
+    p->page_elems[0] = d.h_in;
+    p->page_elems[1] = d.n_classes == 2 ? d.h_out : 0;
+    for (int c = 0; c < d.n_classes; ++c) {
+      p->page_bytes[c] = p->page_elems[c] * p->elem;
+      const int64_t P = d.n_pages[c];
+      p->free_list[c].buf.resize((size_t)P);
+      p->state[c].assign((size_t)P, PAGE_FREE);
+      if (d.free_order[c]) {
+        std::vector<uint8_t> seen((size_t)P, 0);
+        for (int64_t i = 0; i < P; ++i) {
+          const int32_t id = d.free_order[c][i];
+          if (id < 0 || id >= P || seen[id]) {
+            delete p;
+            return fail(SLORA_E_INVAL, "slora_pool_create: free_order must be a permutation of [0, n_pages)");
+          }
+          seen[id] = 1;
+          p->free_list[c].buf[(size_t)i] = id;
+        }
+      } else {
+        for (int64_t i = 0; i < P; ++i) p->free_list[c].buf[(size_t)i] = (int32_t)i;
+      }
+      p->free_list[c].head = 0;
+      p->free_list[c].count = P;
+    }
+    p->adapters.resize((size_t)d.max_adapters);
+    p->count_scratch.assign((size_t)d.max_adapters, 0);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(SLORA_E_NOMEM, "slora_pool_create: out of host memory");
+  }
+  *out = p;
+  return SLORA_OK;
+}
+
+void slora_pool_destroy(slora_pool* p) {
+  if (!p) return;
+  for (int i = 0; i < 2; ++i) {
+    if (p->meta_done[i]) {
+      (void)hipEventSynchronize(p->meta_done[i]);
+      (void)hipEventDestroy(p->meta_done[i]);
+    }
+    if (p->h_meta[i]) (void)hipHostFree(p->h_meta[i]);
+  }
+  if (p->d_stage) (void)hipFree(p->d_stage);
+  if (p->d_pages) (void)hipFree(p->d_pages);
+  if (p->h_stage) (void)hipHostFree(p->h_stage);
+  if (p->h_pages) (void)hipHostFree(p->h_pages);
+  delete p;
+}
+
+slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_pool_set_tuning: NULL pool");
+  switch (key) {
+    case SLORA_TUNE_MFMA_MIN_TOKENS:
+      if (value < 1) return fail(SLORA_E_INVAL, "mfma_min_tokens must be >= 1");
+      p->tune.mfma_min_tokens = value;
+      return SLORA_OK;
+    case SLORA_TUNE_GEMV_EXPAND_ELEMS:
+      if (value < 1) return fail(SLORA_E_INVAL, "gemv_expand_elems must be >= 1");
+      p->tune.gemv_expand_elems = value;
+      return SLORA_OK;
+    case SLORA_TUNE_MFMA_EXPAND_COLS:
+      if (value < kMfmaCols || value % kMfmaCols || value > 65536)
+        return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 256, at most 65536");
+      p->tune.mfma_expand_cols = value;
+      return SLORA_OK;
+    default:
+      return fail(SLORA_E_INVAL, "slora_pool_set_tuning: unknown key");
+  }
+}
+
+int64_t slora_free_count(const slora_pool* p, int32_t cls) {
+  if (!p || cls < 0 || cls >= p->d.n_classes) return -1;
+  return p->free_list[cls].count;
+}
+
+slora_status slora_alloc_pages(slora_pool* p, int32_t cls, int64_t n, int32_t* out_ids) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_alloc_pages: NULL pool");
+  if (cls < 0 || cls >= p->d.n_classes) return fail(SLORA_E_INVAL, "slora_alloc_pages: bad class");
+  if (n < 0 || (n > 0 && !out_ids)) return fail(SLORA_E_INVAL, "slora_alloc_pages: bad count or NULL out_ids");
+  if (n > p->free_list[cls].count) return fail(SLORA_E_NOMEM, "slora_alloc_pages: not enough free pages");
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t id = p->free_list[cls].pop_front();
+    p->state[cls][id] = PAGE_KV;
+    out_ids[i] = id;
+  }
+  return SLORA_OK;
+}
+
+slora_status slora_free_pages(slora_pool* p, int32_t cls, int64_t n, const int32_t* ids) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_free_pages: NULL pool");
+  if (cls < 0 || cls >= p->d.n_classes) return fail(SLORA_E_INVAL, "slora_free_pages: bad class");
+  if (n < 0 || (n > 0 && !ids)) return fail(SLORA_E_INVAL, "slora_free_pages: bad count or NULL ids");
+  const int64_t P = p->d.n_pages[cls];
+  // validate everything first (including duplicates within ids) so failure changes nothing
+  std::vector<int32_t> touched;
+  slora_status st = SLORA_OK;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= P || p->state[cls][id] != PAGE_KV) {
+      st = fail(SLORA_E_INVAL, "slora_free_pages: page " + std::to_string(id) + " is not an allocated KV page");
+      break;
+    }
+    p->state[cls][id] = PAGE_FREE;  // marks duplicates
+    touched.push_back(id);
+  }
+  if (st != SLORA_OK) {
+    for (int32_t id : touched) p->state[cls][id] = PAGE_KV;
+    return st;
+  }
+  for (int64_t i = 0; i < n; ++i) p->free_list[cls].push_back(ids[i]);
+  return SLORA_OK;
+}
+
+slora_status slora_load_adapter(slora_pool* p, int32_t id, int32_t rank, float scale,
+                                const void* const* A, const void* const* B, void* stream) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_load_adapter: NULL pool");
+  if (id < 0 || id >= p->d.max_adapters) return fail(SLORA_E_INVAL, "slora_load_adapter: id out of range");
+  if (rank < 1 || rank > p->d.max_rank) return fail(SLORA_E_INVAL, "slora_load_adapter: rank out of range");
+  if (!std::isfinite(scale)) return fail(SLORA_E_INVAL, "slora_load_adapter: scale must be finite");
+  if ((A == nullptr) != (B == nullptr))
+    return fail(SLORA_E_INVAL, "slora_load_adapter: A and B must both be given or both be NULL");
+  if (p->adapters[id].loaded) return fail(SLORA_E_EXIST, "slora_load_adapter: adapter already loaded");
+  const int np = p->d.n_proj;
+  const int64_t need = (int64_t)rank * np;
+  if (p->d.n_classes == 2) {
+    if (need > p->free_list[0].count || need > p->free_list[1].count)
+      return fail(SLORA_E_NOMEM, "slora_load_adapter: not enough free pages");
+  } else if (2 * need > p->free_list[0].count) {
+    return fail(SLORA_E_NOMEM, "slora_load_adapter: not enough free pages");
+  }
+  AdapterRec rec;
+  rec.rank = rank;
+  rec.scale = scale;
+  rec.a_pages.resize((size_t)need);
+  rec.b_pages.resize((size_t)need);
+  for (int pr = 0; pr < np; ++pr) {
+    for (int j = 0; j < rank; ++j) {
+      const int32_t a = p->free_list[0].pop_front();
+      p->state[0][a] = PAGE_ADAPTER;
+      rec.a_pages[(size_t)pr * rank + j] = a;
+    }
+    for (int j = 0; j < rank; ++j) {
+      const int32_t b = p->free_list[p->b_class()].pop_front();
+      p->state[p->b_class()][b] = PAGE_ADAPTER;
+      rec.b_pages[(size_t)pr * rank + j] = b;
+    }
+  }
+  if (A) {
+    slora_status st = upload_adapter(p, rec, A, B, static_cast<hipStream_t>(stream));
+    if (st != SLORA_OK) {
+      rollback_pages(p, rec);
+      return st;
+    }
+  }
+  rec.loaded = true;
+  rec.gen = ++p->gen_counter;
+  p->adapters[id] = std::move(rec);
+  return SLORA_OK;
+}
+
+slora_status slora_unload_adapter(slora_pool* p, int32_t id) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_unload_adapter: NULL pool");
+  if (id < 0 || id >= p->d.max_adapters) return fail(SLORA_E_INVAL, "slora_unload_adapter: id out of range");
+  AdapterRec& rec = p->adapters[id];
+  if (!rec.loaded) return fail(SLORA_E_NOENT, "slora_unload_adapter: adapter not loaded");
+  for (int pr = 0; pr < p->d.n_proj; ++pr) {
+    for (int j = 0; j < rec.rank; ++j) {
+      const int32_t a = rec.a_pages[(size_t)pr * rec.rank + j];
+      p->state[0][a] = PAGE_FREE;
+      p->free_list[0].push_back(a);
+    }
+    for (int j = 0; j < rec.rank; ++j) {
+      const int32_t b = rec.b_pages[(size_t)pr * rec.rank + j];
+      p->state[p->b_class()][b] = PAGE_FREE;
+      p->free_list[p->b_class()].push_back(b);
+    }
+  }
+  rec = AdapterRec();
+  return SLORA_OK;
+}
+
+slora_status slora_adapter_pages(const slora_pool* p, int32_t id, int32_t proj, int32_t* a_ids,
+                                 int32_t* b_ids, int32_t* rank_out) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_adapter_pages: NULL pool");
+  if (id < 0 || id >= p->d.max_adapters) return fail(SLORA_E_INVAL, "slora_adapter_pages: id out of range");
+  if (proj < 0 || proj >= p->d.n_proj) return fail(SLORA_E_INVAL, "slora_adapter_pages: proj out of range");
+  const AdapterRec& rec = p->adapters[id];
+  if (!rec.loaded) return fail(SLORA_E_NOENT, "slora_adapter_pages: adapter not loaded");
+  if (a_ids) std::memcpy(a_ids, rec.a_pages.data() + (size_t)proj * rec.rank, rec.rank * sizeof(int32_t));
+  if (b_ids) std::memcpy(b_ids, rec.b_pages.data() + (size_t)proj * rec.rank, rec.rank * sizeof(int32_t));
+  if (rank_out) *rank_out = rec.rank;
+  return SLORA_OK;
+}
+
+slora_status slora_build_segments(slora_pool* p, int32_t n_tokens, const int32_t* ids,
+                                  slora_segments** out) {
+  if (!p || !out) return fail(SLORA_E_INVAL, "slora_build_segments: NULL argument");
+  if (n_tokens < 0 || (n_tokens > 0 && !ids)) return fail(SLORA_E_INVAL, "slora_build_segments: bad token count or NULL ids");
+  for (int32_t t = 0; t < n_tokens; ++t) {
+    const int32_t a = ids[t];
+    if (a < 0) continue;
+    if (a >= p->d.max_adapters || !p->adapters[a].loaded)
+      return fail(SLORA_E_NOENT, "slora_build_segments: token " + std::to_string(t) + " names adapter " +
+                                     std::to_string(a) + " which is not loaded");
+  }
+  slora_segments* s = new (std::nothrow) slora_segments();
+  if (!s) return fail(SLORA_E_NOMEM, "slora_build_segments: out of host memory");
+  try {
+    s->pool = p;
+    s->n_tokens = n_tokens;
+    s->n_proj = p->d.n_proj;
+    // Stable counting sort by adapter id; segments in ascending id order.
+    std::vector<int32_t>& cnt = p->count_scratch;
+    std::vector<int32_t> distinct;
+    int32_t routed = 0;
+    for (int32_t t = 0; t < n_tokens; ++t) {
+      const int32_t a = ids[t];
+      if (a < 0) continue;
+      if (cnt[a]++ == 0) distinct.push_back(a);
+      ++routed;
+    }
+    std::sort(distinct.begin(), distinct.end());
+    const int32_t S = (int32_t)distinct.size();
+    s->seg_start.resize(S + 1);
+    s->seg_adapter = distinct;
+    s->seg_rank.resize(S);
+    s->seg_scale.resize(S);
+    s->seg_gen.resize(S);
+    s->seg_page_off.resize(S + 1);
+    s->seg_v_off.resize(S + 1);
+    int32_t cursor = 0;
+    int64_t page_off = 0, v_off = 0;
+    for (int32_t g = 0; g < S; ++g) {
+      const int32_t a = distinct[g];
+      const AdapterRec& rec = p->adapters[a];
+      const int32_t c = cnt[a];
+      s->seg_start[g] = cursor;
+      s->seg_rank[g] = rec.rank;
+      s->seg_scale[g] = rec.scale;
+      s->seg_gen[g] = rec.gen;
+      s->seg_page_off[g] = (int32_t)page_off;
+      s->seg_v_off[g] = v_off;
+      cnt[a] = cursor;  // becomes the write cursor of adapter a
+      cursor += c;
+      page_off += rec.rank;
+      v_off += (int64_t)c * rec.rank;
+    }
+    s->seg_start[S] = cursor;
+    s->seg_page_off[S] = (int32_t)page_off;
+    s->seg_v_off[S] = v_off;
+    s->sum_r = page_off;
+    s->sum_rt = v_off;
+    s->perm.resize(routed);
+    for (int32_t t = 0; t < n_tokens; ++t) {
+      const int32_t a = ids[t];
+      if (a >= 0) s->perm[cnt[a]++] = t;
+    }
+    for (int32_t a : distinct) cnt[a] = 0;
+    const int np = p->d.n_proj;
+    s->a_pages.resize((size_t)np * s->sum_r);
+    s->b_pages.resize((size_t)np * s->sum_r);
+    for (int pr = 0; pr < np; ++pr) {
+      for (int32_t g = 0; g < S; ++g) {
+        const AdapterRec& rec = p->adapters[distinct[g]];
+        const size_t dst = (size_t)pr * s->sum_r + s->seg_page_off[g];
+        std::memcpy(&s->a_pages[dst], rec.a_pages.data() + (size_t)pr * rec.rank, rec.rank * sizeof(int32_t));
+        std::memcpy(&s->b_pages[dst], rec.b_pages.data() + (size_t)pr * rec.rank, rec.rank * sizeof(int32_t));
+      }
+    }
+    if (s->sum_rt > INT32_MAX) {
+      delete s;
+      return fail(SLORA_E_INVAL, "slora_build_segments: batch too large (sum of token ranks >= 2^31)");
+    }
+    build_tiles(s);
+  } catch (const std::bad_alloc&) {
+    for (auto& c : p->count_scratch) c = 0;
+    delete s;
+    return fail(SLORA_E_NOMEM, "slora_build_segments: out of host memory");
+  }
+  *out = s;
+  return SLORA_OK;
+}
+
+void slora_segments_destroy(slora_segments* s) { delete s; }
+
+slora_status slora_segments_get_info(const slora_segments* s, slora_segments_info* info) {
+  if (!s || !info) return fail(SLORA_E_INVAL, "slora_segments_get_info: NULL argument");
+  std::memset(info, 0, sizeof(*info));
+  info->n_tokens = s->n_tokens;
+  info->n_routed = (int32_t)s->perm.size();
+  info->n_segments = (int32_t)s->seg_adapter.size();
+  info->n_proj = s->n_proj;
+  info->sum_rank = s->sum_r;
+  info->sum_rank_tokens = s->sum_rt;
+  info->n_shrink_tiles = s->n_shrink;
+  info->n_expand_tiles = s->n_expand;
+  info->n_mfma_segments = s->n_mfma_segments;
+  info->meta_bytes = std::max<size_t>(16, s->blob.size() * sizeof(int32_t));
+  info->workspace_bytes = std::max<size_t>(16, (size_t)s->sum_rt * sizeof(float));
+  return SLORA_OK;
+}
+
+slora_status slora_segments_export(const slora_segments* s, int32_t* perm, int32_t* seg_start,
+                                   int32_t* seg_adapter, int32_t* seg_rank, float* seg_scale,
+                                   int32_t* seg_page_off, int32_t* a_pages, int32_t* b_pages) {
+  if (!s) return fail(SLORA_E_INVAL, "slora_segments_export: NULL segments");
+  auto cp = [](void* dst, const void* src, size_t n) { if (dst && n) std::memcpy(dst, src, n); };
+  cp(perm, s->perm.data(), s->perm.size() * 4);
+  cp(seg_start, s->seg_start.data(), s->seg_start.size() * 4);
+  cp(seg_adapter, s->seg_adapter.data(), s->seg_adapter.size() * 4);
+  cp(seg_rank, s->seg_rank.data(), s->seg_rank.size() * 4);
+  cp(seg_scale, s->seg_scale.data(), s->seg_scale.size() * 4);
+  cp(seg_page_off, s->seg_page_off.data(), s->seg_page_off.size() * 4);
+  cp(a_pages, s->a_pages.data(), s->a_pages.size() * 4);
+  cp(b_pages, s->b_pages.data(), s->b_pages.size() * 4);
+  return SLORA_OK;
+}
+
+slora_status slora_segments_tiles(const slora_segments* s, int32_t* layout, int32_t* records,
+                                  size_t records_words) {
+  if (!s || !layout) return fail(SLORA_E_INVAL, "slora_segments_tiles: NULL argument");
+  const int32_t lay[8] = {s->n_shrink, s->shrink_stride, s->shrink_tokcap, s->shrink_pagecap,
+                          s->n_expand, s->expand_stride, s->expand_tokcap, s->expand_pagecap};
+  std::memcpy(layout, lay, sizeof(lay));
+  if (records) {
+    if (records_words < s->blob.size()) return fail(SLORA_E_NOMEM, "slora_segments_tiles: records buffer too small");
+    std::memcpy(records, s->blob.data(), s->blob.size() * sizeof(int32_t));
+  }
+  return SLORA_OK;
+}
+
+slora_status slora_segments_upload(slora_segments* s, void* dev_meta, size_t dev_meta_bytes, void* stream) {
+  if (!s || !dev_meta) return fail(SLORA_E_INVAL, "slora_segments_upload: NULL argument");
+  if (reinterpret_cast<uintptr_t>(dev_meta) & 15) return fail(SLORA_E_INVAL, "slora_segments_upload: dev_meta must be 16-byte aligned");
+  const size_t bytes = s->blob.size() * sizeof(int32_t);
+  if (dev_meta_bytes < std::max<size_t>(16, bytes)) return fail(SLORA_E_NOMEM, "slora_segments_upload: dev_meta smaller than meta_bytes");
+  slora_pool* p = s->pool;
+  if (bytes > 0) {
+    slora_status st = set_device(p);
+    if (st != SLORA_OK) return st;
+    const int slot = p->meta_slot;
+    hipError_t e = hipSuccess;
+    if (p->meta_done[slot]) {
+      e = hipEventSynchronize(p->meta_done[slot]);  // the slot's previous copy has finished
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(metadata slot)");
+    } else {
+      e = hipEventCreateWithFlags(&p->meta_done[slot], hipEventDisableTiming);
+      if (e != hipSuccess) { p->meta_done[slot] = nullptr; return hip_fail(e, "hipEventCreate"); }
+    }
+    if (p->h_meta_bytes[slot] < bytes) {
+      if (p->h_meta[slot]) (void)hipHostFree(p->h_meta[slot]);
+      p->h_meta[slot] = nullptr;
+      p->h_meta_bytes[slot] = 0;
+      const size_t want = std::max<size_t>(bytes, 1 << 20);
+      e = hipHostMalloc((void**)&p->h_meta[slot], want, hipHostMallocDefault);
+      if (e != hipSuccess) { p->h_meta[slot] = nullptr; return hip_fail(e, "hipHostMalloc(metadata)"); }
+      p->h_meta_bytes[slot] = want;
+    }
+    std::memcpy(p->h_meta[slot], s->blob.data(), bytes);
+    hipStream_t st_ = static_cast<hipStream_t>(stream);
+    e = hipMemcpyAsync(dev_meta, p->h_meta[slot], bytes, hipMemcpyHostToDevice, st_);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(metadata)");
+    e = hipEventRecord(p->meta_done[slot], st_);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(metadata)");
+    p->meta_slot ^= 1;
+  }
+  s->dev_meta = static_cast<const int32_t*>(dev_meta);
+  return SLORA_OK;
+}
+
+slora_status slora_lora_delta(slora_pool* p, const slora_segments* s, int32_t proj, const void* x, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p || !s) return fail(SLORA_E_INVAL, "slora_lora_delta: NULL pool or segments");
+  if (s->pool != p) return fail(SLORA_E_INVAL, "slora_lora_delta: segments belong to another pool");
+  if (proj < 0 || proj >= p->d.n_proj) return fail(SLORA_E_INVAL, "slora_lora_delta: proj out of range");
+  const int32_t S = (int32_t)s->seg_adapter.size();
+  for (int32_t g = 0; g < S; ++g) {
+    const AdapterRec& rec = p->adapters[s->seg_adapter[g]];
+    if (!rec.loaded || rec.gen != s->seg_gen[g])
+      return fail(SLORA_E_STALE, "slora_lora_delta: adapter " + std::to_string(s->seg_adapter[g]) +
+                                     " changed since the segments were built");
+  }
+  if (s->perm.empty()) return SLORA_OK;
+  if (!x || !y || !workspace) return fail(SLORA_E_INVAL, "slora_lora_delta: NULL x, y or workspace");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(SLORA_E_INVAL, "slora_lora_delta: x, y and workspace must be 16-byte aligned");
+  if (workspace_bytes < (size_t)s->sum_rt * sizeof(float)) return fail(SLORA_E_NOMEM, "slora_lora_delta: workspace smaller than workspace_bytes");
+  if (!s->dev_meta) return fail(SLORA_E_INVAL, "slora_lora_delta: segments not uploaded (call slora_segments_upload)");
+  slora_status st = set_device(p);
+  if (st != SLORA_OK) return st;
+  DeltaLaunch L{};
+  L.pool.base_a = static_cast<const char*>(p->d.class_base[0]);
+  L.pool.base_b = static_cast<const char*>(p->d.class_base[p->b_class()]);
+  L.pool.page_bytes_a = p->page_bytes[0];
+  L.pool.page_bytes_b = p->page_bytes[p->b_class()];
+  L.dtype = p->d.dtype;
+  L.h_in = p->d.h_in;
+  L.h_out = p->d.h_out;
+  L.proj = proj;
+  L.x = x;
+  L.y = y;
+  L.v = static_cast<float*>(workspace);
+  L.shrink_rec = s->dev_meta;
+  L.shrink_stride = s->shrink_stride;
+  L.shrink_tokcap = s->shrink_tokcap;
+  L.shrink_pagecap = s->shrink_pagecap;
+  L.n_shrink = s->n_shrink;
+  L.expand_rec = s->dev_meta + s->expand_off_words;
+  L.expand_stride = s->expand_stride;
+  L.expand_tokcap = s->expand_tokcap;
+  L.expand_pagecap = s->expand_pagecap;
+  L.n_expand = s->n_expand;
+  L.gemv_rows = s->gemv_rows;
+  hipError_t e = launch_delta(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "slora_lora_delta launch");
+  return SLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal interface between the host runtime (slora_host.cpp) and the HIP
+// kernels (slora_kernels.hip): the tile-record layout written by the segment
+// builder and read by the kernels, and the launch entry points.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace slora {
+
+// A tile record is a run of int32 words:
+//   [0] kind        KIND_GEMV (vector ALU) or KIND_MFMA (matrix cores)
+//   [1] ntok        tokens in the tile (all of one segment)
+//   [2] rank        the segment's rank r (row stride of its v block)
+//   [3] pos         shrink: first rank row j0      expand: first column o0
+//   [4] len         shrink: rank rows handled      expand: columns handled
+//   [5] v0          workspace offset of the tile's first token's v row
+//   [6] scale       the segment's scale, float bits
+//   [7] aux         expand GEMV: nominal column width of the tile (thread map)
+//   [HDR .. HDR+tokcap)                   batch indices of the tokens
+//   [HDR+tokcap + p*pagecap .. +npages)   page ids of projection p: shrink
+//                                         holds the A^T pages of rows
+//                                         pos..pos+len, expand all r B pages
+// Records of one kernel share one stride (a multiple of 4 words).
+enum : int32_t {
+  REC_KIND = 0, REC_NTOK = 1, REC_RANK = 2, REC_POS = 3, REC_LEN = 4,
+  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_HDR = 8
+};
+enum : int32_t { KIND_GEMV = 0, KIND_MFMA = 1 };
+
+// Fixed tile geometry shared by the builder and the kernels.
+constexpr int kThreads = 256;           // every tile kernel runs 4 waves of 64
+constexpr int kMfmaTok = 16;            // tokens per MFMA tile (M of 16x16x32)
+constexpr int kMfmaMaxRows = 64;        // rank rows per MFMA shrink tile
+constexpr int kMfmaCols = 256;          // columns staged per MFMA expand pass
+constexpr int kGemvMaxTok = 4;          // tokens per vector-ALU tile
+constexpr int kShrinkRowBudget = 16;    // rows x 16-byte chunks per thread (GEMV shrink)
+
+struct PoolView {
+  const char* base_a;     // class of the A^T pages
+  const char* base_b;     // class of the B pages
+  int64_t page_bytes_a;
+  int64_t page_bytes_b;
+};
+
+struct DeltaLaunch {
+  PoolView pool;
+  int32_t dtype;          // 0 fp32, 1 fp16
+  int32_t h_in, h_out;
+  int32_t proj;
+  const void* x;
+  void* y;
+  float* v;
+  const int32_t* shrink_rec;
+  int32_t shrink_stride, shrink_tokcap, shrink_pagecap, n_shrink;
+  const int32_t* expand_rec;
+  int32_t expand_stride, expand_tokcap, expand_pagecap, n_expand;
+  int32_t gemv_rows;      // rank rows per GEMV shrink tile (host choice)
+};
+
+// Launch the shrink kernel then the expand kernel on `stream`.
+hipError_t launch_delta(const DeltaLaunch& L, hipStream_t stream);
+
+// Copy n_rows rows of row_bytes from src (device, packed) into the pages
+// page_ids[i] of the class at base with page_bytes stride.
+hipError_t launch_scatter_rows(const char* src, int32_t n_rows, int64_t row_bytes,
+                               const int32_t* page_ids, char* base, int64_t page_bytes,
+                               hipStream_t stream);
+
+}  // namespace slora

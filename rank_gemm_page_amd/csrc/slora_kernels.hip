@@ -1,0 +1,581 @@
+// HIP kernels of the paged, heterogeneous-batch LoRA delta for MI355X (gfx950).
+//
+// The delta (S-LoRA summary page, "The mechanism": keep one base W and
+// compute x A B per request on the fly; blog page, section 2 pseudocode: the
+// per-token product times a scaling factor) is split in two stages:
+//
+//   shrink  v[t, j] = sum_k x[t, k] * AT_j[k]           AT_j = page of row j of A^T
+//   expand  y[t, o] = round(y[t, o] + s * sum_j v[t, j] * B_j[o])
+//
+// where the pages are gathered through the per-tile page lists the host
+// segment builder resolved (summary page, "Heterogeneous batching kernels":
+// gather non-contiguous adapter pages, ranks differ across the batch).
+//
+// Each kernel walks a list of self-contained tile records (one record per
+// workgroup, 256 threads), of two kinds:
+//   * GEMV tiles (vector ALU) for segments with few tokens: the decode case is
+//     a bandwidth-bound matrix-vector product, so rows stream from HBM in
+//     16-byte coalesced loads, fp16 pairs go through v_dot2_f32_f16, and the
+//     rank-row partial sums are reduced with a butterfly reduce-scatter over
+//     the wavefront followed by one LDS pass across the four waves.
+//   * MFMA tiles (matrix cores, fp16 only) for segments where at least a
+//     block of 16 tokens share an adapter: the shrink is a 16 x K x rank GEMM
+//     fed straight from global memory (x rows and A^T page rows are both
+//     K-contiguous), the expand stages 32-row slices of the B pages in LDS and
+//     multiplies the fp32 v split into an fp16 high and low part, so the
+//     matrix cores see v with about 22 significant bits and accumulate in fp32.
+// Every output element is written by exactly one thread, once, with one
+// rounding; no atomics, so results are deterministic run to run and do not
+// depend on where the pages sit in the pool.
+#include <hip/hip_runtime.h>
+
+#include "slora_internal.h"
+
+namespace slora {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+template <typename T> struct VecN;
+template <> struct VecN<_Float16> { static constexpr int N = 8; };
+template <> struct VecN<float> { static constexpr int N = 4; };
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, _Float16) {
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a.x), __builtin_bit_cast(half2v, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a.y), __builtin_bit_cast(half2v, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a.z), __builtin_bit_cast(half2v, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a.w), __builtin_bit_cast(half2v, b.w), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, float) {
+  acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+  acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  return acc;
+}
+
+// 16 bytes of T -> VecN<T>::N floats (exact conversions).
+__device__ __forceinline__ void to_float(uint4 v, float (&f)[8], _Float16) {
+  half8 h = __builtin_bit_cast(half8, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)h[e];
+}
+__device__ __forceinline__ void to_float(uint4 v, float (&f)[4], float) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+// y chunk + delta -> one rounding per element back to T.
+__device__ __forceinline__ uint4 add_round(uint4 y, const float (&d)[8], _Float16) {
+  half8 h = __builtin_bit_cast(half8, y);
+  half8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (_Float16)((float)h[e] + d[e]);
+  return __builtin_bit_cast(uint4, o);
+}
+__device__ __forceinline__ uint4 add_round(uint4 y, const float (&d)[4], float) {
+  uint4 o;
+  o.x = __float_as_uint(__uint_as_float(y.x) + d[0]);
+  o.y = __float_as_uint(__uint_as_float(y.y) + d[1]);
+  o.z = __float_as_uint(__uint_as_float(y.z) + d[2]);
+  o.w = __float_as_uint(__uint_as_float(y.w) + d[3]);
+  return o;
+}
+
+// Select by mask on the values themselves (a plain ?: on two array elements
+// can be folded into one dynamically indexed load, which spills the array).
+__device__ __forceinline__ float pick(bool c, float a, float b) {
+  const uint32_t m = 0u - (uint32_t)c;
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+
+// Butterfly reduce-scatter over a wavefront of 64 lanes: on return, lane l
+// holds the wave-wide sum of p[l / (64 / N)] (N a power of two, N <= 64).
+// Each halving step swaps half of the still-live partials with the partner
+// lane, so N partials cost N-1 exchanges instead of N * log2(64).
+template <int N>
+__device__ __forceinline__ float wave_reduce_scatter(float (&p)[N], int lane) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power of two");
+#pragma unroll
+  for (int s = 0; s < 6; ++s) {
+    const int off = 32 >> s;
+    const int n = (N >> s) > 0 ? (N >> s) : 1;  // live partials before this step
+    if (n > 1) {
+      const int half = n / 2;
+      const bool upper = (lane & off) != 0;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        if (i < half) {
+          const float lo = p[i], hi = p[i + half];
+          const float send = pick(upper, lo, hi);
+          const float keep = pick(upper, hi, lo);
+          p[i] = keep + __shfl_xor(send, off, 64);
+        }
+      }
+    } else {
+      p[0] += __shfl_xor(p[0], off, 64);
+    }
+  }
+  return p[0];
+}
+
+// ---------------------------------------------------------------------------
+// Shrink, vector-ALU tile: up to kGemvMaxTok tokens x RB rank rows, whole h_in.
+// Thread tid owns the 16-byte chunks tid, tid+256, ... of every row; the A^T
+// rows stay in registers while each token's x chunks are dotted against them.
+
+template <typename T, int NCK>
+__device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float* red) {
+  constexpr int VEC = VecN<T>::N;
+  constexpr int RB = kShrinkRowBudget / NCK;
+  constexpr int TB = kGemvMaxTok;
+  const int ntok = rec[REC_NTOK];
+  const int rank = rec[REC_RANK];
+  const int j0 = rec[REC_POS];
+  const int nrows = rec[REC_LEN];
+  const int v0 = rec[REC_V0];
+  const int32_t* toks = rec + REC_HDR;
+  const int32_t* pages = rec + REC_HDR + L.shrink_tokcap + L.proj * L.shrink_pagecap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunks = L.h_in / VEC;
+  const T* x = reinterpret_cast<const T*>(L.x);
+
+  uint4 a[RB][NCK];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const char* row = L.pool.base_a + (int64_t)pages[r < nrows ? r : 0] * L.pool.page_bytes_a;
+#pragma unroll
+    for (int ck = 0; ck < NCK; ++ck) {
+      const int c = tid + ck * kThreads;
+      a[r][ck] = (r < nrows && c < nchunks) ? ld16(row + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  uint4 xv[TB][NCK];
+#pragma unroll
+  for (int k = 0; k < TB; ++k) {
+    const T* xr = x + (int64_t)toks[k < ntok ? k : 0] * L.h_in;
+#pragma unroll
+    for (int ck = 0; ck < NCK; ++ck) {
+      const int c = tid + ck * kThreads;
+      xv[k][ck] = (k < ntok && c < nchunks) ? ld16(xr + (int64_t)c * VEC) : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < TB; ++k) {
+    if (k < ntok) {
+      float p[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int ck = 0; ck < NCK; ++ck) acc = dot16(a[r][ck], xv[k][ck], acc, T());
+        p[r] = acc;
+      }
+      const float s = wave_reduce_scatter<RB>(p, lane);
+      constexpr int LPR = 64 / RB;  // lanes per reduced row
+      if ((lane & (LPR - 1)) == 0) red[(k * 4 + wave) * RB + lane / LPR] = s;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < ntok * nrows; i += kThreads) {
+    const int k = i / nrows, r = i - k * nrows;
+    const float* q = red + (k * 4) * RB + r;
+    const float sum = ((q[0] + q[RB]) + q[2 * RB]) + q[3 * RB];
+    L.v[v0 + (int64_t)k * rank + j0 + r] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shrink, MFMA tile: 16 tokens x up to 64 rank rows, whole h_in (fp16).
+// C[m][n] = sum_k X[m][k] * AT_n[k] with v_mfma_f32_16x16x32_f16: lane l feeds
+// row m = l%16 of X and row n = l%16 of A^T, 8 consecutive k at 8*(l/16); the
+// four waves take interleaved 32-wide k steps and are summed through LDS.
+
+template <int NB>
+__device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float* red) {
+  const int ntok = rec[REC_NTOK];
+  const int rank = rec[REC_RANK];
+  const int j0 = rec[REC_POS];
+  const int nrows = rec[REC_LEN];
+  const int v0 = rec[REC_V0];
+  const int32_t* toks = rec + REC_HDR;
+  const int32_t* pages = rec + REC_HDR + L.shrink_tokcap + L.proj * L.shrink_pagecap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+
+  // Rows past ntok / nrows repeat the last valid row (same cache lines); their
+  // outputs are never stored.
+  const _Float16* xrow = reinterpret_cast<const _Float16*>(L.x) +
+                         (int64_t)toks[m < ntok ? m : ntok - 1] * L.h_in + 8 * g;
+  const _Float16* arow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int j = b * 16 + m;
+    arow[b] = reinterpret_cast<const _Float16*>(
+                  L.pool.base_a + (int64_t)pages[j < nrows ? j : nrows - 1] * L.pool.page_bytes_a) + 8 * g;
+  }
+  float4v acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const int n_it = (L.h_in - wave * 32 + 127) >> 7;  // this wave's 32-wide k steps
+#pragma unroll 4
+  for (int it = 0; it < n_it; ++it) {
+    const int k = wave * 32 + it * 128;
+    const half8 xa = __builtin_bit_cast(half8, ld16(xrow + k));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const half8 ab = __builtin_bit_cast(half8, ld16(arow[b] + k));
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ab, acc[b], 0, 0, 0);
+    }
+  }
+  // acc[b][i] is C[token 4g + i][rank row b*16 + l%16]; sum the four waves in LDS.
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * 4 + b) * 16 + (4 * g + i)) * 16 + m] = acc[b][i];
+  }
+  __syncthreads();
+  for (int i = tid; i < ntok * nrows; i += kThreads) {
+    const int mm = i / nrows, j = i - mm * nrows;
+    const int b = j >> 4, n = j & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sum += red[((w * 4 + b) * 16 + mm) * 16 + n];
+    L.v[v0 + (int64_t)mm * rank + j0 + j] = sum;
+  }
+}
+
+template <typename T, int NCK>
+__global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
+  __shared__ float red[4 * 4 * 16 * 16];  // MFMA: 4 waves x 4 blocks x 16 x 16
+  const int32_t* rec = L.shrink_rec + (int64_t)blockIdx.x * L.shrink_stride;
+  if constexpr (sizeof(T) == 2) {
+    if (rec[REC_KIND] == KIND_MFMA) {
+      switch ((rec[REC_LEN] + 15) >> 4) {
+        case 1: shrink_mfma_tile<1>(L, rec, red); break;
+        case 2: shrink_mfma_tile<2>(L, rec, red); break;
+        case 3: shrink_mfma_tile<3>(L, rec, red); break;
+        default: shrink_mfma_tile<4>(L, rec, red); break;
+      }
+      return;
+    }
+  }
+  shrink_gemv_tile<T, NCK>(L, rec, red);
+}
+
+// ---------------------------------------------------------------------------
+// Expand, vector-ALU tile: up to kGemvMaxTok tokens x `width` columns, all r
+// rows.  width/VEC threads cover the columns with one 16-byte chunk each and
+// G = 256 / (width/VEC) groups of them split the r rows; the groups' partial
+// sums meet in LDS and group 0 applies y += s * d with one rounding.
+
+template <typename T>
+__device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float* lds) {
+  constexpr int VEC = VecN<T>::N;
+  constexpr int TB = kGemvMaxTok;
+  const int ntok = rec[REC_NTOK];
+  const int rank = rec[REC_RANK];
+  const int o0 = rec[REC_POS];
+  const int ncol = rec[REC_LEN];
+  const int v0 = rec[REC_V0];
+  const float scale = __int_as_float(rec[REC_SCALE]);
+  const int width = rec[REC_AUX];
+  const int32_t* toks = rec + REC_HDR;
+  const int32_t* pages = rec + REC_HDR + L.expand_tokcap + L.proj * L.expand_pagecap;
+  const int tid = threadIdx.x;
+  const int nct = width / VEC;
+  const int G = kThreads / nct;
+  const int ct = tid % nct, g = tid / nct;
+
+  float* sv = lds;                   // [TB][rank] v of the tile's tokens
+  float* part = lds + TB * 256;      // [G-1][TB][nct][VEC] partial sums of groups 1..G-1
+  for (int i = tid; i < ntok * rank; i += kThreads) sv[i] = L.v[v0 + i];
+  __syncthreads();
+
+  const bool active = ct * VEC < ncol;
+  const int64_t col_byte = (int64_t)(o0 + ct * VEC) * sizeof(T);
+  float acc[TB][VEC];
+#pragma unroll
+  for (int k = 0; k < TB; ++k)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[k][e] = 0.f;
+
+  if (active) {
+    int j = g;
+    for (; j + 3 * G < rank; j += 4 * G) {
+      uint4 bq[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        bq[u] = ld16(L.pool.base_b + (int64_t)pages[j + u * G] * L.pool.page_bytes_b + col_byte);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float bf[VEC];
+        to_float(bq[u], bf, T());
+#pragma unroll
+        for (int k = 0; k < TB; ++k) {
+          if (k < ntok) {
+            const float vk = sv[k * rank + j + u * G];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[k][e] = fmaf(vk, bf[e], acc[k][e]);
+          }
+        }
+      }
+    }
+    for (; j < rank; j += G) {
+      const uint4 b = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + col_byte);
+      float bf[VEC];
+      to_float(b, bf, T());
+#pragma unroll
+      for (int k = 0; k < TB; ++k) {
+        if (k < ntok) {
+          const float vk = sv[k * rank + j];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[k][e] = fmaf(vk, bf[e], acc[k][e]);
+        }
+      }
+    }
+  }
+  if (G > 1) {
+    if (g > 0) {
+#pragma unroll
+      for (int k = 0; k < TB; ++k) {
+        if (k < ntok) {
+          float* q = part + (((int64_t)(g - 1) * TB + k) * nct + ct) * VEC;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) q[e] = acc[k][e];
+        }
+      }
+    }
+    __syncthreads();
+    if (g == 0) {
+      for (int gg = 1; gg < G; ++gg) {
+#pragma unroll
+        for (int k = 0; k < TB; ++k) {
+          if (k < ntok) {
+            const float* q = part + (((int64_t)(gg - 1) * TB + k) * nct + ct) * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[k][e] += q[e];
+          }
+        }
+      }
+    }
+  }
+  if (g == 0 && active) {
+    T* y = reinterpret_cast<T*>(L.y);
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      if (k < ntok) {
+        T* yp = y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC;
+        float d[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d[e] = scale * acc[k][e];
+        st16(yp, add_round(ld16(yp), d, T()));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Expand, MFMA tile (fp16): 16 tokens x `len` columns, all r rows.
+// Y[m][o] += sum_j (s v)[m][j] * B_j[o], with A operand = s*v (16 x 32 slice of
+// j, split hi + lo in fp16 after a power-of-two normalisation of the tile) and
+// B operand = a 32-row x 256-column slice of the B pages staged in LDS.
+// Lane (m = l%16, g = l/16) feeds element i of a k step with j = 32*ks + g + 4*i
+// in both operands (any common k order gives the same sum); that order puts
+// the four lane groups on rows g..g+3 of the LDS slice, which with a row pitch
+// of 272 halves are 8 banks apart, so the column gathers are conflict-free.
+
+constexpr int kMfmaPitchH = kMfmaCols + 16;    // halves per staged B row
+constexpr int kMfmaEpiPitch = kMfmaCols + 4;   // floats per epilogue row
+constexpr int kMaxRankMfma = 256;
+
+__device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float* lds) {
+  const int ntok = rec[REC_NTOK];
+  const int rank = rec[REC_RANK];
+  const int o0 = rec[REC_POS];
+  const int ncol = rec[REC_LEN];
+  const int v0 = rec[REC_V0];
+  const float scale = __int_as_float(rec[REC_SCALE]);
+  const int32_t* toks = rec + REC_HDR;
+  const int32_t* pages = rec + REC_HDR + L.expand_tokcap + L.proj * L.expand_pagecap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int ks_n = (rank + 31) >> 5;
+  const int vp = ks_n * 32 + 4;                       // sv pitch (floats)
+
+  // LDS: sv [16][vp] floats, reused as the epilogue buffer [16][kMfmaEpiPitch];
+  // then the staged B slice [32][kMfmaPitchH] halves; then a reduction slot.
+  float* sv = lds;
+  float* epi = lds;
+  _Float16* sb = reinterpret_cast<_Float16*>(lds + 16 * (kMaxRankMfma + 4));
+  float* wmax = lds + 16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2;
+
+  // s * v of the tile, zero outside ntok x rank, and its largest magnitude.
+  float amax = 0.f;
+  for (int i = tid; i < 16 * ks_n * 32; i += kThreads) {
+    const int mm = i / (ks_n * 32), j = i - mm * (ks_n * 32);
+    float val = 0.f;
+    if (mm < ntok && j < rank) val = scale * L.v[v0 + (int64_t)mm * rank + j];
+    sv[mm * vp + j] = val;
+    amax = fmaxf(amax, fabsf(val));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // Bring the largest |s v| into [2^14, 2^15) so hi and lo stay normal fp16.
+  int ex = 0;
+  if (amax > 0.f) {
+    (void)frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
+    ex = max(ex - 15, -100);   // keep 2^-ex finite for all-subnormal tiles
+  }
+  const float down = ldexpf(1.f, -ex), up = ldexpf(1.f, ex);
+
+  half8 vhi[kMaxRankMfma / 32], vlo[kMaxRankMfma / 32];
+#pragma unroll
+  for (int ks = 0; ks < kMaxRankMfma / 32; ++ks) {
+    if (ks < ks_n) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float s = sv[m * vp + 32 * ks + g + 4 * i] * down;
+        const _Float16 h = (_Float16)s;
+        vhi[ks][i] = h;
+        vlo[ks][i] = (_Float16)(s - (float)h);
+      }
+    }
+  }
+  __syncthreads();  // sv is dead from here; its space becomes the epilogue buffer
+
+  _Float16* yb = reinterpret_cast<_Float16*>(L.y);
+  for (int c0 = 0; c0 < ncol; c0 += kMfmaCols) {
+    float4v acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kMaxRankMfma / 32; ++ks) {
+      if (ks >= ks_n) break;
+      // stage rows 32ks..32ks+31, columns o0+c0 .. +256 (zeros outside r x h_out)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int chunk = tid + q * kThreads;        // 1024 chunks of 8 halves
+        const int jr = chunk >> 5, cc = (chunk & 31) * 8;
+        const int j = 32 * ks + jr;
+        const int col = o0 + c0 + cc;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (j < rank && c0 + cc < ncol)
+          val = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)col * 2);
+        st16(sb + jr * kMfmaPitchH + cc, val);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = wave * 64 + c * 16 + m;
+        half8 bf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bf[i] = sb[(g + 4 * i) * kMfmaPitchH + n];
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi[ks], bf, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo[ks], bf, acc[c], 0, 0, 0);
+      }
+      __syncthreads();
+    }
+    // acc[c][i] = Y[4g + i][wave*64 + c*16 + l%16]; stage, then update y coalesced.
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) epi[(4 * g + i) * kMfmaEpiPitch + wave * 64 + c * 16 + m] = acc[c][i] * up;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int chunk = tid + q * kThreads;          // 16 rows x 32 chunks of 8
+      const int mm = chunk >> 5, cc = (chunk & 31) * 8;
+      if (mm < ntok && c0 + cc < ncol) {
+        _Float16* yp = yb + (int64_t)toks[mm] * L.h_out + o0 + c0 + cc;
+        float d[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = epi[mm * kMfmaEpiPitch + cc + e];
+        st16(yp, add_round(ld16(yp), d, _Float16()));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kExpandLdsFloats =
+    (16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2 + 4) > (kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256)
+        ? (16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2 + 4)
+        : (kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256);
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
+  __shared__ float lds[kExpandLdsFloats];
+  const int32_t* rec = L.expand_rec + (int64_t)blockIdx.x * L.expand_stride;
+  if constexpr (sizeof(T) == 2) {
+    if (rec[REC_KIND] == KIND_MFMA) {
+      expand_mfma_tile(L, rec, lds);
+      return;
+    }
+  }
+  expand_gemv_tile<T>(L, rec, lds);
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename T>
+static hipError_t launch_shrink_t(const DeltaLaunch& L, hipStream_t stream) {
+  constexpr int VEC = VecN<T>::N;
+  const int per_thread = (L.h_in / VEC + kThreads - 1) / kThreads;
+  const dim3 grid(L.n_shrink), block(kThreads);
+  if (per_thread <= 1) shrink_kernel<T, 1><<<grid, block, 0, stream>>>(L);
+  else if (per_thread <= 2) shrink_kernel<T, 2><<<grid, block, 0, stream>>>(L);
+  else if (per_thread <= 4) shrink_kernel<T, 4><<<grid, block, 0, stream>>>(L);
+  else if (per_thread <= 8) shrink_kernel<T, 8><<<grid, block, 0, stream>>>(L);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(const DeltaLaunch& L, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (L.n_shrink > 0) {
+    e = L.dtype == 1 ? launch_shrink_t<_Float16>(L, stream) : launch_shrink_t<float>(L, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (L.n_expand > 0) {
+    const dim3 grid(L.n_expand), block(kThreads);
+    if (L.dtype == 1) expand_kernel<_Float16><<<grid, block, 0, stream>>>(L);
+    else expand_kernel<float><<<grid, block, 0, stream>>>(L);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// Adapter load: copy packed staging rows into their pages (one block per row).
+
+__global__ __launch_bounds__(kThreads) void scatter_rows_kernel(const char* src, int64_t row_bytes,
+                                                                const int32_t* page_ids, char* base,
+                                                                int64_t page_bytes) {
+  const int64_t row = blockIdx.x;
+  const uint4* s = reinterpret_cast<const uint4*>(src + row * row_bytes);
+  uint4* d = reinterpret_cast<uint4*>(base + (int64_t)page_ids[row] * page_bytes);
+  const int64_t n = row_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) d[i] = s[i];
+}
+
+hipError_t launch_scatter_rows(const char* src, int32_t n_rows, int64_t row_bytes,
+                               const int32_t* page_ids, char* base, int64_t page_bytes,
+                               hipStream_t stream) {
+  if (n_rows <= 0) return hipSuccess;
+  scatter_rows_kernel<<<dim3(n_rows), dim3(kThreads), 0, stream>>>(src, row_bytes, page_ids, base,
+                                                                  page_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace slora

@@ -1,0 +1,91 @@
+"""Put a synthetic workload (``synth.Workload``) on the GPU through the C ABI.
+
+Torch provides the device memory (page classes, x, y, metadata, workspace)
+and the stream; every step of the LoRA delta runs in libslora.  Page memory
+starts as NaN, so a read of any page that is not one of the batch's adapter
+rows (KV filler, free pages, reserved adapters) turns into NaN in y.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import slora as S
+
+
+class DeviceWorkload:
+    def __init__(self, w, device="cuda:0", tuning=None, poison=True, load_all_weights=False):
+        import torch
+
+        self.torch = torch
+        self.w = w
+        spec = w.spec
+        self.device = torch.device(device)
+        self.tdtype = torch.float16 if spec.dtype == "f16" else torch.float32
+        self.dtype_code = S.SLORA_F16 if spec.dtype == "f16" else S.SLORA_F32
+        n_classes = 2 if spec.two_classes else 1
+        fill = float("nan") if poison else 0.0
+        self.pages = [torch.full((int(w.n_pages[c]), w.page_elems(c)), fill, dtype=self.tdtype,
+                                 device=self.device) for c in range(n_classes)]
+        self.max_rank = int(max(int(w.ranks.max()), 1))
+        self.pool = S.slora_pool_create(self.dtype_code, spec.h_in, spec.h_out, spec.n_proj,
+                                        spec.n_adapters, self.max_rank, self.pages,
+                                        [int(P) for P in w.n_pages], w.free_order)
+        self.seg = None
+        try:
+            for key, value in (tuning or {}).items():
+                S.slora_pool_set_tuning(self.pool, key, value)
+            self.kv = [S.slora_alloc_pages(self.pool, c, int(n)) for c, n in enumerate(w.kv_pages)]
+            stream = torch.cuda.current_stream(self.device)
+            for a in range(spec.n_adapters):
+                r = int(w.ranks[a])
+                if load_all_weights or w.has_weights(a):
+                    ws = [w.weights(a, p) for p in range(spec.n_proj)]
+                    S.slora_load_adapter(self.pool, a, r, float(w.scales[a]), [m[0] for m in ws],
+                                         [m[1] for m in ws], stream, h_in=spec.h_in,
+                                         h_out=spec.h_out, dtype=w.np_dtype)
+                else:
+                    S.slora_load_adapter(self.pool, a, r, float(w.scales[a]))
+            self.x = [torch.from_numpy(np.ascontiguousarray(x)).to(self.device) for x in w.x]
+            self.y0 = [torch.from_numpy(np.ascontiguousarray(y)).to(self.device) for y in w.y]
+            self.y = [t.clone() for t in self.y0]
+            self.build(w.ids)
+        except Exception:
+            self.close()
+            raise
+
+    # -- segments --------------------------------------------------------------
+    def build(self, ids):
+        torch = self.torch
+        if self.seg is not None:
+            S.slora_segments_destroy(self.seg)
+            self.seg = None
+        self.seg = S.slora_build_segments(self.pool, ids)
+        self.info = S.slora_segments_get_info(self.seg)
+        self.meta = torch.empty(self.info["meta_bytes"], dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(self.info["workspace_bytes"], dtype=torch.uint8,
+                                     device=self.device)
+        self.upload()
+        return self.info
+
+    def upload(self, stream=None):
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        S.slora_segments_upload(self.seg, self.meta, self.info["meta_bytes"], stream)
+
+    # -- the hot path --------------------------------------------------------------
+    def delta(self, proj=0, y=None, stream=None):
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        x = self.x[self.w.spec.proj_x[proj]]
+        S.slora_lora_delta(self.pool, self.seg, proj, x, self.y[proj] if y is None else y,
+                           self.workspace, self.info["workspace_bytes"], stream)
+
+    def reset_y(self):
+        for y, y0 in zip(self.y, self.y0):
+            y.copy_(y0)
+
+    def close(self):
+        if getattr(self, "seg", None) is not None:
+            S.slora_segments_destroy(self.seg)
+            self.seg = None
+        if getattr(self, "pool", None) is not None:
+            S.slora_pool_destroy(self.pool)
+            self.pool = None

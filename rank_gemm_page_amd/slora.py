@@ -1,0 +1,274 @@
+"""ctypes binding of libslora (include/slora.h): the same entry points, by name.
+
+Argument marshalling only: every step of the LoRA delta runs in the HIP
+library.  Device buffers are passed as raw pointers (ints) or as objects with
+``data_ptr()`` (torch tensors); host arrays as numpy arrays; streams as raw
+``hipStream_t`` values (ints) or objects with ``cuda_stream``.  A failed call
+raises ``SloraError`` carrying the status and the library's message.  The
+library must have been built (``rank_gemm_page_amd.build.build()``); there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+from .build import LIB_PATH
+
+SLORA_OK, SLORA_E_INVAL, SLORA_E_NOMEM, SLORA_E_EXIST, SLORA_E_NOENT, SLORA_E_STALE, SLORA_E_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {0: "SLORA_OK", -1: "SLORA_E_INVAL", -2: "SLORA_E_NOMEM", -3: "SLORA_E_EXIST",
+                -4: "SLORA_E_NOENT", -5: "SLORA_E_STALE", -6: "SLORA_E_HIP"}
+SLORA_F32, SLORA_F16 = 0, 1
+SLORA_TUNE_MFMA_MIN_TOKENS, SLORA_TUNE_GEMV_EXPAND_ELEMS, SLORA_TUNE_MFMA_EXPAND_COLS = 0, 1, 2
+
+EXPORTED = [
+    "slora_pool_create", "slora_pool_destroy", "slora_pool_set_tuning", "slora_alloc_pages",
+    "slora_free_pages", "slora_free_count", "slora_load_adapter", "slora_unload_adapter",
+    "slora_adapter_pages", "slora_build_segments", "slora_segments_destroy",
+    "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
+    "slora_segments_upload",
+    "slora_lora_delta", "slora_last_error",
+]
+
+
+class SloraError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} -> {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("dtype", c_int32), ("h_in", c_int32), ("h_out", c_int32), ("n_proj", c_int32),
+                ("max_adapters", c_int32), ("max_rank", c_int32), ("n_classes", c_int32),
+                ("reserved0", c_int32), ("n_pages", c_int64 * 2), ("class_base", c_void_p * 2),
+                ("free_order", POINTER(c_int32) * 2)]
+
+
+class SegmentsInfo(ctypes.Structure):
+    _fields_ = [("n_tokens", c_int32), ("n_routed", c_int32), ("n_segments", c_int32),
+                ("n_proj", c_int32), ("sum_rank", c_int64), ("sum_rank_tokens", c_int64),
+                ("n_shrink_tiles", c_int32), ("n_expand_tiles", c_int32),
+                ("n_mfma_segments", c_int32), ("reserved0", c_int32), ("meta_bytes", c_size_t),
+                ("workspace_bytes", c_size_t)]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libslora.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with rank_gemm_page_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P = c_void_p
+        sig = {
+            "slora_pool_create": (c_int32, [POINTER(PoolDesc), POINTER(P)]),
+            "slora_pool_destroy": (None, [P]),
+            "slora_pool_set_tuning": (c_int32, [P, c_int32, c_int64]),
+            "slora_alloc_pages": (c_int32, [P, c_int32, c_int64, POINTER(c_int32)]),
+            "slora_free_pages": (c_int32, [P, c_int32, c_int64, POINTER(c_int32)]),
+            "slora_free_count": (c_int64, [P, c_int32]),
+            "slora_load_adapter": (c_int32, [P, c_int32, c_int32, c_float, POINTER(P), POINTER(P), P]),
+            "slora_unload_adapter": (c_int32, [P, c_int32]),
+            "slora_adapter_pages": (c_int32, [P, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32),
+                                              POINTER(c_int32)]),
+            "slora_build_segments": (c_int32, [P, c_int32, POINTER(c_int32), POINTER(P)]),
+            "slora_segments_destroy": (None, [P]),
+            "slora_segments_get_info": (c_int32, [P, POINTER(SegmentsInfo)]),
+            "slora_segments_export": (c_int32, [P] + [POINTER(c_int32)] * 4 + [POINTER(c_float)] +
+                                      [POINTER(c_int32)] * 3),
+            "slora_segments_tiles": (c_int32, [P, POINTER(c_int32), POINTER(c_int32), c_size_t]),
+            "slora_segments_upload": (c_int32, [P, P, c_size_t, P]),
+            "slora_lora_delta": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
+            "slora_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, fn: str):
+    if status != SLORA_OK:
+        raise SloraError(status, fn, lib().slora_last_error().decode())
+
+
+def _ptr(obj) -> int:
+    """Raw address of a device buffer: an int, or an object with data_ptr()."""
+    if obj is None:
+        return 0
+    if isinstance(obj, int):
+        return obj
+    return int(obj.data_ptr())
+
+
+def _stream(obj) -> int:
+    if obj is None:
+        return 0
+    if isinstance(obj, int):
+        return obj
+    return int(obj.cuda_stream)
+
+
+def _i32p(arr):
+    return arr.ctypes.data_as(POINTER(c_int32))
+
+
+def slora_last_error() -> str:
+    return lib().slora_last_error().decode()
+
+
+def slora_pool_create(dtype: int, h_in: int, h_out: int, n_proj: int, max_adapters: int,
+                      max_rank: int, class_base, n_pages, free_order=None):
+    """class_base / n_pages / free_order: one entry per page class (1 or 2)."""
+    n_classes = len(n_pages)
+    d = PoolDesc()
+    d.dtype, d.h_in, d.h_out, d.n_proj = dtype, h_in, h_out, n_proj
+    d.max_adapters, d.max_rank, d.n_classes, d.reserved0 = max_adapters, max_rank, n_classes, 0
+    keep = []
+    for c in range(n_classes):
+        d.n_pages[c] = int(n_pages[c])
+        d.class_base[c] = _ptr(class_base[c])
+        fo = None if free_order is None else free_order[c]
+        if fo is not None:
+            fo = np.ascontiguousarray(fo, dtype=np.int32)
+            if fo.shape != (int(n_pages[c]),):
+                raise ValueError("free_order[c] must have n_pages[c] entries")
+            keep.append(fo)
+            d.free_order[c] = _i32p(fo)
+    out = c_void_p()
+    _check(lib().slora_pool_create(ctypes.byref(d), ctypes.byref(out)), "slora_pool_create")
+    return out
+
+
+def slora_pool_destroy(pool) -> None:
+    lib().slora_pool_destroy(pool)
+
+
+def slora_pool_set_tuning(pool, key: int, value: int) -> None:
+    _check(lib().slora_pool_set_tuning(pool, key, int(value)), "slora_pool_set_tuning")
+
+
+def slora_alloc_pages(pool, cls: int, n: int) -> np.ndarray:
+    out = np.empty(max(int(n), 1), dtype=np.int32)
+    _check(lib().slora_alloc_pages(pool, cls, int(n), _i32p(out)), "slora_alloc_pages")
+    return out[:int(n)]
+
+
+def slora_free_pages(pool, cls: int, ids) -> None:
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    _check(lib().slora_free_pages(pool, cls, ids.shape[0], _i32p(ids)), "slora_free_pages")
+
+
+def slora_free_count(pool, cls: int) -> int:
+    return int(lib().slora_free_count(pool, cls))
+
+
+def slora_load_adapter(pool, adapter_id: int, rank: int, scale: float, A=None, B=None,
+                       stream=None, h_in: int = None, h_out: int = None, dtype=None) -> None:
+    """A, B: lists (one per projection) of host arrays h_in x rank and rank x h_out, or None."""
+    if (A is None) != (B is None):
+        raise ValueError("A and B must both be given or both be None")
+    if A is None:
+        _check(lib().slora_load_adapter(pool, adapter_id, rank, float(scale), None, None,
+                                        _stream(stream)), "slora_load_adapter")
+        return
+    keep = []
+    a_ptrs = (c_void_p * len(A))()
+    b_ptrs = (c_void_p * len(B))()
+    for p, (a, b) in enumerate(zip(A, B)):
+        a = np.ascontiguousarray(a, dtype=dtype) if dtype is not None else np.ascontiguousarray(a)
+        b = np.ascontiguousarray(b, dtype=dtype) if dtype is not None else np.ascontiguousarray(b)
+        if a.ndim != 2 or b.ndim != 2 or a.shape[1] != rank or b.shape[0] != rank:
+            raise ValueError("A[p] must be h_in x rank and B[p] rank x h_out")
+        if (h_in is not None and a.shape[0] != h_in) or (h_out is not None and b.shape[1] != h_out):
+            raise ValueError("A[p] / B[p] do not match the pool's h_in / h_out")
+        keep += [a, b]
+        a_ptrs[p] = a.ctypes.data
+        b_ptrs[p] = b.ctypes.data
+    _check(lib().slora_load_adapter(pool, adapter_id, rank, float(scale), a_ptrs, b_ptrs,
+                                    _stream(stream)), "slora_load_adapter")
+
+
+def slora_unload_adapter(pool, adapter_id: int) -> None:
+    _check(lib().slora_unload_adapter(pool, adapter_id), "slora_unload_adapter")
+
+
+def slora_adapter_pages(pool, adapter_id: int, proj: int = 0, max_rank: int = 256):
+    a = np.empty(max_rank, dtype=np.int32)
+    b = np.empty(max_rank, dtype=np.int32)
+    r = c_int32()
+    _check(lib().slora_adapter_pages(pool, adapter_id, proj, _i32p(a), _i32p(b), ctypes.byref(r)),
+           "slora_adapter_pages")
+    return a[:r.value].copy(), b[:r.value].copy()
+
+
+def slora_build_segments(pool, ids):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = c_void_p()
+    _check(lib().slora_build_segments(pool, ids.shape[0], _i32p(ids) if ids.size else None,
+                                      ctypes.byref(out)), "slora_build_segments")
+    return out
+
+
+def slora_segments_destroy(seg) -> None:
+    lib().slora_segments_destroy(seg)
+
+
+def slora_segments_get_info(seg) -> dict:
+    info = SegmentsInfo()
+    _check(lib().slora_segments_get_info(seg, ctypes.byref(info)), "slora_segments_get_info")
+    return {name: getattr(info, name) for name, _ in SegmentsInfo._fields_ if name != "reserved0"}
+
+
+def slora_segments_export(seg) -> dict:
+    info = slora_segments_get_info(seg)
+    S, T, n = info["n_segments"], info["n_routed"], info["n_proj"] * info["sum_rank"]
+    out = {"perm": np.empty(max(T, 1), np.int32), "seg_start": np.empty(S + 1, np.int32),
+           "seg_adapter": np.empty(max(S, 1), np.int32), "seg_rank": np.empty(max(S, 1), np.int32),
+           "seg_scale": np.empty(max(S, 1), np.float32), "seg_page_off": np.empty(S + 1, np.int32),
+           "a_pages": np.empty(max(n, 1), np.int32), "b_pages": np.empty(max(n, 1), np.int32)}
+    _check(lib().slora_segments_export(
+        seg, _i32p(out["perm"]), _i32p(out["seg_start"]), _i32p(out["seg_adapter"]),
+        _i32p(out["seg_rank"]), out["seg_scale"].ctypes.data_as(POINTER(c_float)),
+        _i32p(out["seg_page_off"]), _i32p(out["a_pages"]), _i32p(out["b_pages"])),
+        "slora_segments_export")
+    sizes = {"perm": T, "seg_start": S + 1, "seg_adapter": S, "seg_rank": S, "seg_scale": S,
+             "seg_page_off": S + 1, "a_pages": n, "b_pages": n}
+    return {k: v[:sizes[k]] for k, v in out.items()}
+
+
+def slora_segments_tiles(seg):
+    """(layout dict, shrink records [n, stride], expand records [n, stride]) as int32 arrays."""
+    info = slora_segments_get_info(seg)
+    words = info["meta_bytes"] // 4
+    lay = np.empty(8, np.int32)
+    rec = np.zeros(max(words, 4), np.int32)
+    _check(lib().slora_segments_tiles(seg, _i32p(lay), _i32p(rec), rec.shape[0]),
+           "slora_segments_tiles")
+    keys = ["n_shrink", "shrink_stride", "shrink_tokcap", "shrink_pagecap", "n_expand",
+            "expand_stride", "expand_tokcap", "expand_pagecap"]
+    layout = dict(zip(keys, (int(v) for v in lay)))
+    ns, ss = layout["n_shrink"], layout["shrink_stride"]
+    ne, es = layout["n_expand"], layout["expand_stride"]
+    shrink = rec[:ns * ss].reshape(ns, ss)
+    expand = rec[ns * ss:ns * ss + ne * es].reshape(ne, es)
+    return layout, shrink, expand
+
+
+def slora_segments_upload(seg, dev_meta, dev_meta_bytes: int, stream=None) -> None:
+    _check(lib().slora_segments_upload(seg, _ptr(dev_meta), int(dev_meta_bytes), _stream(stream)),
+           "slora_segments_upload")
+
+
+def slora_lora_delta(pool, seg, proj: int, x, y, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().slora_lora_delta(pool, seg, proj, _ptr(x), _ptr(y), _ptr(workspace),
+                                  int(workspace_bytes), _stream(stream)), "slora_lora_delta")

@@ -1,0 +1,245 @@
+"""HIP path against the fp64 oracle, through the C ABI, on an MI355X.
+
+Every test puts a seeded synthetic workload on the GPU with NaN in all pages
+that are not adapter rows of the batch, runs slora_lora_delta and compares
+with the oracle (gates G1 and G2 of tests/gates.py, or bit-exact where the
+arithmetic is exact).  Routing is forced both ways where it matters: all
+segments on the vector-ALU tiles, all on the MFMA tiles, and the default.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import build_from_workload, round_to, workload_delta  # noqa: E402
+from rank_gemm_page_amd import slora as S  # noqa: E402
+from rank_gemm_page_amd.device_workload import DeviceWorkload  # noqa: E402
+from synth import CONFIGS, generate, small_spec  # noqa: E402
+from tests.gates import check_gates  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ROUTES = {"gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
+          "mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1},
+          "default": {}}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def run_gpu(w, route="default", tuning=None, projs=None, free_order=None):
+    if free_order is not None:
+        w.free_order = free_order
+    t = dict(ROUTES[route])
+    t.update(tuning or {})
+    print(f"[gpu] {w.spec.name} seed={w.seed} route={route} T={w.T}", flush=True)
+    dw = DeviceWorkload(w, "cuda:0", tuning=t)
+    try:
+        out = []
+        for p in projs if projs is not None else range(w.spec.n_proj):
+            dw.delta(p)
+        torch.cuda.synchronize()
+        for p in projs if projs is not None else range(w.spec.n_proj):
+            out.append(dw.y[p].cpu().numpy())
+        return out, dw.info
+    finally:
+        dw.close()
+
+
+def oracle(w, proj=0, tokens=None):
+    return workload_delta(build_from_workload(w), w, proj=proj, tokens=tokens)
+
+
+def test_tiny_fp32():
+    w = generate(CONFIGS["tiny"], 0)
+    (y,), info = run_gpu(w)
+    assert info["n_mfma_segments"] == 0
+    y_ref, sd_ref = oracle(w)
+    check_gates(y, y_ref, sd_ref, np.float32, "tiny")
+
+
+SMALL = [
+    small_spec("sq512", h_in=512, h_out=512, n_adapters=9, batch=("zipf", 96, 1.1),
+               pool=("occ", 3, 5)),
+    small_spec("nonsq", h_in=384, h_out=1288, two_classes=True, n_adapters=6,
+               rank_set=(8, 16, 32, 64, 128), batch=("zipf", 80, 1.0), pool=("occ", 4, 5)),
+    small_spec("proj3", h_in=256, h_out=256, n_adapters=5, n_proj=3, proj_x=(0, 0, 1),
+               batch=("mixed", 2, 40, 17)),
+    small_spec("ragged", h_in=136, h_out=200, two_classes=True, n_adapters=4,
+               rank_set=(1, 3, 13, 40), batch=("zipf", 50, 1.0)),
+    small_spec("scales", h_in=1024, h_out=1024, n_adapters=7, scale_set=(0.5, 1.0, 2.0, 4.0, 0.3),
+               batch=("requests", 5, 3, 40)),
+    small_spec("f32big", dtype="f32", h_in=2048, h_out=1024, two_classes=True, n_adapters=5,
+               rank_set=(4, 16, 64), batch=("zipf", 40, 1.1)),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+@pytest.mark.parametrize("route", list(ROUTES))
+def test_small_shapes(spec, route):
+    w = generate(spec, 1)
+    ys, info = run_gpu(w, route)
+    if route == "mfma" and spec.dtype == "f16" and spec.h_in % 32 == 0:
+        assert info["n_mfma_segments"] == info["n_segments"]
+    for p, y in enumerate(ys):
+        y_ref, sd_ref = oracle(w, p)
+        check_gates(y, y_ref, sd_ref, w.np_dtype, f"{spec.name}/{route}/p{p}")
+
+
+@pytest.mark.parametrize("dtype,h,ranks", [("f32", 256, (1, 4, 8)), ("f16", 128, (1, 2, 4)),
+                                           ("f16", 256, (3, 8))])
+@pytest.mark.parametrize("route", ["gemv", "mfma"])
+def test_integer_inputs_bit_exact(dtype, h, ranks, route):
+    """{-1,0,1} inputs, s = 2: every partial sum is exact, so the GPU must match exactly."""
+    if dtype == "f16" and h == 256:
+        ranks_ok = True  # |y| <= 1 + 2*8*256 = 4097 > 2048: fp16 rounds, compare rounded oracle
+    else:
+        ranks_ok = False
+    spec = small_spec("int", dtype=dtype, h_in=h, h_out=h, n_adapters=5, rank_set=ranks,
+                      values="ternary", scale=2.0, batch=("zipf", 40, 1.0))
+    w = generate(spec, 7)
+    (y,), _ = run_gpu(w, route)
+    y_ref, _ = oracle(w)
+    expect = round_to(y_ref, w.np_dtype)
+    if not ranks_ok:
+        assert np.array_equal(np.round(y_ref), y_ref)
+    np.testing.assert_array_equal(y, expect)
+
+
+def test_page_permutation_invariance_bit_exact():
+    spec = small_spec("perm", h_in=512, h_out=512, n_adapters=8, batch=("zipf", 64, 1.1),
+                      pool=("occ", 3, 5))
+    outs = []
+    for k in range(2):
+        w = generate(spec, 2)
+        rng = np.random.default_rng(100 + k)
+        fo = [rng.permutation(P).astype(np.int32) for P in w.n_pages]
+        (y,), _ = run_gpu(w, "default", tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 8}, free_order=fo)
+        outs.append(y)
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+
+
+@pytest.mark.parametrize("route", ["gemv", "mfma"])
+def test_deterministic_run_to_run(route):
+    spec = small_spec("det", h_in=1024, h_out=1024, n_adapters=6, batch=("zipf", 70, 1.0))
+    w = generate(spec, 3)
+    dw = DeviceWorkload(w, "cuda:0", tuning=ROUTES[route])
+    try:
+        res = []
+        for _ in range(3):
+            dw.reset_y()
+            dw.delta(0)
+            torch.cuda.synchronize()
+            res.append(dw.y[0].cpu().numpy().view(np.uint16).copy())
+        assert all(np.array_equal(res[0], r) for r in res[1:])
+    finally:
+        dw.close()
+
+
+@pytest.mark.parametrize("what", ["zero_B", "zero_scale"])
+@pytest.mark.parametrize("route", ["gemv", "mfma"])
+def test_no_op_leaves_y_unchanged(what, route):
+    spec = small_spec("noop", h_in=256, h_out=512, two_classes=True, n_adapters=4,
+                      batch=("zipf", 40, 1.0), scale=0.0 if what == "zero_scale" else 2.0)
+    w = generate(spec, 4)
+    if what == "zero_B":
+        for a in range(spec.n_adapters):
+            A, B = w.weights(a)
+            w._wcache[(a, 0)] = (A, np.zeros_like(B))
+    (y,), _ = run_gpu(w, route)
+    np.testing.assert_array_equal(y.astype(np.float64), w.y[0].astype(np.float64))
+
+
+def test_negative_ids_leave_rows_untouched():
+    spec = small_spec("neg", h_in=256, h_out=256, n_adapters=3, batch=("zipf", 40, 1.0))
+    w = generate(spec, 5)
+    w.ids = w.ids.copy()
+    w.ids[::3] = -1
+    (y,), _ = run_gpu(w, "default", tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 4})
+    y_ref, sd_ref = oracle(w)
+    check_gates(y, y_ref, sd_ref, np.float16, "neg")
+    assert np.array_equal(y[::3].view(np.uint16), w.y[0][::3].view(np.uint16))
+
+
+def test_unload_reload_same_result_other_pages():
+    spec = small_spec("reload", h_in=512, h_out=512, n_adapters=5, batch=("zipf", 50, 1.0),
+                      pool=("occ", 1, 2))
+    w = generate(spec, 6)
+    dw = DeviceWorkload(w, "cuda:0", tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 8})
+    try:
+        dw.delta(0)
+        torch.cuda.synchronize()
+        y1 = dw.y[0].cpu().numpy().copy()
+        a = int(w.ids[0])
+        before = S.slora_adapter_pages(dw.pool, a)
+        # a stale batch is refused, then the adapter comes back on other pages
+        S.slora_unload_adapter(dw.pool, a)
+        with pytest.raises(S.SloraError) as e:
+            dw.delta(0)
+        assert e.value.status == S.SLORA_E_STALE
+        A, B = w.weights(a)
+        S.slora_load_adapter(dw.pool, a, int(w.ranks[a]), float(w.scales[a]), [A], [B],
+                             torch.cuda.current_stream())
+        after = S.slora_adapter_pages(dw.pool, a)
+        assert set(before[0].tolist()).isdisjoint(after[0].tolist())
+        dw.build(w.ids)
+        dw.reset_y()
+        dw.delta(0)
+        torch.cuda.synchronize()
+        y2 = dw.y[0].cpu().numpy()
+        assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    finally:
+        dw.close()
+
+
+def test_pool_bytes_match_oracle_image():
+    """The loader put every A^T and B row on its page, bit for bit."""
+    spec = small_spec("img", h_in=264, h_out=136, two_classes=True, n_adapters=4,
+                      rank_set=(1, 5, 9), batch=("uniform", 10))
+    w = generate(spec, 8)
+    dw = DeviceWorkload(w, "cuda:0")
+    try:
+        st = build_from_workload(w)
+        pages = [p.cpu().numpy() for p in dw.pages]
+        for (cls, pg), row in st.image.rows.items():
+            assert np.array_equal(pages[cls][pg].view(np.uint16), row.view(np.uint16))
+        n_written = len(st.image.rows)
+        n_nan = sum(int(np.isnan(p).all(axis=1).sum()) for p in pages)
+        assert n_nan == sum(w.n_pages) - n_written
+    finally:
+        dw.close()
+
+
+# ---------------------------------------------------------------------------
+# The five benchmark shapes at full size, default routing (as bench.py runs them)
+
+
+def sample_tokens(w, n, seed=0):
+    rng = np.random.default_rng(seed)
+    ids = w.ids
+    # the first and last token of every segment boundary region, plus random ones
+    order = np.argsort(ids, kind="stable")
+    picks = set(order[:4].tolist()) | set(order[-4:].tolist())
+    picks |= set(rng.choice(w.T, size=min(n, w.T), replace=False).tolist())
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name,n_sample", [("decode7b", None), ("prefill7b", 48),
+                                           ("mixed13b", 40), ("mlp70b", 40)])
+def test_full_size_config(name, n_sample):
+    w = generate(CONFIGS[name], 0)
+    ys, info = run_gpu(w, "default")
+    print(f"[gpu] {name}: segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
+          f"shrink_tiles={info['n_shrink_tiles']} expand_tiles={info['n_expand_tiles']}", flush=True)
+    st = build_from_workload(w)
+    toks = None if n_sample is None else sample_tokens(w, n_sample)
+    for p, y in enumerate(ys):
+        y_ref, sd_ref = workload_delta(st, w, proj=p, tokens=toks)
+        got = y if toks is None else y[toks]
+        check_gates(got, y_ref, sd_ref, np.float16, f"{name}/p{p}")
+        # rows of tokens outside the sample are still finite (no NaN page was read)
+        assert np.isfinite(y).all()

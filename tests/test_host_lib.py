@@ -1,0 +1,358 @@
+"""Host side of libslora on the CPU: exports, allocator, segments, tiles, errors.
+
+No GPU is touched: pools get fake (never dereferenced) page addresses, adapters
+are loaded without data (pages reserved only), and every check runs on
+metadata the library computes on the host.
+"""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import slora_oracle as orc
+from rank_gemm_page_amd import slora as S
+from synth import CONFIGS, generate, small_spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_BASE = [1 << 40, 1 << 41]
+
+
+def make_pool(w, base=FAKE_BASE, tuning=None):
+    spec = w.spec
+    n_classes = 2 if spec.two_classes else 1
+    pool = S.slora_pool_create(S.SLORA_F16 if spec.dtype == "f16" else S.SLORA_F32, spec.h_in,
+                               spec.h_out, spec.n_proj, spec.n_adapters, int(w.ranks.max()),
+                               base[:n_classes], list(w.n_pages), w.free_order)
+    for k, v in (tuning or {}).items():
+        S.slora_pool_set_tuning(pool, k, v)
+    kv = [S.slora_alloc_pages(pool, c, int(n)) for c, n in enumerate(w.kv_pages)]
+    for a in range(spec.n_adapters):
+        S.slora_load_adapter(pool, a, int(w.ranks[a]), float(w.scales[a]))
+    return pool, kv
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "slora.h")).read()
+    declared = set(re.findall(r"\b(slora_[a-z_]+)\s*\(", header))
+    assert declared == set(S.EXPORTED)
+    lib = S.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("case", ["single_class", "two_class_two_proj"])
+def test_allocator_fixture_through_library(case):
+    with open(os.path.join(ROOT, "tests", "golden", "allocator_fifo.json")) as f:
+        g = json.load(f)[case]
+    n_classes = len(g["n_pages"])
+    pool = S.slora_pool_create(S.SLORA_F16, 8, 8 if n_classes == 1 else 16, g["n_proj"], 16, 4,
+                               FAKE_BASE[:n_classes], g["n_pages"], g["free_order"])
+    try:
+        for st in g["steps"]:
+            if st["op"] == "load":
+                S.slora_load_adapter(pool, st["adapter"], st["rank"], 1.0)
+                for p in range(g["n_proj"]):
+                    a, b = S.slora_adapter_pages(pool, st["adapter"], p)
+                    assert a.tolist() == st["a_pages"][p] and b.tolist() == st["b_pages"][p]
+            elif st["op"] == "load_fail":
+                before = [S.slora_free_count(pool, c) for c in range(n_classes)]
+                with pytest.raises(S.SloraError) as e:
+                    S.slora_load_adapter(pool, st["adapter"], st["rank"], 1.0)
+                assert e.value.status == S.SLORA_E_NOMEM
+                assert [S.slora_free_count(pool, c) for c in range(n_classes)] == before
+                assert before == [len(f) for f in st["free_after"]]
+            elif st["op"] == "unload":
+                S.slora_unload_adapter(pool, st["adapter"])
+                assert [S.slora_free_count(pool, c) for c in range(n_classes)] == \
+                    [len(f) for f in st["free_after"]]
+            elif st["op"] == "kv":
+                assert S.slora_alloc_pages(pool, st["cls"], st["n"]).tolist() == st["pages"]
+            elif st["op"] == "kv_fail":
+                with pytest.raises(S.SloraError) as e:
+                    S.slora_alloc_pages(pool, st["cls"], st["n"])
+                assert e.value.status == S.SLORA_E_NOMEM
+        # the free lists' order, read back by draining them, matches the fixture
+        final = g["steps"][-1].get("free_after")
+        if final is not None:
+            for c in range(n_classes):
+                assert S.slora_alloc_pages(pool, c, len(final[c])).tolist() == final[c]
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def oracle_segments(w):
+    st = orc.build_from_workload(w, load_weights=False)
+    return st, orc.segment_model(w.ids, st.alloc)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_metadata_bit_exact_vs_oracle(name):
+    w = generate(CONFIGS[name], 0)
+    pool, kv = make_pool(w)
+    try:
+        st, ref = oracle_segments(w)
+        for c in range(len(kv)):
+            assert kv[c].tolist() == st.kv_pages[c]
+        for a in range(w.spec.n_adapters):
+            for p in range(w.spec.n_proj):
+                ap, bp = S.slora_adapter_pages(pool, a, p)
+                assert ap.tolist() == st.alloc.table[a].a_pages[p]
+                assert bp.tolist() == st.alloc.table[a].b_pages[p]
+        seg = S.slora_build_segments(pool, w.ids)
+        try:
+            got = S.slora_segments_export(seg)
+            for k in ("perm", "seg_start", "seg_adapter", "seg_rank", "seg_page_off", "a_pages",
+                      "b_pages"):
+                np.testing.assert_array_equal(got[k], getattr(ref, k), err_msg=k)
+            assert got["seg_scale"].view(np.uint32).tolist() == ref.seg_scale.view(np.uint32).tolist()
+            info = S.slora_segments_get_info(seg)
+            assert info["n_routed"] == w.T and info["n_segments"] == ref.seg_adapter.shape[0]
+            assert info["sum_rank_tokens"] == int(w.ranks[w.ids].astype(np.int64).sum())
+        finally:
+            S.slora_segments_destroy(seg)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def check_tiles_cover(w, pool, ids):
+    """Every (token, rank row) is shrunk once and every (token, column) expanded once."""
+    seg = S.slora_build_segments(pool, ids)
+    try:
+        info = S.slora_segments_get_info(seg)
+        ex = S.slora_segments_export(seg)
+        lay, sh, exp = S.slora_segments_tiles(seg)
+        spec = w.spec
+        n_seg = info["n_segments"]
+        seg_of = {}
+        for s in range(n_seg):
+            for i in range(ex["seg_start"][s], ex["seg_start"][s + 1]):
+                seg_of[int(ex["perm"][i])] = (s, i)
+        # where each token's v row lives: prefix over sorted tokens of their ranks
+        v_row = {}
+        off = 0
+        for s in range(n_seg):
+            r = int(ex["seg_rank"][s])
+            for i in range(ex["seg_start"][s], ex["seg_start"][s + 1]):
+                v_row[int(ex["perm"][i])] = off
+                off += r
+        assert off == info["sum_rank_tokens"]
+        shrink_seen = np.zeros(max(off, 1), np.int32)
+        for rec in sh:
+            kind, ntok, r, j0, nrows, v0 = (int(v) for v in rec[:6])
+            assert kind in (0, 1) and 1 <= ntok <= lay["shrink_tokcap"] and nrows >= 1
+            assert (kind == 1) <= (spec.dtype == "f16")
+            toks = rec[8:8 + ntok]
+            s, _ = seg_of[int(toks[0])]
+            assert r == ex["seg_rank"][s] and 0 <= j0 and j0 + nrows <= r
+            for k, t in enumerate(toks):
+                assert seg_of[int(t)][0] == s
+                assert v_row[int(t)] == v0 + k * r
+                shrink_seen[v_row[int(t)] + j0:v_row[int(t)] + j0 + nrows] += 1
+            for p in range(spec.n_proj):
+                pg = rec[8 + lay["shrink_tokcap"] + p * lay["shrink_pagecap"]:][:nrows]
+                base = p * info["sum_rank"] + ex["seg_page_off"][s]
+                np.testing.assert_array_equal(pg, ex["a_pages"][base + j0:base + j0 + nrows])
+        assert (shrink_seen[:off] == 1).all()
+        routed = [t for t in range(len(ids)) if ids[t] >= 0]
+        cover = {t: np.zeros(spec.h_out, np.int32) for t in routed}
+        for rec in exp:
+            kind, ntok, r, o0, ncol, v0 = (int(v) for v in rec[:6])
+            assert 1 <= ntok <= lay["expand_tokcap"] and o0 % 8 == 0 and ncol % 8 == 0
+            assert 0 <= o0 and o0 + ncol <= spec.h_out
+            toks = rec[8:8 + ntok]
+            s, _ = seg_of[int(toks[0])]
+            assert np.float32(rec[6:7].view(np.float32)[0]) == ex["seg_scale"][s]
+            for k, t in enumerate(toks):
+                assert seg_of[int(t)][0] == s and v_row[int(t)] == v0 + k * r
+                cover[int(t)][o0:o0 + ncol] += 1
+            if kind == 0:
+                width = int(rec[7])
+                vec = 8 if spec.dtype == "f16" else 4
+                assert width % vec == 0 and 256 % (width // vec) == 0 and ncol <= width
+            for p in range(spec.n_proj):
+                pg = rec[8 + lay["expand_tokcap"] + p * lay["expand_pagecap"]:][:r]
+                base = p * info["sum_rank"] + ex["seg_page_off"][s]
+                np.testing.assert_array_equal(pg, ex["b_pages"][base:base + r])
+        for t in routed:
+            assert (cover[t] == 1).all(), t
+        return info
+    finally:
+        S.slora_segments_destroy(seg)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode7b", "prefill7b", "mixed13b", "mlp70b"])
+@pytest.mark.parametrize("route", ["default", "all_gemv", "all_mfma"])
+def test_tiles_cover_each_output_once(name, route):
+    tuning = {"default": {}, "all_gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
+              "all_mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1}}[route]
+    w = generate(CONFIGS[name], 0)
+    pool, _ = make_pool(w, tuning=tuning)
+    try:
+        info = check_tiles_cover(w, pool, w.ids)
+        if route == "all_gemv" or w.spec.dtype == "f32":
+            assert info["n_mfma_segments"] == 0
+        if route == "all_mfma" and w.spec.dtype == "f16":
+            assert info["n_mfma_segments"] == info["n_segments"]
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_tiles_with_ragged_shapes_and_no_adapter_tokens():
+    spec = small_spec("ragged", h_in=136, h_out=200, two_classes=True, n_adapters=7,
+                      rank_set=(1, 3, 13, 40, 100), batch=("zipf", 60, 1.0))
+    w = generate(spec, 3)
+    ids = w.ids.copy()
+    ids[::5] = -1
+    for route in (1, 5, 1 << 30):
+        pool, _ = make_pool(w, tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: route,
+                                       S.SLORA_TUNE_GEMV_EXPAND_ELEMS: 1000})
+        try:
+            check_tiles_cover(w, pool, ids)
+        finally:
+            S.slora_pool_destroy(pool)
+
+
+# ---------------------------------------------------------------------------
+# Errors: every failure is reported and changes nothing
+
+
+def small_pool(n_pages=64, n_proj=1, max_rank=8, two=False, free_order=None):
+    return S.slora_pool_create(S.SLORA_F16, 16, 32 if two else 16, n_proj, 8, max_rank,
+                               FAKE_BASE[:2 if two else 1], [n_pages] * (2 if two else 1),
+                               free_order)
+
+
+def status_of(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except S.SloraError as e:
+        return e.status
+    return S.SLORA_OK
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(dtype=7), "dtype"), (dict(h_in=12, h_out=12), "h not multiple of 8"),
+    (dict(h_out=24), "one class needs h_in == h_out"), (dict(n_proj=0), "n_proj"),
+    (dict(max_rank=0), "max_rank"), (dict(max_rank=300), "max_rank too big"),
+    (dict(base=[(1 << 40) + 4]), "unaligned base"), (dict(base=[0]), "NULL base"),
+    (dict(free_order=[[0, 0, 1, 2]]), "free order not a permutation"),
+    (dict(n_pages=[0]), "no pages"), (dict(h_in=32768, h_out=32768), "h_in too large"),
+])
+def test_pool_create_rejects(kw, what):
+    args = dict(dtype=S.SLORA_F16, h_in=16, h_out=16, n_proj=1, max_adapters=4, max_rank=4,
+                base=[1 << 40], n_pages=[4], free_order=None)
+    args.update(kw)
+    st = status_of(S.slora_pool_create, args["dtype"], args["h_in"], args["h_out"], args["n_proj"],
+                   args["max_adapters"], args["max_rank"], args["base"], args["n_pages"],
+                   args["free_order"])
+    assert st == S.SLORA_E_INVAL, what
+
+
+def test_load_errors_leave_pool_unchanged():
+    pool = small_pool(n_pages=10)
+    try:
+        S.slora_load_adapter(pool, 0, 4, 1.0)                       # takes 8 pages
+        assert status_of(S.slora_load_adapter, pool, 0, 1, 1.0) == S.SLORA_E_EXIST
+        assert status_of(S.slora_load_adapter, pool, 1, 2, 1.0) == S.SLORA_E_NOMEM
+        assert status_of(S.slora_load_adapter, pool, 9, 1, 1.0) == S.SLORA_E_INVAL
+        assert status_of(S.slora_load_adapter, pool, 1, 0, 1.0) == S.SLORA_E_INVAL
+        assert status_of(S.slora_load_adapter, pool, 1, 9, 1.0) == S.SLORA_E_INVAL
+        assert status_of(S.slora_load_adapter, pool, 1, 1, float("nan")) == S.SLORA_E_INVAL
+        assert S.slora_free_count(pool, 0) == 2
+        S.slora_load_adapter(pool, 1, 1, 1.0)
+        assert S.slora_free_count(pool, 0) == 0
+        assert status_of(S.slora_unload_adapter, pool, 2) == S.SLORA_E_NOENT
+        assert status_of(S.slora_adapter_pages, pool, 2) == S.SLORA_E_NOENT
+        assert "not loaded" in S.slora_last_error()
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_free_pages_rejects_non_kv_and_double_free():
+    pool = small_pool(n_pages=8)
+    try:
+        kv = S.slora_alloc_pages(pool, 0, 3)
+        S.slora_load_adapter(pool, 0, 1, 1.0)
+        a, _ = S.slora_adapter_pages(pool, 0)
+        assert status_of(S.slora_free_pages, pool, 0, a) == S.SLORA_E_INVAL
+        assert status_of(S.slora_free_pages, pool, 0, [kv[0], kv[0]]) == S.SLORA_E_INVAL
+        assert status_of(S.slora_free_pages, pool, 0, [kv[1], 99]) == S.SLORA_E_INVAL
+        assert status_of(S.slora_free_pages, pool, 1, [kv[1]]) == S.SLORA_E_INVAL
+        assert S.slora_free_count(pool, 0) == 3
+        S.slora_free_pages(pool, 0, kv[::-1])
+        assert S.slora_free_count(pool, 0) == 6
+        assert status_of(S.slora_free_pages, pool, 0, kv[:1]) == S.SLORA_E_INVAL
+        # freed pages come back last, in the order they were returned
+        assert S.slora_alloc_pages(pool, 0, 6).tolist()[-3:] == kv[::-1].tolist()
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_segments_errors_and_staleness():
+    pool = small_pool(n_pages=32)
+    try:
+        for a in range(3):
+            S.slora_load_adapter(pool, a, 2, 1.0)
+        assert status_of(S.slora_build_segments, pool, [0, 5]) == S.SLORA_E_NOENT
+        assert status_of(S.slora_build_segments, pool, [0, 8]) == S.SLORA_E_NOENT
+        seg = S.slora_build_segments(pool, [2, -1, 0, 2])
+        try:
+            fake = 1 << 42
+            # not uploaded yet: refused before any device work
+            assert status_of(S.slora_lora_delta, pool, seg, 0, fake, fake, fake, 1 << 20) == S.SLORA_E_INVAL
+            assert status_of(S.slora_lora_delta, pool, seg, 1, fake, fake, fake, 1 << 20) == S.SLORA_E_INVAL
+            S.slora_unload_adapter(pool, 0)
+            assert status_of(S.slora_lora_delta, pool, seg, 0, fake, fake, fake, 1 << 20) == S.SLORA_E_STALE
+            S.slora_load_adapter(pool, 0, 2, 1.0)   # reloaded: a new generation, still stale
+            assert status_of(S.slora_lora_delta, pool, seg, 0, fake, fake, fake, 1 << 20) == S.SLORA_E_STALE
+        finally:
+            S.slora_segments_destroy(seg)
+        ex = S.slora_segments_export(seg2 := S.slora_build_segments(pool, [2, -1, 0, 2]))
+        assert ex["perm"].tolist() == [2, 0, 3] and ex["seg_adapter"].tolist() == [0, 2]
+        S.slora_segments_destroy(seg2)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_empty_and_unrouted_batches_launch_nothing():
+    pool = small_pool()
+    try:
+        S.slora_load_adapter(pool, 0, 2, 1.0)
+        for ids in ([], [-1, -1, -3]):
+            seg = S.slora_build_segments(pool, ids)
+            try:
+                info = S.slora_segments_get_info(seg)
+                assert info["n_routed"] == 0 and info["n_shrink_tiles"] == 0 and info["n_expand_tiles"] == 0
+                # no routed token: returns before touching the device or the pointers
+                S.slora_lora_delta(pool, seg, 0, 0, 0, 0, 0)
+            finally:
+                S.slora_segments_destroy(seg)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_tuning_validation():
+    pool = small_pool()
+    try:
+        assert status_of(S.slora_pool_set_tuning, pool, 0, 0) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, 2, 300) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, 9, 1) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, 2, 1024)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_unload_reload_lands_on_other_pages():
+    """Unloading returns pages to the tail, so a reload takes different pages."""
+    pool = small_pool(n_pages=16)
+    try:
+        S.slora_load_adapter(pool, 0, 2, 1.0)
+        a1, b1 = S.slora_adapter_pages(pool, 0)
+        S.slora_unload_adapter(pool, 0)
+        S.slora_load_adapter(pool, 0, 2, 1.0)
+        a2, b2 = S.slora_adapter_pages(pool, 0)
+        assert set(a1.tolist() + b1.tolist()).isdisjoint(a2.tolist() + b2.tolist())
+    finally:
+        S.slora_pool_destroy(pool)
