@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged, heterogeneous-batch LoRA delta on one MI355X.
+
+One step is one pass of the hot path over one batch: the shrink kernel
+(v = x A from the A^T pages) and the expand kernel (y += s v B from the B
+pages) for every token of the batch, with the batch's segment metadata, x, y
+and the adapter pages already resident in HBM.  Before every step a 1 GiB
+device copy evicts the 256 MB last-level cache, so each step reads its pages
+from HBM as a serving iteration would after the rest of the model ran; the
+copy sits outside the HIP events that time the step.  Host segment building
+and the metadata upload (PCIe) are timed on their own and reported beside the
+step, never inside ``value``.
+
+Prints one JSON line: tokens/s, per-kernel times, the roofline of the dominant
+kernel against MI355X's 8 TB/s HBM, and the fp64 CPU oracle's rate on the
+host cores (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+METRIC = "LoRA-delta tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill)"
+WORKLOAD_NOTES = {
+    "tiny": "H 256->256 fp32, 4 adapters r{4,8,4,8}, 16 tokens uniform ids, 128-page shuffled pool",
+    "decode7b": "Llama-7B shape 4096->4096 fp16, 1000 adapters r in {8,16,32,64}, 256 decode tokens "
+                "with Zipf(1.1) adapter ids, A/B pages scattered among 60% KV pages",
+    "prefill7b": "Llama-7B shape 4096->4096 fp16, 32 requests of 64..512 tokens, one of 100 adapters "
+                 "each, shuffled pool at 50% KV",
+    "mixed13b": "Llama-13B 5120->5120 fp16, q,k,v,o projections, 2000 adapters, 8x256 prefill + "
+                "384 decode tokens, uniform ids",
+    "mlp70b": "8192->28672 fp16, two page classes, 5000 adapters r in {16,32,64,128}, 512 decode "
+              "tokens Zipf(1.0), pool 80% KV",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_gemm_page_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config, dominant):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash() or dominant not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][dominant]
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The fp64 oracle on the host cores over a bounded sample of the batch."""
+    import numpy as np
+
+    from oracle import build_from_workload, workload_delta
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    st = build_from_workload(w)
+    t = time.perf_counter()
+    workload_delta(st, w, tokens=[0])
+    per_tok = max(time.perf_counter() - t, 1e-5)
+    n = int(min(w.T, max(1, budget_s / 3 / per_tok)))
+    toks = np.linspace(0, w.T - 1, n).astype(int).tolist()
+    reps = []
+    for _ in range(3):
+        t = time.perf_counter()
+        workload_delta(st, w, tokens=toks)
+        reps.append(time.perf_counter() - t)
+    med = statistics.median(reps)
+    return {"value": n / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {w.T} tokens of the same batch (projection 0), fp64 NumPy, "
+                      f"median of 3 runs of {med:.3f} s, page-table walk per token",
+            "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode7b",
+                    choices=["tiny", "decode7b", "prefill7b", "mixed13b", "mlp70b"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="device copy between steps that evicts the last-level cache (0: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-min-tokens", type=int, default=None)
+    ap.add_argument("--gemv-expand-elems", type=int, default=None)
+    ap.add_argument("--mfma-expand-cols", type=int, default=None)
+    ap.add_argument("--mfma-shrink-rows", type=int, default=None)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain copy of this size (PMC calibration runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; the delta shards by tokens or columns with no exchange, and this "
+              "build measures one GPU's share.", file=sys.stderr, flush=True)
+        sys.exit(3)
+
+    import numpy as np
+    import torch
+
+    from rank_gemm_page_amd.device_workload import DeviceWorkload
+    from synth import CONFIGS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] generating {args.config} seed={args.seed}")
+    w = generate(CONFIGS[args.config], args.seed)
+    log("[bench] loading pool")
+    from rank_gemm_page_amd import slora as S
+    tuning = {k: v for k, v in ((S.SLORA_TUNE_MFMA_MIN_TOKENS, args.mfma_min_tokens),
+                                (S.SLORA_TUNE_GEMV_EXPAND_ELEMS, args.gemv_expand_elems),
+                                (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
+                                (S.SLORA_TUNE_MFMA_SHRINK_ROWS, args.mfma_shrink_rows))
+              if v is not None}
+    dw = DeviceWorkload(w, dev, tuning=tuning)
+    spec = w.spec
+    n_proj = spec.n_proj
+    info = dw.info
+    log(f"[bench] T={w.T} segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
+        f"shrink_tiles={info['n_shrink_tiles']} expand_tiles={info['n_expand_tiles']}")
+
+    stream = torch.cuda.current_stream(dev)
+    half = args.flush_mib * (1 << 20) // 2
+    flush_src = torch.empty(max(half, 16), dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    flush_src.fill_(1)
+
+    def flush():
+        if args.flush_mib > 0:
+            flush_dst.copy_(flush_src)
+
+    def step(events=None):
+        for p in range(n_proj):
+            if events is not None:
+                events[p][0].record(stream)
+            dw.shrink(p, stream=stream)
+            if events is not None:
+                events[p][1].record(stream)
+            dw.expand(p, stream=stream)
+            if events is not None:
+                events[p][2].record(stream)
+
+    for _ in range(args.warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_proj)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        flush()
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] {K} timed steps done in {wall * 1e3:.1f} ms wall (flushes included)")
+
+    shrink_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][1]) for p in range(n_proj)) for k in range(K)]
+    expand_ms = [sum(ev[k][p][1].elapsed_time(ev[k][p][2]) for p in range(n_proj)) for k in range(K)]
+    step_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][2]) for p in range(n_proj)) for k in range(K)]
+    ms = statistics.fmean(step_ms)
+    sh_ms, ex_ms = statistics.fmean(shrink_ms), statistics.fmean(expand_ms)
+
+    # Host segment build and metadata upload, timed apart (PCIe-inclusive figures).
+    ids = w.ids
+    builds = []
+    for _ in range(20):
+        t = time.perf_counter()
+        seg = S.slora_build_segments(dw.pool, ids)
+        builds.append(time.perf_counter() - t)
+        S.slora_segments_destroy(seg)
+    up_ms = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dw.upload(stream)
+        b.record(stream)
+        b.synchronize()
+        up_ms.append(a.elapsed_time(b))
+    build_us = statistics.median(builds) * 1e6
+    upload_us = statistics.median(up_ms) * 1e3
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            flush()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    sb, eb = dw.algorithmic_bytes()
+    sf, ef = dw.algorithmic_flops()
+    # per step: each projection moves its own pages and y; x counted once per launch
+    bytes_shrink, bytes_expand = n_proj * sb, n_proj * eb
+    flops = n_proj * (sf + ef)
+    dominant = "shrink_kernel" if sh_ms >= ex_ms else "expand_kernel"
+    dom_ms = max(sh_ms, ex_ms) / n_proj
+    dom_bytes = sb if dominant == "shrink_kernel" else eb
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.config, dominant)
+    tokens = int(info["n_routed"])
+    value = tokens / (ms * 1e-3)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.config, "description": WORKLOAD_NOTES[args.config],
+                   "tokens": tokens, "h_in": spec.h_in, "h_out": spec.h_out,
+                   "projections": n_proj, "adapters": spec.n_adapters,
+                   "segments": info["n_segments"], "mfma_segments": info["n_mfma_segments"],
+                   "seed": args.seed, "parallelism": "single GPU",
+                   "tuning": {str(k): v for k, v in tuning.items()}},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                     "avg_launch_us": round(dom_ms * 1e3, 3)},
+        "kernels": {"shrink_us": round(sh_ms * 1e3 / n_proj, 3),
+                    "expand_us": round(ex_ms * 1e3 / n_proj, 3),
+                    "shrink_GBps": round(sb / (sh_ms / n_proj * 1e-3) / 1e9, 1),
+                    "expand_GBps": round(eb / (ex_ms / n_proj * 1e-3) / 1e9, 1),
+                    "step_GBps": round((bytes_shrink + bytes_expand) / (ms * 1e-3) / 1e9, 1),
+                    "step_frac_hbm_peak": round((bytes_shrink + bytes_expand) / (ms * 1e-3) / 1e9
+                                                / HBM_PEAK_GBPS, 4),
+                    "mfma_frac_f16_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 5),
+                    "step_us_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 3),
+                    "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 3),
+                    "shrink_tiles": info["n_shrink_tiles"], "expand_tiles": info["n_expand_tiles"]},
+        "host_build_us": round(build_us, 1),
+        "metadata_upload_us": round(upload_us, 2),
+        "metadata_bytes": int(info["meta_bytes"]),
+        "timing": "HIP events on the launch stream around each stage, mean over steps; a "
+                  f"{args.flush_mib} MiB device copy before every step evicts the LLC and is "
+                  "outside the events",
+        "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(w)
+    dw.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

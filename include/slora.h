@@ -92,11 +92,14 @@ void slora_pool_destroy(slora_pool* pool);
  *                                expand tile; default 32768.
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
  *                                of 256; default 512.
+ *  SLORA_TUNE_MFMA_SHRINK_ROWS - rank rows of one MFMA shrink tile, a
+ *                                multiple of 16 up to 64; default 64.
  * They change how the work is cut, never what is computed. */
 typedef enum {
   SLORA_TUNE_MFMA_MIN_TOKENS = 0,
   SLORA_TUNE_GEMV_EXPAND_ELEMS = 1,
-  SLORA_TUNE_MFMA_EXPAND_COLS = 2
+  SLORA_TUNE_MFMA_EXPAND_COLS = 2,
+  SLORA_TUNE_MFMA_SHRINK_ROWS = 3
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 
@@ -205,6 +208,18 @@ slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t d
 slora_status slora_lora_delta(slora_pool* pool, const slora_segments* seg, int32_t proj,
                               const void* x, void* y, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* The two stages of slora_lora_delta, for callers that schedule or time them
+ * apart: slora_lora_shrink writes v = x A (fp32) for every routed token into
+ * the workspace; slora_lora_expand then applies y += s v B.  Same arguments,
+ * checks and kernels as slora_lora_delta; expand must follow a shrink of the
+ * same segments, projection and x on the same stream, with the workspace
+ * untouched in between. */
+slora_status slora_lora_shrink(slora_pool* pool, const slora_segments* seg, int32_t proj,
+                               const void* x, void* workspace, size_t workspace_bytes,
+                               void* stream);
+slora_status slora_lora_expand(slora_pool* pool, const slora_segments* seg, int32_t proj, void* y,
+                               const void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* slora_last_error(void);

@@ -38,5 +38,45 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def device_assembly(workdir: str) -> str:
+    """Compile the kernels for gfx950 keeping the assembly; return its path."""
+    src = os.path.join(CSRC, "slora_kernels.hip")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-c",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", INCLUDE, "-I", CSRC, "--save-temps", "-o", os.path.join(workdir, "k.o"), src]
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=workdir)
+    if res.returncode != 0:
+        raise RuntimeError(res.stderr)
+    return os.path.join(workdir, "slora_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")
+
+
+def masked_mfma_lines(asm_path: str):
+    """Lines of v_mfma instructions that may run under a partial EXEC mask.
+
+    A matrix instruction executes for the whole wavefront regardless of EXEC,
+    so one placed after an exec-narrowing instruction, with no s_cbranch_execz,
+    label or exec restore in between, would accumulate operands of lanes that
+    were meant to be switched off.
+    """
+    bad, masked = [], False
+    with open(asm_path) as f:
+        for no, line in enumerate(f, 1):
+            t = line.strip()
+            parts = t.split()
+            op = parts[0] if parts else ""
+            dst = parts[1].rstrip(",") if len(parts) > 1 else ""
+            if op in ("s_and_saveexec_b64", "s_andn2_saveexec_b64", "s_or_saveexec_b64") or (
+                    op.startswith("s_") and dst == "exec" and op != "s_or_b64"
+                    and not op.startswith("s_mov")):
+                masked = True
+            if (op.startswith("s_cbranch_execz") or (op == "s_or_b64" and dst == "exec")
+                    or t.endswith(":") or op == "s_branch"
+                    or (op.startswith("s_mov") and dst == "exec")):
+                masked = False
+            if op.startswith("v_mfma") and masked:
+                bad.append(no)
+    return bad
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -83,6 +83,7 @@ struct Tuning {
   int64_t mfma_min_tokens = 16;
   int64_t gemv_expand_elems = 32768;
   int64_t mfma_expand_cols = 512;
+  int64_t mfma_shrink_rows = kMfmaMaxRows;
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -284,8 +285,9 @@ void build_tiles(slora_segments* s) {
       ++s->n_mfma_segments;
       split_tokens(c, kMfmaTok, blocks);
       for (auto& tb : blocks) {
-        for (int32_t j0 = 0; j0 < r; j0 += kMfmaMaxRows)
-          sh.push_back({KIND_MFMA, g, tb.first, tb.second, j0, std::min(kMfmaMaxRows, r - j0), 0});
+        const int32_t rows = (int32_t)p->tune.mfma_shrink_rows;
+        for (int32_t j0 = 0; j0 < r; j0 += rows)
+          sh.push_back({KIND_MFMA, g, tb.first, tb.second, j0, std::min(rows, r - j0), 0});
         const int32_t cols = (int32_t)p->tune.mfma_expand_cols;
         for (int32_t o0 = 0; o0 < hout; o0 += cols)
           ex.push_back({KIND_MFMA, g, tb.first, tb.second, o0, std::min(cols, hout - o0), 0});
@@ -453,6 +455,11 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       if (value < kMfmaCols || value % kMfmaCols || value > 65536)
         return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 256, at most 65536");
       p->tune.mfma_expand_cols = value;
+      return SLORA_OK;
+    case SLORA_TUNE_MFMA_SHRINK_ROWS:
+      if (value < 16 || value > kMfmaMaxRows || value % 16)
+        return fail(SLORA_E_INVAL, "mfma_shrink_rows must be 16, 32, 48 or 64");
+      p->tune.mfma_shrink_rows = value;
       return SLORA_OK;
     default:
       return fail(SLORA_E_INVAL, "slora_pool_set_tuning: unknown key");
@@ -759,24 +766,33 @@ slora_status slora_segments_upload(slora_segments* s, void* dev_meta, size_t dev
   return SLORA_OK;
 }
 
-slora_status slora_lora_delta(slora_pool* p, const slora_segments* s, int32_t proj, const void* x, void* y,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (!p || !s) return fail(SLORA_E_INVAL, "slora_lora_delta: NULL pool or segments");
-  if (s->pool != p) return fail(SLORA_E_INVAL, "slora_lora_delta: segments belong to another pool");
-  if (proj < 0 || proj >= p->d.n_proj) return fail(SLORA_E_INVAL, "slora_lora_delta: proj out of range");
+}  // extern "C"
+
+namespace {
+
+slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_segments* s,
+                        int32_t proj, const void* x, void* y, const void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const std::string f(fn);
+  if (!p || !s) return fail(SLORA_E_INVAL, f + ": NULL pool or segments");
+  if (s->pool != p) return fail(SLORA_E_INVAL, f + ": segments belong to another pool");
+  if (proj < 0 || proj >= p->d.n_proj) return fail(SLORA_E_INVAL, f + ": proj out of range");
   const int32_t S = (int32_t)s->seg_adapter.size();
   for (int32_t g = 0; g < S; ++g) {
     const AdapterRec& rec = p->adapters[s->seg_adapter[g]];
     if (!rec.loaded || rec.gen != s->seg_gen[g])
-      return fail(SLORA_E_STALE, "slora_lora_delta: adapter " + std::to_string(s->seg_adapter[g]) +
+      return fail(SLORA_E_STALE, f + ": adapter " + std::to_string(s->seg_adapter[g]) +
                                      " changed since the segments were built");
   }
   if (s->perm.empty()) return SLORA_OK;
-  if (!x || !y || !workspace) return fail(SLORA_E_INVAL, "slora_lora_delta: NULL x, y or workspace");
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(workspace)) & 15)
-    return fail(SLORA_E_INVAL, "slora_lora_delta: x, y and workspace must be 16-byte aligned");
-  if (workspace_bytes < (size_t)s->sum_rt * sizeof(float)) return fail(SLORA_E_NOMEM, "slora_lora_delta: workspace smaller than workspace_bytes");
-  if (!s->dev_meta) return fail(SLORA_E_INVAL, "slora_lora_delta: segments not uploaded (call slora_segments_upload)");
+  if (((stages & STAGE_SHRINK) && !x) || ((stages & STAGE_EXPAND) && !y) || !workspace)
+    return fail(SLORA_E_INVAL, f + ": NULL x, y or workspace");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(SLORA_E_INVAL, f + ": x, y and workspace must be 16-byte aligned");
+  if (workspace_bytes < (size_t)s->sum_rt * sizeof(float))
+    return fail(SLORA_E_NOMEM, f + ": workspace smaller than workspace_bytes");
+  if (!s->dev_meta) return fail(SLORA_E_INVAL, f + ": segments not uploaded (call slora_segments_upload)");
   slora_status st = set_device(p);
   if (st != SLORA_OK) return st;
   DeltaLaunch L{};
@@ -790,7 +806,7 @@ slora_status slora_lora_delta(slora_pool* p, const slora_segments* s, int32_t pr
   L.proj = proj;
   L.x = x;
   L.y = y;
-  L.v = static_cast<float*>(workspace);
+  L.v = static_cast<float*>(const_cast<void*>(workspace));
   L.shrink_rec = s->dev_meta;
   L.shrink_stride = s->shrink_stride;
   L.shrink_tokcap = s->shrink_tokcap;
@@ -802,9 +818,31 @@ slora_status slora_lora_delta(slora_pool* p, const slora_segments* s, int32_t pr
   L.expand_pagecap = s->expand_pagecap;
   L.n_expand = s->n_expand;
   L.gemv_rows = s->gemv_rows;
-  hipError_t e = launch_delta(L, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "slora_lora_delta launch");
+  hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
   return SLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+slora_status slora_lora_delta(slora_pool* p, const slora_segments* s, int32_t proj, const void* x, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return run_stages("slora_lora_delta", STAGE_SHRINK | STAGE_EXPAND, p, s, proj, x, y, workspace,
+                    workspace_bytes, stream);
+}
+
+slora_status slora_lora_shrink(slora_pool* p, const slora_segments* s, int32_t proj, const void* x,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return run_stages("slora_lora_shrink", STAGE_SHRINK, p, s, proj, x, nullptr, workspace,
+                    workspace_bytes, stream);
+}
+
+slora_status slora_lora_expand(slora_pool* p, const slora_segments* s, int32_t proj, void* y,
+                               const void* workspace, size_t workspace_bytes, void* stream) {
+  return run_stages("slora_lora_expand", STAGE_EXPAND, p, s, proj, nullptr, y, workspace,
+                    workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -58,8 +58,9 @@ struct DeltaLaunch {
   int32_t gemv_rows;      // rank rows per GEMV shrink tile (host choice)
 };
 
-// Launch the shrink kernel then the expand kernel on `stream`.
-hipError_t launch_delta(const DeltaLaunch& L, hipStream_t stream);
+// Launch the shrink kernel (stages & 1) then the expand kernel (stages & 2) on `stream`.
+enum : int { STAGE_SHRINK = 1, STAGE_EXPAND = 2 };
+hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream);
 
 // Copy n_rows rows of row_bytes from src (device, packed) into the pages
 // page_ids[i] of the class at base with page_bytes stride.

@@ -125,46 +125,70 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&p)[N], int lane) {
   return p[0];
 }
 
+
+// Values every lane of a wavefront holds alike (tile header fields, the wave
+// index) are moved to scalar registers.  Control flow on them then branches
+// instead of masking lanes, which matters for MFMA: a matrix instruction runs
+// on the whole wavefront whatever the EXEC mask says, so it must never sit
+// behind a lane mask to be skipped.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Copy the part of a tile record this launch needs (header, tokens and the
+// page list of projection `proj`) into LDS with one batch of independent
+// loads, so that page ids and token ids come from LDS instead of a chain of
+// dependent global loads.  Layout in LDS: [HDR][tokcap][pagecap].
+constexpr int kMaxRecWords = REC_HDR + 16 + 256;
+
+__device__ __forceinline__ void record_to_lds(const int32_t* rec, int tokcap, int pagecap, int proj,
+                                              int32_t* srec) {
+  const int head = REC_HDR + tokcap;
+  const int n = head + pagecap;
+  for (int i = threadIdx.x; i < n; i += kThreads) srec[i] = rec[i < head ? i : i + proj * pagecap];
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Shrink, vector-ALU tile: up to kGemvMaxTok tokens x RB rank rows, whole h_in.
 // Thread tid owns the 16-byte chunks tid, tid+256, ... of every row; the A^T
 // rows stay in registers while each token's x chunks are dotted against them.
 
 template <typename T, int NCK>
-__device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float* red) {
+__device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
   constexpr int VEC = VecN<T>::N;
   constexpr int RB = kShrinkRowBudget / NCK;
   constexpr int TB = kGemvMaxTok;
-  const int ntok = rec[REC_NTOK];
-  const int rank = rec[REC_RANK];
-  const int j0 = rec[REC_POS];
-  const int nrows = rec[REC_LEN];
-  const int v0 = rec[REC_V0];
-  const int32_t* toks = rec + REC_HDR;
-  const int32_t* pages = rec + REC_HDR + L.shrink_tokcap + L.proj * L.shrink_pagecap;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntok = uni(srec[REC_NTOK]);
+  const int rank = uni(srec[REC_RANK]);
+  const int j0 = uni(srec[REC_POS]);
+  const int nrows = uni(srec[REC_LEN]);
+  const int v0 = uni(srec[REC_V0]);
+  const int32_t* toks = srec + REC_HDR;
+  const int32_t* pages = srec + REC_HDR + L.shrink_tokcap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int nchunks = L.h_in / VEC;
   const T* x = reinterpret_cast<const T*>(L.x);
 
+  // All row and token addresses first, then every load of the tile in one batch.
+  const char* arow[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+    arow[r] = L.pool.base_a + (int64_t)pages[r < nrows ? r : 0] * L.pool.page_bytes_a;
+  const T* xrow[TB];
+#pragma unroll
+  for (int k = 0; k < TB; ++k) xrow[k] = x + (int64_t)toks[k < ntok ? k : 0] * L.h_in;
+
   uint4 a[RB][NCK];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const char* row = L.pool.base_a + (int64_t)pages[r < nrows ? r : 0] * L.pool.page_bytes_a;
-#pragma unroll
-    for (int ck = 0; ck < NCK; ++ck) {
-      const int c = tid + ck * kThreads;
-      a[r][ck] = (r < nrows && c < nchunks) ? ld16(row + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
-    }
-  }
   uint4 xv[TB][NCK];
 #pragma unroll
-  for (int k = 0; k < TB; ++k) {
-    const T* xr = x + (int64_t)toks[k < ntok ? k : 0] * L.h_in;
+  for (int ck = 0; ck < NCK; ++ck) {
+    const int c = tid + ck * kThreads;
+    const bool inb = c < nchunks;
 #pragma unroll
-    for (int ck = 0; ck < NCK; ++ck) {
-      const int c = tid + ck * kThreads;
-      xv[k][ck] = (k < ntok && c < nchunks) ? ld16(xr + (int64_t)c * VEC) : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < RB; ++r)
+      a[r][ck] = (inb && r < nrows) ? ld16(arow[r] + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < TB; ++k)
+      xv[k][ck] = (inb && k < ntok) ? ld16(xrow[k] + (int64_t)c * VEC) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int k = 0; k < TB; ++k) {
@@ -198,15 +222,15 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float
 // four waves take interleaved 32-wide k steps and are summed through LDS.
 
 template <int NB>
-__device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float* red) {
-  const int ntok = rec[REC_NTOK];
-  const int rank = rec[REC_RANK];
-  const int j0 = rec[REC_POS];
-  const int nrows = rec[REC_LEN];
-  const int v0 = rec[REC_V0];
-  const int32_t* toks = rec + REC_HDR;
-  const int32_t* pages = rec + REC_HDR + L.shrink_tokcap + L.proj * L.shrink_pagecap;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
+  const int ntok = uni(srec[REC_NTOK]);
+  const int rank = uni(srec[REC_RANK]);
+  const int j0 = uni(srec[REC_POS]);
+  const int nrows = uni(srec[REC_LEN]);
+  const int v0 = uni(srec[REC_V0]);
+  const int32_t* toks = srec + REC_HDR;
+  const int32_t* pages = srec + REC_HDR + L.shrink_tokcap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
 
   // Rows past ntok / nrows repeat the last valid row (same cache lines); their
@@ -224,16 +248,47 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  const int n_it = (L.h_in - wave * 32 + 127) >> 7;  // this wave's 32-wide k steps
-#pragma unroll 4
-  for (int it = 0; it < n_it; ++it) {
-    const int k = wave * 32 + it * 128;
-    const half8 xa = __builtin_bit_cast(half8, ld16(xrow + k));
+  // Wave w takes the 32-wide k steps w, w+4, w+8, ...; two register stages of
+  // two steps each keep the next steps' loads in flight while the current
+  // ones feed the matrix cores.
+  const int n_it = (L.h_in - wave * 32 + 127) >> 7;
+  constexpr int U = 2;
+  const half8 zero8 = {};
+  half8 xs0[U], as0[U][NB], xs1[U], as1[U][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const half8 ab = __builtin_bit_cast(half8, ld16(arow[b] + k));
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ab, acc[b], 0, 0, 0);
+  for (int u = 0; u < U; ++u) {   // a step past n_it could only ever add zero
+    xs0[u] = zero8;
+    xs1[u] = zero8;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) as0[u][b] = as1[u][b] = zero8;
+  }
+  auto load = [&](half8 (&xs)[U], half8 (&as)[U][NB], int it0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (it0 + u < n_it) {
+        const int k = wave * 32 + (it0 + u) * 128;
+        xs[u] = __builtin_bit_cast(half8, ld16(xrow + k));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) as[u][b] = __builtin_bit_cast(half8, ld16(arow[b] + k));
+      }
     }
+  };
+  auto mma = [&](half8 (&xs)[U], half8 (&as)[U][NB], int it0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (it0 + u < n_it) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xs[u], as[u][b], acc[b], 0, 0, 0);
+      }
+    }
+  };
+  load(xs0, as0, 0);
+  for (int it = 0; it < n_it; it += 2 * U) {
+    load(xs1, as1, it + U);
+    mma(xs0, as0, it);
+    load(xs0, as0, it + 2 * U);
+    mma(xs1, as1, it + U);
   }
   // acc[b][i] is C[token 4g + i][rank row b*16 + l%16]; sum the four waves in LDS.
 #pragma unroll
@@ -255,19 +310,21 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float
 template <typename T, int NCK>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
   __shared__ float red[4 * 4 * 16 * 16];  // MFMA: 4 waves x 4 blocks x 16 x 16
+  __shared__ int32_t srec[REC_HDR + 16 + kMfmaMaxRows];
   const int32_t* rec = L.shrink_rec + (int64_t)blockIdx.x * L.shrink_stride;
+  record_to_lds(rec, L.shrink_tokcap, L.shrink_pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
-    if (rec[REC_KIND] == KIND_MFMA) {
-      switch ((rec[REC_LEN] + 15) >> 4) {
-        case 1: shrink_mfma_tile<1>(L, rec, red); break;
-        case 2: shrink_mfma_tile<2>(L, rec, red); break;
-        case 3: shrink_mfma_tile<3>(L, rec, red); break;
-        default: shrink_mfma_tile<4>(L, rec, red); break;
+    if (uni(srec[REC_KIND]) == KIND_MFMA) {
+      switch ((uni(srec[REC_LEN]) + 15) >> 4) {
+        case 1: shrink_mfma_tile<1>(L, srec, red); break;
+        case 2: shrink_mfma_tile<2>(L, srec, red); break;
+        case 3: shrink_mfma_tile<3>(L, srec, red); break;
+        default: shrink_mfma_tile<4>(L, srec, red); break;
       }
       return;
     }
   }
-  shrink_gemv_tile<T, NCK>(L, rec, red);
+  shrink_gemv_tile<T, NCK>(L, srec, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -277,18 +334,19 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
 // sums meet in LDS and group 0 applies y += s * d with one rounding.
 
 template <typename T>
-__device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float* lds) {
+__device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   constexpr int VEC = VecN<T>::N;
   constexpr int TB = kGemvMaxTok;
-  const int ntok = rec[REC_NTOK];
-  const int rank = rec[REC_RANK];
-  const int o0 = rec[REC_POS];
-  const int ncol = rec[REC_LEN];
-  const int v0 = rec[REC_V0];
-  const float scale = __int_as_float(rec[REC_SCALE]);
-  const int width = rec[REC_AUX];
-  const int32_t* toks = rec + REC_HDR;
-  const int32_t* pages = rec + REC_HDR + L.expand_tokcap + L.proj * L.expand_pagecap;
+  constexpr int RCH = 16;  // B rows per thread issued together
+  const int ntok = uni(srec[REC_NTOK]);
+  const int rank = uni(srec[REC_RANK]);
+  const int o0 = uni(srec[REC_POS]);
+  const int ncol = uni(srec[REC_LEN]);
+  const int v0 = uni(srec[REC_V0]);
+  const float scale = __int_as_float(uni(srec[REC_SCALE]));
+  const int width = uni(srec[REC_AUX]);
+  const int32_t* toks = srec + REC_HDR;
+  const int32_t* pages = srec + REC_HDR + L.expand_tokcap;
   const int tid = threadIdx.x;
   const int nct = width / VEC;
   const int G = kThreads / nct;
@@ -296,48 +354,61 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float
 
   float* sv = lds;                   // [TB][rank] v of the tile's tokens
   float* part = lds + TB * 256;      // [G-1][TB][nct][VEC] partial sums of groups 1..G-1
-  for (int i = tid; i < ntok * rank; i += kThreads) sv[i] = L.v[v0 + i];
+  T* y = reinterpret_cast<T*>(L.y);
+
+  // Issue everything the tile reads before waiting on any of it: v, the first
+  // RCH B rows of this thread, and (group 0) the y chunks of the epilogue.
+  float vreg[TB];
+#pragma unroll
+  for (int q = 0; q < TB; ++q) {
+    const int i = tid + q * kThreads;
+    vreg[q] = i < ntok * rank ? L.v[v0 + i] : 0.f;
+  }
+  const bool active = ct * VEC < ncol;
+  const int nrt = (active && g < rank) ? (rank - g + G - 1) / G : 0;   // rows of this thread
+  const int64_t col_byte = (int64_t)(o0 + ct * VEC) * sizeof(T);
+  uint4 bq[RCH];
+#pragma unroll
+  for (int i = 0; i < RCH; ++i)
+    bq[i] = i < nrt ? ld16(L.pool.base_b + (int64_t)pages[g + i * G] * L.pool.page_bytes_b + col_byte)
+                    : make_uint4(0, 0, 0, 0);
+  uint4 yv[TB];
+#pragma unroll
+  for (int k = 0; k < TB; ++k)
+    yv[k] = (g == 0 && active && k < ntok) ? ld16(y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC)
+                                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < TB; ++q) {
+    const int i = tid + q * kThreads;
+    if (i < ntok * rank) sv[i] = vreg[q];
+  }
   __syncthreads();
 
-  const bool active = ct * VEC < ncol;
-  const int64_t col_byte = (int64_t)(o0 + ct * VEC) * sizeof(T);
   float acc[TB][VEC];
 #pragma unroll
   for (int k = 0; k < TB; ++k)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[k][e] = 0.f;
-
-  if (active) {
-    int j = g;
-    for (; j + 3 * G < rank; j += 4 * G) {
-      uint4 bq[4];
+  for (int i0 = 0; i0 < nrt; i0 += RCH) {
+    if (i0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        bq[u] = ld16(L.pool.base_b + (int64_t)pages[j + u * G] * L.pool.page_bytes_b + col_byte);
+      for (int i = 0; i < RCH; ++i)
+        bq[i] = i0 + i < nrt ? ld16(L.pool.base_b + (int64_t)pages[g + (i0 + i) * G] * L.pool.page_bytes_b + col_byte)
+                             : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int i = 0; i < RCH; ++i) {
+      if (i0 + i < nrt) {
+        const int j = g + (i0 + i) * G;
         float bf[VEC];
-        to_float(bq[u], bf, T());
+        to_float(bq[i], bf, T());
 #pragma unroll
         for (int k = 0; k < TB; ++k) {
           if (k < ntok) {
-            const float vk = sv[k * rank + j + u * G];
+            const float vk = sv[k * rank + j];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[k][e] = fmaf(vk, bf[e], acc[k][e]);
           }
-        }
-      }
-    }
-    for (; j < rank; j += G) {
-      const uint4 b = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + col_byte);
-      float bf[VEC];
-      to_float(b, bf, T());
-#pragma unroll
-      for (int k = 0; k < TB; ++k) {
-        if (k < ntok) {
-          const float vk = sv[k * rank + j];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[k][e] = fmaf(vk, bf[e], acc[k][e]);
         }
       }
     }
@@ -368,7 +439,6 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float
     }
   }
   if (g == 0 && active) {
-    T* y = reinterpret_cast<T*>(L.y);
 #pragma unroll
     for (int k = 0; k < TB; ++k) {
       if (k < ntok) {
@@ -376,7 +446,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* rec, float
         float d[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) d[e] = scale * acc[k][e];
-        st16(yp, add_round(ld16(yp), d, T()));
+        st16(yp, add_round(yv[k], d, T()));
       }
     }
   }
@@ -396,19 +466,21 @@ constexpr int kMfmaPitchH = kMfmaCols + 16;    // halves per staged B row
 constexpr int kMfmaEpiPitch = kMfmaCols + 4;   // floats per epilogue row
 constexpr int kMaxRankMfma = 256;
 
-__device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float* lds) {
-  const int ntok = rec[REC_NTOK];
-  const int rank = rec[REC_RANK];
-  const int o0 = rec[REC_POS];
-  const int ncol = rec[REC_LEN];
-  const int v0 = rec[REC_V0];
-  const float scale = __int_as_float(rec[REC_SCALE]);
-  const int32_t* toks = rec + REC_HDR;
-  const int32_t* pages = rec + REC_HDR + L.expand_tokcap + L.proj * L.expand_pagecap;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
+  const int ntok = uni(srec[REC_NTOK]);
+  const int rank = uni(srec[REC_RANK]);
+  const int o0 = uni(srec[REC_POS]);
+  const int ncol = uni(srec[REC_LEN]);
+  const int v0 = uni(srec[REC_V0]);
+  const float scale = __int_as_float(uni(srec[REC_SCALE]));
+  const int32_t* toks = srec + REC_HDR;
+  const int32_t* pages = srec + REC_HDR + L.expand_tokcap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int ks_n = (rank + 31) >> 5;
   const int vp = ks_n * 32 + 4;                       // sv pitch (floats)
+  const int n_pass = (ncol + kMfmaCols - 1) / kMfmaCols;
+  const int n_steps = n_pass * ks_n;                  // (pass, k slice), pass-major
 
   // LDS: sv [16][vp] floats, reused as the epilogue buffer [16][kMfmaEpiPitch];
   // then the staged B slice [32][kMfmaPitchH] halves; then a reduction slot.
@@ -416,6 +488,24 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float
   float* epi = lds;
   _Float16* sb = reinterpret_cast<_Float16*>(lds + 16 * (kMaxRankMfma + 4));
   float* wmax = lds + 16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2;
+  _Float16* yb = reinterpret_cast<_Float16*>(L.y);
+
+  // Thread tid stages chunks tid + 256q (q < 4) of a 32 x 256 slice of B.
+  auto stage_load = [&](int step, uint4 (&r)[4]) {
+    const int pass = step / ks_n, ks = step - pass * ks_n;
+    const int c0 = pass * kMfmaCols;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = tid + q * kThreads;
+      const int jr = chunk >> 5, cc = (chunk & 31) * 8;
+      const int j = 32 * ks + jr;
+      r[q] = (j < rank && c0 + cc < ncol)
+                 ? ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)(o0 + c0 + cc) * 2)
+                 : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 bnext[4];
+  stage_load(0, bnext);
 
   // s * v of the tile, zero outside ntok x rank, and its largest magnitude.
   float amax = 0.f;
@@ -442,6 +532,8 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float
   half8 vhi[kMaxRankMfma / 32], vlo[kMaxRankMfma / 32];
 #pragma unroll
   for (int ks = 0; ks < kMaxRankMfma / 32; ++ks) {
+    vhi[ks] = half8{};
+    vlo[ks] = half8{};
     if (ks < ks_n) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -454,27 +546,31 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float
   }
   __syncthreads();  // sv is dead from here; its space becomes the epilogue buffer
 
-  _Float16* yb = reinterpret_cast<_Float16*>(L.y);
-  for (int c0 = 0; c0 < ncol; c0 += kMfmaCols) {
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int c0 = pass * kMfmaCols;
+    // this pass's y chunks, fetched while the k slices run
+    uint4 yq[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int chunk = tid + q * kThreads;          // 16 rows x 32 chunks of 8
+      const int mm = chunk >> 5, cc = (chunk & 31) * 8;
+      yq[q] = (mm < ntok && c0 + cc < ncol) ? ld16(yb + (int64_t)toks[mm] * L.h_out + o0 + c0 + cc)
+                                             : make_uint4(0, 0, 0, 0);
+    }
     float4v acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kMaxRankMfma / 32; ++ks) {
       if (ks >= ks_n) break;
-      // stage rows 32ks..32ks+31, columns o0+c0 .. +256 (zeros outside r x h_out)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int chunk = tid + q * kThreads;        // 1024 chunks of 8 halves
-        const int jr = chunk >> 5, cc = (chunk & 31) * 8;
-        const int j = 32 * ks + jr;
-        const int col = o0 + c0 + cc;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (j < rank && c0 + cc < ncol)
-          val = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)col * 2);
-        st16(sb + jr * kMfmaPitchH + cc, val);
+        const int chunk = tid + q * kThreads;
+        st16(sb + (chunk >> 5) * kMfmaPitchH + (chunk & 31) * 8, bnext[q]);
       }
       __syncthreads();
+      const int step = pass * ks_n + ks;
+      if (step + 1 < n_steps) stage_load(step + 1, bnext);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int n = wave * 64 + c * 16 + m;
@@ -494,14 +590,14 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* rec, float
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int chunk = tid + q * kThreads;          // 16 rows x 32 chunks of 8
+      const int chunk = tid + q * kThreads;
       const int mm = chunk >> 5, cc = (chunk & 31) * 8;
       if (mm < ntok && c0 + cc < ncol) {
         _Float16* yp = yb + (int64_t)toks[mm] * L.h_out + o0 + c0 + cc;
         float d[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) d[e] = epi[mm * kMfmaEpiPitch + cc + e];
-        st16(yp, add_round(ld16(yp), d, _Float16()));
+        st16(yp, add_round(yq[q], d, _Float16()));
       }
     }
     __syncthreads();
@@ -516,14 +612,16 @@ constexpr int kExpandLdsFloats =
 template <typename T>
 __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
   __shared__ float lds[kExpandLdsFloats];
+  __shared__ int32_t srec[kMaxRecWords];
   const int32_t* rec = L.expand_rec + (int64_t)blockIdx.x * L.expand_stride;
+  record_to_lds(rec, L.expand_tokcap, L.expand_pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
-    if (rec[REC_KIND] == KIND_MFMA) {
-      expand_mfma_tile(L, rec, lds);
+    if (uni(srec[REC_KIND]) == KIND_MFMA) {
+      expand_mfma_tile(L, srec, lds);
       return;
     }
   }
-  expand_gemv_tile<T>(L, rec, lds);
+  expand_gemv_tile<T>(L, srec, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -541,13 +639,13 @@ static hipError_t launch_shrink_t(const DeltaLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_delta(const DeltaLaunch& L, hipStream_t stream) {
+hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream) {
   hipError_t e = hipSuccess;
-  if (L.n_shrink > 0) {
+  if ((stages & STAGE_SHRINK) && L.n_shrink > 0) {
     e = L.dtype == 1 ? launch_shrink_t<_Float16>(L, stream) : launch_shrink_t<float>(L, stream);
     if (e != hipSuccess) return e;
   }
-  if (L.n_expand > 0) {
+  if ((stages & STAGE_EXPAND) && L.n_expand > 0) {
     const dim3 grid(L.n_expand), block(kThreads);
     if (L.dtype == 1) expand_kernel<_Float16><<<grid, block, 0, stream>>>(L);
     else expand_kernel<float><<<grid, block, 0, stream>>>(L);

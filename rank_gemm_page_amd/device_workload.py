@@ -78,6 +78,32 @@ class DeviceWorkload:
         S.slora_lora_delta(self.pool, self.seg, proj, x, self.y[proj] if y is None else y,
                            self.workspace, self.info["workspace_bytes"], stream)
 
+    def shrink(self, proj=0, stream=None):
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        S.slora_lora_shrink(self.pool, self.seg, proj, self.x[self.w.spec.proj_x[proj]],
+                            self.workspace, self.info["workspace_bytes"], stream)
+
+    def expand(self, proj=0, y=None, stream=None):
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        S.slora_lora_expand(self.pool, self.seg, proj, self.y[proj] if y is None else y,
+                            self.workspace, self.info["workspace_bytes"], stream)
+
+    def algorithmic_bytes(self, proj=0):
+        """(shrink, expand) bytes one projection must move: each distinct adapter's
+        pages once, x once (shrink), y read and written (expand)."""
+        spec, w = self.w.spec, self.w
+        e = 2 if spec.dtype == "f16" else 4
+        r_u = int(self.info["sum_rank"])
+        routed = int(self.info["n_routed"])
+        shrink = r_u * spec.h_in * e + routed * spec.h_in * e
+        expand = r_u * spec.h_out * e + 2 * routed * spec.h_out * e
+        return shrink, expand
+
+    def algorithmic_flops(self, proj=0):
+        spec = self.w.spec
+        rt = int(self.info["sum_rank_tokens"])
+        return 2 * rt * spec.h_in, 2 * rt * spec.h_out
+
     def reset_y(self):
         for y, y0 in zip(self.y, self.y0):
             y.copy_(y0)

@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "SLORA_OK", -1: "SLORA_E_INVAL", -2: "SLORA_E_NOMEM", -3: "SL
                 -4: "SLORA_E_NOENT", -5: "SLORA_E_STALE", -6: "SLORA_E_HIP"}
 SLORA_F32, SLORA_F16 = 0, 1
 SLORA_TUNE_MFMA_MIN_TOKENS, SLORA_TUNE_GEMV_EXPAND_ELEMS, SLORA_TUNE_MFMA_EXPAND_COLS = 0, 1, 2
+SLORA_TUNE_MFMA_SHRINK_ROWS = 3
 
 EXPORTED = [
     "slora_pool_create", "slora_pool_destroy", "slora_pool_set_tuning", "slora_alloc_pages",
@@ -31,7 +32,7 @@ EXPORTED = [
     "slora_adapter_pages", "slora_build_segments", "slora_segments_destroy",
     "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
     "slora_segments_upload",
-    "slora_lora_delta", "slora_last_error",
+    "slora_lora_delta", "slora_lora_shrink", "slora_lora_expand", "slora_last_error",
 ]
 
 
@@ -86,6 +87,8 @@ def lib():
             "slora_segments_tiles": (c_int32, [P, POINTER(c_int32), POINTER(c_int32), c_size_t]),
             "slora_segments_upload": (c_int32, [P, P, c_size_t, P]),
             "slora_lora_delta": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
+            "slora_lora_shrink": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
+            "slora_lora_expand": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -272,3 +275,13 @@ def slora_segments_upload(seg, dev_meta, dev_meta_bytes: int, stream=None) -> No
 def slora_lora_delta(pool, seg, proj: int, x, y, workspace, workspace_bytes: int, stream=None) -> None:
     _check(lib().slora_lora_delta(pool, seg, proj, _ptr(x), _ptr(y), _ptr(workspace),
                                   int(workspace_bytes), _stream(stream)), "slora_lora_delta")
+
+
+def slora_lora_shrink(pool, seg, proj: int, x, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().slora_lora_shrink(pool, seg, proj, _ptr(x), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream)), "slora_lora_shrink")
+
+
+def slora_lora_expand(pool, seg, proj: int, y, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().slora_lora_expand(pool, seg, proj, _ptr(y), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream)), "slora_lora_expand")

@@ -356,3 +356,12 @@ def test_unload_reload_lands_on_other_pages():
         assert set(a1.tolist() + b1.tolist()).isdisjoint(a2.tolist() + b2.tolist())
     finally:
         S.slora_pool_destroy(pool)
+
+
+def test_no_mfma_under_partial_exec_mask(tmp_path):
+    """Every matrix instruction sits in wave-uniform control flow (see build.masked_mfma_lines)."""
+    from rank_gemm_page_amd import build
+    asm = build.device_assembly(str(tmp_path))
+    with open(asm) as f:
+        assert sum(1 for line in f if line.strip().startswith("v_mfma")) > 0
+    assert build.masked_mfma_lines(asm) == []
