@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--gemv-expand-elems", type=int, default=None)
     ap.add_argument("--mfma-expand-cols", type=int, default=None)
     ap.add_argument("--mfma-shrink-rows", type=int, default=None)
+    ap.add_argument("--staged", action="store_true",
+                    help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain copy of this size (PMC calibration runs)")
     args = ap.parse_args()
@@ -167,10 +169,13 @@ def main():
         for p in range(n_proj):
             if events is not None:
                 events[p][0].record(stream)
-            dw.shrink(p, stream=stream)
-            if events is not None:
-                events[p][1].record(stream)
-            dw.expand(p, stream=stream)
+            if args.staged:
+                dw.shrink(p, stream=stream)
+                if events is not None:
+                    events[p][1].record(stream)
+                dw.expand(p, stream=stream)
+            else:
+                dw.delta(p, stream=stream)   # one fused launch per projection
             if events is not None:
                 events[p][2].record(stream)
 
@@ -191,11 +196,13 @@ def main():
     wall = time.perf_counter() - t0
     log(f"[bench] {K} timed steps done in {wall * 1e3:.1f} ms wall (flushes included)")
 
-    shrink_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][1]) for p in range(n_proj)) for k in range(K)]
-    expand_ms = [sum(ev[k][p][1].elapsed_time(ev[k][p][2]) for p in range(n_proj)) for k in range(K)]
     step_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][2]) for p in range(n_proj)) for k in range(K)]
     ms = statistics.fmean(step_ms)
-    sh_ms, ex_ms = statistics.fmean(shrink_ms), statistics.fmean(expand_ms)
+    if args.staged:
+        sh_ms = statistics.fmean(sum(ev[k][p][0].elapsed_time(ev[k][p][1]) for p in range(n_proj))
+                                 for k in range(K))
+        ex_ms = ms - sh_ms
+    assert S.slora_segments_read_error(dw.seg, stream) == 0, "a fused launch gave up waiting"
 
     # Host segment build and metadata upload, timed apart (PCIe-inclusive figures).
     ids = w.ids
@@ -230,9 +237,14 @@ def main():
     # per step: each projection moves its own pages and y; x counted once per launch
     bytes_shrink, bytes_expand = n_proj * sb, n_proj * eb
     flops = n_proj * (sf + ef)
-    dominant = "shrink_kernel" if sh_ms >= ex_ms else "expand_kernel"
-    dom_ms = max(sh_ms, ex_ms) / n_proj
-    dom_bytes = sb if dominant == "shrink_kernel" else eb
+    if args.staged:
+        dominant = "shrink_kernel" if sh_ms >= ex_ms else "expand_kernel"
+        dom_ms = max(sh_ms, ex_ms) / n_proj
+        dom_bytes = sb if dominant == "shrink_kernel" else eb
+    else:
+        dominant = "fused_kernel"
+        dom_ms = ms / n_proj
+        dom_bytes = sb + eb
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(args.config, dominant)
     tokens = int(info["n_routed"])
@@ -262,10 +274,12 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3)},
-        "kernels": {"shrink_us": round(sh_ms * 1e3 / n_proj, 3),
-                    "expand_us": round(ex_ms * 1e3 / n_proj, 3),
-                    "shrink_GBps": round(sb / (sh_ms / n_proj * 1e-3) / 1e9, 1),
-                    "expand_GBps": round(eb / (ex_ms / n_proj * 1e-3) / 1e9, 1),
+        "kernels": {**({"shrink_us": round(sh_ms * 1e3 / n_proj, 3),
+                        "expand_us": round(ex_ms * 1e3 / n_proj, 3),
+                        "shrink_GBps": round(sb / (sh_ms / n_proj * 1e-3) / 1e9, 1),
+                        "expand_GBps": round(eb / (ex_ms / n_proj * 1e-3) / 1e9, 1)}
+                       if args.staged else {"launch": "fused (one kernel per projection)",
+                                            "fused_us": round(ms * 1e3 / n_proj, 3)}),
                     "step_GBps": round((bytes_shrink + bytes_expand) / (ms * 1e-3) / 1e9, 1),
                     "step_frac_hbm_peak": round((bytes_shrink + bytes_expand) / (ms * 1e-3) / 1e9
                                                 / HBM_PEAK_GBPS, 4),

@@ -94,12 +94,17 @@ void slora_pool_destroy(slora_pool* pool);
  *                                of 256; default 512.
  *  SLORA_TUNE_MFMA_SHRINK_ROWS - rank rows of one MFMA shrink tile, a
  *                                multiple of 16 up to 64; default 64.
+ *  SLORA_TUNE_FUSED            - 1 (default): slora_lora_delta runs both
+ *                                stages in one launch, each expand tile
+ *                                waiting for its segment's shrink tiles;
+ *                                0: two launches (shrink, then expand).
  * They change how the work is cut, never what is computed. */
 typedef enum {
   SLORA_TUNE_MFMA_MIN_TOKENS = 0,
   SLORA_TUNE_GEMV_EXPAND_ELEMS = 1,
   SLORA_TUNE_MFMA_EXPAND_COLS = 2,
-  SLORA_TUNE_MFMA_SHRINK_ROWS = 3
+  SLORA_TUNE_MFMA_SHRINK_ROWS = 3,
+  SLORA_TUNE_FUSED = 4
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 
@@ -173,24 +178,27 @@ slora_status slora_segments_export(const slora_segments* seg, int32_t* perm, int
                                    int32_t* seg_adapter, int32_t* seg_rank, float* seg_scale,
                                    int32_t* seg_page_off, int32_t* a_pages, int32_t* b_pages);
 
-/* Introspection of the work split (host copies): layout[8] receives
+/* Introspection of the work split (host copies): layout[9] receives
  * {n_shrink_tiles, shrink_stride, shrink_tokcap, shrink_pagecap,
- *  n_expand_tiles, expand_stride, expand_tokcap, expand_pagecap} and, when
- * records is not NULL and holds at least meta_bytes / 4 words, the tile
+ *  n_expand_tiles, expand_stride, expand_tokcap, expand_pagecap, hdr} and,
+ * when records is not NULL and holds at least meta_bytes / 4 words, the tile
  * records: n_shrink_tiles records of shrink_stride int32 words, then the
  * expand records.  Record words: 0 kind (0 vector ALU, 1 MFMA), 1 token count,
  * 2 segment rank, 3 first rank row (shrink) or first column (expand), 4 rows
  * or columns covered, 5 workspace offset of the first token's v row, 6 scale
- * (float bits), 7 expand thread-map width; then tokcap batch indices of the
- * tokens, then per projection pagecap page ids (shrink: the rows covered;
- * expand: all rank B rows).  For tests and tools; the layout may change. */
+ * (float bits), 7 expand thread-map width, 8 segment index, 9 (expand) shrink
+ * tiles of the segment; from word hdr, tokcap batch indices of the tokens,
+ * then per projection pagecap page ids (shrink: the rows covered; expand: all
+ * rank B rows).  For tests and tools; the layout may change. */
 slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, int32_t* records,
                                   size_t records_words);
 
 /* Copy the tile metadata to caller-owned device memory dev_meta (at least
  * meta_bytes, 16-byte aligned) on `stream` and remember that address for
  * later deltas.  The copy is asynchronous; dev_meta must stay untouched while
- * deltas that use it are in flight. */
+ * deltas that use it are in flight.  The metadata also holds per-segment
+ * completion counters used by the fused launch (the copy resets them), so
+ * every slora_lora_delta that uses one upload must be ordered on one stream. */
 slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t dev_meta_bytes,
                                    void* stream);
 
@@ -208,6 +216,12 @@ slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t d
 slora_status slora_lora_delta(slora_pool* pool, const slora_segments* seg, int32_t proj,
                               const void* x, void* y, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Reads (synchronously, on `stream`) whether any fused launch since the last
+ * upload gave up waiting for a segment's shrink tiles: *flag = 1 if so, which
+ * would mean its results are wrong; 0 otherwise.  A wait gives up only after
+ * about 2^21 polls, so a healthy GPU never raises it. */
+slora_status slora_segments_read_error(const slora_segments* seg, void* stream, int32_t* flag);
 
 /* The two stages of slora_lora_delta, for callers that schedule or time them
  * apart: slora_lora_shrink writes v = x A (fp32) for every routed token into

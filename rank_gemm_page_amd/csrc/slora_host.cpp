@@ -84,6 +84,7 @@ struct Tuning {
   int64_t gemv_expand_elems = 32768;
   int64_t mfma_expand_cols = 512;
   int64_t mfma_shrink_rows = kMfmaMaxRows;
+  int64_t fused = 1;
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -143,8 +144,10 @@ struct slora_segments {
   int32_t shrink_stride = 0, shrink_tokcap = 0, shrink_pagecap = 0;
   int32_t expand_stride = 0, expand_tokcap = 0, expand_pagecap = 0;
   int64_t expand_off_words = 0;
+  int64_t counter_off_words = 0;   // S per-segment completion counters, then one error word
   int32_t gemv_rows = 0;
   const int32_t* dev_meta = nullptr;
+  mutable uint32_t epoch = 0;      // fused launches since the last upload
 };
 
 namespace {
@@ -310,6 +313,8 @@ void build_tiles(slora_segments* s) {
   std::stable_sort(sh.begin(), sh.end(), heavier_first);
   std::stable_sort(ex.begin(), ex.end(), heavier_first);
 
+  std::vector<int32_t> shrink_tiles_of(S, 0);
+  for (const TileSpec& t : sh) ++shrink_tiles_of[t.seg];
   const int np = s->n_proj;
   s->shrink_tokcap = std::max(kGemvMaxTok, kMfmaTok);
   s->shrink_pagecap = std::max(gemv_rows, kMfmaMaxRows);
@@ -320,7 +325,8 @@ void build_tiles(slora_segments* s) {
   s->n_shrink = (int32_t)sh.size();
   s->n_expand = (int32_t)ex.size();
   s->expand_off_words = (int64_t)s->n_shrink * s->shrink_stride;
-  s->blob.assign((size_t)s->expand_off_words + (size_t)s->n_expand * s->expand_stride, 0);
+  s->counter_off_words = s->expand_off_words + (int64_t)s->n_expand * s->expand_stride;
+  s->blob.assign((size_t)s->counter_off_words + (size_t)((S + 1 + 3) & ~3), 0);
 
   auto fill = [&](int32_t* rec, const TileSpec& t, int32_t tokcap, int32_t pagecap, bool shrink) {
     const int32_t g = t.seg;
@@ -334,6 +340,8 @@ void build_tiles(slora_segments* s) {
     float sc = s->seg_scale[g];
     std::memcpy(&rec[REC_SCALE], &sc, 4);
     rec[REC_AUX] = t.aux;
+    rec[REC_SEG] = g;
+    rec[REC_WAIT] = shrink_tiles_of[g];
     const int32_t first = s->seg_start[g] + t.i0;
     for (int32_t k = 0; k < t.ntok; ++k) rec[REC_HDR + k] = s->perm[first + k];
     for (int pr = 0; pr < np; ++pr) {
@@ -455,6 +463,10 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       if (value < kMfmaCols || value % kMfmaCols || value > 65536)
         return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 256, at most 65536");
       p->tune.mfma_expand_cols = value;
+      return SLORA_OK;
+    case SLORA_TUNE_FUSED:
+      if (value != 0 && value != 1) return fail(SLORA_E_INVAL, "fused must be 0 or 1");
+      p->tune.fused = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_SHRINK_ROWS:
       if (value < 16 || value > kMfmaMaxRows || value % 16)
@@ -717,12 +729,13 @@ slora_status slora_segments_export(const slora_segments* s, int32_t* perm, int32
 slora_status slora_segments_tiles(const slora_segments* s, int32_t* layout, int32_t* records,
                                   size_t records_words) {
   if (!s || !layout) return fail(SLORA_E_INVAL, "slora_segments_tiles: NULL argument");
-  const int32_t lay[8] = {s->n_shrink, s->shrink_stride, s->shrink_tokcap, s->shrink_pagecap,
-                          s->n_expand, s->expand_stride, s->expand_tokcap, s->expand_pagecap};
+  const int32_t lay[9] = {s->n_shrink, s->shrink_stride, s->shrink_tokcap, s->shrink_pagecap,
+                          s->n_expand, s->expand_stride, s->expand_tokcap, s->expand_pagecap, REC_HDR};
   std::memcpy(layout, lay, sizeof(lay));
   if (records) {
-    if (records_words < s->blob.size()) return fail(SLORA_E_NOMEM, "slora_segments_tiles: records buffer too small");
-    std::memcpy(records, s->blob.data(), s->blob.size() * sizeof(int32_t));
+    const size_t words = (size_t)s->counter_off_words;
+    if (records_words < words) return fail(SLORA_E_NOMEM, "slora_segments_tiles: records buffer too small");
+    std::memcpy(records, s->blob.data(), words * sizeof(int32_t));
   }
   return SLORA_OK;
 }
@@ -763,6 +776,21 @@ slora_status slora_segments_upload(slora_segments* s, void* dev_meta, size_t dev
     p->meta_slot ^= 1;
   }
   s->dev_meta = static_cast<const int32_t*>(dev_meta);
+  s->epoch = 0;   // the copy above reset the device counters to zero
+  return SLORA_OK;
+}
+
+slora_status slora_segments_read_error(const slora_segments* s, void* stream, int32_t* flag) {
+  if (!s || !flag) return fail(SLORA_E_INVAL, "slora_segments_read_error: NULL argument");
+  *flag = 0;
+  if (!s->dev_meta || s->blob.empty()) return SLORA_OK;
+  slora_status st = set_device(s->pool);
+  if (st != SLORA_OK) return st;
+  const int32_t* src = s->dev_meta + s->counter_off_words + s->seg_adapter.size();
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(flag, src, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e, "slora_segments_read_error");
   return SLORA_OK;
 }
 
@@ -818,6 +846,12 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.expand_pagecap = s->expand_pagecap;
   L.n_expand = s->n_expand;
   L.gemv_rows = s->gemv_rows;
+  L.counters = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->counter_off_words));
+  L.error_flag = L.counters + s->seg_adapter.size();
+  if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
+    stages = STAGE_FUSED;
+    L.epoch = ++s->epoch;
+  }
   hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
   return SLORA_OK;

@@ -17,6 +17,9 @@ namespace slora {
 //   [5] v0          workspace offset of the tile's first token's v row
 //   [6] scale       the segment's scale, float bits
 //   [7] aux         expand GEMV: nominal column width of the tile (thread map)
+//   [8] seg         index of the tile's segment (its completion counter)
+//   [9] wait        expand: shrink tiles of the segment a fused launch waits for
+//   [10..11]        reserved
 //   [HDR .. HDR+tokcap)                   batch indices of the tokens
 //   [HDR+tokcap + p*pagecap .. +npages)   page ids of projection p: shrink
 //                                         holds the A^T pages of rows
@@ -24,7 +27,7 @@ namespace slora {
 // Records of one kernel share one stride (a multiple of 4 words).
 enum : int32_t {
   REC_KIND = 0, REC_NTOK = 1, REC_RANK = 2, REC_POS = 3, REC_LEN = 4,
-  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_HDR = 8
+  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_SEG = 8, REC_WAIT = 9, REC_HDR = 12
 };
 enum : int32_t { KIND_GEMV = 0, KIND_MFMA = 1 };
 
@@ -56,10 +59,18 @@ struct DeltaLaunch {
   const int32_t* expand_rec;
   int32_t expand_stride, expand_tokcap, expand_pagecap, n_expand;
   int32_t gemv_rows;      // rank rows per GEMV shrink tile (host choice)
+  // fused launch: per-segment completion counters (cumulative over launches
+  // since the metadata upload), the launch's epoch (1, 2, ... per upload) and
+  // a flag raised if a wait gave up
+  uint32_t* counters;
+  uint32_t* error_flag;
+  uint32_t epoch;
 };
 
-// Launch the shrink kernel (stages & 1) then the expand kernel (stages & 2) on `stream`.
-enum : int { STAGE_SHRINK = 1, STAGE_EXPAND = 2 };
+// Launch the shrink kernel (stages & 1) then the expand kernel (stages & 2) on
+// `stream`, or both in one launch (STAGE_FUSED) in which each expand tile waits
+// for the shrink tiles of its segment.
+enum : int { STAGE_SHRINK = 1, STAGE_EXPAND = 2, STAGE_FUSED = 4 };
 hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream);
 
 // Copy n_rows rows of row_bytes from src (device, packed) into the pages

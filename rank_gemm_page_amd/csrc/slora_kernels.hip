@@ -147,12 +147,67 @@ __device__ __forceinline__ void record_to_lds(const int32_t* rec, int tokcap, in
   __syncthreads();
 }
 
+// Fused launch: the shrink tiles of segment s each add 1 to counters[s] once
+// their v values are stored, and an expand tile of s waits until the counter
+// reaches epoch * (shrink tiles of s) before it reads v.
+//
+// Ordering without cache-wide fences: in a fused launch v is written and read
+// only with agent-scope atomic accesses, which are coherent across the XCDs by
+// themselves (they never leave dirty or stale copies in an XCD's L2).  Each
+// producer thread waits for its v stores to complete (s_waitcnt 0) before the
+// workgroup barrier, and only then does one thread increment the counter; a
+// consumer issues its v loads only after one of its threads has observed the
+// count and the workgroup has passed a barrier.  A release/acquire fence pair
+// would do the same but writes back and invalidates the whole L2 of the XCD
+// on every tile.
+//
+// Progress: shrink tiles occupy the lower block indices and never wait, and
+// workgroups are dispatched in index order, so every shrink tile a waiting
+// expand tile depends on has been dispatched and finishes.  The wait is
+// bounded all the same: past kMaxSpins polls it raises error_flag and goes on,
+// so every wave of the grid always exits.
+constexpr uint32_t kMaxSpins = 1u << 21;
+
+template <bool FUSED>
+__device__ __forceinline__ void store_v(float* p, float x) {
+  if constexpr (FUSED) __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = x;
+}
+template <bool FUSED>
+__device__ __forceinline__ float load_v(const float* p) {
+  if constexpr (FUSED) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
+__device__ __forceinline__ void signal_segment(const DeltaLaunch& L, int seg) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's v stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(L.counters + seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_segment(const DeltaLaunch& L, int seg, int n_wait) {
+  if (threadIdx.x == 0) {
+    const uint32_t target = L.epoch * (uint32_t)n_wait;
+    for (uint32_t spins = 0;; ++spins) {
+      const uint32_t now = __hip_atomic_load(L.counters + seg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int32_t)(now - target) >= 0) break;
+      if (spins >= kMaxSpins) {
+        __hip_atomic_store(L.error_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Shrink, vector-ALU tile: up to kGemvMaxTok tokens x RB rank rows, whole h_in.
 // Thread tid owns the 16-byte chunks tid, tid+256, ... of every row; the A^T
 // rows stay in registers while each token's x chunks are dotted against them.
 
-template <typename T, int NCK>
+template <typename T, int NCK, bool FUSED>
 __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
   constexpr int VEC = VecN<T>::N;
   constexpr int RB = kShrinkRowBudget / NCK;
@@ -211,8 +266,9 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     const int k = i / nrows, r = i - k * nrows;
     const float* q = red + (k * 4) * RB + r;
     const float sum = ((q[0] + q[RB]) + q[2 * RB]) + q[3 * RB];
-    L.v[v0 + (int64_t)k * rank + j0 + r] = sum;
+    store_v<FUSED>(L.v + v0 + (int64_t)k * rank + j0 + r, sum);
   }
+  if constexpr (FUSED) signal_segment(L, uni(srec[REC_SEG]));
 }
 
 // ---------------------------------------------------------------------------
@@ -221,7 +277,7 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 // row m = l%16 of X and row n = l%16 of A^T, 8 consecutive k at 8*(l/16); the
 // four waves take interleaved 32-wide k steps and are summed through LDS.
 
-template <int NB>
+template <int NB, bool FUSED>
 __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
@@ -303,7 +359,18 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) sum += red[((w * 4 + b) * 16 + mm) * 16 + n];
-    L.v[v0 + (int64_t)mm * rank + j0 + j] = sum;
+    store_v<FUSED>(L.v + v0 + (int64_t)mm * rank + j0 + j, sum);
+  }
+  if constexpr (FUSED) signal_segment(L, uni(srec[REC_SEG]));
+}
+
+template <bool FUSED>
+__device__ __forceinline__ void shrink_mfma_dispatch(const DeltaLaunch& L, const int32_t* srec, float* red) {
+  switch ((uni(srec[REC_LEN]) + 15) >> 4) {
+    case 1: shrink_mfma_tile<1, FUSED>(L, srec, red); break;
+    case 2: shrink_mfma_tile<2, FUSED>(L, srec, red); break;
+    case 3: shrink_mfma_tile<3, FUSED>(L, srec, red); break;
+    default: shrink_mfma_tile<4, FUSED>(L, srec, red); break;
   }
 }
 
@@ -315,16 +382,11 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
   record_to_lds(rec, L.shrink_tokcap, L.shrink_pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
     if (uni(srec[REC_KIND]) == KIND_MFMA) {
-      switch ((uni(srec[REC_LEN]) + 15) >> 4) {
-        case 1: shrink_mfma_tile<1>(L, srec, red); break;
-        case 2: shrink_mfma_tile<2>(L, srec, red); break;
-        case 3: shrink_mfma_tile<3>(L, srec, red); break;
-        default: shrink_mfma_tile<4>(L, srec, red); break;
-      }
+      shrink_mfma_dispatch<false>(L, srec, red);
       return;
     }
   }
-  shrink_gemv_tile<T, NCK>(L, srec, red);
+  shrink_gemv_tile<T, NCK, false>(L, srec, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -333,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
 // G = 256 / (width/VEC) groups of them split the r rows; the groups' partial
 // sums meet in LDS and group 0 applies y += s * d with one rounding.
 
-template <typename T>
+template <typename T, bool FUSED>
 __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   constexpr int VEC = VecN<T>::N;
   constexpr int TB = kGemvMaxTok;
@@ -356,14 +418,9 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   float* part = lds + TB * 256;      // [G-1][TB][nct][VEC] partial sums of groups 1..G-1
   T* y = reinterpret_cast<T*>(L.y);
 
-  // Issue everything the tile reads before waiting on any of it: v, the first
-  // RCH B rows of this thread, and (group 0) the y chunks of the epilogue.
-  float vreg[TB];
-#pragma unroll
-  for (int q = 0; q < TB; ++q) {
-    const int i = tid + q * kThreads;
-    vreg[q] = i < ntok * rank ? L.v[v0 + i] : 0.f;
-  }
+  // Issue everything the tile reads before waiting on any of it: the first
+  // RCH B rows of this thread, (group 0) the y chunks of the epilogue, and v
+  // (in a fused launch, once the segment's shrink tiles are done).
   const bool active = ct * VEC < ncol;
   const int nrt = (active && g < rank) ? (rank - g + G - 1) / G : 0;   // rows of this thread
   const int64_t col_byte = (int64_t)(o0 + ct * VEC) * sizeof(T);
@@ -377,6 +434,13 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   for (int k = 0; k < TB; ++k)
     yv[k] = (g == 0 && active && k < ntok) ? ld16(y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC)
                                            : make_uint4(0, 0, 0, 0);
+  if constexpr (FUSED) wait_segment(L, uni(srec[REC_SEG]), uni(srec[REC_WAIT]));
+  float vreg[TB];
+#pragma unroll
+  for (int q = 0; q < TB; ++q) {
+    const int i = tid + q * kThreads;
+    vreg[q] = i < ntok * rank ? load_v<FUSED>(L.v + v0 + i) : 0.f;
+  }
 #pragma unroll
   for (int q = 0; q < TB; ++q) {
     const int i = tid + q * kThreads;
@@ -466,6 +530,7 @@ constexpr int kMfmaPitchH = kMfmaCols + 16;    // halves per staged B row
 constexpr int kMfmaEpiPitch = kMfmaCols + 4;   // floats per epilogue row
 constexpr int kMaxRankMfma = 256;
 
+template <bool FUSED>
 __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
@@ -506,13 +571,14 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   };
   uint4 bnext[4];
   stage_load(0, bnext);
+  if constexpr (FUSED) wait_segment(L, uni(srec[REC_SEG]), uni(srec[REC_WAIT]));
 
   // s * v of the tile, zero outside ntok x rank, and its largest magnitude.
   float amax = 0.f;
   for (int i = tid; i < 16 * ks_n * 32; i += kThreads) {
     const int mm = i / (ks_n * 32), j = i - mm * (ks_n * 32);
     float val = 0.f;
-    if (mm < ntok && j < rank) val = scale * L.v[v0 + (int64_t)mm * rank + j];
+    if (mm < ntok && j < rank) val = scale * load_v<FUSED>(L.v + v0 + (int64_t)mm * rank + j);
     sv[mm * vp + j] = val;
     amax = fmaxf(amax, fabsf(val));
   }
@@ -617,11 +683,41 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
   record_to_lds(rec, L.expand_tokcap, L.expand_pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
     if (uni(srec[REC_KIND]) == KIND_MFMA) {
-      expand_mfma_tile(L, srec, lds);
+      expand_mfma_tile<false>(L, srec, lds);
       return;
     }
   }
-  expand_gemv_tile<T>(L, srec, lds);
+  expand_gemv_tile<T, false>(L, srec, lds);
+}
+
+// Both stages in one launch: blocks [0, n_shrink) run shrink tiles, the rest
+// expand tiles that wait for their segment (see signal_segment/wait_segment).
+template <typename T, int NCK>
+__global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
+  __shared__ float lds[kExpandLdsFloats];
+  __shared__ int32_t srec[kMaxRecWords];
+  const int b = blockIdx.x;
+  if (b < L.n_shrink) {
+    record_to_lds(L.shrink_rec + (int64_t)b * L.shrink_stride, L.shrink_tokcap, L.shrink_pagecap,
+                  L.proj, srec);
+    if constexpr (sizeof(T) == 2) {
+      if (uni(srec[REC_KIND]) == KIND_MFMA) {
+        shrink_mfma_dispatch<true>(L, srec, lds);
+        return;
+      }
+    }
+    shrink_gemv_tile<T, NCK, true>(L, srec, lds);
+    return;
+  }
+  record_to_lds(L.expand_rec + (int64_t)(b - L.n_shrink) * L.expand_stride, L.expand_tokcap,
+                L.expand_pagecap, L.proj, srec);
+  if constexpr (sizeof(T) == 2) {
+    if (uni(srec[REC_KIND]) == KIND_MFMA) {
+      expand_mfma_tile<true>(L, srec, lds);
+      return;
+    }
+  }
+  expand_gemv_tile<T, true>(L, srec, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -639,8 +735,25 @@ static hipError_t launch_shrink_t(const DeltaLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_fused_t(const DeltaLaunch& L, hipStream_t stream) {
+  constexpr int VEC = VecN<T>::N;
+  const int per_thread = (L.h_in / VEC + kThreads - 1) / kThreads;
+  const dim3 grid(L.n_shrink + L.n_expand), block(kThreads);
+  if (per_thread <= 1) fused_kernel<T, 1><<<grid, block, 0, stream>>>(L);
+  else if (per_thread <= 2) fused_kernel<T, 2><<<grid, block, 0, stream>>>(L);
+  else if (per_thread <= 4) fused_kernel<T, 4><<<grid, block, 0, stream>>>(L);
+  else if (per_thread <= 8) fused_kernel<T, 8><<<grid, block, 0, stream>>>(L);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  if (stages & STAGE_FUSED) {
+    if (L.n_shrink + L.n_expand == 0) return hipSuccess;
+    return L.dtype == 1 ? launch_fused_t<_Float16>(L, stream) : launch_fused_t<float>(L, stream);
+  }
   if ((stages & STAGE_SHRINK) && L.n_shrink > 0) {
     e = L.dtype == 1 ? launch_shrink_t<_Float16>(L, stream) : launch_shrink_t<float>(L, stream);
     if (e != hipSuccess) return e;

@@ -24,14 +24,14 @@ STATUS_NAMES = {0: "SLORA_OK", -1: "SLORA_E_INVAL", -2: "SLORA_E_NOMEM", -3: "SL
                 -4: "SLORA_E_NOENT", -5: "SLORA_E_STALE", -6: "SLORA_E_HIP"}
 SLORA_F32, SLORA_F16 = 0, 1
 SLORA_TUNE_MFMA_MIN_TOKENS, SLORA_TUNE_GEMV_EXPAND_ELEMS, SLORA_TUNE_MFMA_EXPAND_COLS = 0, 1, 2
-SLORA_TUNE_MFMA_SHRINK_ROWS = 3
+SLORA_TUNE_MFMA_SHRINK_ROWS, SLORA_TUNE_FUSED = 3, 4
 
 EXPORTED = [
     "slora_pool_create", "slora_pool_destroy", "slora_pool_set_tuning", "slora_alloc_pages",
     "slora_free_pages", "slora_free_count", "slora_load_adapter", "slora_unload_adapter",
     "slora_adapter_pages", "slora_build_segments", "slora_segments_destroy",
     "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
-    "slora_segments_upload",
+    "slora_segments_upload", "slora_segments_read_error",
     "slora_lora_delta", "slora_lora_shrink", "slora_lora_expand", "slora_last_error",
 ]
 
@@ -86,6 +86,7 @@ def lib():
                                       [POINTER(c_int32)] * 3),
             "slora_segments_tiles": (c_int32, [P, POINTER(c_int32), POINTER(c_int32), c_size_t]),
             "slora_segments_upload": (c_int32, [P, P, c_size_t, P]),
+            "slora_segments_read_error": (c_int32, [P, P, POINTER(c_int32)]),
             "slora_lora_delta": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
             "slora_lora_shrink": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_lora_expand": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
@@ -253,12 +254,12 @@ def slora_segments_tiles(seg):
     """(layout dict, shrink records [n, stride], expand records [n, stride]) as int32 arrays."""
     info = slora_segments_get_info(seg)
     words = info["meta_bytes"] // 4
-    lay = np.empty(8, np.int32)
+    lay = np.empty(9, np.int32)
     rec = np.zeros(max(words, 4), np.int32)
     _check(lib().slora_segments_tiles(seg, _i32p(lay), _i32p(rec), rec.shape[0]),
            "slora_segments_tiles")
     keys = ["n_shrink", "shrink_stride", "shrink_tokcap", "shrink_pagecap", "n_expand",
-            "expand_stride", "expand_tokcap", "expand_pagecap"]
+            "expand_stride", "expand_tokcap", "expand_pagecap", "hdr"]
     layout = dict(zip(keys, (int(v) for v in lay)))
     ns, ss = layout["n_shrink"], layout["shrink_stride"]
     ne, es = layout["n_expand"], layout["expand_stride"]
@@ -270,6 +271,13 @@ def slora_segments_tiles(seg):
 def slora_segments_upload(seg, dev_meta, dev_meta_bytes: int, stream=None) -> None:
     _check(lib().slora_segments_upload(seg, _ptr(dev_meta), int(dev_meta_bytes), _stream(stream)),
            "slora_segments_upload")
+
+
+def slora_segments_read_error(seg, stream=None) -> int:
+    flag = c_int32()
+    _check(lib().slora_segments_read_error(seg, _stream(stream), ctypes.byref(flag)),
+           "slora_segments_read_error")
+    return int(flag.value)
 
 
 def slora_lora_delta(pool, seg, proj: int, x, y, workspace, workspace_bytes: int, stream=None) -> None:

@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 ROUTES = {"gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
           "mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1},
           "default": {}}
+LAUNCH = {"fused": {S.SLORA_TUNE_FUSED: 1}, "two": {S.SLORA_TUNE_FUSED: 0}}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,10 +32,11 @@ def _gpu():
     S.lib()
 
 
-def run_gpu(w, route="default", tuning=None, projs=None, free_order=None):
+def run_gpu(w, route="default", tuning=None, projs=None, free_order=None, launch="fused"):
     if free_order is not None:
         w.free_order = free_order
     t = dict(ROUTES[route])
+    t.update(LAUNCH[launch])
     t.update(tuning or {})
     print(f"[gpu] {w.spec.name} seed={w.seed} route={route} T={w.T}", flush=True)
     dw = DeviceWorkload(w, "cuda:0", tuning=t)
@@ -45,6 +47,7 @@ def run_gpu(w, route="default", tuning=None, projs=None, free_order=None):
         torch.cuda.synchronize()
         for p in projs if projs is not None else range(w.spec.n_proj):
             out.append(dw.y[p].cpu().numpy())
+        assert S.slora_segments_read_error(dw.seg) == 0
         return out, dw.info
     finally:
         dw.close()
@@ -80,9 +83,10 @@ SMALL = [
 
 @pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
 @pytest.mark.parametrize("route", list(ROUTES))
-def test_small_shapes(spec, route):
+@pytest.mark.parametrize("launch", list(LAUNCH))
+def test_small_shapes(spec, route, launch):
     w = generate(spec, 1)
-    ys, info = run_gpu(w, route)
+    ys, info = run_gpu(w, route, launch=launch)
     if route == "mfma" and spec.dtype == "f16" and spec.h_in % 32 == 0:
         assert info["n_mfma_segments"] == info["n_segments"]
     for p, y in enumerate(ys):
@@ -122,16 +126,29 @@ def test_page_permutation_invariance_bit_exact():
 
 @pytest.mark.parametrize("route", ["gemv", "mfma"])
 def test_deterministic_run_to_run(route):
+    """Same result bit for bit from repeated fused launches on one upload (epochs
+    1, 2, 3, ...), after a re-upload (epoch reset), from two launches and from
+    the two stage entry points."""
     spec = small_spec("det", h_in=1024, h_out=1024, n_adapters=6, batch=("zipf", 70, 1.0))
     w = generate(spec, 3)
     dw = DeviceWorkload(w, "cuda:0", tuning=ROUTES[route])
     try:
         res = []
-        for _ in range(3):
+
+        def run(fn):
             dw.reset_y()
-            dw.delta(0)
+            fn()
             torch.cuda.synchronize()
             res.append(dw.y[0].cpu().numpy().view(np.uint16).copy())
+
+        for _ in range(3):
+            run(lambda: dw.delta(0))
+        dw.upload()
+        run(lambda: dw.delta(0))
+        run(lambda: (dw.shrink(0), dw.expand(0)))
+        S.slora_pool_set_tuning(dw.pool, S.SLORA_TUNE_FUSED, 0)
+        run(lambda: dw.delta(0))
+        assert S.slora_segments_read_error(dw.seg) == 0
         assert all(np.array_equal(res[0], r) for r in res[1:])
     finally:
         dw.close()

@@ -143,26 +143,31 @@ def check_tiles_cover(w, pool, ids):
             kind, ntok, r, j0, nrows, v0 = (int(v) for v in rec[:6])
             assert kind in (0, 1) and 1 <= ntok <= lay["shrink_tokcap"] and nrows >= 1
             assert (kind == 1) <= (spec.dtype == "f16")
-            toks = rec[8:8 + ntok]
+            hdr = lay["hdr"]
+            toks = rec[hdr:hdr + ntok]
             s, _ = seg_of[int(toks[0])]
+            assert rec[8] == s
             assert r == ex["seg_rank"][s] and 0 <= j0 and j0 + nrows <= r
             for k, t in enumerate(toks):
                 assert seg_of[int(t)][0] == s
                 assert v_row[int(t)] == v0 + k * r
                 shrink_seen[v_row[int(t)] + j0:v_row[int(t)] + j0 + nrows] += 1
             for p in range(spec.n_proj):
-                pg = rec[8 + lay["shrink_tokcap"] + p * lay["shrink_pagecap"]:][:nrows]
+                pg = rec[hdr + lay["shrink_tokcap"] + p * lay["shrink_pagecap"]:][:nrows]
                 base = p * info["sum_rank"] + ex["seg_page_off"][s]
                 np.testing.assert_array_equal(pg, ex["a_pages"][base + j0:base + j0 + nrows])
         assert (shrink_seen[:off] == 1).all()
+        n_shrink_of = np.bincount(sh[:, 8], minlength=n_seg) if len(sh) else np.zeros(n_seg, int)
         routed = [t for t in range(len(ids)) if ids[t] >= 0]
         cover = {t: np.zeros(spec.h_out, np.int32) for t in routed}
         for rec in exp:
             kind, ntok, r, o0, ncol, v0 = (int(v) for v in rec[:6])
             assert 1 <= ntok <= lay["expand_tokcap"] and o0 % 8 == 0 and ncol % 8 == 0
             assert 0 <= o0 and o0 + ncol <= spec.h_out
-            toks = rec[8:8 + ntok]
+            hdr = lay["hdr"]
+            toks = rec[hdr:hdr + ntok]
             s, _ = seg_of[int(toks[0])]
+            assert rec[8] == s and rec[9] == n_shrink_of[s] > 0
             assert np.float32(rec[6:7].view(np.float32)[0]) == ex["seg_scale"][s]
             for k, t in enumerate(toks):
                 assert seg_of[int(t)][0] == s and v_row[int(t)] == v0 + k * r
@@ -172,7 +177,7 @@ def check_tiles_cover(w, pool, ids):
                 vec = 8 if spec.dtype == "f16" else 4
                 assert width % vec == 0 and 256 % (width // vec) == 0 and ncol <= width
             for p in range(spec.n_proj):
-                pg = rec[8 + lay["expand_tokcap"] + p * lay["expand_pagecap"]:][:r]
+                pg = rec[hdr + lay["expand_tokcap"] + p * lay["expand_pagecap"]:][:r]
                 base = p * info["sum_rank"] + ex["seg_page_off"][s]
                 np.testing.assert_array_equal(pg, ex["b_pages"][base:base + r])
         for t in routed:
@@ -339,6 +344,7 @@ def test_tuning_validation():
         assert status_of(S.slora_pool_set_tuning, pool, 0, 0) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, 2, 300) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, 9, 1) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FUSED, 2) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, 2, 1024)
     finally:
         S.slora_pool_destroy(pool)
