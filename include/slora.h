@@ -87,13 +87,13 @@ void slora_pool_destroy(slora_pool* pool);
 
 /* Tuning knobs of the tile builder (applied by later slora_build_segments):
  *  SLORA_TUNE_MFMA_MIN_TOKENS  - fp16 segments with at least this many tokens
- *                                use the matrix-core (MFMA) tiles; default 16.
+ *                                use the matrix-core (MFMA) tiles; default 64.
  *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
  *                                expand tile; default 32768.
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
- *                                of 256; default 512.
+ *                                of 256; default 1024.
  *  SLORA_TUNE_MFMA_SHRINK_ROWS - rank rows of one MFMA shrink tile, a
- *                                multiple of 16 up to 64; default 64.
+ *                                multiple of 16 up to 64; default 32.
  *  SLORA_TUNE_FUSED            - 1 (default): slora_lora_delta runs both
  *                                stages in one launch, each expand tile
  *                                waiting for its segment's shrink tiles;
@@ -216,6 +216,16 @@ slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t d
 slora_status slora_lora_delta(slora_pool* pool, const slora_segments* seg, int32_t proj,
                               const void* x, void* y, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* slora_lora_delta with timing: the caller's HIP events (hipEvent_t as void*,
+ * created with timing enabled; either may be NULL) are recorded by the kernel
+ * dispatch itself, start when its first kernel begins and stop when its last
+ * kernel ends, so hipEventElapsedTime gives the kernels' own duration without
+ * the queue overhead of a separate hipEventRecord.  With no routed tokens
+ * nothing is launched and the events are not recorded. */
+slora_status slora_lora_delta_timed(slora_pool* pool, const slora_segments* seg, int32_t proj,
+                                    const void* x, void* y, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* start_event, void* stop_event);
 
 /* Reads (synchronously, on `stream`) whether any fused launch since the last
  * upload gave up waiting for a segment's shrink tiles: *flag = 1 if so, which

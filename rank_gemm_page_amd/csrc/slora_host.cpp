@@ -79,11 +79,14 @@ struct AdapterRec {
   std::vector<int32_t> b_pages;  // [n_proj][rank]
 };
 
+// Defaults chosen by measurement on MI355X (decode, prefill and 70B-MLP
+// shapes): segments below 64 tokens stream faster through the vector-ALU
+// tiles, which cut their work finer; long segments need the matrix cores.
 struct Tuning {
-  int64_t mfma_min_tokens = 16;
+  int64_t mfma_min_tokens = 64;
   int64_t gemv_expand_elems = 32768;
-  int64_t mfma_expand_cols = 512;
-  int64_t mfma_shrink_rows = kMfmaMaxRows;
+  int64_t mfma_expand_cols = 1024;
+  int64_t mfma_shrink_rows = 32;
   int64_t fused = 1;
 };
 
@@ -800,7 +803,8 @@ namespace {
 
 slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_segments* s,
                         int32_t proj, const void* x, void* y, const void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, void* ev_start = nullptr,
+                        void* ev_stop = nullptr) {
   const std::string f(fn);
   if (!p || !s) return fail(SLORA_E_INVAL, f + ": NULL pool or segments");
   if (s->pool != p) return fail(SLORA_E_INVAL, f + ": segments belong to another pool");
@@ -846,13 +850,15 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.expand_pagecap = s->expand_pagecap;
   L.n_expand = s->n_expand;
   L.gemv_rows = s->gemv_rows;
+  L.has_mfma = s->n_mfma_segments > 0;
   L.counters = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->counter_off_words));
   L.error_flag = L.counters + s->seg_adapter.size();
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
     stages = STAGE_FUSED;
     L.epoch = ++s->epoch;
   }
-  hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream),
+                              static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop));
   if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
   return SLORA_OK;
 }
@@ -865,6 +871,13 @@ slora_status slora_lora_delta(slora_pool* p, const slora_segments* s, int32_t pr
                               void* workspace, size_t workspace_bytes, void* stream) {
   return run_stages("slora_lora_delta", STAGE_SHRINK | STAGE_EXPAND, p, s, proj, x, y, workspace,
                     workspace_bytes, stream);
+}
+
+slora_status slora_lora_delta_timed(slora_pool* p, const slora_segments* s, int32_t proj,
+                                    const void* x, void* y, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* ev_start, void* ev_stop) {
+  return run_stages("slora_lora_delta_timed", STAGE_SHRINK | STAGE_EXPAND, p, s, proj, x, y,
+                    workspace, workspace_bytes, stream, ev_start, ev_stop);
 }
 
 slora_status slora_lora_shrink(slora_pool* p, const slora_segments* s, int32_t proj, const void* x,

@@ -59,6 +59,7 @@ struct DeltaLaunch {
   const int32_t* expand_rec;
   int32_t expand_stride, expand_tokcap, expand_pagecap, n_expand;
   int32_t gemv_rows;      // rank rows per GEMV shrink tile (host choice)
+  int32_t has_mfma;       // some tile of this launch is an MFMA tile
   // fused launch: per-segment completion counters (cumulative over launches
   // since the metadata upload), the launch's epoch (1, 2, ... per upload) and
   // a flag raised if a wait gave up
@@ -71,7 +72,10 @@ struct DeltaLaunch {
 // `stream`, or both in one launch (STAGE_FUSED) in which each expand tile waits
 // for the shrink tiles of its segment.
 enum : int { STAGE_SHRINK = 1, STAGE_EXPAND = 2, STAGE_FUSED = 4 };
-hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream);
+// Optional start/stop events are recorded by the dispatch itself (start when
+// the first kernel begins, stop when the last one ends).
+hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Copy n_rows rows of row_bytes from src (device, packed) into the pages
 // page_ids[i] of the class at base with page_bytes stride.

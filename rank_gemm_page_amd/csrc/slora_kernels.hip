@@ -27,6 +27,7 @@
 // Every output element is written by exactly one thread, once, with one
 // rounding; no atomics, so results are deterministic run to run and do not
 // depend on where the pages sit in the pool.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "slora_internal.h"
@@ -399,7 +400,7 @@ template <typename T, bool FUSED>
 __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   constexpr int VEC = VecN<T>::N;
   constexpr int TB = kGemvMaxTok;
-  constexpr int RCH = 16;  // B rows per thread issued together
+  constexpr int RCH = 8;  // B rows per thread issued together
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
   const int o0 = uni(srec[REC_POS]);
@@ -692,7 +693,10 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
 
 // Both stages in one launch: blocks [0, n_shrink) run shrink tiles, the rest
 // expand tiles that wait for their segment (see signal_segment/wait_segment).
-template <typename T, int NCK>
+// MFMA=false leaves the matrix-core tiles out (a batch without them), which
+// keeps the register budget, and so the workgroups resident per CU, of the
+// vector-ALU tiles alone.
+template <typename T, int NCK, bool MFMA>
 __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
   __shared__ float lds[kExpandLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
@@ -700,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
   if (b < L.n_shrink) {
     record_to_lds(L.shrink_rec + (int64_t)b * L.shrink_stride, L.shrink_tokcap, L.shrink_pagecap,
                   L.proj, srec);
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && MFMA) {
       if (uni(srec[REC_KIND]) == KIND_MFMA) {
         shrink_mfma_dispatch<true>(L, srec, lds);
         return;
@@ -711,7 +715,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
   }
   record_to_lds(L.expand_rec + (int64_t)(b - L.n_shrink) * L.expand_stride, L.expand_tokcap,
                 L.expand_pagecap, L.proj, srec);
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2 && MFMA) {
     if (uni(srec[REC_KIND]) == KIND_MFMA) {
       expand_mfma_tile<true>(L, srec, lds);
       return;
@@ -722,49 +726,76 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
 
 // ---------------------------------------------------------------------------
 
+// One launch of `kernel` over `blocks` workgroups; with events, through
+// hipExtLaunchKernel so that the timestamps come from the dispatch itself.
+static hipError_t launch_one(const void* kernel, int blocks, const DeltaLaunch& L, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+  void* args[] = {const_cast<DeltaLaunch*>(&L)};
+  if (!start && !stop)
+    return hipLaunchKernel(kernel, dim3(blocks), dim3(kThreads), args, 0, stream);
+  return hipExtLaunchKernel(kernel, dim3(blocks), dim3(kThreads), args, 0, stream, start, stop, 0);
+}
+
+// Instantiation for the GEMV shrink geometry: 16-byte chunks per thread per
+// row, rounded up to a power of two.
 template <typename T>
-static hipError_t launch_shrink_t(const DeltaLaunch& L, hipStream_t stream) {
-  constexpr int VEC = VecN<T>::N;
-  const int per_thread = (L.h_in / VEC + kThreads - 1) / kThreads;
-  const dim3 grid(L.n_shrink), block(kThreads);
-  if (per_thread <= 1) shrink_kernel<T, 1><<<grid, block, 0, stream>>>(L);
-  else if (per_thread <= 2) shrink_kernel<T, 2><<<grid, block, 0, stream>>>(L);
-  else if (per_thread <= 4) shrink_kernel<T, 4><<<grid, block, 0, stream>>>(L);
-  else if (per_thread <= 8) shrink_kernel<T, 8><<<grid, block, 0, stream>>>(L);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+static int chunks_per_thread(int h_in) {
+  const int per = (h_in / VecN<T>::N + kThreads - 1) / kThreads;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
 }
 
 template <typename T>
-static hipError_t launch_fused_t(const DeltaLaunch& L, hipStream_t stream) {
-  constexpr int VEC = VecN<T>::N;
-  const int per_thread = (L.h_in / VEC + kThreads - 1) / kThreads;
-  const dim3 grid(L.n_shrink + L.n_expand), block(kThreads);
-  if (per_thread <= 1) fused_kernel<T, 1><<<grid, block, 0, stream>>>(L);
-  else if (per_thread <= 2) fused_kernel<T, 2><<<grid, block, 0, stream>>>(L);
-  else if (per_thread <= 4) fused_kernel<T, 4><<<grid, block, 0, stream>>>(L);
-  else if (per_thread <= 8) fused_kernel<T, 8><<<grid, block, 0, stream>>>(L);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream) {
-  hipError_t e = hipSuccess;
-  if (stages & STAGE_FUSED) {
-    if (L.n_shrink + L.n_expand == 0) return hipSuccess;
-    return L.dtype == 1 ? launch_fused_t<_Float16>(L, stream) : launch_fused_t<float>(L, stream);
+static const void* shrink_fn(int nck) {
+  switch (nck) {
+    case 1: return reinterpret_cast<const void*>(&shrink_kernel<T, 1>);
+    case 2: return reinterpret_cast<const void*>(&shrink_kernel<T, 2>);
+    case 4: return reinterpret_cast<const void*>(&shrink_kernel<T, 4>);
+    case 8: return reinterpret_cast<const void*>(&shrink_kernel<T, 8>);
+    default: return nullptr;
   }
-  if ((stages & STAGE_SHRINK) && L.n_shrink > 0) {
-    e = L.dtype == 1 ? launch_shrink_t<_Float16>(L, stream) : launch_shrink_t<float>(L, stream);
+}
+
+template <typename T, bool MFMA>
+static const void* fused_fn(int nck) {
+  switch (nck) {
+    case 1: return reinterpret_cast<const void*>(&fused_kernel<T, 1, MFMA>);
+    case 2: return reinterpret_cast<const void*>(&fused_kernel<T, 2, MFMA>);
+    case 4: return reinterpret_cast<const void*>(&fused_kernel<T, 4, MFMA>);
+    case 8: return reinterpret_cast<const void*>(&fused_kernel<T, 8, MFMA>);
+    default: return nullptr;
+  }
+}
+
+template <typename T>
+static hipError_t launch_delta_t(const DeltaLaunch& L, int stages, hipStream_t stream,
+                                 hipEvent_t start, hipEvent_t stop) {
+  const int nck = chunks_per_thread<T>(L.h_in);
+  if (stages & STAGE_FUSED) {
+    const int blocks = L.n_shrink + L.n_expand;
+    if (blocks == 0) return hipSuccess;
+    const void* k = (sizeof(T) == 2 && L.has_mfma) ? fused_fn<T, true>(nck) : fused_fn<T, false>(nck);
+    if (!k) return hipErrorInvalidValue;
+    return launch_one(k, blocks, L, stream, start, stop);
+  }
+  const bool sh = (stages & STAGE_SHRINK) && L.n_shrink > 0;
+  const bool ex = (stages & STAGE_EXPAND) && L.n_expand > 0;
+  if (sh) {
+    const void* k = shrink_fn<T>(nck);
+    if (!k) return hipErrorInvalidValue;
+    hipError_t e = launch_one(k, L.n_shrink, L, stream, start, ex ? nullptr : stop);
     if (e != hipSuccess) return e;
   }
-  if ((stages & STAGE_EXPAND) && L.n_expand > 0) {
-    const dim3 grid(L.n_expand), block(kThreads);
-    if (L.dtype == 1) expand_kernel<_Float16><<<grid, block, 0, stream>>>(L);
-    else expand_kernel<float><<<grid, block, 0, stream>>>(L);
-    e = hipGetLastError();
+  if (ex) {
+    const void* k = reinterpret_cast<const void*>(&expand_kernel<T>);
+    return launch_one(k, L.n_expand, L, stream, sh ? nullptr : start, stop);
   }
-  return e;
+  return hipSuccess;
+}
+
+hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
+  return L.dtype == 1 ? launch_delta_t<_Float16>(L, stages, stream, start, stop)
+                      : launch_delta_t<float>(L, stages, stream, start, stop);
 }
 
 // ---------------------------------------------------------------------------

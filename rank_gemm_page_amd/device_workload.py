@@ -78,6 +78,13 @@ class DeviceWorkload:
         S.slora_lora_delta(self.pool, self.seg, proj, x, self.y[proj] if y is None else y,
                            self.workspace, self.info["workspace_bytes"], stream)
 
+    def delta_timed(self, proj, start_event, stop_event, stream=None):
+        """delta() with the dispatch recording two raw hipEvent_t handles."""
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        x = self.x[self.w.spec.proj_x[proj]]
+        S.slora_lora_delta_timed(self.pool, self.seg, proj, x, self.y[proj], self.workspace,
+                                 self.info["workspace_bytes"], stream, start_event, stop_event)
+
     def shrink(self, proj=0, stream=None):
         stream = stream or self.torch.cuda.current_stream(self.device)
         S.slora_lora_shrink(self.pool, self.seg, proj, self.x[self.w.spec.proj_x[proj]],

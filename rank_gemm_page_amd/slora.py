@@ -32,7 +32,8 @@ EXPORTED = [
     "slora_adapter_pages", "slora_build_segments", "slora_segments_destroy",
     "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
     "slora_segments_upload", "slora_segments_read_error",
-    "slora_lora_delta", "slora_lora_shrink", "slora_lora_expand", "slora_last_error",
+    "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
+    "slora_last_error",
 ]
 
 
@@ -88,6 +89,7 @@ def lib():
             "slora_segments_upload": (c_int32, [P, P, c_size_t, P]),
             "slora_segments_read_error": (c_int32, [P, P, POINTER(c_int32)]),
             "slora_lora_delta": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
+            "slora_lora_delta_timed": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P, P, P]),
             "slora_lora_shrink": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_lora_expand": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_last_error": (ctypes.c_char_p, []),
@@ -283,6 +285,14 @@ def slora_segments_read_error(seg, stream=None) -> int:
 def slora_lora_delta(pool, seg, proj: int, x, y, workspace, workspace_bytes: int, stream=None) -> None:
     _check(lib().slora_lora_delta(pool, seg, proj, _ptr(x), _ptr(y), _ptr(workspace),
                                   int(workspace_bytes), _stream(stream)), "slora_lora_delta")
+
+
+def slora_lora_delta_timed(pool, seg, proj: int, x, y, workspace, workspace_bytes: int, stream,
+                           start_event: int, stop_event: int) -> None:
+    """start_event / stop_event: raw hipEvent_t handles (ints)."""
+    _check(lib().slora_lora_delta_timed(pool, seg, proj, _ptr(x), _ptr(y), _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream), start_event,
+                                        stop_event), "slora_lora_delta_timed")
 
 
 def slora_lora_shrink(pool, seg, proj: int, x, workspace, workspace_bytes: int, stream=None) -> None:
