@@ -14,7 +14,7 @@ Sources for the shapes and distributions:
     Llama-13B mixed q/k/v/o batch, Llama-70B-width MLP projection) with their
     adapter counts, rank sets, id distributions and pool occupancies.
 
-Readings taken where the sources are silent (each is listed in the design doc):
+Readings taken where the sources are silent:
   * "N(0, 0.02)" is a standard deviation of 0.02, drawn in fp32 and rounded to
     the storage dtype with round-to-nearest-even (numpy ``astype``).
   * x and the base y are N(0, 1) wherever a shape does not say otherwise.
