@@ -96,7 +96,7 @@ void slora_pool_destroy(slora_pool* pool);
  *                                multiple of 16 up to 64; default 32.
  *  SLORA_TUNE_FUSED            - 1 (default): slora_lora_delta runs both
  *                                stages in one launch, each expand tile
- *                                waiting for its segment's shrink tiles;
+ *                                waiting for its tokens' x A values;
  *                                0: two launches (shrink, then expand).
  * They change how the work is cut, never what is computed. */
 typedef enum {
@@ -196,9 +196,10 @@ slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, in
 /* Copy the tile metadata to caller-owned device memory dev_meta (at least
  * meta_bytes, 16-byte aligned) on `stream` and remember that address for
  * later deltas.  The copy is asynchronous; dev_meta must stay untouched while
- * deltas that use it are in flight.  The metadata also holds per-segment
- * completion counters used by the fused launch (the copy resets them), so
- * every slora_lora_delta that uses one upload must be ordered on one stream. */
+ * deltas that use it are in flight.  The metadata also holds the area where
+ * a fused launch passes x A between its stages (the upload zeroes it on
+ * `stream`), so every slora_lora_delta that uses one upload must be ordered
+ * on one stream. */
 slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t dev_meta_bytes,
                                    void* stream);
 
@@ -228,9 +229,9 @@ slora_status slora_lora_delta_timed(slora_pool* pool, const slora_segments* seg,
                                     void* stream, void* start_event, void* stop_event);
 
 /* Reads (synchronously, on `stream`) whether any fused launch since the last
- * upload gave up waiting for a segment's shrink tiles: *flag = 1 if so, which
- * would mean its results are wrong; 0 otherwise.  A wait gives up only after
- * about 2^21 polls, so a healthy GPU never raises it. */
+ * upload gave up waiting for the x A values of its tokens: *flag = 1 if so,
+ * which would mean its results are wrong; 0 otherwise.  A wait gives up only
+ * after about 2^20 polls, so a healthy GPU never raises it. */
 slora_status slora_segments_read_error(const slora_segments* seg, void* stream, int32_t* flag);
 
 /* The two stages of slora_lora_delta, for callers that schedule or time them

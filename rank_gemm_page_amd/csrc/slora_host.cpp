@@ -147,13 +147,21 @@ struct slora_segments {
   int32_t shrink_stride = 0, shrink_tokcap = 0, shrink_pagecap = 0;
   int32_t expand_stride = 0, expand_tokcap = 0, expand_pagecap = 0;
   int64_t expand_off_words = 0;
-  int64_t counter_off_words = 0;   // S per-segment completion counters, then one error word
+  int64_t records_words = 0;       // shrink and expand records (the uploaded part)
+  int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
+  int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
   const int32_t* dev_meta = nullptr;
   mutable uint32_t epoch = 0;      // fused launches since the last upload
 };
 
 namespace {
+
+// Device metadata: the tile records, an error word, then 8 bytes per
+// (token, rank row) of v pairs for the fused launch.
+size_t meta_bytes_of(const slora_segments* s) {
+  return (size_t)(s->vtag_off_words * 4) + (size_t)s->sum_rt * 8;
+}
 
 slora_status set_device(slora_pool* p) {
   int cur = -1;
@@ -328,8 +336,10 @@ void build_tiles(slora_segments* s) {
   s->n_shrink = (int32_t)sh.size();
   s->n_expand = (int32_t)ex.size();
   s->expand_off_words = (int64_t)s->n_shrink * s->shrink_stride;
-  s->counter_off_words = s->expand_off_words + (int64_t)s->n_expand * s->expand_stride;
-  s->blob.assign((size_t)s->counter_off_words + (size_t)((S + 1 + 3) & ~3), 0);
+  s->records_words = s->expand_off_words + (int64_t)s->n_expand * s->expand_stride;
+  s->error_off_words = s->records_words;            // records end 16-byte aligned
+  s->vtag_off_words = s->error_off_words + 4;       // 8-byte pairs, 16-byte aligned
+  s->blob.assign((size_t)s->records_words, 0);
 
   auto fill = [&](int32_t* rec, const TileSpec& t, int32_t tokcap, int32_t pagecap, bool shrink) {
     const int32_t g = t.seg;
@@ -708,7 +718,7 @@ slora_status slora_segments_get_info(const slora_segments* s, slora_segments_inf
   info->n_shrink_tiles = s->n_shrink;
   info->n_expand_tiles = s->n_expand;
   info->n_mfma_segments = s->n_mfma_segments;
-  info->meta_bytes = std::max<size_t>(16, s->blob.size() * sizeof(int32_t));
+  info->meta_bytes = meta_bytes_of(s);
   info->workspace_bytes = std::max<size_t>(16, (size_t)s->sum_rt * sizeof(float));
   return SLORA_OK;
 }
@@ -736,7 +746,7 @@ slora_status slora_segments_tiles(const slora_segments* s, int32_t* layout, int3
                           s->n_expand, s->expand_stride, s->expand_tokcap, s->expand_pagecap, REC_HDR};
   std::memcpy(layout, lay, sizeof(lay));
   if (records) {
-    const size_t words = (size_t)s->counter_off_words;
+    const size_t words = (size_t)s->records_words;
     if (records_words < words) return fail(SLORA_E_NOMEM, "slora_segments_tiles: records buffer too small");
     std::memcpy(records, s->blob.data(), words * sizeof(int32_t));
   }
@@ -747,7 +757,7 @@ slora_status slora_segments_upload(slora_segments* s, void* dev_meta, size_t dev
   if (!s || !dev_meta) return fail(SLORA_E_INVAL, "slora_segments_upload: NULL argument");
   if (reinterpret_cast<uintptr_t>(dev_meta) & 15) return fail(SLORA_E_INVAL, "slora_segments_upload: dev_meta must be 16-byte aligned");
   const size_t bytes = s->blob.size() * sizeof(int32_t);
-  if (dev_meta_bytes < std::max<size_t>(16, bytes)) return fail(SLORA_E_NOMEM, "slora_segments_upload: dev_meta smaller than meta_bytes");
+  if (dev_meta_bytes < meta_bytes_of(s)) return fail(SLORA_E_NOMEM, "slora_segments_upload: dev_meta smaller than meta_bytes");
   slora_pool* p = s->pool;
   if (bytes > 0) {
     slora_status st = set_device(p);
@@ -777,9 +787,13 @@ slora_status slora_segments_upload(slora_segments* s, void* dev_meta, size_t dev
     e = hipEventRecord(p->meta_done[slot], st_);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(metadata)");
     p->meta_slot ^= 1;
+    // error word and v pairs start at zero; fused launches count epochs from 1
+    e = launch_zero_words(static_cast<int32_t*>(dev_meta) + s->error_off_words,
+                          (int64_t)(meta_bytes_of(s) / 4) - s->error_off_words, st_);
+    if (e != hipSuccess) return hip_fail(e, "zeroing the fused-launch area");
   }
   s->dev_meta = static_cast<const int32_t*>(dev_meta);
-  s->epoch = 0;   // the copy above reset the device counters to zero
+  s->epoch = 0;
   return SLORA_OK;
 }
 
@@ -789,7 +803,7 @@ slora_status slora_segments_read_error(const slora_segments* s, void* stream, in
   if (!s->dev_meta || s->blob.empty()) return SLORA_OK;
   slora_status st = set_device(s->pool);
   if (st != SLORA_OK) return st;
-  const int32_t* src = s->dev_meta + s->counter_off_words + s->seg_adapter.size();
+  const int32_t* src = s->dev_meta + s->error_off_words;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(flag, src, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
   if (e == hipSuccess) e = hipStreamSynchronize(hs);
@@ -851,10 +865,16 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.n_expand = s->n_expand;
   L.gemv_rows = s->gemv_rows;
   L.has_mfma = s->n_mfma_segments > 0;
-  L.counters = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->counter_off_words));
-  L.error_flag = L.counters + s->seg_adapter.size();
+  L.error_flag = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->error_off_words));
+  L.vtag = reinterpret_cast<unsigned long long*>(const_cast<int32_t*>(s->dev_meta + s->vtag_off_words));
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
     stages = STAGE_FUSED;
+    if (s->epoch == 0xFFFFFFFFu) {   // epochs would wrap to pairs still zero: clear them first
+      hipError_t z = launch_zero_words(const_cast<int32_t*>(s->dev_meta) + s->vtag_off_words,
+                                       (int64_t)s->sum_rt * 2, static_cast<hipStream_t>(stream));
+      if (z != hipSuccess) return hip_fail(z, (f + " clearing v pairs").c_str());
+      s->epoch = 0;
+    }
     L.epoch = ++s->epoch;
   }
   hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream),

@@ -60,10 +60,10 @@ struct DeltaLaunch {
   int32_t expand_stride, expand_tokcap, expand_pagecap, n_expand;
   int32_t gemv_rows;      // rank rows per GEMV shrink tile (host choice)
   int32_t has_mfma;       // some tile of this launch is an MFMA tile
-  // fused launch: per-segment completion counters (cumulative over launches
-  // since the metadata upload), the launch's epoch (1, 2, ... per upload) and
-  // a flag raised if a wait gave up
-  uint32_t* counters;
+  // fused launch: v as (value, epoch) pairs in the metadata buffer (zeroed at
+  // upload), the launch's epoch (1, 2, ... per upload) and a flag raised if a
+  // wait gave up
+  unsigned long long* vtag;
   uint32_t* error_flag;
   uint32_t epoch;
 };
@@ -76,6 +76,9 @@ enum : int { STAGE_SHRINK = 1, STAGE_EXPAND = 2, STAGE_FUSED = 4 };
 // the first kernel begins, stop when the last one ends).
 hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+
+// Zero n_words 32-bit words at p (a fill kernel; no memset node in the stream).
+hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t stream);
 
 // Copy n_rows rows of row_bytes from src (device, packed) into the pages
 // page_ids[i] of the class at base with page_bytes stride.

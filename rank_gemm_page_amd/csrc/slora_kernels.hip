@@ -148,59 +148,69 @@ __device__ __forceinline__ void record_to_lds(const int32_t* rec, int tokcap, in
   __syncthreads();
 }
 
-// Fused launch: the shrink tiles of segment s each add 1 to counters[s] once
-// their v values are stored, and an expand tile of s waits until the counter
-// reaches epoch * (shrink tiles of s) before it reads v.
-//
-// Ordering without cache-wide fences: in a fused launch v is written and read
-// only with agent-scope atomic accesses, which are coherent across the XCDs by
-// themselves (they never leave dirty or stale copies in an XCD's L2).  Each
-// producer thread waits for its v stores to complete (s_waitcnt 0) before the
-// workgroup barrier, and only then does one thread increment the counter; a
-// consumer issues its v loads only after one of its threads has observed the
-// count and the workgroup has passed a barrier.  A release/acquire fence pair
-// would do the same but writes back and invalidates the whole L2 of the XCD
-// on every tile.
+// Fused launch: shrink tiles and expand tiles run in one grid, and v passes
+// from one to the other as self-validating (value, epoch) pairs.  A shrink
+// tile stores each v value together with the launch's epoch in one 64-bit
+// agent-scope atomic store; an expand tile loads its tokens' v pairs with
+// agent-scope atomic loads and goes on once every pair carries the current
+// epoch, polling again otherwise.  Agent-scope atomics are coherent across the
+// XCDs by themselves (they leave no dirty or stale copy in an XCD's L2) and a
+// 64-bit aligned store is seen whole or not at all, so no fence, counter or
+// completion wait is needed on either side.  The pairs live in the metadata
+// buffer, which the upload zeroes, and epochs count 1, 2, ... from there, so
+// no stale pair can carry the current epoch.
 //
 // Progress: shrink tiles occupy the lower block indices and never wait, and
 // workgroups are dispatched in index order, so every shrink tile a waiting
 // expand tile depends on has been dispatched and finishes.  The wait is
 // bounded all the same: past kMaxSpins polls it raises error_flag and goes on,
 // so every wave of the grid always exits.
-constexpr uint32_t kMaxSpins = 1u << 21;
+constexpr uint32_t kMaxSpins = 1u << 20;
 
 template <bool FUSED>
-__device__ __forceinline__ void store_v(float* p, float x) {
-  if constexpr (FUSED) __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = x;
-}
-template <bool FUSED>
-__device__ __forceinline__ float load_v(const float* p) {
-  if constexpr (FUSED) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-
-__device__ __forceinline__ void signal_segment(const DeltaLaunch& L, int seg) {
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's v stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(L.counters + seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float x) {
+  if constexpr (FUSED) {
+    const unsigned long long pair = ((unsigned long long)L.epoch << 32) | __float_as_uint(x);
+    __hip_atomic_store(L.vtag + idx, pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    L.v[idx] = x;
+  }
 }
 
-__device__ __forceinline__ void wait_segment(const DeltaLaunch& L, int seg, int n_wait) {
-  if (threadIdx.x == 0) {
-    const uint32_t target = L.epoch * (uint32_t)n_wait;
+// Loads v[idx] of every (valid) slot this thread owns, polling until all
+// threads of the workgroup hold current values.  get(q) gives slot q's index
+// (or -1), put(q, value) receives the value; N slots per thread.
+template <bool FUSED, int N, typename Get, typename Put>
+__device__ __forceinline__ void load_v(const DeltaLaunch& L, Get get, Put put) {
+  if constexpr (!FUSED) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const int64_t idx = get(q);
+      put(q, idx >= 0 ? L.v[idx] : 0.f);
+    }
+  } else {
     for (uint32_t spins = 0;; ++spins) {
-      const uint32_t now = __hip_atomic_load(L.counters + seg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((int32_t)(now - target) >= 0) break;
+      bool ok = true;
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        const int64_t idx = get(q);
+        float val = 0.f;
+        if (idx >= 0) {
+          const unsigned long long pair =
+              __hip_atomic_load(L.vtag + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = ok && (uint32_t)(pair >> 32) == L.epoch;
+          val = __uint_as_float((uint32_t)pair);
+        }
+        put(q, val);
+      }
+      if (__syncthreads_and(ok)) break;
       if (spins >= kMaxSpins) {
-        __hip_atomic_store(L.error_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(L.error_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -267,9 +277,8 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     const int k = i / nrows, r = i - k * nrows;
     const float* q = red + (k * 4) * RB + r;
     const float sum = ((q[0] + q[RB]) + q[2 * RB]) + q[3 * RB];
-    store_v<FUSED>(L.v + v0 + (int64_t)k * rank + j0 + r, sum);
+    store_v<FUSED>(L, v0 + (int64_t)k * rank + j0 + r, sum);
   }
-  if constexpr (FUSED) signal_segment(L, uni(srec[REC_SEG]));
 }
 
 // ---------------------------------------------------------------------------
@@ -360,9 +369,8 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) sum += red[((w * 4 + b) * 16 + mm) * 16 + n];
-    store_v<FUSED>(L.v + v0 + (int64_t)mm * rank + j0 + j, sum);
+    store_v<FUSED>(L, v0 + (int64_t)mm * rank + j0 + j, sum);
   }
-  if constexpr (FUSED) signal_segment(L, uni(srec[REC_SEG]));
 }
 
 template <bool FUSED>
@@ -435,18 +443,9 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   for (int k = 0; k < TB; ++k)
     yv[k] = (g == 0 && active && k < ntok) ? ld16(y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC)
                                            : make_uint4(0, 0, 0, 0);
-  if constexpr (FUSED) wait_segment(L, uni(srec[REC_SEG]), uni(srec[REC_WAIT]));
-  float vreg[TB];
-#pragma unroll
-  for (int q = 0; q < TB; ++q) {
-    const int i = tid + q * kThreads;
-    vreg[q] = i < ntok * rank ? load_v<FUSED>(L.v + v0 + i) : 0.f;
-  }
-#pragma unroll
-  for (int q = 0; q < TB; ++q) {
-    const int i = tid + q * kThreads;
-    if (i < ntok * rank) sv[i] = vreg[q];
-  }
+  load_v<FUSED, TB>(
+      L, [&](int q) -> int64_t { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
+      [&](int q, float val) { const int i = tid + q * kThreads; if (i < ntok * rank) sv[i] = val; });
   __syncthreads();
 
   float acc[TB][VEC];
@@ -572,16 +571,23 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   };
   uint4 bnext[4];
   stage_load(0, bnext);
-  if constexpr (FUSED) wait_segment(L, uni(srec[REC_SEG]), uni(srec[REC_WAIT]));
 
   // s * v of the tile, zero outside ntok x rank, and its largest magnitude.
+  const int kw = ks_n * 32;
+  load_v<FUSED, (16 * kMaxRankMfma) / kThreads>(
+      L,
+      [&](int q) -> int64_t {
+        const int i = tid + q * kThreads, mm = i / kw, j = i - mm * kw;
+        return (i < 16 * kw && mm < ntok && j < rank) ? v0 + (int64_t)mm * rank + j : -1;
+      },
+      [&](int q, float val) {
+        const int i = tid + q * kThreads, mm = i / kw, j = i - mm * kw;
+        if (i < 16 * kw) sv[mm * vp + j] = scale * val;
+      });
   float amax = 0.f;
-  for (int i = tid; i < 16 * ks_n * 32; i += kThreads) {
-    const int mm = i / (ks_n * 32), j = i - mm * (ks_n * 32);
-    float val = 0.f;
-    if (mm < ntok && j < rank) val = scale * load_v<FUSED>(L.v + v0 + (int64_t)mm * rank + j);
-    sv[mm * vp + j] = val;
-    amax = fmaxf(amax, fabsf(val));
+  for (int i = tid; i < 16 * kw; i += kThreads) {
+    const int mm = i / kw, j = i - mm * kw;
+    amax = fmaxf(amax, fabsf(sv[mm * vp + j]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -692,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
 }
 
 // Both stages in one launch: blocks [0, n_shrink) run shrink tiles, the rest
-// expand tiles that wait for their segment (see signal_segment/wait_segment).
+// expand tiles that wait for their tokens' v (see store_v / load_v).
 // MFMA=false leaves the matrix-core tiles out (a batch without them), which
 // keeps the register budget, and so the workgroups resident per CU, of the
 // vector-ALU tiles alone.
@@ -796,6 +802,19 @@ hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream, hi
                         hipEvent_t stop) {
   return L.dtype == 1 ? launch_delta_t<_Float16>(L, stages, stream, start, stop)
                       : launch_delta_t<float>(L, stages, stream, start, stop);
+}
+
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t stream) {
+  if (n_words <= 0) return hipSuccess;
+  int64_t blocks = (n_words + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  zero_words_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(static_cast<uint32_t*>(p), n_words);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
