@@ -179,17 +179,17 @@ slora_status slora_segments_export(const slora_segments* seg, int32_t* perm, int
                                    int32_t* seg_page_off, int32_t* a_pages, int32_t* b_pages);
 
 /* Introspection of the work split (host copies): layout[9] receives
- * {n_shrink_tiles, shrink_stride, shrink_tokcap, shrink_pagecap,
- *  n_expand_tiles, expand_stride, expand_tokcap, expand_pagecap, hdr} and,
- * when records is not NULL and holds at least meta_bytes / 4 words, the tile
- * records: n_shrink_tiles records of shrink_stride int32 words, then the
- * expand records.  Record words: 0 kind (0 vector ALU, 1 MFMA), 1 token count,
+ * {n_tiles, stride, tokcap, pagecap, n_shrink_tiles, n_expand_tiles, hdr, 0, 0}
+ * and, when records is not NULL and holds at least n_tiles * stride words,
+ * the tile records in launch order (every shrink tile before every expand
+ * tile), stride int32 words each.  Record words:
+ * 0 kind (bit 0: matrix-core (MFMA) tile, bit 1: expand tile), 1 token count,
  * 2 segment rank, 3 first rank row (shrink) or first column (expand), 4 rows
  * or columns covered, 5 workspace offset of the first token's v row, 6 scale
- * (float bits), 7 expand thread-map width, 8 segment index, 9 (expand) shrink
- * tiles of the segment; from word hdr, tokcap batch indices of the tokens,
- * then per projection pagecap page ids (shrink: the rows covered; expand: all
- * rank B rows).  For tests and tools; the layout may change. */
+ * (float bits), 7 expand thread-map width, 8 segment index; from word hdr,
+ * tokcap batch indices of the tokens, then per projection pagecap page ids
+ * (shrink: the A^T pages of the rows covered; expand: all rank B pages).
+ * For tests and tools; the layout may change. */
 slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, int32_t* records,
                                   size_t records_words);
 

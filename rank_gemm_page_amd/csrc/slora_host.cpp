@@ -143,11 +143,10 @@ struct slora_segments {
   int32_t n_mfma_segments = 0;
   // tile records: shrink records, then expand records
   std::vector<int32_t> blob;
-  int32_t n_shrink = 0, n_expand = 0;
-  int32_t shrink_stride = 0, shrink_tokcap = 0, shrink_pagecap = 0;
-  int32_t expand_stride = 0, expand_tokcap = 0, expand_pagecap = 0;
-  int64_t expand_off_words = 0;
-  int64_t records_words = 0;       // shrink and expand records (the uploaded part)
+  int32_t n_tiles = 0, n_shrink = 0, n_expand = 0;
+  int32_t stride = 0, tokcap = 0, pagecap = 0;
+  int64_t shrink_idx_off_words = 0, expand_idx_off_words = 0;
+  int64_t records_words = 0;       // records and index lists (the uploaded part)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -286,62 +285,65 @@ void build_tiles(slora_segments* s) {
   const int gemv_rows = kShrinkRowBudget / nck;
   s->gemv_rows = gemv_rows;
 
-  std::vector<TileSpec> sh, ex;
+  std::vector<TileSpec> tiles;
   std::vector<std::pair<int32_t, int32_t>> blocks;
   int32_t max_rank = 1;
   s->n_mfma_segments = 0;
+  s->n_shrink = s->n_expand = 0;
   for (int32_t g = 0; g < S; ++g) {
     const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
     const int32_t r = s->seg_rank[g];
     max_rank = std::max(max_rank, r);
     const bool mfma = f16 && c >= p->tune.mfma_min_tokens && hin % 32 == 0;
-    if (mfma) {
-      ++s->n_mfma_segments;
-      split_tokens(c, kMfmaTok, blocks);
-      for (auto& tb : blocks) {
-        const int32_t rows = (int32_t)p->tune.mfma_shrink_rows;
-        for (int32_t j0 = 0; j0 < r; j0 += rows)
-          sh.push_back({KIND_MFMA, g, tb.first, tb.second, j0, std::min(rows, r - j0), 0});
-        const int32_t cols = (int32_t)p->tune.mfma_expand_cols;
-        for (int32_t o0 = 0; o0 < hout; o0 += cols)
-          ex.push_back({KIND_MFMA, g, tb.first, tb.second, o0, std::min(cols, hout - o0), 0});
-      }
-    } else {
-      split_tokens(c, kGemvMaxTok, blocks);
-      // expand width: largest of vec*{256,128,64,32} with rank x width within budget
-      int32_t width = vec * 256;
-      while (width > vec * 32 && (int64_t)r * width > p->tune.gemv_expand_elems) width /= 2;
-      for (auto& tb : blocks) {
-        for (int32_t j0 = 0; j0 < r; j0 += gemv_rows)
-          sh.push_back({KIND_GEMV, g, tb.first, tb.second, j0, std::min(gemv_rows, r - j0), 0});
-        for (int32_t o0 = 0; o0 < hout; o0 += width)
-          ex.push_back({KIND_GEMV, g, tb.first, tb.second, o0, std::min(width, hout - o0), width});
-      }
+    if (mfma) ++s->n_mfma_segments;
+    split_tokens(c, mfma ? kMfmaTok : kGemvMaxTok, blocks);
+    // vector-ALU expand width: largest of vec*{256,128,64,32} with rank x width within budget
+    int32_t width = vec * 256;
+    while (width > vec * 32 && (int64_t)r * width > p->tune.gemv_expand_elems) width /= 2;
+    const int32_t rows = mfma ? (int32_t)p->tune.mfma_shrink_rows : gemv_rows;
+    const int32_t cols = mfma ? (int32_t)p->tune.mfma_expand_cols : width;
+    for (auto& tb : blocks) {
+      for (int32_t j0 = 0; j0 < r; j0 += rows, ++s->n_shrink)
+        tiles.push_back({mfma ? KIND_SHRINK_MFMA : KIND_SHRINK_GEMV, g, tb.first, tb.second, j0,
+                         std::min(rows, r - j0), 0});
+      for (int32_t o0 = 0; o0 < hout; o0 += cols, ++s->n_expand)
+        tiles.push_back({mfma ? KIND_EXPAND_MFMA : KIND_EXPAND_GEMV, g, tb.first, tb.second, o0,
+                         std::min(cols, hout - o0), mfma ? 0 : width});
     }
   }
-  // Heavier (MFMA) tiles first so they start early; stable otherwise.
-  auto heavier_first = [](const TileSpec& a, const TileSpec& b) { return a.kind > b.kind; };
-  std::stable_sort(sh.begin(), sh.end(), heavier_first);
-  std::stable_sort(ex.begin(), ex.end(), heavier_first);
 
-  std::vector<int32_t> shrink_tiles_of(S, 0);
-  for (const TileSpec& t : sh) ++shrink_tiles_of[t.seg];
+  // Launch order: every shrink tile before every expand tile, the matrix-core
+  // tiles (the heavier ones) first within each stage, segment order otherwise.
+  // Producers first keeps the waiting expand tiles of a fused launch from
+  // holding the workgroup slots the shrink tiles need (measured: putting each
+  // token block's expand tiles right after its shrink tiles is 20-50 % slower).
+  auto launch_rank = [](const TileSpec& t) {
+    return ((t.kind & KIND_EXPAND_BIT) ? 2 : 0) + ((t.kind & KIND_MFMA_BIT) ? 0 : 1);
+  };
+  std::stable_sort(tiles.begin(), tiles.end(), [&](const TileSpec& a, const TileSpec& b) {
+    return launch_rank(a) < launch_rank(b);
+  });
+
   const int np = s->n_proj;
-  s->shrink_tokcap = std::max(kGemvMaxTok, kMfmaTok);
-  s->shrink_pagecap = std::max(gemv_rows, kMfmaMaxRows);
-  s->shrink_stride = (REC_HDR + s->shrink_tokcap + np * s->shrink_pagecap + 3) & ~3;
-  s->expand_tokcap = std::max(kGemvMaxTok, kMfmaTok);
-  s->expand_pagecap = (max_rank + 3) & ~3;
-  s->expand_stride = (REC_HDR + s->expand_tokcap + np * s->expand_pagecap + 3) & ~3;
-  s->n_shrink = (int32_t)sh.size();
-  s->n_expand = (int32_t)ex.size();
-  s->expand_off_words = (int64_t)s->n_shrink * s->shrink_stride;
-  s->records_words = s->expand_off_words + (int64_t)s->n_expand * s->expand_stride;
+  s->n_tiles = (int32_t)tiles.size();
+  s->tokcap = std::max(kGemvMaxTok, kMfmaTok);
+  s->pagecap = (std::max({gemv_rows, kMfmaMaxRows, max_rank}) + 3) & ~3;
+  s->stride = (REC_HDR + s->tokcap + np * s->pagecap + 3) & ~3;
+  s->shrink_idx_off_words = (int64_t)s->n_tiles * s->stride;
+  s->expand_idx_off_words = s->shrink_idx_off_words + s->n_shrink;
+  s->records_words = (s->expand_idx_off_words + s->n_expand + 3) & ~(int64_t)3;
   s->error_off_words = s->records_words;            // records end 16-byte aligned
   s->vtag_off_words = s->error_off_words + 4;       // 8-byte pairs, 16-byte aligned
   s->blob.assign((size_t)s->records_words, 0);
 
-  auto fill = [&](int32_t* rec, const TileSpec& t, int32_t tokcap, int32_t pagecap, bool shrink) {
+  int32_t* shrink_idx = s->blob.data() + s->shrink_idx_off_words;
+  int32_t* expand_idx = s->blob.data() + s->expand_idx_off_words;
+  int32_t ns = 0, ne = 0;
+  for (int32_t i = 0; i < s->n_tiles; ++i) {
+    const TileSpec& t = tiles[i];
+    int32_t* rec = s->blob.data() + (size_t)i * s->stride;
+    const bool expand = (t.kind & KIND_EXPAND_BIT) != 0;
+    (expand ? expand_idx[ne++] : shrink_idx[ns++]) = i;
     const int32_t g = t.seg;
     const int32_t r = s->seg_rank[g];
     rec[REC_KIND] = t.kind;
@@ -354,24 +356,18 @@ void build_tiles(slora_segments* s) {
     std::memcpy(&rec[REC_SCALE], &sc, 4);
     rec[REC_AUX] = t.aux;
     rec[REC_SEG] = g;
-    rec[REC_WAIT] = shrink_tiles_of[g];
     const int32_t first = s->seg_start[g] + t.i0;
     for (int32_t k = 0; k < t.ntok; ++k) rec[REC_HDR + k] = s->perm[first + k];
     for (int pr = 0; pr < np; ++pr) {
-      int32_t* pg = rec + REC_HDR + tokcap + pr * pagecap;
-      const int32_t* src = (shrink ? s->a_pages.data() : s->b_pages.data()) +
+      int32_t* pg = rec + REC_HDR + s->tokcap + pr * s->pagecap;
+      const int32_t* src = (expand ? s->b_pages.data() : s->a_pages.data()) +
                            (size_t)pr * s->sum_r + s->seg_page_off[g];
-      if (shrink)
-        for (int32_t j = 0; j < t.len; ++j) pg[j] = src[t.pos + j];
-      else
+      if (expand)
         for (int32_t j = 0; j < r; ++j) pg[j] = src[j];
+      else
+        for (int32_t j = 0; j < t.len; ++j) pg[j] = src[t.pos + j];
     }
-  };
-  for (int32_t i = 0; i < s->n_shrink; ++i)
-    fill(s->blob.data() + (size_t)i * s->shrink_stride, sh[i], s->shrink_tokcap, s->shrink_pagecap, true);
-  for (int32_t i = 0; i < s->n_expand; ++i)
-    fill(s->blob.data() + (size_t)s->expand_off_words + (size_t)i * s->expand_stride, ex[i],
-         s->expand_tokcap, s->expand_pagecap, false);
+  }
 }
 
 }  // namespace
@@ -742,11 +738,11 @@ slora_status slora_segments_export(const slora_segments* s, int32_t* perm, int32
 slora_status slora_segments_tiles(const slora_segments* s, int32_t* layout, int32_t* records,
                                   size_t records_words) {
   if (!s || !layout) return fail(SLORA_E_INVAL, "slora_segments_tiles: NULL argument");
-  const int32_t lay[9] = {s->n_shrink, s->shrink_stride, s->shrink_tokcap, s->shrink_pagecap,
-                          s->n_expand, s->expand_stride, s->expand_tokcap, s->expand_pagecap, REC_HDR};
+  const int32_t lay[9] = {s->n_tiles, s->stride, s->tokcap, s->pagecap, s->n_shrink, s->n_expand,
+                          REC_HDR, 0, 0};
   std::memcpy(layout, lay, sizeof(lay));
   if (records) {
-    const size_t words = (size_t)s->records_words;
+    const size_t words = (size_t)s->n_tiles * s->stride;
     if (records_words < words) return fail(SLORA_E_NOMEM, "slora_segments_tiles: records buffer too small");
     std::memcpy(records, s->blob.data(), words * sizeof(int32_t));
   }
@@ -853,16 +849,15 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.x = x;
   L.y = y;
   L.v = static_cast<float*>(const_cast<void*>(workspace));
-  L.shrink_rec = s->dev_meta;
-  L.shrink_stride = s->shrink_stride;
-  L.shrink_tokcap = s->shrink_tokcap;
-  L.shrink_pagecap = s->shrink_pagecap;
+  L.rec = s->dev_meta;
+  L.stride = s->stride;
+  L.tokcap = s->tokcap;
+  L.pagecap = s->pagecap;
+  L.n_tiles = s->n_tiles;
   L.n_shrink = s->n_shrink;
-  L.expand_rec = s->dev_meta + s->expand_off_words;
-  L.expand_stride = s->expand_stride;
-  L.expand_tokcap = s->expand_tokcap;
-  L.expand_pagecap = s->expand_pagecap;
   L.n_expand = s->n_expand;
+  L.shrink_idx = s->dev_meta + s->shrink_idx_off_words;
+  L.expand_idx = s->dev_meta + s->expand_idx_off_words;
   L.gemv_rows = s->gemv_rows;
   L.has_mfma = s->n_mfma_segments > 0;
   L.error_flag = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->error_off_words));

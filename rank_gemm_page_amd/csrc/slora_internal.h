@@ -9,7 +9,8 @@
 namespace slora {
 
 // A tile record is a run of int32 words:
-//   [0] kind        KIND_GEMV (vector ALU) or KIND_MFMA (matrix cores)
+//   [0] kind        KIND_{SHRINK,EXPAND}_{GEMV,MFMA}: bit 0 set for the
+//                   matrix-core (MFMA) tiles, bit 1 set for expand tiles
 //   [1] ntok        tokens in the tile (all of one segment)
 //   [2] rank        the segment's rank r (row stride of its v block)
 //   [3] pos         shrink: first rank row j0      expand: first column o0
@@ -17,19 +18,23 @@ namespace slora {
 //   [5] v0          workspace offset of the tile's first token's v row
 //   [6] scale       the segment's scale, float bits
 //   [7] aux         expand GEMV: nominal column width of the tile (thread map)
-//   [8] seg         index of the tile's segment (its completion counter)
-//   [9] wait        expand: shrink tiles of the segment a fused launch waits for
-//   [10..11]        reserved
+//   [8] seg         index of the tile's segment
+//   [9..11]         reserved
 //   [HDR .. HDR+tokcap)                   batch indices of the tokens
 //   [HDR+tokcap + p*pagecap .. +npages)   page ids of projection p: shrink
 //                                         holds the A^T pages of rows
 //                                         pos..pos+len, expand all r B pages
-// Records of one kernel share one stride (a multiple of 4 words).
+// All records share one stride (a multiple of 4 words) and sit in launch
+// order: every shrink tile before every expand tile.  Two index lists give the
+// shrink and the expand records for launches that run the stages separately.
 enum : int32_t {
   REC_KIND = 0, REC_NTOK = 1, REC_RANK = 2, REC_POS = 3, REC_LEN = 4,
-  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_SEG = 8, REC_WAIT = 9, REC_HDR = 12
+  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_SEG = 8, REC_HDR = 12
 };
-enum : int32_t { KIND_GEMV = 0, KIND_MFMA = 1 };
+enum : int32_t {
+  KIND_SHRINK_GEMV = 0, KIND_SHRINK_MFMA = 1, KIND_EXPAND_GEMV = 2, KIND_EXPAND_MFMA = 3,
+  KIND_MFMA_BIT = 1, KIND_EXPAND_BIT = 2
+};
 
 // Fixed tile geometry shared by the builder and the kernels.
 constexpr int kThreads = 256;           // every tile kernel runs 4 waves of 64
@@ -54,10 +59,11 @@ struct DeltaLaunch {
   const void* x;
   void* y;
   float* v;
-  const int32_t* shrink_rec;
-  int32_t shrink_stride, shrink_tokcap, shrink_pagecap, n_shrink;
-  const int32_t* expand_rec;
-  int32_t expand_stride, expand_tokcap, expand_pagecap, n_expand;
+  const int32_t* rec;             // all tile records, launch order
+  int32_t stride, tokcap, pagecap;
+  int32_t n_tiles, n_shrink, n_expand;
+  const int32_t* shrink_idx;      // record index of each shrink tile
+  const int32_t* expand_idx;      // record index of each expand tile
   int32_t gemv_rows;      // rank rows per GEMV shrink tile (host choice)
   int32_t has_mfma;       // some tile of this launch is an MFMA tile
   // fused launch: v as (value, epoch) pairs in the metadata buffer (zeroed at

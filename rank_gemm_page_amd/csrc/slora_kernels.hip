@@ -229,7 +229,7 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int nrows = uni(srec[REC_LEN]);
   const int v0 = uni(srec[REC_V0]);
   const int32_t* toks = srec + REC_HDR;
-  const int32_t* pages = srec + REC_HDR + L.shrink_tokcap;
+  const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int nchunks = L.h_in / VEC;
   const T* x = reinterpret_cast<const T*>(L.x);
@@ -295,7 +295,7 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int nrows = uni(srec[REC_LEN]);
   const int v0 = uni(srec[REC_V0]);
   const int32_t* toks = srec + REC_HDR;
-  const int32_t* pages = srec + REC_HDR + L.shrink_tokcap;
+  const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
 
@@ -386,11 +386,11 @@ __device__ __forceinline__ void shrink_mfma_dispatch(const DeltaLaunch& L, const
 template <typename T, int NCK>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
   __shared__ float red[4 * 4 * 16 * 16];  // MFMA: 4 waves x 4 blocks x 16 x 16
-  __shared__ int32_t srec[REC_HDR + 16 + kMfmaMaxRows];
-  const int32_t* rec = L.shrink_rec + (int64_t)blockIdx.x * L.shrink_stride;
-  record_to_lds(rec, L.shrink_tokcap, L.shrink_pagecap, L.proj, srec);
+  __shared__ int32_t srec[kMaxRecWords];
+  const int32_t* rec = L.rec + (int64_t)L.shrink_idx[blockIdx.x] * L.stride;
+  record_to_lds(rec, L.tokcap, L.pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
-    if (uni(srec[REC_KIND]) == KIND_MFMA) {
+    if (uni(srec[REC_KIND]) & KIND_MFMA_BIT) {
       shrink_mfma_dispatch<false>(L, srec, red);
       return;
     }
@@ -417,7 +417,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const float scale = __int_as_float(uni(srec[REC_SCALE]));
   const int width = uni(srec[REC_AUX]);
   const int32_t* toks = srec + REC_HDR;
-  const int32_t* pages = srec + REC_HDR + L.expand_tokcap;
+  const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x;
   const int nct = width / VEC;
   const int G = kThreads / nct;
@@ -539,7 +539,7 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int v0 = uni(srec[REC_V0]);
   const float scale = __int_as_float(uni(srec[REC_SCALE]));
   const int32_t* toks = srec + REC_HDR;
-  const int32_t* pages = srec + REC_HDR + L.expand_tokcap;
+  const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int ks_n = (rank + 31) >> 5;
@@ -686,10 +686,10 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
   __shared__ float lds[kExpandLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
-  const int32_t* rec = L.expand_rec + (int64_t)blockIdx.x * L.expand_stride;
-  record_to_lds(rec, L.expand_tokcap, L.expand_pagecap, L.proj, srec);
+  const int32_t* rec = L.rec + (int64_t)L.expand_idx[blockIdx.x] * L.stride;
+  record_to_lds(rec, L.tokcap, L.pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
-    if (uni(srec[REC_KIND]) == KIND_MFMA) {
+    if (uni(srec[REC_KIND]) & KIND_MFMA_BIT) {
       expand_mfma_tile<false>(L, srec, lds);
       return;
     }
@@ -697,8 +697,8 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
   expand_gemv_tile<T, false>(L, srec, lds);
 }
 
-// Both stages in one launch: blocks [0, n_shrink) run shrink tiles, the rest
-// expand tiles that wait for their tokens' v (see store_v / load_v).
+// Both stages in one launch over the records in launch order: shrink tiles
+// and expand tiles that wait for their tokens' v (see store_v / load_v).
 // MFMA=false leaves the matrix-core tiles out (a batch without them), which
 // keeps the register budget, and so the workgroups resident per CU, of the
 // vector-ALU tiles alone.
@@ -706,12 +706,11 @@ template <typename T, int NCK, bool MFMA>
 __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
   __shared__ float lds[kExpandLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
-  const int b = blockIdx.x;
-  if (b < L.n_shrink) {
-    record_to_lds(L.shrink_rec + (int64_t)b * L.shrink_stride, L.shrink_tokcap, L.shrink_pagecap,
-                  L.proj, srec);
+  record_to_lds(L.rec + (int64_t)blockIdx.x * L.stride, L.tokcap, L.pagecap, L.proj, srec);
+  const int kind = uni(srec[REC_KIND]);
+  if (!(kind & KIND_EXPAND_BIT)) {
     if constexpr (sizeof(T) == 2 && MFMA) {
-      if (uni(srec[REC_KIND]) == KIND_MFMA) {
+      if (kind & KIND_MFMA_BIT) {
         shrink_mfma_dispatch<true>(L, srec, lds);
         return;
       }
@@ -719,10 +718,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
     shrink_gemv_tile<T, NCK, true>(L, srec, lds);
     return;
   }
-  record_to_lds(L.expand_rec + (int64_t)(b - L.n_shrink) * L.expand_stride, L.expand_tokcap,
-                L.expand_pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2 && MFMA) {
-    if (uni(srec[REC_KIND]) == KIND_MFMA) {
+    if (kind & KIND_MFMA_BIT) {
       expand_mfma_tile<true>(L, srec, lds);
       return;
     }
@@ -777,7 +774,7 @@ static hipError_t launch_delta_t(const DeltaLaunch& L, int stages, hipStream_t s
                                  hipEvent_t start, hipEvent_t stop) {
   const int nck = chunks_per_thread<T>(L.h_in);
   if (stages & STAGE_FUSED) {
-    const int blocks = L.n_shrink + L.n_expand;
+    const int blocks = L.n_tiles;
     if (blocks == 0) return hipSuccess;
     const void* k = (sizeof(T) == 2 && L.has_mfma) ? fused_fn<T, true>(nck) : fused_fn<T, false>(nck);
     if (!k) return hipErrorInvalidValue;

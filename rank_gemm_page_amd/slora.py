@@ -253,21 +253,17 @@ def slora_segments_export(seg) -> dict:
 
 
 def slora_segments_tiles(seg):
-    """(layout dict, shrink records [n, stride], expand records [n, stride]) as int32 arrays."""
+    """(layout dict, records [n_tiles, stride]) as int32 arrays, in launch order."""
     info = slora_segments_get_info(seg)
-    words = info["meta_bytes"] // 4
     lay = np.empty(9, np.int32)
-    rec = np.zeros(max(words, 4), np.int32)
+    _check(lib().slora_segments_tiles(seg, _i32p(lay), None, 0), "slora_segments_tiles")
+    keys = ["n_tiles", "stride", "tokcap", "pagecap", "n_shrink", "n_expand", "hdr"]
+    layout = dict(zip(keys, (int(v) for v in lay)))
+    n, st = layout["n_tiles"], layout["stride"]
+    rec = np.zeros(max(n * st, 4), np.int32)
     _check(lib().slora_segments_tiles(seg, _i32p(lay), _i32p(rec), rec.shape[0]),
            "slora_segments_tiles")
-    keys = ["n_shrink", "shrink_stride", "shrink_tokcap", "shrink_pagecap", "n_expand",
-            "expand_stride", "expand_tokcap", "expand_pagecap", "hdr"]
-    layout = dict(zip(keys, (int(v) for v in lay)))
-    ns, ss = layout["n_shrink"], layout["shrink_stride"]
-    ne, es = layout["n_expand"], layout["expand_stride"]
-    shrink = rec[:ns * ss].reshape(ns, ss)
-    expand = rec[ns * ss:ns * ss + ne * es].reshape(ne, es)
-    return layout, shrink, expand
+    return layout, rec[:n * st].reshape(n, st)
 
 
 def slora_segments_upload(seg, dev_meta, dev_meta_bytes: int, stream=None) -> None:

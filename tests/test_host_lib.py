@@ -117,18 +117,22 @@ def test_metadata_bit_exact_vs_oracle(name):
 
 
 def check_tiles_cover(w, pool, ids):
-    """Every (token, rank row) is shrunk once and every (token, column) expanded once."""
+    """Every (token, rank row) is shrunk once and every (token, column) expanded
+    once, and every expand tile comes after the shrink tiles of its tokens."""
     seg = S.slora_build_segments(pool, ids)
     try:
         info = S.slora_segments_get_info(seg)
         ex = S.slora_segments_export(seg)
-        lay, sh, exp = S.slora_segments_tiles(seg)
+        lay, recs = S.slora_segments_tiles(seg)
         spec = w.spec
         n_seg = info["n_segments"]
+        hdr, tokcap, pagecap = lay["hdr"], lay["tokcap"], lay["pagecap"]
+        assert lay["n_tiles"] == len(recs) == lay["n_shrink"] + lay["n_expand"]
+        assert lay["n_shrink"] == info["n_shrink_tiles"] and lay["n_expand"] == info["n_expand_tiles"]
         seg_of = {}
         for s in range(n_seg):
             for i in range(ex["seg_start"][s], ex["seg_start"][s + 1]):
-                seg_of[int(ex["perm"][i])] = (s, i)
+                seg_of[int(ex["perm"][i])] = s
         # where each token's v row lives: prefix over sorted tokens of their ranks
         v_row = {}
         off = 0
@@ -139,47 +143,45 @@ def check_tiles_cover(w, pool, ids):
                 off += r
         assert off == info["sum_rank_tokens"]
         shrink_seen = np.zeros(max(off, 1), np.int32)
-        for rec in sh:
-            kind, ntok, r, j0, nrows, v0 = (int(v) for v in rec[:6])
-            assert kind in (0, 1) and 1 <= ntok <= lay["shrink_tokcap"] and nrows >= 1
-            assert (kind == 1) <= (spec.dtype == "f16")
-            hdr = lay["hdr"]
-            toks = rec[hdr:hdr + ntok]
-            s, _ = seg_of[int(toks[0])]
-            assert rec[8] == s
-            assert r == ex["seg_rank"][s] and 0 <= j0 and j0 + nrows <= r
-            for k, t in enumerate(toks):
-                assert seg_of[int(t)][0] == s
-                assert v_row[int(t)] == v0 + k * r
-                shrink_seen[v_row[int(t)] + j0:v_row[int(t)] + j0 + nrows] += 1
-            for p in range(spec.n_proj):
-                pg = rec[hdr + lay["shrink_tokcap"] + p * lay["shrink_pagecap"]:][:nrows]
-                base = p * info["sum_rank"] + ex["seg_page_off"][s]
-                np.testing.assert_array_equal(pg, ex["a_pages"][base + j0:base + j0 + nrows])
-        assert (shrink_seen[:off] == 1).all()
-        n_shrink_of = np.bincount(sh[:, 8], minlength=n_seg) if len(sh) else np.zeros(n_seg, int)
+        last_shrink_of_token = {}
         routed = [t for t in range(len(ids)) if ids[t] >= 0]
         cover = {t: np.zeros(spec.h_out, np.int32) for t in routed}
-        for rec in exp:
-            kind, ntok, r, o0, ncol, v0 = (int(v) for v in rec[:6])
-            assert 1 <= ntok <= lay["expand_tokcap"] and o0 % 8 == 0 and ncol % 8 == 0
-            assert 0 <= o0 and o0 + ncol <= spec.h_out
-            hdr = lay["hdr"]
+        n_sh = n_ex = 0
+        for idx, rec in enumerate(recs):
+            kind, ntok, r, pos, length, v0 = (int(v) for v in rec[:6])
+            assert kind in (0, 1, 2, 3) and 1 <= ntok <= tokcap and length >= 1
+            assert (kind & 1) <= (spec.dtype == "f16")
             toks = rec[hdr:hdr + ntok]
-            s, _ = seg_of[int(toks[0])]
-            assert rec[8] == s and rec[9] == n_shrink_of[s] > 0
-            assert np.float32(rec[6:7].view(np.float32)[0]) == ex["seg_scale"][s]
+            s = seg_of[int(toks[0])]
+            assert rec[8] == s and r == ex["seg_rank"][s]
             for k, t in enumerate(toks):
-                assert seg_of[int(t)][0] == s and v_row[int(t)] == v0 + k * r
-                cover[int(t)][o0:o0 + ncol] += 1
-            if kind == 0:
-                width = int(rec[7])
-                vec = 8 if spec.dtype == "f16" else 4
-                assert width % vec == 0 and 256 % (width // vec) == 0 and ncol <= width
-            for p in range(spec.n_proj):
-                pg = rec[hdr + lay["expand_tokcap"] + p * lay["expand_pagecap"]:][:r]
-                base = p * info["sum_rank"] + ex["seg_page_off"][s]
-                np.testing.assert_array_equal(pg, ex["b_pages"][base:base + r])
+                assert seg_of[int(t)] == s and v_row[int(t)] == v0 + k * r
+            base = [p * info["sum_rank"] + ex["seg_page_off"][s] for p in range(spec.n_proj)]
+            if not kind & 2:            # shrink
+                n_sh += 1
+                assert 0 <= pos and pos + length <= r
+                for t in toks:
+                    shrink_seen[v_row[int(t)] + pos:v_row[int(t)] + pos + length] += 1
+                    last_shrink_of_token[int(t)] = idx
+                for p in range(spec.n_proj):
+                    pg = rec[hdr + tokcap + p * pagecap:][:length]
+                    np.testing.assert_array_equal(pg, ex["a_pages"][base[p] + pos:base[p] + pos + length])
+            else:                       # expand
+                n_ex += 1
+                assert pos % 8 == 0 and length % 8 == 0 and 0 <= pos and pos + length <= spec.h_out
+                assert np.float32(rec[6:7].view(np.float32)[0]) == ex["seg_scale"][s]
+                for t in toks:
+                    cover[int(t)][pos:pos + length] += 1
+                    assert last_shrink_of_token[int(t)] < idx   # launch order
+                if not kind & 1:
+                    width = int(rec[7])
+                    vec = 8 if spec.dtype == "f16" else 4
+                    assert width % vec == 0 and 256 % (width // vec) == 0 and length <= width
+                for p in range(spec.n_proj):
+                    pg = rec[hdr + tokcap + p * pagecap:][:r]
+                    np.testing.assert_array_equal(pg, ex["b_pages"][base[p]:base[p] + r])
+        assert n_sh == lay["n_shrink"] and n_ex == lay["n_expand"]
+        assert (shrink_seen[:off] == 1).all()
         for t in routed:
             assert (cover[t] == 1).all(), t
         return info
