@@ -128,7 +128,7 @@ def write_summary(config, trace_dir, fetch_dir, write_dir, command, flush_mib, o
         lines.append(f"  {k}: fetch {v['fetch_kib_raw']:.1f} KiB raw -> {v['fetch_bytes'] / 1e6:.2f} MB, "
                      f"write {v['write_kib_raw']:.1f} KiB raw -> {v['write_bytes'] / 1e6:.2f} MB "
                      f"({v['dispatches']} dispatches)")
-        if algorithmic_bytes:
+        if algorithmic_bytes and k == "fused_kernel":
             tot = v["fetch_bytes"] + v["write_bytes"]
             lines.append(f"    traffic / algorithmic bytes = {tot / 1e6:.2f} / "
                          f"{algorithmic_bytes / 1e6:.2f} MB = {tot / algorithmic_bytes:.3f}")
