@@ -47,6 +47,36 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Streaming (non-temporal) 16-byte load and store, for data read once per
+// launch or nearly so: page rows of the vector-ALU tiles and y.  Measured on
+// MI355X, row gathers of 60-240 MB stream 1.5-1.7x faster with the
+// non-temporal hint than with ordinary loads.  The x rows of the MFMA shrink
+// (read by every rank block of the token block, and across XCDs) and the B
+// slices of the MFMA expand (read by every token block of the segment) keep
+// ordinary loads: with the hint, the re-reads miss and the launch is slower.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+#ifndef SLORA_NT_A
+#define SLORA_NT_A 1
+#endif
+#ifndef SLORA_NT_B
+#define SLORA_NT_B 1
+#endif
+#ifndef SLORA_NT_Y
+#define SLORA_NT_Y 1
+#endif
+#ifndef SLORA_NT_X
+#define SLORA_NT_X 0
+#endif
+template <bool NT> __device__ __forceinline__ uint4 ldsel(const void* p) { return NT ? ld16_nt(p) : ld16(p); }
+template <bool NT> __device__ __forceinline__ void stsel(void* p, uint4 v) { if (NT) st16_nt(p, v); else st16(p, v); }
+
 __device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, _Float16) {
   acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a.x), __builtin_bit_cast(half2v, b.x), acc, false);
   acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a.y), __builtin_bit_cast(half2v, b.y), acc, false);
@@ -134,6 +164,15 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&p)[N], int lane) {
 // behind a lane mask to be skipped.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wave wait for all of its global
+// loads still in flight (prefetches included) before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Copy the part of a tile record this launch needs (header, tokens and the
 // page list of projection `proj`) into LDS with one batch of independent
 // loads, so that page ids and token ids come from LDS instead of a chain of
@@ -179,29 +218,38 @@ __device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float
 
 // Loads v[idx] of every (valid) slot this thread owns, polling until all
 // threads of the workgroup hold current values.  get(q) gives slot q's index
-// (or -1), put(q, value) receives the value; N slots per thread.
+// (or -1), put(q, value) receives the value; the first nq (uniform, <= N)
+// slots of each thread are in use.  All loads of a poll are issued before
+// any is consumed, at index `safe` (any valid v index) for a slot with no
+// value, so they travel to memory together instead of one round trip each.
 template <bool FUSED, int N, typename Get, typename Put>
-__device__ __forceinline__ void load_v(const DeltaLaunch& L, Get get, Put put) {
-  if constexpr (!FUSED) {
+__device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int64_t safe, Get get, Put put) {
+  int64_t idx[N];
 #pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const int64_t idx = get(q);
-      put(q, idx >= 0 ? L.v[idx] : 0.f);
-    }
+  for (int q = 0; q < N; ++q) idx[q] = q < nq ? get(q) : -1;
+  if constexpr (!FUSED) {
+    float val[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (q < nq) val[q] = L.v[idx[q] >= 0 ? idx[q] : safe];
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (q < nq) put(q, idx[q] >= 0 ? val[q] : 0.f);
   } else {
     for (uint32_t spins = 0;; ++spins) {
+      unsigned long long pair[N];
+#pragma unroll
+      for (int q = 0; q < N; ++q)
+        if (q < nq)
+          pair[q] = __hip_atomic_load(L.vtag + (idx[q] >= 0 ? idx[q] : safe), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
       bool ok = true;
 #pragma unroll
       for (int q = 0; q < N; ++q) {
-        const int64_t idx = get(q);
-        float val = 0.f;
-        if (idx >= 0) {
-          const unsigned long long pair =
-              __hip_atomic_load(L.vtag + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = ok && (uint32_t)(pair >> 32) == L.epoch;
-          val = __uint_as_float((uint32_t)pair);
+        if (q < nq) {
+          ok = ok && (idx[q] < 0 || (uint32_t)(pair[q] >> 32) == L.epoch);
+          put(q, idx[q] >= 0 ? __uint_as_float((uint32_t)pair[q]) : 0.f);
         }
-        put(q, val);
       }
       if (__syncthreads_and(ok)) break;
       if (spins >= kMaxSpins) {
@@ -251,7 +299,7 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     const bool inb = c < nchunks;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-      a[r][ck] = (inb && r < nrows) ? ld16(arow[r] + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
+      a[r][ck] = (inb && r < nrows) ? ldsel<SLORA_NT_A>(arow[r] + (int64_t)c * 16) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int k = 0; k < TB; ++k)
       xv[k][ck] = (inb && k < ntok) ? ld16(xrow[k] + (int64_t)c * VEC) : make_uint4(0, 0, 0, 0);
@@ -287,6 +335,13 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 // row m = l%16 of X and row n = l%16 of A^T, 8 consecutive k at 8*(l/16); the
 // four waves take interleaved 32-wide k steps and are summed through LDS.
 
+#ifndef SLORA_SHRINK_RING
+#define SLORA_SHRINK_RING 16
+#endif
+// Register ring of the MFMA shrink, in 16-byte loads per lane (D stages of
+// 1 + NB loads each).
+constexpr int kShrinkRingHalf8 = SLORA_SHRINK_RING;
+
 template <int NB, bool FUSED>
 __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
   const int ntok = uni(srec[REC_NTOK]);
@@ -314,47 +369,42 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // Wave w takes the 32-wide k steps w, w+4, w+8, ...; two register stages of
-  // two steps each keep the next steps' loads in flight while the current
-  // ones feed the matrix cores.
+  // Wave w takes the 32-wide k steps w, w+4, w+8, ...: n_it of them.  Loads
+  // run D steps ahead of the matrix cores in a ring of registers.  Every load
+  // is issued unconditionally (a step past the end re-reads the wave's last
+  // step and is never multiplied), so the same number of loads is in flight
+  // on every path and the wait before a step covers that step's loads only;
+  // a load behind a branch would make the compiler wait for all of them.
   const int n_it = (L.h_in - wave * 32 + 127) >> 7;
-  constexpr int U = 2;
-  const half8 zero8 = {};
-  half8 xs0[U], as0[U][NB], xs1[U], as1[U][NB];
+  const int last = n_it > 0 ? n_it - 1 : 0;
+  const int kbase = n_it > 0 ? wave * 32 : 0;   // a wave with no step re-reads k = 0
+  constexpr int D = kShrinkRingHalf8 / (1 + NB) < 2 ? 2 : kShrinkRingHalf8 / (1 + NB);
+  half8 xs[D], as[D][NB];
+  auto load = [&](int slot, int it) {
+    const int k = kbase + (it < last ? it : last) * 128;
+    xs[slot] = __builtin_bit_cast(half8, ldsel<SLORA_NT_X>(xrow + k));
 #pragma unroll
-  for (int u = 0; u < U; ++u) {   // a step past n_it could only ever add zero
-    xs0[u] = zero8;
-    xs1[u] = zero8;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) as0[u][b] = as1[u][b] = zero8;
-  }
-  auto load = [&](half8 (&xs)[U], half8 (&as)[U][NB], int it0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (it0 + u < n_it) {
-        const int k = wave * 32 + (it0 + u) * 128;
-        xs[u] = __builtin_bit_cast(half8, ld16(xrow + k));
-#pragma unroll
-        for (int b = 0; b < NB; ++b) as[u][b] = __builtin_bit_cast(half8, ld16(arow[b] + k));
-      }
-    }
+    for (int b = 0; b < NB; ++b) as[slot][b] = __builtin_bit_cast(half8, ld16(arow[b] + k));
   };
-  auto mma = [&](half8 (&xs)[U], half8 (&as)[U][NB], int it0) {
+  // The ring is filled in slot order and kept in that order (no reordering
+  // across the barriers): the wait before slot s then only needs the loads
+  // older than slot s + 1's.
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (it0 + u < n_it) {
+  for (int slot = 0; slot < D; ++slot) {
+    load(slot, slot);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int it0 = 0; it0 < n_it; it0 += D) {
+#pragma unroll
+    for (int slot = 0; slot < D; ++slot) {
+      if (it0 + slot < n_it) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xs[u], as[u][b], acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xs[slot], as[slot][b], acc[b], 0, 0, 0);
       }
+      load(slot, it0 + slot + D);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  load(xs0, as0, 0);
-  for (int it = 0; it < n_it; it += 2 * U) {
-    load(xs1, as1, it + U);
-    mma(xs0, as0, it);
-    load(xs0, as0, it + 2 * U);
-    mma(xs1, as1, it + U);
   }
   // acc[b][i] is C[token 4g + i][rank row b*16 + l%16]; sum the four waves in LDS.
 #pragma unroll
@@ -436,15 +486,16 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   uint4 bq[RCH];
 #pragma unroll
   for (int i = 0; i < RCH; ++i)
-    bq[i] = i < nrt ? ld16(L.pool.base_b + (int64_t)pages[g + i * G] * L.pool.page_bytes_b + col_byte)
+    bq[i] = i < nrt ? ldsel<SLORA_NT_B>(L.pool.base_b + (int64_t)pages[g + i * G] * L.pool.page_bytes_b + col_byte)
                     : make_uint4(0, 0, 0, 0);
   uint4 yv[TB];
 #pragma unroll
   for (int k = 0; k < TB; ++k)
-    yv[k] = (g == 0 && active && k < ntok) ? ld16(y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC)
+    yv[k] = (g == 0 && active && k < ntok) ? ldsel<SLORA_NT_Y>(y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC)
                                            : make_uint4(0, 0, 0, 0);
   load_v<FUSED, TB>(
-      L, [&](int q) -> int64_t { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
+      L, (ntok * rank + kThreads - 1) / kThreads, v0,
+      [&](int q) -> int64_t { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
       [&](int q, float val) { const int i = tid + q * kThreads; if (i < ntok * rank) sv[i] = val; });
   __syncthreads();
 
@@ -457,7 +508,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     if (i0 > 0) {
 #pragma unroll
       for (int i = 0; i < RCH; ++i)
-        bq[i] = i0 + i < nrt ? ld16(L.pool.base_b + (int64_t)pages[g + (i0 + i) * G] * L.pool.page_bytes_b + col_byte)
+        bq[i] = i0 + i < nrt ? ldsel<SLORA_NT_B>(L.pool.base_b + (int64_t)pages[g + (i0 + i) * G] * L.pool.page_bytes_b + col_byte)
                              : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -510,7 +561,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
         float d[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) d[e] = scale * acc[k][e];
-        st16(yp, add_round(yv[k], d, T()));
+        stsel<SLORA_NT_Y>(yp, add_round(yv[k], d, T()));
       }
     }
   }
@@ -556,17 +607,22 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   _Float16* yb = reinterpret_cast<_Float16*>(L.y);
 
   // Thread tid stages chunks tid + 256q (q < 4) of a 32 x 256 slice of B.
+  // Every global access of the pass loop below is issued unconditionally,
+  // at a clamped address where it falls outside the tile, so that the same
+  // number of memory operations is in flight on every path and each wait
+  // covers only the operands it is for.  A clamped B row (j >= rank) meets a
+  // zero s*v; a clamped column lands in an output column that is dropped.
   auto stage_load = [&](int step, uint4 (&r)[4]) {
+    step = step < n_steps ? step : n_steps - 1;
     const int pass = step / ks_n, ks = step - pass * ks_n;
     const int c0 = pass * kMfmaCols;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int chunk = tid + q * kThreads;
       const int jr = chunk >> 5, cc = (chunk & 31) * 8;
-      const int j = 32 * ks + jr;
-      r[q] = (j < rank && c0 + cc < ncol)
-                 ? ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)(o0 + c0 + cc) * 2)
-                 : make_uint4(0, 0, 0, 0);
+      const int j = min(32 * ks + jr, rank - 1);
+      const int col = min(c0 + cc, ncol - 8);
+      r[q] = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)(o0 + col) * 2);
     }
   };
   uint4 bnext[4];
@@ -575,7 +631,7 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   // s * v of the tile, zero outside ntok x rank, and its largest magnitude.
   const int kw = ks_n * 32;
   load_v<FUSED, (16 * kMaxRankMfma) / kThreads>(
-      L,
+      L, (16 * kw) / kThreads, v0,
       [&](int q) -> int64_t {
         const int i = tid + q * kThreads, mm = i / kw, j = i - mm * kw;
         return (i < 16 * kw && mm < ntok && j < rank) ? v0 + (int64_t)mm * rank + j : -1;
@@ -619,17 +675,27 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   }
   __syncthreads();  // sv is dead from here; its space becomes the epilogue buffer
 
-  for (int pass = 0; pass < n_pass; ++pass) {
-    const int c0 = pass * kMfmaCols;
-    // this pass's y chunks, fetched while the k slices run
-    uint4 yq[2];
+  // y chunks of a pass: 16 rows x 32 chunks of 8 columns, two per thread.  A
+  // thread whose chunk lies outside the tile takes the nearest chunk inside
+  // it instead (same row clamp as the column clamp), reads it, and later
+  // writes back exactly the bytes the chunk's owner writes.
+  auto y_chunk = [&](int pass, int q) -> _Float16* {
+    const int chunk = tid + q * kThreads;
+    const int mm = min(chunk >> 5, ntok - 1);
+    const int col = min(pass * kMfmaCols + (chunk & 31) * 8, ncol - 8);
+    return yb + (int64_t)toks[mm] * L.h_out + o0 + col;
+  };
+  auto load_y = [&](int pass, uint4 (&yq)[2]) {
+    pass = pass < n_pass ? pass : n_pass - 1;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int chunk = tid + q * kThreads;          // 16 rows x 32 chunks of 8
-      const int mm = chunk >> 5, cc = (chunk & 31) * 8;
-      yq[q] = (mm < ntok && c0 + cc < ncol) ? ld16(yb + (int64_t)toks[mm] * L.h_out + o0 + c0 + cc)
-                                             : make_uint4(0, 0, 0, 0);
-    }
+    for (int q = 0; q < 2; ++q) yq[q] = ldsel<SLORA_NT_Y>(y_chunk(pass, q));
+  };
+  // One pass: 256 columns, all k slices, then the epilogue.  yc holds this
+  // pass's y (fetched a pass earlier), yn receives the next pass's; the two
+  // register sets swap roles from pass to pass (a register copy would wait
+  // for the load in flight).
+  auto pass_body = [&](int pass, uint4 (&yc)[2], uint4 (&yn)[2]) {
+    const int c0 = pass * kMfmaCols;
     float4v acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -641,9 +707,9 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
         const int chunk = tid + q * kThreads;
         st16(sb + (chunk >> 5) * kMfmaPitchH + (chunk & 31) * 8, bnext[q]);
       }
-      __syncthreads();
-      const int step = pass * ks_n + ks;
-      if (step + 1 < n_steps) stage_load(step + 1, bnext);
+      lds_barrier();
+      stage_load(pass * ks_n + ks + 1, bnext);
+      if (ks == 0) load_y(pass + 1, yn);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int n = wave * 64 + c * 16 + m;
@@ -653,27 +719,33 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi[ks], bf, acc[c], 0, 0, 0);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo[ks], bf, acc[c], 0, 0, 0);
       }
-      __syncthreads();
+      lds_barrier();
     }
     // acc[c][i] = Y[4g + i][wave*64 + c*16 + l%16]; stage, then update y coalesced.
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) epi[(4 * g + i) * kMfmaEpiPitch + wave * 64 + c * 16 + m] = acc[c][i] * up;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int chunk = tid + q * kThreads;
-      const int mm = chunk >> 5, cc = (chunk & 31) * 8;
-      if (mm < ntok && c0 + cc < ncol) {
-        _Float16* yp = yb + (int64_t)toks[mm] * L.h_out + o0 + c0 + cc;
-        float d[8];
+      const int mm = min(chunk >> 5, ntok - 1);
+      const int cc = min(c0 + (chunk & 31) * 8, ncol - 8) - c0;
+      float d[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d[e] = epi[mm * kMfmaEpiPitch + cc + e];
-        st16(yp, add_round(yq[q], d, _Float16()));
-      }
+      for (int e = 0; e < 8; ++e) d[e] = epi[mm * kMfmaEpiPitch + cc + e];
+      stsel<SLORA_NT_Y>(y_chunk(pass, q), add_round(yc[q], d, _Float16()));
     }
-    __syncthreads();
+    lds_barrier();
+  };
+  uint4 y0[2], y1[2];
+  load_y(0, y0);
+  for (int pass = 0;; pass += 2) {
+    pass_body(pass, y0, y1);
+    if (pass + 1 >= n_pass) break;
+    pass_body(pass + 1, y1, y0);
+    if (pass + 2 >= n_pass) break;
   }
 }
 
