@@ -89,7 +89,9 @@ void slora_pool_destroy(slora_pool* pool);
  *  SLORA_TUNE_MFMA_MIN_TOKENS  - fp16 segments with at least this many tokens
  *                                use the matrix-core (MFMA) tiles; default 64.
  *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
- *                                expand tile; default 32768.
+ *                                expand tile; 0 (default): chosen from the
+ *                                batch (16K to 128K, growing with the
+ *                                batch's vector-ALU expand work).
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
  *                                of 256; default 1024.
  *  SLORA_TUNE_MFMA_SHRINK_ROWS - rank rows of one MFMA shrink tile, a
@@ -198,8 +200,9 @@ slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, in
  * later deltas.  The copy is asynchronous; dev_meta must stay untouched while
  * deltas that use it are in flight.  The metadata also holds the area where
  * a fused launch passes x A between its stages (the upload zeroes it on
- * `stream`), so every slora_lora_delta that uses one upload must be ordered
- * on one stream. */
+ * `stream`) and a small scratch area the kernels write and never read, so
+ * every slora_lora_delta that uses one upload must be ordered on one
+ * stream. */
 slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t dev_meta_bytes,
                                    void* stream);
 

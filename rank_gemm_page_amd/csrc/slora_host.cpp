@@ -84,7 +84,7 @@ struct AdapterRec {
 // tiles, which cut their work finer; long segments need the matrix cores.
 struct Tuning {
   int64_t mfma_min_tokens = 64;
-  int64_t gemv_expand_elems = 32768;
+  int64_t gemv_expand_elems = 0;   // 0: sized from the batch (auto_expand_elems)
   int64_t mfma_expand_cols = 1024;
   int64_t mfma_shrink_rows = 32;
   int64_t fused = 1;
@@ -149,6 +149,7 @@ struct slora_segments {
   int64_t records_words = 0;       // records and index lists (the uploaded part)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
+  int64_t sink_off_words = 0;      // kSinkWords words that take discarded stores
   int32_t gemv_rows = 0;
   const int32_t* dev_meta = nullptr;
   mutable uint32_t epoch = 0;      // fused launches since the last upload
@@ -159,7 +160,7 @@ namespace {
 // Device metadata: the tile records, an error word, then 8 bytes per
 // (token, rank row) of v pairs for the fused launch.
 size_t meta_bytes_of(const slora_segments* s) {
-  return (size_t)(s->vtag_off_words * 4) + (size_t)s->sum_rt * 8;
+  return (size_t)(s->sink_off_words + kSinkWords) * 4;
 }
 
 slora_status set_device(slora_pool* p) {
@@ -285,6 +286,25 @@ void build_tiles(slora_segments* s) {
   const int gemv_rows = kShrinkRowBudget / nck;
   s->gemv_rows = gemv_rows;
 
+  // Work per vector-ALU expand tile (rank x columns).  A small batch needs
+  // many small tiles to keep enough loads in flight; a large one runs faster
+  // with fewer, larger tiles (less per-tile setup).  Measured on MI355X the
+  // best budget tracks the batch's vector-ALU expand work / 1024, rounded
+  // down to a power of two and clamped to [16K, 128K] elements: 16K for 256
+  // Llama-7B decode tokens, 32K for the 13B mixed batch, 128K for 512 tokens
+  // of the 70B MLP projection.
+  int64_t expand_elems = p->tune.gemv_expand_elems;
+  if (expand_elems == 0) {
+    int64_t work = 0;
+    for (int32_t g = 0; g < S; ++g) {
+      const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
+      const bool mfma_seg = f16 && c >= p->tune.mfma_min_tokens && hin % 32 == 0;
+      if (!mfma_seg) work += (int64_t)((c + kGemvMaxTok - 1) / kGemvMaxTok) * s->seg_rank[g] * hout;
+    }
+    expand_elems = 16384;
+    while (expand_elems < 131072 && expand_elems * 2 <= work / 1024) expand_elems *= 2;
+  }
+
   std::vector<TileSpec> tiles;
   std::vector<std::pair<int32_t, int32_t>> blocks;
   int32_t max_rank = 1;
@@ -299,7 +319,7 @@ void build_tiles(slora_segments* s) {
     split_tokens(c, mfma ? kMfmaTok : kGemvMaxTok, blocks);
     // vector-ALU expand width: largest of vec*{256,128,64,32} with rank x width within budget
     int32_t width = vec * 256;
-    while (width > vec * 32 && (int64_t)r * width > p->tune.gemv_expand_elems) width /= 2;
+    while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
     const int32_t rows = mfma ? (int32_t)p->tune.mfma_shrink_rows : gemv_rows;
     const int32_t cols = mfma ? (int32_t)p->tune.mfma_expand_cols : width;
     for (auto& tb : blocks) {
@@ -334,6 +354,7 @@ void build_tiles(slora_segments* s) {
   s->records_words = (s->expand_idx_off_words + s->n_expand + 3) & ~(int64_t)3;
   s->error_off_words = s->records_words;            // records end 16-byte aligned
   s->vtag_off_words = s->error_off_words + 4;       // 8-byte pairs, 16-byte aligned
+  s->sink_off_words = (s->vtag_off_words + 2 * (int64_t)s->sum_rt + 63) & ~(int64_t)63;   // 256-byte aligned
   s->blob.assign((size_t)s->records_words, 0);
 
   int32_t* shrink_idx = s->blob.data() + s->shrink_idx_off_words;
@@ -465,7 +486,7 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       p->tune.mfma_min_tokens = value;
       return SLORA_OK;
     case SLORA_TUNE_GEMV_EXPAND_ELEMS:
-      if (value < 1) return fail(SLORA_E_INVAL, "gemv_expand_elems must be >= 1");
+      if (value < 0) return fail(SLORA_E_INVAL, "gemv_expand_elems must be >= 0 (0: automatic)");
       p->tune.gemv_expand_elems = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_EXPAND_COLS:
@@ -862,6 +883,7 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.has_mfma = s->n_mfma_segments > 0;
   L.error_flag = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->error_off_words));
   L.vtag = reinterpret_cast<unsigned long long*>(const_cast<int32_t*>(s->dev_meta + s->vtag_off_words));
+  L.sink = reinterpret_cast<uint4*>(const_cast<int32_t*>(s->dev_meta + s->sink_off_words));
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
     stages = STAGE_FUSED;
     if (s->epoch == 0xFFFFFFFFu) {   // epochs would wrap to pairs still zero: clear them first

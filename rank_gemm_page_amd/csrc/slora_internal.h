@@ -41,6 +41,7 @@ constexpr int kThreads = 256;           // every tile kernel runs 4 waves of 64
 constexpr int kMfmaTok = 16;            // tokens per MFMA tile (M of 16x16x32)
 constexpr int kMfmaMaxRows = 64;        // rank rows per MFMA shrink tile
 constexpr int kMfmaCols = 256;          // columns staged per MFMA expand pass
+constexpr int kSinkWords = 2048;        // 8 KB: one 16-byte slot per thread and y chunk of a tile
 constexpr int kGemvMaxTok = 4;          // tokens per vector-ALU tile
 constexpr int kShrinkRowBudget = 16;    // rows x 16-byte chunks per thread (GEMV shrink)
 
@@ -71,6 +72,7 @@ struct DeltaLaunch {
   // wait gave up
   unsigned long long* vtag;
   uint32_t* error_flag;
+  uint4* sink;                  // kSinkWords words in the metadata buffer for stores a tile discards
   uint32_t epoch;
 };
 

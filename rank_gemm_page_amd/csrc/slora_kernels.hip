@@ -676,14 +676,19 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   __syncthreads();  // sv is dead from here; its space becomes the epilogue buffer
 
   // y chunks of a pass: 16 rows x 32 chunks of 8 columns, two per thread.  A
-  // thread whose chunk lies outside the tile takes the nearest chunk inside
-  // it instead (same row clamp as the column clamp), reads it, and later
-  // writes back exactly the bytes the chunk's owner writes.
+  // thread whose chunk lies outside the tile reads the nearest chunk inside
+  // it instead and sends its result to the sink (a scratch area of the
+  // metadata buffer), so every load and store of the loop is issued.
   auto y_chunk = [&](int pass, int q) -> _Float16* {
     const int chunk = tid + q * kThreads;
     const int mm = min(chunk >> 5, ntok - 1);
     const int col = min(pass * kMfmaCols + (chunk & 31) * 8, ncol - 8);
     return yb + (int64_t)toks[mm] * L.h_out + o0 + col;
+  };
+  auto y_dest = [&](int pass, int q) -> void* {
+    const int chunk = tid + q * kThreads;
+    const bool in = (chunk >> 5) < ntok && pass * kMfmaCols + (chunk & 31) * 8 < ncol;
+    return in ? static_cast<void*>(y_chunk(pass, q)) : static_cast<void*>(L.sink + chunk);
   };
   auto load_y = [&](int pass, uint4 (&yq)[2]) {
     pass = pass < n_pass ? pass : n_pass - 1;
@@ -735,7 +740,7 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
       float d[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) d[e] = epi[mm * kMfmaEpiPitch + cc + e];
-      stsel<SLORA_NT_Y>(y_chunk(pass, q), add_round(yc[q], d, _Float16()));
+      stsel<SLORA_NT_Y>(y_dest(pass, q), add_round(yc[q], d, _Float16()));
     }
     lds_barrier();
   };

@@ -344,6 +344,8 @@ def test_tuning_validation():
     pool = small_pool()
     try:
         assert status_of(S.slora_pool_set_tuning, pool, 0, 0) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_GEMV_EXPAND_ELEMS, -1) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_GEMV_EXPAND_ELEMS, 0)
         assert status_of(S.slora_pool_set_tuning, pool, 2, 300) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, 9, 1) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FUSED, 2) == S.SLORA_E_INVAL
