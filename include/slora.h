@@ -87,13 +87,16 @@ void slora_pool_destroy(slora_pool* pool);
 
 /* Tuning knobs of the tile builder (applied by later slora_build_segments):
  *  SLORA_TUNE_MFMA_MIN_TOKENS  - fp16 segments with at least this many tokens
- *                                use the matrix-core (MFMA) tiles; default 64.
+ *                                (and rank at most SLORA_MFMA_MAX_RANK, h_in
+ *                                a multiple of 32, n_tokens x h_out x 2
+ *                                below 4 GiB) use the matrix-core (MFMA)
+ *                                tiles; default 64.
  *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
  *                                expand tile; 0 (default): chosen from the
  *                                batch (16K to 128K, growing with the
  *                                batch's vector-ALU expand work).
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
- *                                of 256; default 1024.
+ *                                of 128; default 1024.
  *  SLORA_TUNE_MFMA_SHRINK_ROWS - rank rows of one MFMA shrink tile, a
  *                                multiple of 16 up to 64; default 32.
  *  SLORA_TUNE_FUSED            - 1 (default): slora_lora_delta runs both
@@ -101,6 +104,7 @@ void slora_pool_destroy(slora_pool* pool);
  *                                waiting for its tokens' x A values;
  *                                0: two launches (shrink, then expand).
  * They change how the work is cut, never what is computed. */
+#define SLORA_MFMA_MAX_RANK 64
 typedef enum {
   SLORA_TUNE_MFMA_MIN_TOKENS = 0,
   SLORA_TUNE_GEMV_EXPAND_ELEMS = 1,
@@ -200,9 +204,8 @@ slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, in
  * later deltas.  The copy is asynchronous; dev_meta must stay untouched while
  * deltas that use it are in flight.  The metadata also holds the area where
  * a fused launch passes x A between its stages (the upload zeroes it on
- * `stream`) and a small scratch area the kernels write and never read, so
- * every slora_lora_delta that uses one upload must be ordered on one
- * stream. */
+ * `stream`), so every slora_lora_delta that uses one upload must be
+ * ordered on one stream. */
 slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t dev_meta_bytes,
                                    void* stream);
 

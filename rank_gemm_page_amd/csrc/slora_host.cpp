@@ -149,7 +149,6 @@ struct slora_segments {
   int64_t records_words = 0;       // records and index lists (the uploaded part)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
-  int64_t sink_off_words = 0;      // kSinkWords words that take discarded stores
   int32_t gemv_rows = 0;
   const int32_t* dev_meta = nullptr;
   mutable uint32_t epoch = 0;      // fused launches since the last upload
@@ -160,7 +159,7 @@ namespace {
 // Device metadata: the tile records, an error word, then 8 bytes per
 // (token, rank row) of v pairs for the fused launch.
 size_t meta_bytes_of(const slora_segments* s) {
-  return (size_t)(s->sink_off_words + kSinkWords) * 4;
+  return (size_t)(s->vtag_off_words * 4) + (size_t)s->sum_rt * 8;
 }
 
 slora_status set_device(slora_pool* p) {
@@ -286,6 +285,10 @@ void build_tiles(slora_segments* s) {
   const int gemv_rows = kShrinkRowBudget / nck;
   s->gemv_rows = gemv_rows;
 
+  // Matrix-core tiles need fp16, h_in a multiple of 32 and a y that the
+  // expand can address through one buffer descriptor.
+  const bool mfma_ok = f16 && hin % 32 == 0 && (int64_t)s->n_tokens * hout * 2 <= kMaxBufferBytes;
+
   // Work per vector-ALU expand tile (rank x columns).  A small batch needs
   // many small tiles to keep enough loads in flight; a large one runs faster
   // with fewer, larger tiles (less per-tile setup).  Measured on MI355X the
@@ -298,7 +301,7 @@ void build_tiles(slora_segments* s) {
     int64_t work = 0;
     for (int32_t g = 0; g < S; ++g) {
       const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
-      const bool mfma_seg = f16 && c >= p->tune.mfma_min_tokens && hin % 32 == 0;
+      const bool mfma_seg = mfma_ok && c >= p->tune.mfma_min_tokens && s->seg_rank[g] <= kMaxRankMfma;
       if (!mfma_seg) work += (int64_t)((c + kGemvMaxTok - 1) / kGemvMaxTok) * s->seg_rank[g] * hout;
     }
     expand_elems = 16384;
@@ -306,7 +309,7 @@ void build_tiles(slora_segments* s) {
   }
 
   std::vector<TileSpec> tiles;
-  std::vector<std::pair<int32_t, int32_t>> blocks;
+  std::vector<std::pair<int32_t, int32_t>> blocks, eblocks;   // shrink, expand token blocks
   int32_t max_rank = 1;
   s->n_mfma_segments = 0;
   s->n_shrink = s->n_expand = 0;
@@ -314,18 +317,20 @@ void build_tiles(slora_segments* s) {
     const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
     const int32_t r = s->seg_rank[g];
     max_rank = std::max(max_rank, r);
-    const bool mfma = f16 && c >= p->tune.mfma_min_tokens && hin % 32 == 0;
+    const bool mfma = mfma_ok && c >= p->tune.mfma_min_tokens && r <= kMaxRankMfma;
     if (mfma) ++s->n_mfma_segments;
     split_tokens(c, mfma ? kMfmaTok : kGemvMaxTok, blocks);
+    split_tokens(c, mfma ? kMfmaExpandTok : kGemvMaxTok, eblocks);
     // vector-ALU expand width: largest of vec*{256,128,64,32} with rank x width within budget
     int32_t width = vec * 256;
     while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
     const int32_t rows = mfma ? (int32_t)p->tune.mfma_shrink_rows : gemv_rows;
     const int32_t cols = mfma ? (int32_t)p->tune.mfma_expand_cols : width;
-    for (auto& tb : blocks) {
+    for (auto& tb : blocks)
       for (int32_t j0 = 0; j0 < r; j0 += rows, ++s->n_shrink)
         tiles.push_back({mfma ? KIND_SHRINK_MFMA : KIND_SHRINK_GEMV, g, tb.first, tb.second, j0,
                          std::min(rows, r - j0), 0});
+    for (auto& tb : eblocks) {
       for (int32_t o0 = 0; o0 < hout; o0 += cols, ++s->n_expand)
         tiles.push_back({mfma ? KIND_EXPAND_MFMA : KIND_EXPAND_GEMV, g, tb.first, tb.second, o0,
                          std::min(cols, hout - o0), mfma ? 0 : width});
@@ -346,15 +351,14 @@ void build_tiles(slora_segments* s) {
 
   const int np = s->n_proj;
   s->n_tiles = (int32_t)tiles.size();
-  s->tokcap = std::max(kGemvMaxTok, kMfmaTok);
-  s->pagecap = (std::max({gemv_rows, kMfmaMaxRows, max_rank}) + 3) & ~3;
+  s->tokcap = kTokCap;
+  s->pagecap = (std::max({gemv_rows, kMfmaMaxRows, max_rank}) + 3) & ~3;   // <= kMaxPageCap
   s->stride = (REC_HDR + s->tokcap + np * s->pagecap + 3) & ~3;
   s->shrink_idx_off_words = (int64_t)s->n_tiles * s->stride;
   s->expand_idx_off_words = s->shrink_idx_off_words + s->n_shrink;
   s->records_words = (s->expand_idx_off_words + s->n_expand + 3) & ~(int64_t)3;
   s->error_off_words = s->records_words;            // records end 16-byte aligned
   s->vtag_off_words = s->error_off_words + 4;       // 8-byte pairs, 16-byte aligned
-  s->sink_off_words = (s->vtag_off_words + 2 * (int64_t)s->sum_rt + 63) & ~(int64_t)63;   // 256-byte aligned
   s->blob.assign((size_t)s->records_words, 0);
 
   int32_t* shrink_idx = s->blob.data() + s->shrink_idx_off_words;
@@ -490,8 +494,8 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       p->tune.gemv_expand_elems = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_EXPAND_COLS:
-      if (value < kMfmaCols || value % kMfmaCols || value > 65536)
-        return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 256, at most 65536");
+      if (value < kMfmaPass || value % kMfmaPass || value > 65536)
+        return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 128, at most 65536");
       p->tune.mfma_expand_cols = value;
       return SLORA_OK;
     case SLORA_TUNE_FUSED:
@@ -883,7 +887,7 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.has_mfma = s->n_mfma_segments > 0;
   L.error_flag = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->error_off_words));
   L.vtag = reinterpret_cast<unsigned long long*>(const_cast<int32_t*>(s->dev_meta + s->vtag_off_words));
-  L.sink = reinterpret_cast<uint4*>(const_cast<int32_t*>(s->dev_meta + s->sink_off_words));
+  L.y_bytes = (uint32_t)std::min<int64_t>((int64_t)s->n_tokens * p->d.h_out * elem_bytes(p->d.dtype), kMaxBufferBytes);
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
     stages = STAGE_FUSED;
     if (s->epoch == 0xFFFFFFFFu) {   // epochs would wrap to pairs still zero: clear them first

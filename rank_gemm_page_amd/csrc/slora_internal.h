@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+#include "slora.h"
+
 namespace slora {
 
 // A tile record is a run of int32 words:
@@ -38,12 +40,21 @@ enum : int32_t {
 
 // Fixed tile geometry shared by the builder and the kernels.
 constexpr int kThreads = 256;           // every tile kernel runs 4 waves of 64
-constexpr int kMfmaTok = 16;            // tokens per MFMA tile (M of 16x16x32)
+constexpr int kMfmaTok = 16;            // tokens per MFMA shrink tile (M of 16x16x32)
+constexpr int kMfmaExpandTok = 64;      // tokens per MFMA expand tile (four waves of 16)
+constexpr int kMaxRankMfma = SLORA_MFMA_MAX_RANK;   // rank limit of MFMA segments
+constexpr int kTokCap = 64;             // token slots of every record (>= every tile kind's)
+constexpr int kMaxPageCap = 256;        // page slots per projection (max_rank <= 256)
 constexpr int kMfmaMaxRows = 64;        // rank rows per MFMA shrink tile
-constexpr int kMfmaCols = 256;          // columns staged per MFMA expand pass
-constexpr int kSinkWords = 2048;        // 8 KB: one 16-byte slot per thread and y chunk of a tile
+constexpr int kMfmaPass = 128;          // columns per MFMA expand pass
+// The MFMA expand addresses y through a buffer descriptor (stores past its
+// extent are dropped by the hardware): MFMA tiles are used only while y fits
+// in this many bytes.
+constexpr int64_t kMaxBufferBytes = 0xFFFFFF00LL;
 constexpr int kGemvMaxTok = 4;          // tokens per vector-ALU tile
 constexpr int kShrinkRowBudget = 16;    // rows x 16-byte chunks per thread (GEMV shrink)
+static_assert(kTokCap >= kGemvMaxTok && kTokCap >= kMfmaTok && kTokCap >= kMfmaExpandTok, "token slots");
+static_assert(kMfmaMaxRows <= kMaxPageCap, "page slots");
 
 struct PoolView {
   const char* base_a;     // class of the A^T pages
@@ -72,7 +83,7 @@ struct DeltaLaunch {
   // wait gave up
   unsigned long long* vtag;
   uint32_t* error_flag;
-  uint4* sink;                  // kSinkWords words in the metadata buffer for stores a tile discards
+  uint32_t y_bytes;       // extent of y (n_tokens x h_out x element), < kMaxBufferBytes when has_mfma
   uint32_t epoch;
 };
 

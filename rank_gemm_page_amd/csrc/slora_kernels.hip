@@ -177,7 +177,7 @@ __device__ __forceinline__ void lds_barrier() {
 // page list of projection `proj`) into LDS with one batch of independent
 // loads, so that page ids and token ids come from LDS instead of a chain of
 // dependent global loads.  Layout in LDS: [HDR][tokcap][pagecap].
-constexpr int kMaxRecWords = REC_HDR + 16 + 256;
+constexpr int kMaxRecWords = REC_HDR + kTokCap + kMaxPageCap;
 
 __device__ __forceinline__ void record_to_lds(const int32_t* rec, int tokcap, int pagecap, int proj,
                                               int32_t* srec) {
@@ -223,8 +223,8 @@ __device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float
 // any is consumed, at index `safe` (any valid v index) for a slot with no
 // value, so they travel to memory together instead of one round trip each.
 template <bool FUSED, int N, typename Get, typename Put>
-__device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int64_t safe, Get get, Put put) {
-  int64_t idx[N];
+__device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, Get get, Put put) {
+  int idx[N];
 #pragma unroll
   for (int q = 0; q < N; ++q) idx[q] = q < nq ? get(q) : -1;
   if constexpr (!FUSED) {
@@ -495,7 +495,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
                                            : make_uint4(0, 0, 0, 0);
   load_v<FUSED, TB>(
       L, (ntok * rank + kThreads - 1) / kThreads, v0,
-      [&](int q) -> int64_t { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
+      [&](int q) -> int { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
       [&](int q, float val) { const int i = tid + q * kThreads; if (i < ntok * rank) sv[i] = val; });
   __syncthreads();
 
@@ -568,20 +568,34 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 }
 
 // ---------------------------------------------------------------------------
-// Expand, MFMA tile (fp16): 16 tokens x `len` columns, all r rows.
-// Y[m][o] += sum_j (s v)[m][j] * B_j[o], with A operand = s*v (16 x 32 slice of
-// j, split hi + lo in fp16 after a power-of-two normalisation of the tile) and
-// B operand = a 32-row x 256-column slice of the B pages staged in LDS.
-// Lane (m = l%16, g = l/16) feeds element i of a k step with j = 32*ks + g + 4*i
-// in both operands (any common k order gives the same sum); that order puts
-// the four lane groups on rows g..g+3 of the LDS slice, which with a row pitch
-// of 272 halves are 8 banks apart, so the column gathers are conflict-free.
+// Expand, MFMA tile (fp16): up to 64 tokens x `len` columns, all r rows
+// (r <= kMaxRankMfma).  Y[t][o] += sum_j (s v)[t][j] * B_j[o] with
+// v_mfma_f32_16x16x32_f16: the A operand is 16 tokens x 32 rows of s*v, split
+// into an fp16 high and low part after a per-token power-of-two
+// normalisation (about 22 significant bits, registers); the B operand is 32
+// rows x 16 columns of a B slice staged row-major in LDS and read with
+// ds_read_b64_tr_b16, which hands each lane 4 rows of one column.  Wave w
+// owns tokens 16w .. 16w+15 and every column of a pass, so the four waves
+// share each staged slice (a quarter of the B reads of 16-token tiles).  The
+// accumulators leave through LDS, so y is read and written in whole
+// 128-byte lines.
 
-constexpr int kMfmaPitchH = kMfmaCols + 16;    // halves per staged B row
-constexpr int kMfmaEpiPitch = kMfmaCols + 4;   // floats per epilogue row
-constexpr int kMaxRankMfma = 256;
+constexpr int kSliceRowDw = kMfmaPass / 2;      // dwords per 128-column row
+constexpr int kSliceDw = 32 * kSliceRowDw;      // one staged 32-row slice (8 KB)
+constexpr int kEpiPitch = kMfmaPass + 4;        // floats per epilogue row
+constexpr int kMfmaExpandLds = 2 * kSliceDw + kMfmaExpandTok * kEpiPitch + kMfmaExpandTok;
 
-template <bool FUSED>
+// Dword offset of column quad q (4 columns) of row r of a staged slice.  The
+// quads are XOR-swizzled by row so that the 8 rows the two lane groups of a
+// half-wave read together (8g + t, t = 0..3) land in distinct banks.
+__device__ __forceinline__ int quad_dw(int r, int q) {
+  return r * kSliceRowDw + 2 * (q ^ (4 * ((r & 3) + 4 * ((r >> 3) & 1))));
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+constexpr int kBufferFormat = 0x00020000;   // descriptor word 3: raw 32-bit buffer
+
+template <bool FUSED, int KS>
 __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
@@ -593,159 +607,147 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
-  const int ks_n = (rank + 31) >> 5;
-  const int vp = ks_n * 32 + 4;                       // sv pitch (floats)
-  const int n_pass = (ncol + kMfmaCols - 1) / kMfmaCols;
-  const int n_steps = n_pass * ks_n;                  // (pass, k slice), pass-major
-
-  // LDS: sv [16][vp] floats, reused as the epilogue buffer [16][kMfmaEpiPitch];
-  // then the staged B slice [32][kMfmaPitchH] halves; then a reduction slot.
-  float* sv = lds;
-  float* epi = lds;
-  _Float16* sb = reinterpret_cast<_Float16*>(lds + 16 * (kMaxRankMfma + 4));
-  float* wmax = lds + 16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2;
+  const int ks_n = (rank + 31) >> 5;                   // <= KS
+  const int n_pass = (ncol + kMfmaPass - 1) / kMfmaPass;
+  const int n_steps = n_pass * ks_n;                   // (pass, k slice), pass-major
+  uint32_t* slice = reinterpret_cast<uint32_t*>(lds);  // two slices, used in turn
+  float* epi = lds + 2 * kSliceDw;                     // [64][kEpiPitch]
+  float* up_tok = epi + kMfmaExpandTok * kEpiPitch;    // per-token scale back
   _Float16* yb = reinterpret_cast<_Float16*>(L.y);
+  const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(L.y, 0, (int)L.y_bytes, kBufferFormat);
 
-  // Thread tid stages chunks tid + 256q (q < 4) of a 32 x 256 slice of B.
-  // Every global access of the pass loop below is issued unconditionally,
-  // at a clamped address where it falls outside the tile, so that the same
-  // number of memory operations is in flight on every path and each wait
-  // covers only the operands it is for.  A clamped B row (j >= rank) meets a
-  // zero s*v; a clamped column lands in an output column that is dropped.
-  auto stage_load = [&](int step, uint4 (&r)[4]) {
+  // Every global access below is issued unconditionally (loads at a clamped
+  // address where they fall outside the tile), so that each wait covers only
+  // the operands it is for.  A clamped B row (j >= rank) meets a zero s*v.
+  //
+  // Staging: thread tid moves 8 columns (chunk tid & 15) of rows tid >> 4 and
+  // 16 + (tid >> 4) of a slice: 16 threads cover a row's 256 bytes.
+  const int s_chunk = tid & 15, s_row = tid >> 4;
+  auto stage_load = [&](int step, uint4 (&r)[2]) {
     step = step < n_steps ? step : n_steps - 1;
     const int pass = step / ks_n, ks = step - pass * ks_n;
-    const int c0 = pass * kMfmaCols;
+    const int col = min(pass * kMfmaPass + 8 * s_chunk, ncol - 8);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int chunk = tid + q * kThreads;
-      const int jr = chunk >> 5, cc = (chunk & 31) * 8;
-      const int j = min(32 * ks + jr, rank - 1);
-      const int col = min(c0 + cc, ncol - 8);
-      r[q] = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)(o0 + col) * 2);
+    for (int h = 0; h < 2; ++h) {
+      const int j = min(32 * ks + s_row + 16 * h, rank - 1);
+      r[h] = ld16(L.pool.base_b + (int64_t)pages[j] * L.pool.page_bytes_b + (int64_t)(o0 + col) * 2);
     }
   };
-  uint4 bnext[4];
-  stage_load(0, bnext);
-
-  // s * v of the tile, zero outside ntok x rank, and its largest magnitude.
-  const int kw = ks_n * 32;
-  load_v<FUSED, (16 * kMaxRankMfma) / kThreads>(
-      L, (16 * kw) / kThreads, v0,
-      [&](int q) -> int64_t {
-        const int i = tid + q * kThreads, mm = i / kw, j = i - mm * kw;
-        return (i < 16 * kw && mm < ntok && j < rank) ? v0 + (int64_t)mm * rank + j : -1;
-      },
-      [&](int q, float val) {
-        const int i = tid + q * kThreads, mm = i / kw, j = i - mm * kw;
-        if (i < 16 * kw) sv[mm * vp + j] = scale * val;
-      });
-  float amax = 0.f;
-  for (int i = tid; i < 16 * kw; i += kThreads) {
-    const int mm = i / kw, j = i - mm * kw;
-    amax = fmaxf(amax, fabsf(sv[mm * vp + j]));
-  }
+  auto stage_store = [&](uint32_t* dst, const uint4 (&r)[2]) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if (lane == 0) wmax[wave] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  // Bring the largest |s v| into [2^14, 2^15) so hi and lo stay normal fp16.
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint4*>(dst + quad_dw(s_row + 16 * h, 2 * s_chunk)) = r[h];
+  };
+  // y chunks of a pass: thread tid takes 8 columns (chunk tid & 15) of tile
+  // rows (tid >> 4) + 16k, k = 0..3.
+  auto y_row = [&](int k) { return (tid >> 4) + 16 * k; };
+  auto y_col = [&](int pass) { return pass * kMfmaPass + 8 * (tid & 15); };
+  auto load_y = [&](int pass, uint4 (&yq)[4]) {
+    pass = pass < n_pass ? pass : n_pass - 1;
+    const int col = min(y_col(pass), ncol - 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      yq[k] = ldsel<SLORA_NT_Y>(yb + (int64_t)toks[min(y_row(k), ntok - 1)] * L.h_out + o0 + col);
+  };
+
+  uint4 bnext[2];
+  stage_load(0, bnext);
+  uint4 y0[4], y1[4];
+  load_y(0, y0);
+
+  // s*v of this lane's token (16 wave + m) at rows 32ks + 8g + i, zero past
+  // ntok / rank.
+  const int tok = 16 * wave + m;
+  float sv[8 * KS];
+  load_v<FUSED, 8 * KS>(
+      L, 8 * ks_n, v0,
+      [&](int q) -> int {
+        const int j = 32 * (q >> 3) + 8 * g + (q & 7);
+        return (tok < ntok && j < rank) ? v0 + tok * rank + j : -1;
+      },
+      [&](int q, float val) { sv[q] = scale * val; });
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8 * KS; ++q)
+    if (q < 8 * ks_n) amax = fmaxf(amax, fabsf(sv[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  // Bring the token's largest |s v| into [2^14, 2^15) so hi and lo stay normal fp16.
   int ex = 0;
   if (amax > 0.f) {
-    (void)frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
-    ex = max(ex - 15, -100);   // keep 2^-ex finite for all-subnormal tiles
+    (void)frexpf(amax, &ex);
+    ex = max(ex - 15, -100);
   }
-  const float down = ldexpf(1.f, -ex), up = ldexpf(1.f, ex);
-
-  half8 vhi[kMaxRankMfma / 32], vlo[kMaxRankMfma / 32];
+  const float down = ldexpf(1.f, -ex);
+  if (g == 0) up_tok[tok] = ldexpf(1.f, ex);
+  half8 vhi[KS], vlo[KS];
 #pragma unroll
-  for (int ks = 0; ks < kMaxRankMfma / 32; ++ks) {
-    vhi[ks] = half8{};
-    vlo[ks] = half8{};
-    if (ks < ks_n) {
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float s = sv[m * vp + 32 * ks + g + 4 * i] * down;
-        const _Float16 h = (_Float16)s;
-        vhi[ks][i] = h;
-        vlo[ks][i] = (_Float16)(s - (float)h);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const float f = sv[8 * ks + i] * down;
+      const _Float16 h = (_Float16)f;
+      vhi[ks][i] = h;
+      vlo[ks][i] = (_Float16)(f - (float)h);
     }
   }
-  __syncthreads();  // sv is dead from here; its space becomes the epilogue buffer
 
-  // y chunks of a pass: 16 rows x 32 chunks of 8 columns, two per thread.  A
-  // thread whose chunk lies outside the tile reads the nearest chunk inside
-  // it instead and sends its result to the sink (a scratch area of the
-  // metadata buffer), so every load and store of the loop is issued.
-  auto y_chunk = [&](int pass, int q) -> _Float16* {
-    const int chunk = tid + q * kThreads;
-    const int mm = min(chunk >> 5, ntok - 1);
-    const int col = min(pass * kMfmaCols + (chunk & 31) * 8, ncol - 8);
-    return yb + (int64_t)toks[mm] * L.h_out + o0 + col;
-  };
-  auto y_dest = [&](int pass, int q) -> void* {
-    const int chunk = tid + q * kThreads;
-    const bool in = (chunk >> 5) < ntok && pass * kMfmaCols + (chunk & 31) * 8 < ncol;
-    return in ? static_cast<void*>(y_chunk(pass, q)) : static_cast<void*>(L.sink + chunk);
-  };
-  auto load_y = [&](int pass, uint4 (&yq)[2]) {
-    pass = pass < n_pass ? pass : n_pass - 1;
+  // One pass: kMfmaPass columns, all k slices, then the epilogue.  yc holds
+  // this pass's y (fetched a pass earlier), yn receives the next pass's; the
+  // two register sets swap roles from pass to pass.  Slices alternate between
+  // two LDS buffers, so one barrier per slice suffices: a buffer is written
+  // again only after every wave has passed the barrier of the slice that
+  // followed its last read.
+  auto pass_body = [&](int pass, uint4 (&yc)[4], uint4 (&yn)[4]) {
+    float4v acc[kMfmaPass / 16];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) yq[q] = ldsel<SLORA_NT_Y>(y_chunk(pass, q));
-  };
-  // One pass: 256 columns, all k slices, then the epilogue.  yc holds this
-  // pass's y (fetched a pass earlier), yn receives the next pass's; the two
-  // register sets swap roles from pass to pass (a register copy would wait
-  // for the load in flight).
-  auto pass_body = [&](int pass, uint4 (&yc)[2], uint4 (&yn)[2]) {
-    const int c0 = pass * kMfmaCols;
-    float4v acc[4];
+    for (int c = 0; c < kMfmaPass / 16; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kMaxRankMfma / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       if (ks >= ks_n) break;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int chunk = tid + q * kThreads;
-        st16(sb + (chunk >> 5) * kMfmaPitchH + (chunk & 31) * 8, bnext[q]);
-      }
+      const int step = pass * ks_n + ks;
+      uint32_t* buf = slice + (step & 1) * kSliceDw;
+      stage_store(buf, bnext);
       lds_barrier();
-      stage_load(pass * ks_n + ks + 1, bnext);
+      stage_load(step + 1, bnext);
       if (ks == 0) load_y(pass + 1, yn);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int n = wave * 64 + c * 16 + m;
-        half8 bf;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bf[i] = sb[(g + 4 * i) * kMfmaPitchH + n];
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi[ks], bf, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo[ks], bf, acc[c], 0, 0, 0);
+      for (int cb = 0; cb < kMfmaPass / 16; ++cb) {
+        // lane (m, g) reads row 8g + m/4 (+4), columns 16cb + 4(m%4) .. +3;
+        // the transposing read returns rows 8g .. 8g+3 (+4) of column 16cb + m.
+        const uint32_t* p0 = buf + quad_dw(8 * g + (m >> 2), 4 * cb + (m & 3));
+        const uint32_t* p1 = buf + quad_dw(8 * g + 4 + (m >> 2), 4 * cb + (m & 3));
+        const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(p0));
+        const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(p1));
+        const half8 bop = __builtin_bit_cast(half8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi[ks], bop, acc[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo[ks], bop, acc[cb], 0, 0, 0);
       }
-      lds_barrier();
     }
-    // acc[c][i] = Y[4g + i][wave*64 + c*16 + l%16]; stage, then update y coalesced.
+    // acc[cb][i] = Y[token 16 wave + 4g + i][column 16cb + m] (before the scale back)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int cb = 0; cb < kMfmaPass / 16; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) epi[(4 * g + i) * kMfmaEpiPitch + wave * 64 + c * 16 + m] = acc[c][i] * up;
+      for (int i = 0; i < 4; ++i) epi[(16 * wave + 4 * g + i) * kEpiPitch + 16 * cb + m] = acc[cb][i];
     lds_barrier();
+    const int col = y_col(pass);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int chunk = tid + q * kThreads;
-      const int mm = min(chunk >> 5, ntok - 1);
-      const int cc = min(c0 + (chunk & 31) * 8, ncol - 8) - c0;
+    for (int k = 0; k < 4; ++k) {
+      const int row = y_row(k);
+      const float* e = epi + row * kEpiPitch + 8 * (tid & 15);
+      const float u = up_tok[row];
       float d[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d[e] = epi[mm * kMfmaEpiPitch + cc + e];
-      stsel<SLORA_NT_Y>(y_dest(pass, q), add_round(yc[q], d, _Float16()));
+      for (int i = 0; i < 8; ++i) d[i] = e[i] * u;
+      const uint4 out = add_round(yc[k], d, _Float16());
+      // A row or column outside the tile stores past the descriptor's extent,
+      // which the hardware drops: no branch, no traffic.
+      const uint32_t off = (row < ntok && col < ncol) ? 2u * ((uint32_t)toks[row] * L.h_out + o0 + col) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{out.x, out.y, out.z, out.w}, yrsrc, off, 0, SLORA_NT_Y ? 2 : 0);
     }
-    lds_barrier();
   };
-  uint4 y0[2], y1[2];
-  load_y(0, y0);
   for (int pass = 0;; pass += 2) {
     pass_body(pass, y0, y1);
     if (pass + 1 >= n_pass) break;
@@ -754,20 +756,26 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   }
 }
 
-constexpr int kExpandLdsFloats =
-    (16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2 + 4) > (kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256)
-        ? (16 * (kMaxRankMfma + 4) + (32 * kMfmaPitchH) / 2 + 4)
-        : (kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256);
+template <bool FUSED>
+__device__ __forceinline__ void expand_mfma_dispatch(const DeltaLaunch& L, const int32_t* srec, float* lds) {
+  expand_mfma_tile<FUSED, kMaxRankMfma / 32>(L, srec, lds);
+}
+
+// LDS of the expand tiles: the vector-ALU tiles need kGemvLdsFloats, the
+// MFMA tiles kMfmaExpandLds.  Kernels that never run an MFMA tile allocate
+// the smaller size, which keeps four of them resident per CU.
+constexpr int kGemvLdsFloats = kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256;
+constexpr int kExpandLdsFloats = kMfmaExpandLds > kGemvLdsFloats ? kMfmaExpandLds : kGemvLdsFloats;
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
-  __shared__ float lds[kExpandLdsFloats];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void expand_kernel(DeltaLaunch L) {
+  __shared__ float lds[sizeof(T) == 2 ? kExpandLdsFloats : kGemvLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
   const int32_t* rec = L.rec + (int64_t)L.expand_idx[blockIdx.x] * L.stride;
   record_to_lds(rec, L.tokcap, L.pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
     if (uni(srec[REC_KIND]) & KIND_MFMA_BIT) {
-      expand_mfma_tile<false>(L, srec, lds);
+      expand_mfma_dispatch<false>(L, srec, lds);
       return;
     }
   }
@@ -779,9 +787,13 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(DeltaLaunch L) {
 // MFMA=false leaves the matrix-core tiles out (a batch without them), which
 // keeps the register budget, and so the workgroups resident per CU, of the
 // vector-ALU tiles alone.
+// Three workgroups per CU fit the matrix-core tiles' registers without
+// spilling (fewer would leave slots empty); the widest vector-ALU shrink
+// (h_in above 8192) needs more registers and runs two.
 template <typename T, int NCK, bool MFMA>
-__global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
-  __shared__ float lds[kExpandLdsFloats];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCK == 8 ? 2 : 3)))
+void fused_kernel(DeltaLaunch L) {
+  __shared__ float lds[sizeof(T) == 2 && MFMA ? kExpandLdsFloats : kGemvLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
   record_to_lds(L.rec + (int64_t)blockIdx.x * L.stride, L.tokcap, L.pagecap, L.proj, srec);
   const int kind = uni(srec[REC_KIND]);
@@ -797,7 +809,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(DeltaLaunch L) {
   }
   if constexpr (sizeof(T) == 2 && MFMA) {
     if (kind & KIND_MFMA_BIT) {
-      expand_mfma_tile<true>(L, srec, lds);
+      expand_mfma_dispatch<true>(L, srec, lds);
       return;
     }
   }
