@@ -109,6 +109,7 @@ def main():
     ap.add_argument("--gemv-expand-elems", type=int, default=None)
     ap.add_argument("--mfma-expand-cols", type=int, default=None)
     ap.add_argument("--mfma-shrink-rows", type=int, default=None)
+    ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -141,7 +142,8 @@ def main():
     tuning = {k: v for k, v in ((S.SLORA_TUNE_MFMA_MIN_TOKENS, args.mfma_min_tokens),
                                 (S.SLORA_TUNE_GEMV_EXPAND_ELEMS, args.gemv_expand_elems),
                                 (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
-                                (S.SLORA_TUNE_MFMA_SHRINK_ROWS, args.mfma_shrink_rows))
+                                (S.SLORA_TUNE_MFMA_SHRINK_ROWS, args.mfma_shrink_rows),
+                                (S.SLORA_TUNE_XCDS, args.xcds))
               if v is not None}
     dw = DeviceWorkload(w, dev, tuning=tuning)
     spec = w.spec

@@ -103,6 +103,9 @@ void slora_pool_destroy(slora_pool* pool);
  *                                stages in one launch, each expand tile
  *                                waiting for its tokens' x A values;
  *                                0: two launches (shrink, then expand).
+ *  SLORA_TUNE_XCDS             - n > 1: the shrink tiles of each token block
+ *                                go to one of n XCDs (workgroup i runs on
+ *                                XCD i mod n); 1 (default): no grouping.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
@@ -110,7 +113,8 @@ typedef enum {
   SLORA_TUNE_GEMV_EXPAND_ELEMS = 1,
   SLORA_TUNE_MFMA_EXPAND_COLS = 2,
   SLORA_TUNE_MFMA_SHRINK_ROWS = 3,
-  SLORA_TUNE_FUSED = 4
+  SLORA_TUNE_FUSED = 4,
+  SLORA_TUNE_XCDS = 5
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 

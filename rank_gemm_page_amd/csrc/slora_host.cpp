@@ -88,6 +88,7 @@ struct Tuning {
   int64_t mfma_expand_cols = 1024;
   int64_t mfma_shrink_rows = 32;
   int64_t fused = 1;
+  int64_t xcds = 1;             // XCD groups of the shrink placement (1: none)
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -261,6 +262,7 @@ slora_status upload_adapter(slora_pool* p, const AdapterRec& rec, const void* co
 
 struct TileSpec {
   int32_t kind, seg, i0, ntok, pos, len, aux;
+  int32_t grp;   // token group for the XCD placement (tiles sharing x rows)
 };
 
 void split_tokens(int32_t c, int32_t cap, std::vector<std::pair<int32_t, int32_t>>& out) {
@@ -311,6 +313,7 @@ void build_tiles(slora_segments* s) {
   std::vector<TileSpec> tiles;
   std::vector<std::pair<int32_t, int32_t>> blocks, eblocks;   // shrink, expand token blocks
   int32_t max_rank = 1;
+  int32_t n_groups = 0;
   s->n_mfma_segments = 0;
   s->n_shrink = s->n_expand = 0;
   for (int32_t g = 0; g < S; ++g) {
@@ -326,15 +329,22 @@ void build_tiles(slora_segments* s) {
     while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
     const int32_t rows = mfma ? (int32_t)p->tune.mfma_shrink_rows : gemv_rows;
     const int32_t cols = mfma ? (int32_t)p->tune.mfma_expand_cols : width;
+    // Placement group: the expand block holding the tile's first token.
+    auto grp_of = [&](int32_t i0) {
+      size_t b = 0;
+      while (b + 1 < eblocks.size() && eblocks[b + 1].first <= i0) ++b;
+      return n_groups + (int32_t)b;
+    };
     for (auto& tb : blocks)
       for (int32_t j0 = 0; j0 < r; j0 += rows, ++s->n_shrink)
         tiles.push_back({mfma ? KIND_SHRINK_MFMA : KIND_SHRINK_GEMV, g, tb.first, tb.second, j0,
-                         std::min(rows, r - j0), 0});
+                         std::min(rows, r - j0), 0, grp_of(tb.first)});
     for (auto& tb : eblocks) {
       for (int32_t o0 = 0; o0 < hout; o0 += cols, ++s->n_expand)
         tiles.push_back({mfma ? KIND_EXPAND_MFMA : KIND_EXPAND_GEMV, g, tb.first, tb.second, o0,
-                         std::min(cols, hout - o0), mfma ? 0 : width});
+                         std::min(cols, hout - o0), mfma ? 0 : width, grp_of(tb.first)});
     }
+    n_groups += (int32_t)eblocks.size();
   }
 
   // Launch order: every shrink tile before every expand tile, the matrix-core
@@ -348,6 +358,49 @@ void build_tiles(slora_segments* s) {
   std::stable_sort(tiles.begin(), tiles.end(), [&](const TileSpec& a, const TileSpec& b) {
     return launch_rank(a) < launch_rank(b);
   });
+
+  // Optional XCD-aware placement of the shrink tiles (SLORA_TUNE_XCDS > 1).
+  // Workgroup i of a launch runs on XCD i mod 8 (checked on MI355X), and each
+  // XCD has its own L2.  The shrink tiles of one token block all read the
+  // block's x rows; they are given one XCD (greedily, by the bytes they move)
+  // and laid out so that position i holds a tile of XCD i mod n.  Measured,
+  // it does not pay on the benchmark batches: the 7B decode is 1.5 us slower
+  // (the stage no longer spreads evenly over all XCDs) and the 70B MLP
+  // projection shows no change beyond its +-8 % run-to-run spread, so it is
+  // off by default.
+  const int nx = (int)p->tune.xcds;
+  if (nx > 1 && s->n_shrink > 0) {
+    const int e = f16 ? 2 : 4;
+    std::vector<double> grp_work(n_groups, 0.0);
+    for (int32_t i = 0; i < s->n_shrink; ++i)
+      grp_work[tiles[i].grp] += (double)e * hin * (tiles[i].len + (double)tiles[i].ntok);
+    std::vector<int32_t> order(n_groups);
+    for (int32_t k = 0; k < n_groups; ++k) order[k] = k;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return grp_work[a] > grp_work[b]; });
+    std::vector<double> load(nx, 0.0);
+    std::vector<int> grp_xcd(n_groups, 0);
+    for (int32_t k : order) {
+      const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      grp_xcd[k] = x;
+      load[x] += grp_work[k];
+    }
+    std::vector<TileSpec> placed;
+    placed.reserve(tiles.size());
+    std::vector<std::vector<TileSpec>> q(nx);
+    std::vector<size_t> head(nx, 0);
+    for (int32_t i = 0; i < s->n_shrink; ++i) q[grp_xcd[tiles[i].grp]].push_back(tiles[i]);
+    for (int32_t pos = 0; pos < s->n_shrink; ++pos) {
+      int x = pos % nx;
+      if (head[x] == q[x].size()) {   // this XCD's queue is spent: take from the longest remaining
+        size_t best = 0;
+        for (int y = 0; y < nx; ++y)
+          if (q[y].size() - head[y] > best) best = q[y].size() - head[y], x = y;
+      }
+      placed.push_back(q[x][head[x]++]);
+    }
+    placed.insert(placed.end(), tiles.begin() + s->n_shrink, tiles.end());
+    tiles.swap(placed);
+  }
 
   const int np = s->n_proj;
   s->n_tiles = (int32_t)tiles.size();
@@ -497,6 +550,10 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       if (value < kMfmaPass || value % kMfmaPass || value > 65536)
         return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 128, at most 65536");
       p->tune.mfma_expand_cols = value;
+      return SLORA_OK;
+    case SLORA_TUNE_XCDS:
+      if (value < 1 || value > 64) return fail(SLORA_E_INVAL, "xcds must be 1..64");
+      p->tune.xcds = value;
       return SLORA_OK;
     case SLORA_TUNE_FUSED:
       if (value != 0 && value != 1) return fail(SLORA_E_INVAL, "fused must be 0 or 1");

@@ -124,6 +124,23 @@ def test_page_permutation_invariance_bit_exact():
     assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
 
 
+@pytest.mark.parametrize("launch", list(LAUNCH))
+def test_xcd_placement_changes_nothing(launch):
+    """Grouping the shrink tiles by XCD reorders the launch, never the
+    arithmetic of a tile: results are bit-identical to the ungrouped order."""
+    spec = small_spec("xcd", h_in=1024, h_out=768, two_classes=True, n_adapters=12,
+                      batch=("zipf", 96, 1.1), pool=("occ", 1, 2))
+    outs = []
+    for xcds in (1, 8, 3):
+        w = generate(spec, 4)
+        (y,), _ = run_gpu(w, "default", launch=launch,
+                          tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 8, S.SLORA_TUNE_XCDS: xcds})
+        outs.append(y)
+    y_ref, sd_ref = oracle(w)
+    check_gates(outs[0], y_ref, sd_ref, w.np_dtype, "xcd")
+    assert all(np.array_equal(outs[0].view(np.uint16), o.view(np.uint16)) for o in outs[1:])
+
+
 @pytest.mark.parametrize("route", ["gemv", "mfma"])
 def test_deterministic_run_to_run(route):
     """Same result bit for bit from repeated fused launches on one upload (epochs
