@@ -108,7 +108,7 @@ def main():
     ap.add_argument("--mfma-min-tokens", type=int, default=None)
     ap.add_argument("--gemv-expand-elems", type=int, default=None)
     ap.add_argument("--mfma-expand-cols", type=int, default=None)
-    ap.add_argument("--mfma-shrink-rows", type=int, default=None)
+    ap.add_argument("--mfma-shrink-splits", type=int, default=None)
     ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
@@ -142,7 +142,7 @@ def main():
     tuning = {k: v for k, v in ((S.SLORA_TUNE_MFMA_MIN_TOKENS, args.mfma_min_tokens),
                                 (S.SLORA_TUNE_GEMV_EXPAND_ELEMS, args.gemv_expand_elems),
                                 (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
-                                (S.SLORA_TUNE_MFMA_SHRINK_ROWS, args.mfma_shrink_rows),
+                                (S.SLORA_TUNE_MFMA_SHRINK_SPLITS, args.mfma_shrink_splits),
                                 (S.SLORA_TUNE_XCDS, args.xcds))
               if v is not None}
     dw = DeviceWorkload(w, dev, tuning=tuning)

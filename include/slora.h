@@ -88,7 +88,7 @@ void slora_pool_destroy(slora_pool* pool);
 /* Tuning knobs of the tile builder (applied by later slora_build_segments):
  *  SLORA_TUNE_MFMA_MIN_TOKENS  - fp16 segments with at least this many tokens
  *                                (and rank at most SLORA_MFMA_MAX_RANK, h_in
- *                                a multiple of 32, n_tokens x h_out x 2
+ *                                a multiple of 64, n_tokens x h_out x 2
  *                                below 4 GiB) use the matrix-core (MFMA)
  *                                tiles; default 64.
  *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
@@ -97,8 +97,9 @@ void slora_pool_destroy(slora_pool* pool);
  *                                batch's vector-ALU expand work).
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
  *                                of 128; default 1024.
- *  SLORA_TUNE_MFMA_SHRINK_ROWS - rank rows of one MFMA shrink tile, a
- *                                multiple of 16 up to 64; default 32.
+ *  SLORA_TUNE_MFMA_SHRINK_SPLITS - K splits of each 64-token MFMA shrink
+ *                                block, 1..4; 0 (default): enough for about
+ *                                512 shrink tiles.
  *  SLORA_TUNE_FUSED            - 1 (default): slora_lora_delta runs both
  *                                stages in one launch, each expand tile
  *                                waiting for its tokens' x A values;
@@ -112,7 +113,7 @@ typedef enum {
   SLORA_TUNE_MFMA_MIN_TOKENS = 0,
   SLORA_TUNE_GEMV_EXPAND_ELEMS = 1,
   SLORA_TUNE_MFMA_EXPAND_COLS = 2,
-  SLORA_TUNE_MFMA_SHRINK_ROWS = 3,
+  SLORA_TUNE_MFMA_SHRINK_SPLITS = 3,
   SLORA_TUNE_FUSED = 4,
   SLORA_TUNE_XCDS = 5
 } slora_tune_key;
@@ -172,7 +173,7 @@ typedef struct {
   int32_t n_shrink_tiles;
   int32_t n_expand_tiles;
   int32_t n_mfma_segments;/* segments routed to the matrix-core (MFMA) tiles */
-  int32_t reserved0;
+  int32_t n_combine_tiles;/* tiles summing the K-split partials of MFMA shrink blocks */
   size_t meta_bytes;      /* device metadata size for slora_segments_upload */
   size_t workspace_bytes; /* device workspace size for slora_lora_delta */
 } slora_segments_info;
@@ -189,16 +190,23 @@ slora_status slora_segments_export(const slora_segments* seg, int32_t* perm, int
                                    int32_t* seg_page_off, int32_t* a_pages, int32_t* b_pages);
 
 /* Introspection of the work split (host copies): layout[9] receives
- * {n_tiles, stride, tokcap, pagecap, n_shrink_tiles, n_expand_tiles, hdr, 0, 0}
- * and, when records is not NULL and holds at least n_tiles * stride words,
- * the tile records in launch order (every shrink tile before every expand
- * tile), stride int32 words each.  Record words:
- * 0 kind (bit 0: matrix-core (MFMA) tile, bit 1: expand tile), 1 token count,
- * 2 segment rank, 3 first rank row (shrink) or first column (expand), 4 rows
- * or columns covered, 5 workspace offset of the first token's v row, 6 scale
- * (float bits), 7 expand thread-map width, 8 segment index; from word hdr,
- * tokcap batch indices of the tokens, then per projection pagecap page ids
- * (shrink: the A^T pages of the rows covered; expand: all rank B pages).
+ * {n_tiles, stride, tokcap, pagecap, n_shrink_tiles, n_expand_tiles, hdr,
+ *  n_combine_tiles, n_splits} and, when records is not NULL and holds at
+ * least n_tiles * stride words, the tile records in launch order (every
+ * shrink tile, then every combine tile, then every expand tile), stride int32
+ * words each.  Record words:
+ * 0 kind (bit 0: matrix-core (MFMA) tile, bit 1: expand tile, bit 2: combine
+ * tile), 1 token count, 2 segment rank, 3 first rank row (vector-ALU shrink),
+ * first k (MFMA shrink) or first column (expand), 4 rows, k extent or columns
+ * covered, 5 workspace offset of the first token's v row, 6 scale (float
+ * bits), 7 expand thread-map width / K split of an MFMA shrink tile / splits
+ * summed by a combine tile, 8 segment index, 9 K splits of an MFMA shrink
+ * tile's token block; from word hdr, tokcap batch indices of the tokens, then
+ * per projection pagecap page ids (vector-ALU shrink: the A^T pages of the
+ * rows covered; MFMA shrink: all rank A^T pages; expand: all rank B pages).
+ * MFMA shrink tiles split over K (n_splits > 1) write partial x A to
+ * workspace area `split` (each area sum_rank_tokens values); a combine tile
+ * sums the areas of its tokens into area 0.
  * For tests and tools; the layout may change. */
 slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, int32_t* records,
                                   size_t records_words);
@@ -218,7 +226,8 @@ slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t d
  * n_tokens x h_in and y of n_tokens x h_out, both row-major in batch order
  * and of the pool dtype; y is updated in place with one rounding of
  * fp32(y) + s * d per element, where d is accumulated in fp32.  workspace is
- * device memory of at least workspace_bytes (fp32 x A products), 16-byte
+ * device memory of at least workspace_bytes (fp32 x A products and their
+ * K-split partials), 16-byte
  * aligned.  Launches the shrink and expand kernels on `stream` and returns
  * without waiting; launch errors return SLORA_E_HIP, device faults surface at
  * the caller's next synchronisation.  Requires a prior slora_segments_upload.

@@ -86,7 +86,7 @@ struct Tuning {
   int64_t mfma_min_tokens = 64;
   int64_t gemv_expand_elems = 0;   // 0: sized from the batch (auto_expand_elems)
   int64_t mfma_expand_cols = 1024;
-  int64_t mfma_shrink_rows = 32;
+  int64_t mfma_shrink_splits = 0;   // K splits per MFMA shrink block (0: automatic)
   int64_t fused = 1;
   int64_t xcds = 1;             // XCD groups of the shrink placement (1: none)
 };
@@ -142,6 +142,8 @@ struct slora_segments {
   std::vector<int64_t> seg_v_off;
   int64_t sum_r = 0, sum_rt = 0;
   int32_t n_mfma_segments = 0;
+  int32_t n_combine = 0;           // combine tiles (MFMA shrink blocks split over K)
+  int32_t n_splits = 1;            // K splits of the MFMA shrink blocks (1: none)
   // tile records: shrink records, then expand records
   std::vector<int32_t> blob;
   int32_t n_tiles = 0, n_shrink = 0, n_expand = 0;
@@ -160,7 +162,7 @@ namespace {
 // Device metadata: the tile records, an error word, then 8 bytes per
 // (token, rank row) of v pairs for the fused launch.
 size_t meta_bytes_of(const slora_segments* s) {
-  return (size_t)(s->vtag_off_words * 4) + (size_t)s->sum_rt * 8;
+  return (size_t)(s->vtag_off_words * 4) + (size_t)s->n_splits * s->sum_rt * 8;
 }
 
 slora_status set_device(slora_pool* p) {
@@ -287,9 +289,9 @@ void build_tiles(slora_segments* s) {
   const int gemv_rows = kShrinkRowBudget / nck;
   s->gemv_rows = gemv_rows;
 
-  // Matrix-core tiles need fp16, h_in a multiple of 32 and a y that the
+  // Matrix-core tiles need fp16, h_in a multiple of 64 and a y that the
   // expand can address through one buffer descriptor.
-  const bool mfma_ok = f16 && hin % 32 == 0 && (int64_t)s->n_tokens * hout * 2 <= kMaxBufferBytes;
+  const bool mfma_ok = f16 && hin % kShrinkKc == 0 && (int64_t)s->n_tokens * hout * 2 <= kMaxBufferBytes;
 
   // Work per vector-ALU expand tile (rank x columns).  A small batch needs
   // many small tiles to keep enough loads in flight; a large one runs faster
@@ -298,6 +300,25 @@ void build_tiles(slora_segments* s) {
   // down to a power of two and clamped to [16K, 128K] elements: 16K for 256
   // Llama-7B decode tokens, 32K for the 13B mixed batch, 128K for 512 tokens
   // of the 70B MLP projection.
+  // K splits of the MFMA shrink: enough tiles to give every CU about two
+  // (512), at most kMaxSplits; with more than one, a combine tile per 16
+  // tokens sums the splits' partial x A in a fixed order.
+  int64_t mfma_blocks = 0;
+  for (int32_t g = 0; g < S; ++g) {
+    const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
+    if (mfma_ok && c >= p->tune.mfma_min_tokens && s->seg_rank[g] <= kMaxRankMfma)
+      mfma_blocks += (c + kMfmaExpandTok - 1) / kMfmaExpandTok;
+  }
+  int32_t splits = 1;
+  const int32_t n_kc = hin / kShrinkKc;
+  if (p->tune.mfma_shrink_splits > 0) {
+    splits = (int32_t)std::min<int64_t>(p->tune.mfma_shrink_splits, n_kc);
+  } else {
+    while (splits < kMaxSplits && splits * 2 <= n_kc && mfma_blocks * splits < 512) splits *= 2;
+  }
+  if (mfma_blocks == 0) splits = 1;
+  s->n_splits = splits;
+
   int64_t expand_elems = p->tune.gemv_expand_elems;
   if (expand_elems == 0) {
     int64_t work = 0;
@@ -311,49 +332,54 @@ void build_tiles(slora_segments* s) {
   }
 
   std::vector<TileSpec> tiles;
-  std::vector<std::pair<int32_t, int32_t>> blocks, eblocks;   // shrink, expand token blocks
+  std::vector<std::pair<int32_t, int32_t>> eblocks;   // token blocks of a segment
   int32_t max_rank = 1;
   int32_t n_groups = 0;
   s->n_mfma_segments = 0;
-  s->n_shrink = s->n_expand = 0;
+  s->n_shrink = s->n_expand = s->n_combine = 0;
   for (int32_t g = 0; g < S; ++g) {
     const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
     const int32_t r = s->seg_rank[g];
     max_rank = std::max(max_rank, r);
     const bool mfma = mfma_ok && c >= p->tune.mfma_min_tokens && r <= kMaxRankMfma;
     if (mfma) ++s->n_mfma_segments;
-    split_tokens(c, mfma ? kMfmaTok : kGemvMaxTok, blocks);
     split_tokens(c, mfma ? kMfmaExpandTok : kGemvMaxTok, eblocks);
     // vector-ALU expand width: largest of vec*{256,128,64,32} with rank x width within budget
     int32_t width = vec * 256;
     while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
-    const int32_t rows = mfma ? (int32_t)p->tune.mfma_shrink_rows : gemv_rows;
     const int32_t cols = mfma ? (int32_t)p->tune.mfma_expand_cols : width;
-    // Placement group: the expand block holding the tile's first token.
-    auto grp_of = [&](int32_t i0) {
-      size_t b = 0;
-      while (b + 1 < eblocks.size() && eblocks[b + 1].first <= i0) ++b;
-      return n_groups + (int32_t)b;
-    };
-    for (auto& tb : blocks)
-      for (int32_t j0 = 0; j0 < r; j0 += rows, ++s->n_shrink)
-        tiles.push_back({mfma ? KIND_SHRINK_MFMA : KIND_SHRINK_GEMV, g, tb.first, tb.second, j0,
-                         std::min(rows, r - j0), 0, grp_of(tb.first)});
-    for (auto& tb : eblocks) {
+    for (size_t b = 0; b < eblocks.size(); ++b) {
+      const auto& tb = eblocks[b];
+      const int32_t grp = n_groups + (int32_t)b;
+      if (mfma) {
+        // 64-token shrink tiles over all r rows, one per K split
+        for (int32_t sp = 0; sp < splits; ++sp, ++s->n_shrink) {
+          const int32_t c0 = (int32_t)((int64_t)sp * n_kc / splits), c1 = (int32_t)((int64_t)(sp + 1) * n_kc / splits);
+          tiles.push_back({KIND_SHRINK_MFMA, g, tb.first, tb.second, c0 * kShrinkKc, (c1 - c0) * kShrinkKc, sp, grp});
+        }
+        if (splits > 1)
+          for (int32_t k = 0; k < tb.second; k += kCombineTok, ++s->n_combine)
+            tiles.push_back({KIND_COMBINE, g, tb.first + k, std::min(kCombineTok, tb.second - k), 0, r, splits, grp});
+      } else {
+        for (int32_t j0 = 0; j0 < r; j0 += gemv_rows, ++s->n_shrink)
+          tiles.push_back({KIND_SHRINK_GEMV, g, tb.first, tb.second, j0, std::min(gemv_rows, r - j0), 0, grp});
+      }
       for (int32_t o0 = 0; o0 < hout; o0 += cols, ++s->n_expand)
         tiles.push_back({mfma ? KIND_EXPAND_MFMA : KIND_EXPAND_GEMV, g, tb.first, tb.second, o0,
-                         std::min(cols, hout - o0), mfma ? 0 : width, grp_of(tb.first)});
+                         std::min(cols, hout - o0), mfma ? 0 : width, grp});
     }
     n_groups += (int32_t)eblocks.size();
   }
 
-  // Launch order: every shrink tile before every expand tile, the matrix-core
+  // Launch order: every shrink tile, then the combine tiles, then every
+  // expand tile; within each stage the matrix-core
   // tiles (the heavier ones) first within each stage, segment order otherwise.
   // Producers first keeps the waiting expand tiles of a fused launch from
   // holding the workgroup slots the shrink tiles need (measured: putting each
   // token block's expand tiles right after its shrink tiles is 20-50 % slower).
   auto launch_rank = [](const TileSpec& t) {
-    return ((t.kind & KIND_EXPAND_BIT) ? 2 : 0) + ((t.kind & KIND_MFMA_BIT) ? 0 : 1);
+    if (t.kind & KIND_COMBINE_BIT) return 2;
+    return ((t.kind & KIND_EXPAND_BIT) ? 3 : 0) + ((t.kind & KIND_MFMA_BIT) ? 0 : 1);
   };
   std::stable_sort(tiles.begin(), tiles.end(), [&](const TileSpec& a, const TileSpec& b) {
     return launch_rank(a) < launch_rank(b);
@@ -405,7 +431,7 @@ void build_tiles(slora_segments* s) {
   const int np = s->n_proj;
   s->n_tiles = (int32_t)tiles.size();
   s->tokcap = kTokCap;
-  s->pagecap = (std::max({gemv_rows, kMfmaMaxRows, max_rank}) + 3) & ~3;   // <= kMaxPageCap
+  s->pagecap = (std::max(gemv_rows, max_rank) + 3) & ~3;   // <= kMaxPageCap
   s->stride = (REC_HDR + s->tokcap + np * s->pagecap + 3) & ~3;
   s->shrink_idx_off_words = (int64_t)s->n_tiles * s->stride;
   s->expand_idx_off_words = s->shrink_idx_off_words + s->n_shrink;
@@ -421,7 +447,8 @@ void build_tiles(slora_segments* s) {
     const TileSpec& t = tiles[i];
     int32_t* rec = s->blob.data() + (size_t)i * s->stride;
     const bool expand = (t.kind & KIND_EXPAND_BIT) != 0;
-    (expand ? expand_idx[ne++] : shrink_idx[ns++]) = i;
+    const bool combine = (t.kind & KIND_COMBINE_BIT) != 0;
+    if (!combine) (expand ? expand_idx[ne++] : shrink_idx[ns++]) = i;
     const int32_t g = t.seg;
     const int32_t r = s->seg_rank[g];
     rec[REC_KIND] = t.kind;
@@ -434,13 +461,15 @@ void build_tiles(slora_segments* s) {
     std::memcpy(&rec[REC_SCALE], &sc, 4);
     rec[REC_AUX] = t.aux;
     rec[REC_SEG] = g;
+    rec[REC_NSPLIT] = (t.kind == KIND_SHRINK_MFMA) ? s->n_splits : 0;
     const int32_t first = s->seg_start[g] + t.i0;
     for (int32_t k = 0; k < t.ntok; ++k) rec[REC_HDR + k] = s->perm[first + k];
     for (int pr = 0; pr < np; ++pr) {
       int32_t* pg = rec + REC_HDR + s->tokcap + pr * s->pagecap;
       const int32_t* src = (expand ? s->b_pages.data() : s->a_pages.data()) +
                            (size_t)pr * s->sum_r + s->seg_page_off[g];
-      if (expand)
+      if (combine) continue;
+      if (expand || t.kind == KIND_SHRINK_MFMA)
         for (int32_t j = 0; j < r; ++j) pg[j] = src[j];
       else
         for (int32_t j = 0; j < t.len; ++j) pg[j] = src[t.pos + j];
@@ -559,10 +588,9 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       if (value != 0 && value != 1) return fail(SLORA_E_INVAL, "fused must be 0 or 1");
       p->tune.fused = value;
       return SLORA_OK;
-    case SLORA_TUNE_MFMA_SHRINK_ROWS:
-      if (value < 16 || value > kMfmaMaxRows || value % 16)
-        return fail(SLORA_E_INVAL, "mfma_shrink_rows must be 16, 32, 48 or 64");
-      p->tune.mfma_shrink_rows = value;
+    case SLORA_TUNE_MFMA_SHRINK_SPLITS:
+      if (value < 0 || value > kMaxSplits) return fail(SLORA_E_INVAL, "mfma_shrink_splits must be 0..4 (0: automatic)");
+      p->tune.mfma_shrink_splits = value;
       return SLORA_OK;
     default:
       return fail(SLORA_E_INVAL, "slora_pool_set_tuning: unknown key");
@@ -796,8 +824,9 @@ slora_status slora_segments_get_info(const slora_segments* s, slora_segments_inf
   info->n_shrink_tiles = s->n_shrink;
   info->n_expand_tiles = s->n_expand;
   info->n_mfma_segments = s->n_mfma_segments;
+  info->n_combine_tiles = s->n_combine;
   info->meta_bytes = meta_bytes_of(s);
-  info->workspace_bytes = std::max<size_t>(16, (size_t)s->sum_rt * sizeof(float));
+  info->workspace_bytes = std::max<size_t>(16, (size_t)s->n_splits * s->sum_rt * sizeof(float));
   return SLORA_OK;
 }
 
@@ -821,7 +850,7 @@ slora_status slora_segments_tiles(const slora_segments* s, int32_t* layout, int3
                                   size_t records_words) {
   if (!s || !layout) return fail(SLORA_E_INVAL, "slora_segments_tiles: NULL argument");
   const int32_t lay[9] = {s->n_tiles, s->stride, s->tokcap, s->pagecap, s->n_shrink, s->n_expand,
-                          REC_HDR, 0, 0};
+                          REC_HDR, s->n_combine, s->n_splits};
   std::memcpy(layout, lay, sizeof(lay));
   if (records) {
     const size_t words = (size_t)s->n_tiles * s->stride;
@@ -914,7 +943,7 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
        reinterpret_cast<uintptr_t>(workspace)) & 15)
     return fail(SLORA_E_INVAL, f + ": x, y and workspace must be 16-byte aligned");
-  if (workspace_bytes < (size_t)s->sum_rt * sizeof(float))
+  if (workspace_bytes < (size_t)s->n_splits * s->sum_rt * sizeof(float))
     return fail(SLORA_E_NOMEM, f + ": workspace smaller than workspace_bytes");
   if (!s->dev_meta) return fail(SLORA_E_INVAL, f + ": segments not uploaded (call slora_segments_upload)");
   slora_status st = set_device(p);
@@ -945,11 +974,16 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.error_flag = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(s->dev_meta + s->error_off_words));
   L.vtag = reinterpret_cast<unsigned long long*>(const_cast<int32_t*>(s->dev_meta + s->vtag_off_words));
   L.y_bytes = (uint32_t)std::min<int64_t>((int64_t)s->n_tokens * p->d.h_out * elem_bytes(p->d.dtype), kMaxBufferBytes);
+  L.sum_rt = (int32_t)s->sum_rt;
+  L.n_combine = s->n_combine;
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
     stages = STAGE_FUSED;
-    if (s->epoch == 0xFFFFFFFFu) {   // epochs would wrap to pairs still zero: clear them first
+    // Epochs run 1 .. 2^31 - 1 (partial sums of K-split shrink tiles carry the
+    // epoch with bit 31 set); before they would wrap, clear the pairs so that
+    // no stale pair can match a new epoch.
+    if (s->epoch == 0x7FFFFFFFu) {
       hipError_t z = launch_zero_words(const_cast<int32_t*>(s->dev_meta) + s->vtag_off_words,
-                                       (int64_t)s->sum_rt * 2, static_cast<hipStream_t>(stream));
+                                       (int64_t)s->n_splits * s->sum_rt * 2, static_cast<hipStream_t>(stream));
       if (z != hipSuccess) return hip_fail(z, (f + " clearing v pairs").c_str());
       s->epoch = 0;
     }

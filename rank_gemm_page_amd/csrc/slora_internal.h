@@ -15,37 +15,44 @@ namespace slora {
 //                   matrix-core (MFMA) tiles, bit 1 set for expand tiles
 //   [1] ntok        tokens in the tile (all of one segment)
 //   [2] rank        the segment's rank r (row stride of its v block)
-//   [3] pos         shrink: first rank row j0      expand: first column o0
-//   [4] len         shrink: rank rows handled      expand: columns handled
+//   [3] pos         shrink: first rank row j0 (MFMA: first k)   expand: first column o0
+//   [4] len         shrink: rank rows handled (MFMA: k extent)  expand: columns handled
 //   [5] v0          workspace offset of the tile's first token's v row
 //   [6] scale       the segment's scale, float bits
-//   [7] aux         expand GEMV: nominal column width of the tile (thread map)
+//   [7] aux         expand GEMV: nominal column width of the tile (thread map);
+//                   MFMA shrink: its K split; combine: the number of splits
 //   [8] seg         index of the tile's segment
-//   [9..11]         reserved
+//   [9] nsplit      MFMA shrink: the K splits of its token block (1: writes v
+//                   itself; more: a combine tile sums the splits' partials)
+//   [10..11]        reserved
 //   [HDR .. HDR+tokcap)                   batch indices of the tokens
-//   [HDR+tokcap + p*pagecap .. +npages)   page ids of projection p: shrink
-//                                         holds the A^T pages of rows
-//                                         pos..pos+len, expand all r B pages
+//   [HDR+tokcap + p*pagecap .. +npages)   page ids of projection p: GEMV
+//                                         shrink holds the A^T pages of rows
+//                                         pos..pos+len, MFMA shrink all r A^T
+//                                         pages, expand all r B pages
 // All records share one stride (a multiple of 4 words) and sit in launch
-// order: every shrink tile before every expand tile.  Two index lists give the
-// shrink and the expand records for launches that run the stages separately.
+// order: every shrink tile, then every combine tile, then every expand tile.
+// Two index lists give the shrink and the expand records for launches that
+// run the stages separately; combine records follow the shrink records.
 enum : int32_t {
   REC_KIND = 0, REC_NTOK = 1, REC_RANK = 2, REC_POS = 3, REC_LEN = 4,
-  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_SEG = 8, REC_HDR = 12
+  REC_V0 = 5, REC_SCALE = 6, REC_AUX = 7, REC_SEG = 8, REC_NSPLIT = 9, REC_HDR = 12
 };
 enum : int32_t {
   KIND_SHRINK_GEMV = 0, KIND_SHRINK_MFMA = 1, KIND_EXPAND_GEMV = 2, KIND_EXPAND_MFMA = 3,
-  KIND_MFMA_BIT = 1, KIND_EXPAND_BIT = 2
+  KIND_COMBINE = 5,
+  KIND_MFMA_BIT = 1, KIND_EXPAND_BIT = 2, KIND_COMBINE_BIT = 4
 };
 
 // Fixed tile geometry shared by the builder and the kernels.
 constexpr int kThreads = 256;           // every tile kernel runs 4 waves of 64
-constexpr int kMfmaTok = 16;            // tokens per MFMA shrink tile (M of 16x16x32)
-constexpr int kMfmaExpandTok = 64;      // tokens per MFMA expand tile (four waves of 16)
+constexpr int kMfmaExpandTok = 64;      // tokens per MFMA shrink / expand tile (four waves of 16)
+constexpr int kCombineTok = 16;         // tokens per combine tile
+constexpr int kMaxSplits = 4;           // K splits of an MFMA shrink token block
+constexpr int kShrinkKc = 64;           // k elements per staged MFMA shrink chunk
 constexpr int kMaxRankMfma = SLORA_MFMA_MAX_RANK;   // rank limit of MFMA segments
 constexpr int kTokCap = 64;             // token slots of every record (>= every tile kind's)
 constexpr int kMaxPageCap = 256;        // page slots per projection (max_rank <= 256)
-constexpr int kMfmaMaxRows = 64;        // rank rows per MFMA shrink tile
 constexpr int kMfmaPass = 128;          // columns per MFMA expand pass
 // The MFMA expand addresses y through a buffer descriptor (stores past its
 // extent are dropped by the hardware): MFMA tiles are used only while y fits
@@ -53,8 +60,8 @@ constexpr int kMfmaPass = 128;          // columns per MFMA expand pass
 constexpr int64_t kMaxBufferBytes = 0xFFFFFF00LL;
 constexpr int kGemvMaxTok = 4;          // tokens per vector-ALU tile
 constexpr int kShrinkRowBudget = 16;    // rows x 16-byte chunks per thread (GEMV shrink)
-static_assert(kTokCap >= kGemvMaxTok && kTokCap >= kMfmaTok && kTokCap >= kMfmaExpandTok, "token slots");
-static_assert(kMfmaMaxRows <= kMaxPageCap, "page slots");
+static_assert(kTokCap >= kGemvMaxTok && kTokCap >= kMfmaExpandTok && kTokCap >= kCombineTok, "token slots");
+static_assert(kMaxRankMfma <= 64, "the MFMA shrink holds at most four 16-row blocks of A^T");
 
 struct PoolView {
   const char* base_a;     // class of the A^T pages
@@ -83,6 +90,8 @@ struct DeltaLaunch {
   // wait gave up
   unsigned long long* vtag;
   uint32_t* error_flag;
+  int32_t sum_rt;         // v values of the batch (stride between the K-split partial areas)
+  int32_t n_combine;      // combine tiles (records n_shrink .. n_shrink + n_combine)
   uint32_t y_bytes;       // extent of y (n_tokens x h_out x element), < kMaxBufferBytes when has_mfma
   uint32_t epoch;
 };

@@ -27,6 +27,8 @@
 // Every output element is written by exactly one thread, once, with one
 // rounding; no atomics, so results are deterministic run to run and do not
 // depend on where the pages sit in the pool.
+#include <type_traits>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -48,12 +50,12 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Streaming (non-temporal) 16-byte load and store, for data read once per
-// launch or nearly so: page rows of the vector-ALU tiles and y.  Measured on
-// MI355X, row gathers of 60-240 MB stream 1.5-1.7x faster with the
-// non-temporal hint than with ordinary loads.  The x rows of the MFMA shrink
-// (read by every rank block of the token block, and across XCDs) and the B
-// slices of the MFMA expand (read by every token block of the segment) keep
-// ordinary loads: with the hint, the re-reads miss and the launch is slower.
+// launch: page rows of the vector-ALU tiles, x rows of the MFMA shrink (each
+// K split of a 64-token block reads its own k range once), and y.  Measured
+// on MI355X, row gathers of 60-240 MB stream 1.5-1.7x faster with the
+// non-temporal hint than with ordinary loads.  The A^T rows of the MFMA
+// shrink and the B slices of the MFMA expand, read again by every token block
+// of the segment, keep ordinary loads.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -72,7 +74,7 @@ __device__ __forceinline__ void st16_nt(void* p, uint4 v) {
 #define SLORA_NT_Y 1
 #endif
 #ifndef SLORA_NT_X
-#define SLORA_NT_X 0
+#define SLORA_NT_X 1
 #endif
 template <bool NT> __device__ __forceinline__ uint4 ldsel(const void* p) { return NT ? ld16_nt(p) : ld16(p); }
 template <bool NT> __device__ __forceinline__ void stsel(void* p, uint4 v) { if (NT) st16_nt(p, v); else st16(p, v); }
@@ -199,17 +201,24 @@ __device__ __forceinline__ void record_to_lds(const int32_t* rec, int tokcap, in
 // buffer, which the upload zeroes, and epochs count 1, 2, ... from there, so
 // no stale pair can carry the current epoch.
 //
+// A 64-token MFMA shrink block split over K writes partial sums tagged with
+// the epoch and bit 31 set (kPartialTag), each split into its own area of
+// sum_rt pairs; a combine tile waits for all of a block's partials, adds them
+// in split order and writes the value with the plain epoch into area 0, where
+// the expand tiles look.  A partial can therefore never pass for a value.
+//
 // Progress: shrink tiles occupy the lower block indices and never wait, and
 // workgroups are dispatched in index order, so every shrink tile a waiting
 // expand tile depends on has been dispatched and finishes.  The wait is
 // bounded all the same: past kMaxSpins polls it raises error_flag and goes on,
 // so every wave of the grid always exits.
 constexpr uint32_t kMaxSpins = 1u << 20;
+constexpr uint32_t kPartialTag = 0x80000000u;
 
 template <bool FUSED>
-__device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float x) {
+__device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float x, uint32_t tag) {
   if constexpr (FUSED) {
-    const unsigned long long pair = ((unsigned long long)L.epoch << 32) | __float_as_uint(x);
+    const unsigned long long pair = ((unsigned long long)tag << 32) | __float_as_uint(x);
     __hip_atomic_store(L.vtag + idx, pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     L.v[idx] = x;
@@ -217,13 +226,13 @@ __device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float
 }
 
 // Loads v[idx] of every (valid) slot this thread owns, polling until all
-// threads of the workgroup hold current values.  get(q) gives slot q's index
-// (or -1), put(q, value) receives the value; the first nq (uniform, <= N)
-// slots of each thread are in use.  All loads of a poll are issued before
+// threads of the workgroup hold current values (pairs tagged `want`).  get(q)
+// gives slot q's index (or -1), put(q, value) receives the value; the first nq
+// (uniform, <= N) slots of each thread are in use.  All loads of a poll are issued before
 // any is consumed, at index `safe` (any valid v index) for a slot with no
 // value, so they travel to memory together instead of one round trip each.
 template <bool FUSED, int N, typename Get, typename Put>
-__device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, Get get, Put put) {
+__device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, Get get, Put put, uint32_t want) {
   int idx[N];
 #pragma unroll
   for (int q = 0; q < N; ++q) idx[q] = q < nq ? get(q) : -1;
@@ -247,7 +256,7 @@ __device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, G
 #pragma unroll
       for (int q = 0; q < N; ++q) {
         if (q < nq) {
-          ok = ok && (idx[q] < 0 || (uint32_t)(pair[q] >> 32) == L.epoch);
+          ok = ok && (idx[q] < 0 || (uint32_t)(pair[q] >> 32) == want);
           put(q, idx[q] >= 0 ? __uint_as_float((uint32_t)pair[q]) : 0.f);
         }
       }
@@ -325,127 +334,180 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     const int k = i / nrows, r = i - k * nrows;
     const float* q = red + (k * 4) * RB + r;
     const float sum = ((q[0] + q[RB]) + q[2 * RB]) + q[3 * RB];
-    store_v<FUSED>(L, v0 + (int64_t)k * rank + j0 + r, sum);
+    store_v<FUSED>(L, v0 + (int64_t)k * rank + j0 + r, sum, L.epoch);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Shrink, MFMA tile: 16 tokens x up to 64 rank rows, whole h_in (fp16).
-// C[m][n] = sum_k X[m][k] * AT_n[k] with v_mfma_f32_16x16x32_f16: lane l feeds
-// row m = l%16 of X and row n = l%16 of A^T, 8 consecutive k at 8*(l/16); the
-// four waves take interleaved 32-wide k steps and are summed through LDS.
+// Shrink, MFMA tile (fp16): up to 64 tokens x all r rows (r <= 64) over the
+// k range [pos, pos + len) of one K split.  C[t][j] = sum_k x[t][k] AT_j[k]
+// with v_mfma_f32_16x16x32_f16: wave w owns tokens 16w .. 16w+15 and all
+// rank rows, so the four waves share each staged chunk of A^T.  x and A^T
+// stream through LDS in chunks of 64 k (128 bytes per row): a wave loads 8
+// whole rows per instruction, and a lane's MFMA operand (8 consecutive k of
+// one row) is one 16-byte LDS read; the 16-byte chunks of a row are
+// XOR-swizzled by row.  Three chunks of loads run ahead of the matrix cores
+// in registers; the LDS chunks alternate between two buffers, one barrier per
+// chunk.
 
-#ifndef SLORA_SHRINK_RING
-#define SLORA_SHRINK_RING 16
-#endif
-// Register ring of the MFMA shrink, in 16-byte loads per lane (D stages of
-// 1 + NB loads each).
-constexpr int kShrinkRingHalf8 = SLORA_SHRINK_RING;
+constexpr int kShrinkStageDw = 2 * kMfmaExpandTok * (kShrinkKc / 2);   // x and A^T rows of one chunk
+constexpr int kShrinkLdsFloats = 2 * kShrinkStageDw;                   // two chunks (32 KB)
 
-template <int NB, bool FUSED>
-__device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
+__device__ __forceinline__ int chunk_dw(int row, int c) { return row * (kShrinkKc / 2) + 4 * (c ^ (row & 7)); }
+
+template <bool FUSED>
+__device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
-  const int j0 = uni(srec[REC_POS]);
-  const int nrows = uni(srec[REC_LEN]);
+  const int k0 = uni(srec[REC_POS]);
+  const int klen = uni(srec[REC_LEN]);
   const int v0 = uni(srec[REC_V0]);
+  const int split = uni(srec[REC_AUX]);
+  const int nsplit = uni(srec[REC_NSPLIT]);
   const int32_t* toks = srec + REC_HDR;
   const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
+  const int nb = (rank + 15) >> 4;                   // 16-row blocks of A^T
+  const int nkc = klen / kShrinkKc;
+  uint32_t* stage = reinterpret_cast<uint32_t*>(lds);
 
-  // Rows past ntok / nrows repeat the last valid row (same cache lines); their
-  // outputs are never stored.
-  const _Float16* xrow = reinterpret_cast<const _Float16*>(L.x) +
-                         (int64_t)toks[m < ntok ? m : ntok - 1] * L.h_in + 8 * g;
-  const _Float16* arow[NB];
+  // Loader: thread tid moves the 16-byte chunk tid & 7 of rows tid >> 3 and
+  // 32 + (tid >> 3) of x and of A^T; rows past ntok / rank repeat the last
+  // one (their results are never stored).
+  const int lr = tid >> 3, lc = tid & 7;
+  const _Float16* xr[2];
+  const char* ar[2];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int j = b * 16 + m;
-    arow[b] = reinterpret_cast<const _Float16*>(
-                  L.pool.base_a + (int64_t)pages[j < nrows ? j : nrows - 1] * L.pool.page_bytes_a) + 8 * g;
+  for (int h = 0; h < 2; ++h) {
+    const int row = lr + 32 * h;
+    xr[h] = reinterpret_cast<const _Float16*>(L.x) + (int64_t)toks[min(row, ntok - 1)] * L.h_in + k0 + 8 * lc;
+    ar[h] = L.pool.base_a + (int64_t)pages[min(row, rank - 1)] * L.pool.page_bytes_a + (int64_t)(k0 + 8 * lc) * 2;
   }
-  float4v acc[NB];
+  auto load_chunk = [&](int kc, uint4 (&r)[4]) {
+    kc = kc < nkc ? kc : nkc - 1;   // loads past the end re-read the last chunk, unused
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  // Wave w takes the 32-wide k steps w, w+4, w+8, ...: n_it of them.  Loads
-  // run D steps ahead of the matrix cores in a ring of registers.  Every load
-  // is issued unconditionally (a step past the end re-reads the wave's last
-  // step and is never multiplied), so the same number of loads is in flight
-  // on every path and the wait before a step covers that step's loads only;
-  // a load behind a branch would make the compiler wait for all of them.
-  const int n_it = (L.h_in - wave * 32 + 127) >> 7;
-  const int last = n_it > 0 ? n_it - 1 : 0;
-  const int kbase = n_it > 0 ? wave * 32 : 0;   // a wave with no step re-reads k = 0
-  constexpr int D = kShrinkRingHalf8 / (1 + NB) < 2 ? 2 : kShrinkRingHalf8 / (1 + NB);
-  half8 xs[D], as[D][NB];
-  auto load = [&](int slot, int it) {
-    const int k = kbase + (it < last ? it : last) * 128;
-    xs[slot] = __builtin_bit_cast(half8, ldsel<SLORA_NT_X>(xrow + k));
-#pragma unroll
-    for (int b = 0; b < NB; ++b) as[slot][b] = __builtin_bit_cast(half8, ld16(arow[b] + k));
+    for (int h = 0; h < 2; ++h) {
+      r[h] = ldsel<SLORA_NT_X>(xr[h] + kShrinkKc * kc);
+      r[2 + h] = ld16(ar[h] + 2 * kShrinkKc * kc);
+    }
   };
-  // The ring is filled in slot order and kept in that order (no reordering
-  // across the barriers): the wait before slot s then only needs the loads
-  // older than slot s + 1's.
+  auto store_chunk = [&](uint32_t* buf, const uint4 (&r)[4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = lr + 32 * h;
+      *reinterpret_cast<uint4*>(buf + chunk_dw(row, lc)) = r[h];
+      *reinterpret_cast<uint4*>(buf + kShrinkStageDw / 2 + chunk_dw(row, lc)) = r[2 + h];
+    }
+  };
+
+  float4v acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = float4v{0.f, 0.f, 0.f, 0.f};
+  // Ring of three chunks in registers, filled in order (no reordering across
+  // the scheduling barriers), so each wait covers only the oldest chunk.  All
+  // loads, LDS stores and barriers run for every slot of the last round too;
+  // only the matrix work of chunks past the end is skipped.
+  constexpr int D = 3;
+  uint4 ring[D][4];
 #pragma unroll
   for (int slot = 0; slot < D; ++slot) {
-    load(slot, slot);
+    load_chunk(slot, ring[slot]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int it0 = 0; it0 < n_it; it0 += D) {
+  for (int kc0 = 0; kc0 < nkc; kc0 += D) {
 #pragma unroll
     for (int slot = 0; slot < D; ++slot) {
-      if (it0 + slot < n_it) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xs[slot], as[slot][b], acc[b], 0, 0, 0);
-      }
-      load(slot, it0 + slot + D);
+      const int kc = kc0 + slot;
+      uint32_t* buf = stage + (kc & 1) * kShrinkStageDw;
+      store_chunk(buf, ring[slot]);
+      lds_barrier();
+      load_chunk(kc + D, ring[slot]);
       __builtin_amdgcn_sched_barrier(0);
+      if (kc < nkc) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int rx = 16 * wave + m;
+          const half8 xop = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(buf + chunk_dw(rx, 4 * ks + g)));
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            if (b < nb) {
+              const int ra = 16 * b + m;
+              const half8 aop = __builtin_bit_cast(
+                  half8, *reinterpret_cast<const uint4*>(buf + kShrinkStageDw / 2 + chunk_dw(ra, 4 * ks + g)));
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, aop, acc[b], 0, 0, 0);
+            }
+          }
+        }
+      }
     }
   }
-  // acc[b][i] is C[token 4g + i][rank row b*16 + l%16]; sum the four waves in LDS.
+  // acc[b][i] = C[token 16 wave + 4g + i][rank row 16b + m]
+  const uint32_t tag = nsplit > 1 ? (L.epoch | kPartialTag) : L.epoch;
+  const int64_t area = (int64_t)split * L.sum_rt;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+  for (int b = 0; b < 4; ++b) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[((wave * 4 + b) * 16 + (4 * g + i)) * 16 + m] = acc[b][i];
-  }
-  __syncthreads();
-  for (int i = tid; i < ntok * nrows; i += kThreads) {
-    const int mm = i / nrows, j = i - mm * nrows;
-    const int b = j >> 4, n = j & 15;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) sum += red[((w * 4 + b) * 16 + mm) * 16 + n];
-    store_v<FUSED>(L, v0 + (int64_t)mm * rank + j0 + j, sum);
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * wave + 4 * g + i, j = 16 * b + m;
+      if (b < nb && t < ntok && j < rank) store_v<FUSED>(L, area + v0 + (int64_t)t * rank + j, acc[b][i], tag);
+    }
   }
 }
 
+// ---------------------------------------------------------------------------
+// Combine tile: up to 16 tokens of a 64-token MFMA shrink block split over K.
+// v = sum over splits s = 0, 1, ... of the partial in area s, added in that
+// order (deterministic), written to area 0 with the plain epoch.
 template <bool FUSED>
-__device__ __forceinline__ void shrink_mfma_dispatch(const DeltaLaunch& L, const int32_t* srec, float* red) {
-  switch ((uni(srec[REC_LEN]) + 15) >> 4) {
-    case 1: shrink_mfma_tile<1, FUSED>(L, srec, red); break;
-    case 2: shrink_mfma_tile<2, FUSED>(L, srec, red); break;
-    case 3: shrink_mfma_tile<3, FUSED>(L, srec, red); break;
-    default: shrink_mfma_tile<4, FUSED>(L, srec, red); break;
+__device__ void combine_tile(const DeltaLaunch& L, const int32_t* srec) {
+  const int ntok = uni(srec[REC_NTOK]);
+  const int rank = uni(srec[REC_RANK]);
+  const int v0 = uni(srec[REC_V0]);
+  const int nsplit = uni(srec[REC_AUX]);
+  const int tid = threadIdx.x;
+  const int n = ntok * rank;                           // <= 16 x 64 = 4 per thread
+  constexpr int Q = kCombineTok * kMaxRankMfma / kThreads;
+  // slot q * kMaxSplits + s: value tid + 256 q of split s
+  float part[Q * kMaxSplits];
+  load_v<FUSED, Q * kMaxSplits>(
+      L, Q * kMaxSplits, v0,
+      [&](int qs) -> int {
+        const int q = qs / kMaxSplits, sp = qs % kMaxSplits, i = tid + q * kThreads;
+        return (i < n && sp < nsplit) ? sp * L.sum_rt + v0 + i : -1;
+      },
+      [&](int qs, float val) { part[qs] = val; }, L.epoch | kPartialTag);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = tid + q * kThreads;
+    float sum = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      if (sp < nsplit) sum += part[q * kMaxSplits + sp];
+    if (i < n) store_v<FUSED>(L, v0 + i, sum, L.epoch);
   }
 }
 
 template <typename T, int NCK>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
-  __shared__ float red[4 * 4 * 16 * 16];  // MFMA: 4 waves x 4 blocks x 16 x 16
+  __shared__ float red[sizeof(T) == 2 ? kShrinkLdsFloats : 4 * 4 * 16];
   __shared__ int32_t srec[kMaxRecWords];
   const int32_t* rec = L.rec + (int64_t)L.shrink_idx[blockIdx.x] * L.stride;
   record_to_lds(rec, L.tokcap, L.pagecap, L.proj, srec);
   if constexpr (sizeof(T) == 2) {
     if (uni(srec[REC_KIND]) & KIND_MFMA_BIT) {
-      shrink_mfma_dispatch<false>(L, srec, red);
+      shrink_mfma_tile<false>(L, srec, red);
       return;
     }
   }
   shrink_gemv_tile<T, NCK, false>(L, srec, red);
+}
+
+// Staged launches: the combine tiles, records n_shrink .. n_shrink + n_combine.
+__global__ __launch_bounds__(kThreads) void combine_kernel(DeltaLaunch L) {
+  __shared__ int32_t srec[kMaxRecWords];
+  record_to_lds(L.rec + (int64_t)(L.n_shrink + blockIdx.x) * L.stride, L.tokcap, L.pagecap, L.proj, srec);
+  combine_tile<false>(L, srec);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,7 +558,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   load_v<FUSED, TB>(
       L, (ntok * rank + kThreads - 1) / kThreads, v0,
       [&](int q) -> int { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
-      [&](int q, float val) { const int i = tid + q * kThreads; if (i < ntok * rank) sv[i] = val; });
+      [&](int q, float val) { const int i = tid + q * kThreads; if (i < ntok * rank) sv[i] = val; }, L.epoch);
   __syncthreads();
 
   float acc[TB][VEC];
@@ -595,7 +657,7 @@ __device__ __forceinline__ int quad_dw(int r, int q) {
 typedef short short4v __attribute__((ext_vector_type(4)));
 constexpr int kBufferFormat = 0x00020000;   // descriptor word 3: raw 32-bit buffer
 
-template <bool FUSED, int KS>
+template <bool FUSED, int KS>   // KS: 32-row k slices of the rank (1 or 2), fixed per instantiation
 __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
@@ -607,7 +669,7 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
-  const int ks_n = (rank + 31) >> 5;                   // <= KS
+  constexpr int ks_n = KS;                             // (rank + 31) / 32
   const int n_pass = (ncol + kMfmaPass - 1) / kMfmaPass;
   const int n_steps = n_pass * ks_n;                   // (pass, k slice), pass-major
   uint32_t* slice = reinterpret_cast<uint32_t*>(lds);  // two slices, used in turn
@@ -650,8 +712,11 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
       yq[k] = ldsel<SLORA_NT_Y>(yb + (int64_t)toks[min(y_row(k), ntok - 1)] * L.h_out + o0 + col);
   };
 
-  uint4 bnext[2];
-  stage_load(0, bnext);
+  // Two staged slices in flight in registers (steps s and s+1), so each wait
+  // covers a load issued two steps earlier.
+  uint4 bs0[2], bs1[2];
+  stage_load(0, bs0);
+  stage_load(1, bs1);
   uint4 y0[4], y1[4];
   load_y(0, y0);
 
@@ -665,7 +730,7 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
         const int j = 32 * (q >> 3) + 8 * g + (q & 7);
         return (tok < ntok && j < rank) ? v0 + tok * rank + j : -1;
       },
-      [&](int q, float val) { sv[q] = scale * val; });
+      [&](int q, float val) { sv[q] = scale * val; }, L.epoch);
   float amax = 0.f;
 #pragma unroll
   for (int q = 0; q < 8 * KS; ++q)
@@ -694,22 +759,26 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
 
   // One pass: kMfmaPass columns, all k slices, then the epilogue.  yc holds
   // this pass's y (fetched a pass earlier), yn receives the next pass's; the
-  // two register sets swap roles from pass to pass.  Slices alternate between
-  // two LDS buffers, so one barrier per slice suffices: a buffer is written
-  // again only after every wave has passed the barrier of the slice that
-  // followed its last read.
-  auto pass_body = [&](int pass, uint4 (&yc)[4], uint4 (&yn)[4]) {
+  // two register sets swap roles from pass to pass.  Step s (pass-major)
+  // stages register slot and LDS buffer s & 1 -- static here, since the pass
+  // loop is unrolled by two and KS is fixed.  Slices alternate between two LDS
+  // buffers, so one barrier per slice suffices: a buffer is written again only
+  // after every wave has passed the barrier of the slice that followed its
+  // last read.
+  auto pass_body = [&](auto par, int pass, uint4 (&yc)[4], uint4 (&yn)[4]) {
     float4v acc[kMfmaPass / 16];
 #pragma unroll
     for (int c = 0; c < kMfmaPass / 16; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks >= ks_n) break;
       const int step = pass * ks_n + ks;
-      uint32_t* buf = slice + (step & 1) * kSliceDw;
-      stage_store(buf, bnext);
+      constexpr int kpar = decltype(par)::value;
+      const int slot = KS == 2 ? ks : kpar;             // == step & 1
+      uint4 (&cur)[2] = slot ? bs1 : bs0;
+      uint32_t* buf = slice + slot * kSliceDw;
+      stage_store(buf, cur);
       lds_barrier();
-      stage_load(step + 1, bnext);
+      stage_load(step + 2, cur);
       if (ks == 0) load_y(pass + 1, yn);
 #pragma unroll
       for (int cb = 0; cb < kMfmaPass / 16; ++cb) {
@@ -749,16 +818,20 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
     }
   };
   for (int pass = 0;; pass += 2) {
-    pass_body(pass, y0, y1);
+    pass_body(std::integral_constant<int, 0>{}, pass, y0, y1);
     if (pass + 1 >= n_pass) break;
-    pass_body(pass + 1, y1, y0);
+    pass_body(std::integral_constant<int, 1>{}, pass + 1, y1, y0);
     if (pass + 2 >= n_pass) break;
   }
 }
 
 template <bool FUSED>
 __device__ __forceinline__ void expand_mfma_dispatch(const DeltaLaunch& L, const int32_t* srec, float* lds) {
-  expand_mfma_tile<FUSED, kMaxRankMfma / 32>(L, srec, lds);
+  static_assert(kMaxRankMfma == 64, "two instantiations cover ranks 1..64");
+  if (uni(srec[REC_RANK]) <= 32)
+    expand_mfma_tile<FUSED, 1>(L, srec, lds);
+  else
+    expand_mfma_tile<FUSED, 2>(L, srec, lds);
 }
 
 // LDS of the expand tiles: the vector-ALU tiles need kGemvLdsFloats, the
@@ -766,6 +839,7 @@ __device__ __forceinline__ void expand_mfma_dispatch(const DeltaLaunch& L, const
 // the smaller size, which keeps four of them resident per CU.
 constexpr int kGemvLdsFloats = kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256;
 constexpr int kExpandLdsFloats = kMfmaExpandLds > kGemvLdsFloats ? kMfmaExpandLds : kGemvLdsFloats;
+static_assert(kShrinkLdsFloats <= kExpandLdsFloats, "the fused kernel's LDS holds the MFMA shrink stages");
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void expand_kernel(DeltaLaunch L) {
@@ -799,8 +873,12 @@ void fused_kernel(DeltaLaunch L) {
   const int kind = uni(srec[REC_KIND]);
   if (!(kind & KIND_EXPAND_BIT)) {
     if constexpr (sizeof(T) == 2 && MFMA) {
+      if (kind & KIND_COMBINE_BIT) {
+        combine_tile<true>(L, srec);
+        return;
+      }
       if (kind & KIND_MFMA_BIT) {
-        shrink_mfma_dispatch<true>(L, srec, lds);
+        shrink_mfma_tile<true>(L, srec, lds);
         return;
       }
     }
@@ -869,17 +947,25 @@ static hipError_t launch_delta_t(const DeltaLaunch& L, int stages, hipStream_t s
     if (!k) return hipErrorInvalidValue;
     return launch_one(k, blocks, L, stream, start, stop);
   }
+  // Staged: shrink, combine (K-split MFMA blocks), expand; the events bracket
+  // whichever launches run.
   const bool sh = (stages & STAGE_SHRINK) && L.n_shrink > 0;
+  const bool co = (stages & STAGE_SHRINK) && L.n_combine > 0;
   const bool ex = (stages & STAGE_EXPAND) && L.n_expand > 0;
   if (sh) {
     const void* k = shrink_fn<T>(nck);
     if (!k) return hipErrorInvalidValue;
-    hipError_t e = launch_one(k, L.n_shrink, L, stream, start, ex ? nullptr : stop);
+    hipError_t e = launch_one(k, L.n_shrink, L, stream, start, (co || ex) ? nullptr : stop);
+    if (e != hipSuccess) return e;
+  }
+  if (co) {
+    hipError_t e = launch_one(reinterpret_cast<const void*>(&combine_kernel), L.n_combine, L, stream,
+                              sh ? nullptr : start, ex ? nullptr : stop);
     if (e != hipSuccess) return e;
   }
   if (ex) {
     const void* k = reinterpret_cast<const void*>(&expand_kernel<T>);
-    return launch_one(k, L.n_expand, L, stream, sh ? nullptr : start, stop);
+    return launch_one(k, L.n_expand, L, stream, (sh || co) ? nullptr : start, stop);
   }
   return hipSuccess;
 }

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "SLORA_OK", -1: "SLORA_E_INVAL", -2: "SLORA_E_NOMEM", -3: "SL
 SLORA_F32, SLORA_F16 = 0, 1
 SLORA_TUNE_MFMA_MIN_TOKENS, SLORA_TUNE_GEMV_EXPAND_ELEMS, SLORA_TUNE_MFMA_EXPAND_COLS = 0, 1, 2
 SLORA_MFMA_MAX_RANK = 64          # segments of higher rank always take the vector-ALU tiles
-SLORA_TUNE_MFMA_SHRINK_ROWS, SLORA_TUNE_FUSED, SLORA_TUNE_XCDS = 3, 4, 5
+SLORA_TUNE_MFMA_SHRINK_SPLITS, SLORA_TUNE_FUSED, SLORA_TUNE_XCDS = 3, 4, 5
 
 EXPORTED = [
     "slora_pool_create", "slora_pool_destroy", "slora_pool_set_tuning", "slora_alloc_pages",
@@ -55,7 +55,7 @@ class SegmentsInfo(ctypes.Structure):
     _fields_ = [("n_tokens", c_int32), ("n_routed", c_int32), ("n_segments", c_int32),
                 ("n_proj", c_int32), ("sum_rank", c_int64), ("sum_rank_tokens", c_int64),
                 ("n_shrink_tiles", c_int32), ("n_expand_tiles", c_int32),
-                ("n_mfma_segments", c_int32), ("reserved0", c_int32), ("meta_bytes", c_size_t),
+                ("n_mfma_segments", c_int32), ("n_combine_tiles", c_int32), ("meta_bytes", c_size_t),
                 ("workspace_bytes", c_size_t)]
 
 
@@ -258,7 +258,8 @@ def slora_segments_tiles(seg):
     info = slora_segments_get_info(seg)
     lay = np.empty(9, np.int32)
     _check(lib().slora_segments_tiles(seg, _i32p(lay), None, 0), "slora_segments_tiles")
-    keys = ["n_tiles", "stride", "tokcap", "pagecap", "n_shrink", "n_expand", "hdr"]
+    keys = ["n_tiles", "stride", "tokcap", "pagecap", "n_shrink", "n_expand", "hdr", "n_combine",
+            "n_splits"]
     layout = dict(zip(keys, (int(v) for v in lay)))
     n, st = layout["n_tiles"], layout["stride"]
     rec = np.zeros(max(n * st, 4), np.int32)

@@ -117,8 +117,10 @@ def test_metadata_bit_exact_vs_oracle(name):
 
 
 def check_tiles_cover(w, pool, ids):
-    """Every (token, rank row) is shrunk once and every (token, column) expanded
-    once, and every expand tile comes after the shrink tiles of its tokens."""
+    """Every (token, rank row) is shrunk once (MFMA shrink: once per K split,
+    the splits' k ranges tiling [0, h_in), summed by exactly one combine tile
+    when there are several), every (token, column) expanded once, and every
+    expand tile comes after the shrink and combine tiles of its tokens."""
     seg = S.slora_build_segments(pool, ids)
     try:
         info = S.slora_segments_get_info(seg)
@@ -127,7 +129,8 @@ def check_tiles_cover(w, pool, ids):
         spec = w.spec
         n_seg = info["n_segments"]
         hdr, tokcap, pagecap = lay["hdr"], lay["tokcap"], lay["pagecap"]
-        assert lay["n_tiles"] == len(recs) == lay["n_shrink"] + lay["n_expand"]
+        assert lay["n_tiles"] == len(recs) == lay["n_shrink"] + lay["n_combine"] + lay["n_expand"]
+        assert lay["n_combine"] == info["n_combine_tiles"]
         assert lay["n_shrink"] == info["n_shrink_tiles"] and lay["n_expand"] == info["n_expand_tiles"]
         seg_of = {}
         for s in range(n_seg):
@@ -143,13 +146,16 @@ def check_tiles_cover(w, pool, ids):
                 off += r
         assert off == info["sum_rank_tokens"]
         shrink_seen = np.zeros(max(off, 1), np.int32)
+        combine_seen = np.zeros(max(off, 1), np.int32)
+        k_cover = {}                    # MFMA shrink: token -> h_in coverage by k
         last_shrink_of_token = {}
+        n_co = 0
         routed = [t for t in range(len(ids)) if ids[t] >= 0]
         cover = {t: np.zeros(spec.h_out, np.int32) for t in routed}
         n_sh = n_ex = 0
         for idx, rec in enumerate(recs):
             kind, ntok, r, pos, length, v0 = (int(v) for v in rec[:6])
-            assert kind in (0, 1, 2, 3) and 1 <= ntok <= tokcap and length >= 1
+            assert kind in (0, 1, 2, 3, 5) and 1 <= ntok <= tokcap and length >= 1
             assert (kind & 1) <= (spec.dtype == "f16")
             toks = rec[hdr:hdr + ntok]
             s = seg_of[int(toks[0])]
@@ -157,7 +163,30 @@ def check_tiles_cover(w, pool, ids):
             for k, t in enumerate(toks):
                 assert seg_of[int(t)] == s and v_row[int(t)] == v0 + k * r
             base = [p * info["sum_rank"] + ex["seg_page_off"][s] for p in range(spec.n_proj)]
-            if not kind & 2:            # shrink
+            if kind == 5:               # combine: after every shrink tile of its tokens
+                n_co += 1
+                assert idx >= lay["n_shrink"] and ntok <= 16 and length == r
+                assert int(rec[7]) == lay["n_splits"] > 1
+                for t in toks:
+                    assert last_shrink_of_token[int(t)] < idx
+                    combine_seen[v_row[int(t)]:v_row[int(t)] + r] += 1
+                    last_shrink_of_token[int(t)] = idx
+                continue
+            if kind == 1:               # MFMA shrink: all r rows over one K split
+                n_sh += 1
+                assert int(rec[9]) == lay["n_splits"] and 0 <= int(rec[7]) < lay["n_splits"]
+                assert pos % 64 == 0 and length % 64 == 0 and pos + length <= spec.h_in
+                for t in toks:
+                    cov = k_cover.setdefault(int(t), np.zeros(spec.h_in, np.int32))
+                    cov[pos:pos + length] += 1
+                    if pos == 0:
+                        shrink_seen[v_row[int(t)]:v_row[int(t)] + r] += 1
+                    last_shrink_of_token[int(t)] = idx
+                for p in range(spec.n_proj):
+                    pg = rec[hdr + tokcap + p * pagecap:][:r]
+                    np.testing.assert_array_equal(pg, ex["a_pages"][base[p]:base[p] + r])
+                continue
+            if not kind & 2:            # vector-ALU shrink
                 n_sh += 1
                 assert 0 <= pos and pos + length <= r
                 for t in toks:
@@ -180,8 +209,13 @@ def check_tiles_cover(w, pool, ids):
                 for p in range(spec.n_proj):
                     pg = rec[hdr + tokcap + p * pagecap:][:r]
                     np.testing.assert_array_equal(pg, ex["b_pages"][base[p]:base[p] + r])
-        assert n_sh == lay["n_shrink"] and n_ex == lay["n_expand"]
+        assert n_sh == lay["n_shrink"] and n_ex == lay["n_expand"] and n_co == lay["n_combine"]
         assert (shrink_seen[:off] == 1).all()
+        for cov in k_cover.values():
+            assert (cov == 1).all()
+        if lay["n_splits"] > 1:         # every MFMA token's v is combined exactly once
+            for t in k_cover:
+                assert (combine_seen[v_row[t]:v_row[t] + int(ex["seg_rank"][seg_of[t]])] == 1).all()
         for t in routed:
             assert (cover[t] == 1).all(), t
         return info
