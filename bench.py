@@ -94,6 +94,81 @@ def cpu_baseline(w, budget_s=10.0):
             "host_cpu_count": os.cpu_count()}
 
 
+def measure_prefetch(dw, w, m, steps, flush, step, stream):
+    """Walkthrough step 2 of the summary page: the next batch's adapters are
+    fetched into the pool while the current batch computes.  m adapters the
+    batch does not reference are evicted, then fetched again from pinned host
+    images on a second stream, first alone and then while the step's delta
+    runs; after every step they are evicted again.  One
+    slora_load_adapters_async call per step queues all m image copies and one
+    scatter launch."""
+    import numpy as np
+    import torch
+
+    from rank_gemm_page_amd import slora as S
+    cand = [a for a in range(w.spec.n_adapters) if not w.referenced[a]][:m]
+    images = {a: dw.pack(a) for a in cand}
+    for a in cand:
+        S.slora_unload_adapter(dw.pool, a)
+    side = torch.cuda.Stream()
+    nbytes = sum(int(w.spec.n_proj * w.ranks[a] * (w.spec.h_in + w.spec.h_out)
+                     * (2 if w.spec.dtype == "f16" else 4)) for a in cand)
+
+    def fetch_round(with_delta):
+        t0, td, tl = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        flush()
+        t0.record(stream)
+        side.wait_event(t0)
+        if with_delta:
+            step()
+            td.record(stream)
+        h = time.perf_counter()
+        dw.load_async(cand, side, images=[images[a] for a in cand])
+        host_s = time.perf_counter() - h
+        tl.record(side)
+        torch.cuda.synchronize()
+        dw.images.clear()
+        for a in cand:
+            S.slora_unload_adapter(dw.pool, a)
+        return (t0.elapsed_time(td) if with_delta else None), t0.elapsed_time(tl), host_s
+
+    for _ in range(2):
+        fetch_round(False)
+        fetch_round(True)
+    alone = [fetch_round(False) for _ in range(steps)]
+    both = [fetch_round(True) for _ in range(steps)]
+    delta_ms = statistics.fmean(b[0] for b in both)
+    load_ms = statistics.fmean(a[1] for a in alone)
+    host_us = statistics.median(a[2] for a in alone) * 1e6
+    load_ov_ms = statistics.fmean(b[1] for b in both)
+    # the step alone, timed the same way (flush, then events on the launch stream)
+    solo = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush()
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        solo.append(a.elapsed_time(b))
+    solo_ms = statistics.fmean(solo)
+    for a in cand:
+        S.slora_load_adapter(dw.pool, a, int(w.ranks[a]), float(w.scales[a]))
+    return {"adapters": len(cand), "bytes": nbytes,
+            "ranks": np.bincount(w.ranks[cand]).nonzero()[0].tolist(),
+            "host_enqueue_us": round(host_us, 1),
+            "fetch_us_alone": round(load_ms * 1e3, 2),
+            "h2d_GBps_alone": round(nbytes / (load_ms * 1e-3) / 1e9, 2),
+            "fetch_us_with_step": round(load_ov_ms * 1e3, 2),
+            "h2d_GBps_with_step": round(nbytes / (load_ov_ms * 1e-3) / 1e9, 2),
+            "step_us_alone": round(solo_ms * 1e3, 2),
+            "step_us_with_fetch": round(delta_ms * 1e3, 2),
+            "step_slowdown": round(delta_ms / solo_ms - 1.0, 4),
+            "timing": "HIP events: the step on the launch stream, the fetch on a second stream "
+                      "that starts with the step; means over the timed steps, cache flushed "
+                      "before each"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +187,9 @@ def main():
     ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
+    ap.add_argument("--prefetch", type=int, default=0, metavar="M",
+                    help="also fetch M adapters the batch does not use from pinned host images "
+                         "on a second stream, alone and while the step runs (slora_load_adapter_async)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain copy of this size (PMC calibration runs)")
     args = ap.parse_args()
@@ -317,6 +395,9 @@ def main():
                   "last-level cache and is outside both",
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
     }
+    if args.prefetch > 0:
+        log(f"[bench] adapter fetch: {args.prefetch} adapters per step")
+        out["prefetch"] = measure_prefetch(dw, w, args.prefetch, K, flush, step, stream)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -135,14 +135,59 @@ int64_t slora_free_count(const slora_pool* pool, int32_t cls);
  * pages for the A^T rows j = 0..rank-1 and then rank pages for the B rows (B
  * rows come from class 1 when the pool has two classes).  A and B are host
  * arrays of n_proj pointers: A[p] is h_in x rank row-major, B[p] is
- * rank x h_out row-major, both of the pool dtype.  The rows are copied to the
- * pages through pinned staging on `stream`, and the call returns after the
- * copy has completed, so A and B may be freed at once.  A == NULL and
+ * rank x h_out row-major, both of the pool dtype.  The rows are packed into a
+ * pinned staging image and fetched into the pages on `stream` as by
+ * slora_load_adapters_async, and the call returns after the fetch has
+ * completed, so A and B may be freed at once.  A == NULL and
  * B == NULL together reserve the pages and block-table entry without writing
  * them (the pages keep their previous content).  1 <= rank <= max_rank; scale
  * must be finite. */
 slora_status slora_load_adapter(slora_pool* pool, int32_t id, int32_t rank, float scale,
                                 const void* const* A, const void* const* B, void* stream);
+
+/* Asynchronous adapter fetch (summary page, "Host-resident adapter store" and
+ * walkthrough step 2: the next iteration's adapters are copied into the pool
+ * while the current one computes).  An adapter image is the byte layout one load
+ * moves to the device: the n_proj x rank A^T rows (h_in elements each,
+ * projection-major), then the n_proj x rank B rows (h_out elements), then
+ * 2 x n_proj x rank int32 page ids that the load writes; padded to 256 bytes.
+ * slora_adapter_image_bytes returns its size for `rank` (0 on a bad pool or
+ * rank). */
+size_t slora_adapter_image_bytes(const slora_pool* pool, int32_t rank);
+/* Fill an image (host, image_bytes >= slora_adapter_image_bytes(rank)) from
+ * A and B laid out as for slora_load_adapter: A^T rows are A's columns.  Host
+ * only, no device call; done once when an adapter enters the host store, so
+ * that a later fetch is one copy. */
+slora_status slora_pack_adapter(const slora_pool* pool, int32_t rank, const void* const* A,
+                                const void* const* B, void* image, size_t image_bytes);
+/* Fetch n adapters at once.  For k = 0..n-1 in order, take pages for adapter
+ * ids[k] (rank ranks[k], scale scales[k]) exactly as slora_load_adapter would
+ * (same free-list order) and write their ids into images[k]; then queue on
+ * `stream` one host-to-device copy per image into dev_stage (image k at the
+ * sum of the earlier images' slora_adapter_image_bytes), all copies first so
+ * the copy engine runs them back to back, and then one kernel launch per 64
+ * adapters that moves every row into its page; return without waiting.  The
+ * copies run on a copy engine, not on the compute units, so a delta running
+ * meanwhile loses little.  images[k] is an image packed by slora_pack_adapter
+ * for ranks[k], in pinned host memory (hipHostMalloc, or a pinned torch
+ * tensor); dev_stage is device memory of the pool's device of dev_stage_bytes
+ * >= the images' total size.  Every argument is checked first (bad id, rank or
+ * scale, an id twice, an unpinned image, a dev_stage too small or not on the
+ * device: SLORA_E_INVAL; an id already loaded: SLORA_E_EXIST; too few free
+ * pages for the whole batch: SLORA_E_NOMEM) and a failure takes no page.
+ * Ownership stays with the caller; neither the images nor dev_stage may be
+ * written, reused or freed until `stream` has passed this call.  The adapters
+ * count as loaded at once (segments may be built against them), but their
+ * pages hold the rows only once `stream` has passed the call: a
+ * slora_lora_delta that reads them must be queued after it on the same stream
+ * or wait for an event recorded there.  Likewise, unloading an adapter whose
+ * pages a queued delta still reads and fetching another into them races unless
+ * the fetch's stream waits for the delta.  A failed queue call returns
+ * SLORA_E_HIP with every page given back; device faults surface at the
+ * caller's synchronisation.  n == 0 does nothing. */
+slora_status slora_load_adapters_async(slora_pool* pool, int32_t n, const int32_t* ids,
+                                       const int32_t* ranks, const float* scales, void* const* images,
+                                       void* dev_stage, size_t dev_stage_bytes, void* stream);
 /* Drop adapter `id` from the pool (summary page, walkthrough step 4: unused
  * adapters leave GPU memory).  Its pages go to the tail of the free list in the
  * order they were taken.  Segments built against it become stale. */

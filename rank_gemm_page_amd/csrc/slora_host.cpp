@@ -113,13 +113,12 @@ struct slora_pool {
   std::vector<AdapterRec> adapters;
   uint64_t gen_counter = 0;
   Tuning tune;
-  // load staging (lazily allocated on the first load with data)
+  // synchronous-load staging: one adapter image of max_rank, pinned on the
+  // host and on the device (allocated on the first load with data)
   int device = -1;
   char* h_stage = nullptr;
   char* d_stage = nullptr;
   size_t stage_bytes = 0;
-  int32_t* h_pages = nullptr;
-  int32_t* d_pages = nullptr;
   // metadata upload arena (pinned, two slots used in turn)
   char* h_meta[2] = {nullptr, nullptr};
   size_t h_meta_bytes[2] = {0, 0};
@@ -177,26 +176,73 @@ slora_status set_device(slora_pool* p) {
   return SLORA_OK;
 }
 
+// Adapter image: the byte layout shared by the synchronous load's pinned
+// staging buffer and the caller's images for slora_load_adapters_async.
+struct ImageLayout {
+  size_t a_bytes;     // n_proj x rank A^T rows of h_in elements
+  size_t rows_bytes;  // + n_proj x rank B rows of h_out elements
+  size_t ids_off;     // 2 x n_proj x rank int32 page ids (A^T pages, then B pages)
+  size_t used;        // bytes the load copies to the device
+  size_t total;       // used, rounded up to 256
+};
+
+ImageLayout image_layout(const slora_pool* p, int32_t rank) {
+  ImageLayout L;
+  const size_t rows = (size_t)p->d.n_proj * (size_t)rank;
+  L.a_bytes = rows * (size_t)p->d.h_in * (size_t)p->elem;
+  L.rows_bytes = L.a_bytes + rows * (size_t)p->d.h_out * (size_t)p->elem;
+  L.ids_off = L.rows_bytes;   // a multiple of 16: h_in and h_out are multiples of 8
+  L.used = L.ids_off + 2 * rows * sizeof(int32_t);
+  L.total = (L.used + 255) / 256 * 256;
+  return L;
+}
+
 slora_status ensure_stage(slora_pool* p) {
   if (p->h_stage) return SLORA_OK;
   slora_status st = set_device(p);
   if (st != SLORA_OK) return st;
-  const size_t rows = (size_t)p->d.n_proj * (size_t)p->d.max_rank;
-  const size_t bytes = rows * (size_t)(p->d.h_in + p->d.h_out) * (size_t)p->elem;
-  const size_t pbytes = 2 * rows * sizeof(int32_t);
+  const size_t bytes = image_layout(p, p->d.max_rank).total;
   hipError_t e = hipHostMalloc((void**)&p->h_stage, bytes, hipHostMallocDefault);
   if (e != hipSuccess) { p->h_stage = nullptr; return hip_fail(e, "hipHostMalloc(load staging)"); }
-  e = hipHostMalloc((void**)&p->h_pages, pbytes, hipHostMallocDefault);
-  if (e == hipSuccess) e = hipMalloc((void**)&p->d_stage, bytes);
-  if (e == hipSuccess) e = hipMalloc((void**)&p->d_pages, pbytes);
+  e = hipMalloc((void**)&p->d_stage, bytes);
   if (e != hipSuccess) {
-    if (p->d_stage) (void)hipFree(p->d_stage);
-    if (p->h_pages) (void)hipHostFree(p->h_pages);
     (void)hipHostFree(p->h_stage);
-    p->h_stage = nullptr; p->d_stage = nullptr; p->h_pages = nullptr; p->d_pages = nullptr;
-    return hip_fail(e, "load staging allocation");
+    p->h_stage = nullptr; p->d_stage = nullptr;
+    return hip_fail(e, "hipMalloc(load staging)");
   }
   p->stage_bytes = bytes;
+  return SLORA_OK;
+}
+
+// A^T row j of projection p is column j of the h_in x rank row-major A[p];
+// the transpose goes in blocks of 64 source rows to stay in cache.
+template <typename E>
+void transpose_into(E* dst, const E* src, int64_t hin, int32_t r) {
+  constexpr int64_t KB = 64;
+  for (int64_t k0 = 0; k0 < hin; k0 += KB) {
+    const int64_t k1 = std::min(hin, k0 + KB);
+    for (int32_t j = 0; j < r; ++j) {
+      E* d = dst + (size_t)j * hin;
+      for (int64_t k = k0; k < k1; ++k) d[k] = src[(size_t)k * r + j];
+    }
+  }
+}
+
+slora_status pack_image(const slora_pool* p, int32_t r, const void* const* A, const void* const* B,
+                        char* image, const char* fn) {
+  const int np = p->d.n_proj, e = p->elem;
+  const int64_t hin = p->d.h_in, hout = p->d.h_out;
+  const ImageLayout L = image_layout(p, r);
+  for (int pr = 0; pr < np; ++pr)
+    if (!A[pr] || !B[pr]) return fail(SLORA_E_INVAL, std::string(fn) + ": NULL A[p] or B[p]");
+  for (int pr = 0; pr < np; ++pr) {
+    char* dst = image + (size_t)pr * r * hin * e;
+    if (e == 2)
+      transpose_into(reinterpret_cast<uint16_t*>(dst), static_cast<const uint16_t*>(A[pr]), hin, r);
+    else
+      transpose_into(reinterpret_cast<uint32_t*>(dst), static_cast<const uint32_t*>(A[pr]), hin, r);
+    std::memcpy(image + L.a_bytes + (size_t)pr * r * hout * e, B[pr], (size_t)r * hout * e);
+  }
   return SLORA_OK;
 }
 
@@ -217,45 +263,109 @@ void rollback_pages(slora_pool* p, const AdapterRec& rec) {
   }
 }
 
+// For each adapter k: write its page ids into images[k] and queue on `stream`
+// the copy of the image to dev_stage + (sum of the earlier images' sizes);
+// then queue the scatters of all rows into their pages, kMaxFetch adapters
+// per launch.  All copies go first so the copy engine runs them back to back.
+slora_status enqueue_images(slora_pool* p, const std::vector<const AdapterRec*>& recs,
+                            char* const* images, char* dev_stage, hipStream_t stream) {
+  const int np = p->d.n_proj;
+  const size_t n = recs.size();
+  std::vector<size_t> off(n + 1, 0);
+  for (size_t k = 0; k < n; ++k) {
+    const AdapterRec& rec = *recs[k];
+    const int r = rec.rank;
+    const ImageLayout L = image_layout(p, r);
+    int32_t* ids = reinterpret_cast<int32_t*>(images[k] + L.ids_off);
+    std::memcpy(ids, rec.a_pages.data(), (size_t)np * r * sizeof(int32_t));
+    std::memcpy(ids + (size_t)np * r, rec.b_pages.data(), (size_t)np * r * sizeof(int32_t));
+    hipError_t he = hipMemcpyAsync(dev_stage + off[k], images[k], L.used, hipMemcpyHostToDevice, stream);
+    if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(adapter image)");
+    off[k + 1] = off[k] + L.total;
+  }
+  for (size_t k0 = 0; k0 < n; k0 += kMaxFetch) {
+    ScatterLaunch S{};
+    S.stage = dev_stage;
+    S.n = (int32_t)std::min<size_t>(kMaxFetch, n - k0);
+    S.n_proj = np;
+    S.a_row_bytes = p->d.h_in * (int64_t)p->elem;
+    S.b_row_bytes = p->d.h_out * (int64_t)p->elem;
+    S.a_base = static_cast<char*>(p->d.class_base[0]);
+    S.b_base = static_cast<char*>(p->d.class_base[p->b_class()]);
+    S.a_page_bytes = p->page_bytes[0];
+    S.b_page_bytes = p->page_bytes[p->b_class()];
+    S.row_start[0] = 0;
+    for (int i = 0; i < S.n; ++i) {
+      S.rank[i] = recs[k0 + i]->rank;
+      S.img_off[i] = (int64_t)off[k0 + i];
+      S.row_start[i + 1] = S.row_start[i] + 2 * np * S.rank[i];
+    }
+    hipError_t he = launch_scatter_pages(S, stream);
+    if (he != hipSuccess) return hip_fail(he, "scatter adapter rows");
+  }
+  return SLORA_OK;
+}
+
 slora_status upload_adapter(slora_pool* p, const AdapterRec& rec, const void* const* A,
                             const void* const* B, hipStream_t stream) {
   slora_status st = ensure_stage(p);
   if (st != SLORA_OK) return st;
-  const int r = rec.rank, np = p->d.n_proj, e = p->elem;
-  const int64_t hin = p->d.h_in, hout = p->d.h_out;
-  char* a_rows = p->h_stage;
-  char* b_rows = p->h_stage + (size_t)np * r * hin * e;
-  for (int pr = 0; pr < np; ++pr) {
-    const char* Ap = static_cast<const char*>(A[pr]);
-    const char* Bp = static_cast<const char*>(B[pr]);
-    if (!Ap || !Bp) return fail(SLORA_E_INVAL, "slora_load_adapter: NULL A[p] or B[p]");
-    // A^T row j is column j of the h_in x r row-major A.
-    char* dst = a_rows + (size_t)pr * r * hin * e;
-    for (int64_t k = 0; k < hin; ++k)
-      for (int j = 0; j < r; ++j)
-        std::memcpy(dst + ((size_t)j * hin + k) * e, Ap + ((size_t)k * r + j) * e, e);
-    std::memcpy(b_rows + (size_t)pr * r * hout * e, Bp, (size_t)r * hout * e);
-    std::memcpy(p->h_pages + (size_t)pr * r, rec.a_pages.data() + (size_t)pr * r, r * sizeof(int32_t));
-    std::memcpy(p->h_pages + (size_t)(np + pr) * r, rec.b_pages.data() + (size_t)pr * r,
-                r * sizeof(int32_t));
-  }
-  const size_t bytes = (size_t)np * r * (hin + hout) * e;
-  hipError_t he = hipMemcpyAsync(p->d_stage, p->h_stage, bytes, hipMemcpyHostToDevice, stream);
-  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(adapter rows)");
-  he = hipMemcpyAsync(p->d_pages, p->h_pages, (size_t)2 * np * r * sizeof(int32_t),
-                      hipMemcpyHostToDevice, stream);
-  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(page ids)");
-  he = launch_scatter_rows(p->d_stage, np * r, hin * e, p->d_pages,
-                           static_cast<char*>(p->d.class_base[0]), p->page_bytes[0], stream);
-  if (he != hipSuccess) return hip_fail(he, "scatter A^T rows");
-  he = launch_scatter_rows(p->d_stage + (size_t)np * r * hin * e, np * r, hout * e,
-                           p->d_pages + (size_t)np * r,
-                           static_cast<char*>(p->d.class_base[p->b_class()]),
-                           p->page_bytes[p->b_class()], stream);
-  if (he != hipSuccess) return hip_fail(he, "scatter B rows");
-  he = hipStreamSynchronize(stream);
+  st = pack_image(p, rec.rank, A, B, p->h_stage, "slora_load_adapter");
+  if (st != SLORA_OK) return st;
+  char* img = p->h_stage;
+  st = enqueue_images(p, {&rec}, &img, p->d_stage, stream);
+  if (st != SLORA_OK) return st;
+  hipError_t he = hipStreamSynchronize(stream);
   if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize(adapter load)");
   return SLORA_OK;
+}
+
+// Argument checks shared by the two loads (no device call).
+slora_status check_load(const slora_pool* p, int32_t id, int32_t rank, float scale, const char* fn) {
+  const std::string f(fn);
+  if (!p) return fail(SLORA_E_INVAL, f + ": NULL pool");
+  if (id < 0 || id >= p->d.max_adapters) return fail(SLORA_E_INVAL, f + ": id out of range");
+  if (rank < 1 || rank > p->d.max_rank) return fail(SLORA_E_INVAL, f + ": rank out of range");
+  if (!std::isfinite(scale)) return fail(SLORA_E_INVAL, f + ": scale must be finite");
+  if (p->adapters[id].loaded) return fail(SLORA_E_EXIST, f + ": adapter already loaded");
+  const int64_t need = (int64_t)rank * p->d.n_proj;
+  if (p->d.n_classes == 2) {
+    if (need > p->free_list[0].count || need > p->free_list[1].count)
+      return fail(SLORA_E_NOMEM, f + ": not enough free pages");
+  } else if (2 * need > p->free_list[0].count) {
+    return fail(SLORA_E_NOMEM, f + ": not enough free pages");
+  }
+  return SLORA_OK;
+}
+
+// Take the adapter's pages from the head of the free list: per projection,
+// rank pages for the A^T rows, then rank pages for the B rows.
+AdapterRec take_pages(slora_pool* p, int32_t rank, float scale) {
+  const int np = p->d.n_proj;
+  AdapterRec rec;
+  rec.rank = rank;
+  rec.scale = scale;
+  rec.a_pages.resize((size_t)rank * np);
+  rec.b_pages.resize((size_t)rank * np);
+  for (int pr = 0; pr < np; ++pr) {
+    for (int j = 0; j < rank; ++j) {
+      const int32_t a = p->free_list[0].pop_front();
+      p->state[0][a] = PAGE_ADAPTER;
+      rec.a_pages[(size_t)pr * rank + j] = a;
+    }
+    for (int j = 0; j < rank; ++j) {
+      const int32_t b = p->free_list[p->b_class()].pop_front();
+      p->state[p->b_class()][b] = PAGE_ADAPTER;
+      rec.b_pages[(size_t)pr * rank + j] = b;
+    }
+  }
+  return rec;
+}
+
+void commit_adapter(slora_pool* p, int32_t id, AdapterRec&& rec) {
+  rec.loaded = true;
+  rec.gen = ++p->gen_counter;
+  p->adapters[id] = std::move(rec);
 }
 
 // ---------------------------------------------------------------------------
@@ -558,9 +668,7 @@ void slora_pool_destroy(slora_pool* p) {
     if (p->h_meta[i]) (void)hipHostFree(p->h_meta[i]);
   }
   if (p->d_stage) (void)hipFree(p->d_stage);
-  if (p->d_pages) (void)hipFree(p->d_pages);
   if (p->h_stage) (void)hipHostFree(p->h_stage);
-  if (p->h_pages) (void)hipHostFree(p->h_pages);
   delete p;
 }
 
@@ -642,48 +750,98 @@ slora_status slora_free_pages(slora_pool* p, int32_t cls, int64_t n, const int32
 
 slora_status slora_load_adapter(slora_pool* p, int32_t id, int32_t rank, float scale,
                                 const void* const* A, const void* const* B, void* stream) {
-  if (!p) return fail(SLORA_E_INVAL, "slora_load_adapter: NULL pool");
-  if (id < 0 || id >= p->d.max_adapters) return fail(SLORA_E_INVAL, "slora_load_adapter: id out of range");
-  if (rank < 1 || rank > p->d.max_rank) return fail(SLORA_E_INVAL, "slora_load_adapter: rank out of range");
-  if (!std::isfinite(scale)) return fail(SLORA_E_INVAL, "slora_load_adapter: scale must be finite");
+  slora_status st = check_load(p, id, rank, scale, "slora_load_adapter");
+  if (st != SLORA_OK) return st;
   if ((A == nullptr) != (B == nullptr))
     return fail(SLORA_E_INVAL, "slora_load_adapter: A and B must both be given or both be NULL");
-  if (p->adapters[id].loaded) return fail(SLORA_E_EXIST, "slora_load_adapter: adapter already loaded");
-  const int np = p->d.n_proj;
-  const int64_t need = (int64_t)rank * np;
-  if (p->d.n_classes == 2) {
-    if (need > p->free_list[0].count || need > p->free_list[1].count)
-      return fail(SLORA_E_NOMEM, "slora_load_adapter: not enough free pages");
-  } else if (2 * need > p->free_list[0].count) {
-    return fail(SLORA_E_NOMEM, "slora_load_adapter: not enough free pages");
-  }
-  AdapterRec rec;
-  rec.rank = rank;
-  rec.scale = scale;
-  rec.a_pages.resize((size_t)need);
-  rec.b_pages.resize((size_t)need);
-  for (int pr = 0; pr < np; ++pr) {
-    for (int j = 0; j < rank; ++j) {
-      const int32_t a = p->free_list[0].pop_front();
-      p->state[0][a] = PAGE_ADAPTER;
-      rec.a_pages[(size_t)pr * rank + j] = a;
-    }
-    for (int j = 0; j < rank; ++j) {
-      const int32_t b = p->free_list[p->b_class()].pop_front();
-      p->state[p->b_class()][b] = PAGE_ADAPTER;
-      rec.b_pages[(size_t)pr * rank + j] = b;
-    }
-  }
+  AdapterRec rec = take_pages(p, rank, scale);
   if (A) {
-    slora_status st = upload_adapter(p, rec, A, B, static_cast<hipStream_t>(stream));
+    st = upload_adapter(p, rec, A, B, static_cast<hipStream_t>(stream));
     if (st != SLORA_OK) {
       rollback_pages(p, rec);
       return st;
     }
   }
-  rec.loaded = true;
-  rec.gen = ++p->gen_counter;
-  p->adapters[id] = std::move(rec);
+  commit_adapter(p, id, std::move(rec));
+  return SLORA_OK;
+}
+
+size_t slora_adapter_image_bytes(const slora_pool* p, int32_t rank) {
+  if (!p || rank < 1 || rank > p->d.max_rank) return 0;
+  return image_layout(p, rank).total;
+}
+
+slora_status slora_pack_adapter(const slora_pool* p, int32_t rank, const void* const* A,
+                                const void* const* B, void* image, size_t image_bytes) {
+  if (!p) return fail(SLORA_E_INVAL, "slora_pack_adapter: NULL pool");
+  if (rank < 1 || rank > p->d.max_rank) return fail(SLORA_E_INVAL, "slora_pack_adapter: rank out of range");
+  if (!A || !B || !image) return fail(SLORA_E_INVAL, "slora_pack_adapter: NULL A, B or image");
+  if (image_bytes < image_layout(p, rank).total)
+    return fail(SLORA_E_INVAL, "slora_pack_adapter: image smaller than slora_adapter_image_bytes(rank)");
+  return pack_image(p, rank, A, B, static_cast<char*>(image), "slora_pack_adapter");
+}
+
+slora_status slora_load_adapters_async(slora_pool* p, int32_t n, const int32_t* ids,
+                                       const int32_t* ranks, const float* scales, void* const* images,
+                                       void* dev_stage, size_t dev_stage_bytes, void* stream) {
+  const char* fn = "slora_load_adapters_async";
+  if (!p) return fail(SLORA_E_INVAL, std::string(fn) + ": NULL pool");
+  if (n < 0) return fail(SLORA_E_INVAL, std::string(fn) + ": n must be >= 0");
+  if (n == 0) return SLORA_OK;
+  if (!ids || !ranks || !scales || !images || !dev_stage)
+    return fail(SLORA_E_INVAL, std::string(fn) + ": NULL ids, ranks, scales, images or dev_stage");
+  // Every check before any page is taken: ids, ranks, scales, duplicates,
+  // free pages for the whole batch, staging size, then the buffers' kinds.
+  std::vector<char> seen((size_t)p->d.max_adapters, 0);
+  int64_t need[2] = {0, 0};
+  size_t stage_need = 0;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t id = ids[k], r = ranks[k];
+    if (id < 0 || id >= p->d.max_adapters) return fail(SLORA_E_INVAL, std::string(fn) + ": id out of range");
+    if (r < 1 || r > p->d.max_rank) return fail(SLORA_E_INVAL, std::string(fn) + ": rank out of range");
+    if (!std::isfinite(scales[k])) return fail(SLORA_E_INVAL, std::string(fn) + ": scale must be finite");
+    if (!images[k]) return fail(SLORA_E_INVAL, std::string(fn) + ": NULL image");
+    if (seen[id]) return fail(SLORA_E_INVAL, std::string(fn) + ": an id appears twice");
+    seen[id] = 1;
+    if (p->adapters[id].loaded) return fail(SLORA_E_EXIST, std::string(fn) + ": adapter already loaded");
+    need[0] += (int64_t)r * p->d.n_proj;
+    need[p->b_class()] += (int64_t)r * p->d.n_proj;
+    stage_need += image_layout(p, r).total;
+  }
+  for (int c = 0; c < p->d.n_classes; ++c)
+    if (need[c] > p->free_list[c].count) return fail(SLORA_E_NOMEM, std::string(fn) + ": not enough free pages");
+  if (dev_stage_bytes < stage_need)
+    return fail(SLORA_E_INVAL, std::string(fn) + ": dev_stage smaller than the images' total size");
+  slora_status st = set_device(p);
+  if (st != SLORA_OK) return st;
+  // The copies are asynchronous only from pinned memory, and the scatter reads
+  // dev_stage on the pool's device.
+  for (int32_t k = 0; k < n; ++k) {
+    hipPointerAttribute_t at{};
+    hipError_t he = hipPointerGetAttributes(&at, images[k]);
+    if (he != hipSuccess || at.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(SLORA_E_INVAL, std::string(fn) + ": an image is not pinned host memory");
+    }
+  }
+  hipPointerAttribute_t at{};
+  hipError_t he = hipPointerGetAttributes(&at, dev_stage);
+  if (he != hipSuccess || at.type != hipMemoryTypeDevice || at.device != p->device) {
+    (void)hipGetLastError();
+    return fail(SLORA_E_INVAL, std::string(fn) + ": dev_stage is not device memory of the pool's device");
+  }
+  std::vector<AdapterRec> recs;
+  recs.reserve((size_t)n);
+  for (int32_t k = 0; k < n; ++k) recs.push_back(take_pages(p, ranks[k], scales[k]));
+  std::vector<const AdapterRec*> rp;
+  for (const AdapterRec& r : recs) rp.push_back(&r);
+  st = enqueue_images(p, rp, reinterpret_cast<char* const*>(images), static_cast<char*>(dev_stage),
+                      static_cast<hipStream_t>(stream));
+  if (st != SLORA_OK) {
+    for (int32_t k = n - 1; k >= 0; --k) rollback_pages(p, recs[(size_t)k]);
+    return st;
+  }
+  for (int32_t k = 0; k < n; ++k) commit_adapter(p, ids[k], std::move(recs[(size_t)k]));
   return SLORA_OK;
 }
 

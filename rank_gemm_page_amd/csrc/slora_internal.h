@@ -108,10 +108,25 @@ hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
 // Zero n_words 32-bit words at p (a fill kernel; no memset node in the stream).
 hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t stream);
 
-// Copy n_rows rows of row_bytes from src (device, packed) into the pages
-// page_ids[i] of the class at base with page_bytes stride.
-hipError_t launch_scatter_rows(const char* src, int32_t n_rows, int64_t row_bytes,
-                               const int32_t* page_ids, char* base, int64_t page_bytes,
-                               hipStream_t stream);
+// Adapter images staged on the device for one scatter launch.  Image i sits
+// at stage + img_off[i]: n_proj x rank[i] A^T rows of a_row_bytes, then as many
+// B rows of b_row_bytes, then the 2 x n_proj x rank[i] destination page ids
+// (A^T pages, then B pages).  Workgroup g moves global row g; adapter i owns
+// rows row_start[i] .. row_start[i + 1].
+constexpr int kMaxFetch = 64;
+struct ScatterLaunch {
+  const char* stage;
+  int32_t n, n_proj;
+  int64_t a_row_bytes, b_row_bytes;
+  char* a_base;
+  char* b_base;
+  int64_t a_page_bytes, b_page_bytes;
+  int32_t row_start[kMaxFetch + 1];
+  int32_t rank[kMaxFetch];
+  int64_t img_off[kMaxFetch];
+};
+
+// Copy every row of the staged images into its page (one launch).
+hipError_t launch_scatter_pages(const ScatterLaunch& S, hipStream_t stream);
 
 }  // namespace slora

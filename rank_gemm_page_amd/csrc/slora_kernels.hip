@@ -990,24 +990,34 @@ hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Adapter load: copy packed staging rows into their pages (one block per row).
+// Adapter fetch, second half: the images are already in device staging (one
+// copy-engine transfer each); one workgroup per row moves the row into its
+// page.  Row sizes are multiples of 16 bytes (h_in and h_out are multiples of
+// 8 elements).
 
-__global__ __launch_bounds__(kThreads) void scatter_rows_kernel(const char* src, int64_t row_bytes,
-                                                                const int32_t* page_ids, char* base,
-                                                                int64_t page_bytes) {
-  const int64_t row = blockIdx.x;
-  const uint4* s = reinterpret_cast<const uint4*>(src + row * row_bytes);
-  uint4* d = reinterpret_cast<uint4*>(base + (int64_t)page_ids[row] * page_bytes);
-  const int64_t n = row_bytes / 16;
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) d[i] = s[i];
+__global__ __launch_bounds__(kThreads) void scatter_pages_kernel(ScatterLaunch S) {
+  const int32_t g = blockIdx.x;
+  int lo = 0, hi = S.n - 1;          // adapter i with row_start[i] <= g < row_start[i + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.row_start[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  const int64_t q = g - S.row_start[lo];
+  const int64_t n_a = (int64_t)S.n_proj * S.rank[lo];
+  const char* img = S.stage + S.img_off[lo];
+  const int32_t* ids = reinterpret_cast<const int32_t*>(img + n_a * (S.a_row_bytes + S.b_row_bytes));
+  const bool is_a = q < n_a;
+  const int64_t n16 = (is_a ? S.a_row_bytes : S.b_row_bytes) / 16;
+  const uint4* src = reinterpret_cast<const uint4*>(
+      img + (is_a ? q * S.a_row_bytes : n_a * S.a_row_bytes + (q - n_a) * S.b_row_bytes));
+  uint4* dst = reinterpret_cast<uint4*>(is_a ? S.a_base + (int64_t)ids[q] * S.a_page_bytes
+                                             : S.b_base + (int64_t)ids[q] * S.b_page_bytes);
+  for (int64_t i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
 }
 
-hipError_t launch_scatter_rows(const char* src, int32_t n_rows, int64_t row_bytes,
-                               const int32_t* page_ids, char* base, int64_t page_bytes,
-                               hipStream_t stream) {
-  if (n_rows <= 0) return hipSuccess;
-  scatter_rows_kernel<<<dim3(n_rows), dim3(kThreads), 0, stream>>>(src, row_bytes, page_ids, base,
-                                                                  page_bytes);
+hipError_t launch_scatter_pages(const ScatterLaunch& S, hipStream_t stream) {
+  if (S.n <= 0 || S.row_start[S.n] <= 0) return hipSuccess;
+  scatter_pages_kernel<<<dim3((unsigned)S.row_start[S.n]), dim3(kThreads), 0, stream>>>(S);
   return hipGetLastError();
 }
 

@@ -13,7 +13,11 @@ from . import slora as S
 
 
 class DeviceWorkload:
-    def __init__(self, w, device="cuda:0", tuning=None, poison=True, load_all_weights=False):
+    def __init__(self, w, device="cuda:0", tuning=None, poison=True, load_all_weights=False,
+                 load="sync"):
+        """load: "sync" (slora_load_adapter) or "async" (packed pinned images
+        fetched with slora_load_adapters_async on a second stream, which the
+        current stream then waits for)."""
         import torch
 
         self.torch = torch
@@ -31,20 +35,38 @@ class DeviceWorkload:
                                         spec.n_adapters, self.max_rank, self.pages,
                                         [int(P) for P in w.n_pages], w.free_order)
         self.seg = None
+        self.images = []          # pinned adapter images a queued load may still read
+        self.stages = {}          # device staging buffer per fetch stream
+        self.load_stream = None
         try:
             for key, value in (tuning or {}).items():
                 S.slora_pool_set_tuning(self.pool, key, value)
             self.kv = [S.slora_alloc_pages(self.pool, c, int(n)) for c, n in enumerate(w.kv_pages)]
             stream = torch.cuda.current_stream(self.device)
+            if load == "async":
+                self.load_stream = torch.cuda.Stream(self.device)
+            fetch = []
             for a in range(spec.n_adapters):
                 r = int(w.ranks[a])
                 if load_all_weights or w.has_weights(a):
+                    if load == "async":
+                        fetch.append(a)
+                        continue
                     ws = [w.weights(a, p) for p in range(spec.n_proj)]
                     S.slora_load_adapter(self.pool, a, r, float(w.scales[a]), [m[0] for m in ws],
                                          [m[1] for m in ws], stream, h_in=spec.h_in,
                                          h_out=spec.h_out, dtype=w.np_dtype)
                 else:
+                    if fetch:   # pages are taken in id order, as the oracle's model does
+                        self.load_async(fetch, self.load_stream)
+                        fetch = []
                     S.slora_load_adapter(self.pool, a, r, float(w.scales[a]))
+            if fetch:
+                self.load_async(fetch, self.load_stream)
+            if load == "async":
+                done = torch.cuda.Event()
+                done.record(self.load_stream)
+                stream.wait_event(done)
             self.x = [torch.from_numpy(np.ascontiguousarray(x)).to(self.device) for x in w.x]
             self.y0 = [torch.from_numpy(np.ascontiguousarray(y)).to(self.device) for y in w.y]
             self.y = [t.clone() for t in self.y0]
@@ -52,6 +74,40 @@ class DeviceWorkload:
         except Exception:
             self.close()
             raise
+
+    # -- adapter fetch ---------------------------------------------------------
+    def pack(self, a):
+        """Pinned host image of adapter a (the host-resident store's form)."""
+        torch, w, spec = self.torch, self.w, self.w.spec
+        r = int(w.ranks[a])
+        nb = S.slora_adapter_image_bytes(self.pool, r)
+        img = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+        ws = [w.weights(a, p) for p in range(spec.n_proj)]
+        S.slora_pack_adapter(self.pool, r, [m[0] for m in ws], [m[1] for m in ws], img, nb,
+                             h_in=spec.h_in, h_out=spec.h_out, dtype=w.np_dtype)
+        return img
+
+    def stage_for(self, stream, nbytes):
+        """Device staging of at least nbytes for fetches queued on `stream`:
+        stream order lets every fetch on one stream reuse it."""
+        key = int(stream.cuda_stream)
+        if key not in self.stages or self.stages[key].numel() < nbytes:
+            if key in self.stages:
+                stream.synchronize()
+            self.stages[key] = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
+        return self.stages[key]
+
+    def load_async(self, adapters, stream, images=None):
+        """Queue the fetch of `adapters` (one batch) on `stream`; return at once."""
+        w = self.w
+        adapters = [int(a) for a in adapters]
+        imgs = [self.pack(a) for a in adapters] if images is None else list(images)
+        self.images.extend(imgs)
+        ranks = [int(w.ranks[a]) for a in adapters]
+        need = sum(S.slora_adapter_image_bytes(self.pool, r) for r in ranks)
+        stage = self.stage_for(stream, max(need, 256))
+        S.slora_load_adapters_async(self.pool, adapters, ranks, [float(w.scales[a]) for a in adapters],
+                                    imgs, stage, stage.numel(), stream)
 
     # -- segments --------------------------------------------------------------
     def build(self, ids):
@@ -116,6 +172,9 @@ class DeviceWorkload:
             y.copy_(y0)
 
     def close(self):
+        if self.images or self.stages:
+            self.torch.cuda.synchronize(self.device)
+            self.images, self.stages = [], {}
         if getattr(self, "seg", None) is not None:
             S.slora_segments_destroy(self.seg)
             self.seg = None

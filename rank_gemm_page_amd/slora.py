@@ -30,6 +30,7 @@ SLORA_TUNE_MFMA_SHRINK_SPLITS, SLORA_TUNE_FUSED, SLORA_TUNE_XCDS = 3, 4, 5
 EXPORTED = [
     "slora_pool_create", "slora_pool_destroy", "slora_pool_set_tuning", "slora_alloc_pages",
     "slora_free_pages", "slora_free_count", "slora_load_adapter", "slora_unload_adapter",
+    "slora_adapter_image_bytes", "slora_pack_adapter", "slora_load_adapters_async",
     "slora_adapter_pages", "slora_build_segments", "slora_segments_destroy",
     "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
     "slora_segments_upload", "slora_segments_read_error",
@@ -79,6 +80,10 @@ def lib():
             "slora_free_count": (c_int64, [P, c_int32]),
             "slora_load_adapter": (c_int32, [P, c_int32, c_int32, c_float, POINTER(P), POINTER(P), P]),
             "slora_unload_adapter": (c_int32, [P, c_int32]),
+            "slora_adapter_image_bytes": (c_size_t, [P, c_int32]),
+            "slora_pack_adapter": (c_int32, [P, c_int32, POINTER(P), POINTER(P), P, c_size_t]),
+            "slora_load_adapters_async": (c_int32, [P, c_int32, POINTER(c_int32), POINTER(c_int32),
+                                                    POINTER(c_float), POINTER(P), P, c_size_t, P]),
             "slora_adapter_pages": (c_int32, [P, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32),
                                               POINTER(c_int32)]),
             "slora_build_segments": (c_int32, [P, c_int32, POINTER(c_int32), POINTER(P)]),
@@ -188,6 +193,14 @@ def slora_load_adapter(pool, adapter_id: int, rank: int, scale: float, A=None, B
         _check(lib().slora_load_adapter(pool, adapter_id, rank, float(scale), None, None,
                                         _stream(stream)), "slora_load_adapter")
         return
+    keep, a_ptrs, b_ptrs = _factor_ptrs(A, B, rank, h_in, h_out, dtype)
+    _check(lib().slora_load_adapter(pool, adapter_id, rank, float(scale), a_ptrs, b_ptrs,
+                                    _stream(stream)), "slora_load_adapter")
+
+
+def _factor_ptrs(A, B, rank, h_in, h_out, dtype):
+    """Contiguous host copies of A[p] (h_in x rank) and B[p] (rank x h_out) and
+    ctypes arrays of their addresses (the copies must outlive the call)."""
     keep = []
     a_ptrs = (c_void_p * len(A))()
     b_ptrs = (c_void_p * len(B))()
@@ -201,8 +214,40 @@ def slora_load_adapter(pool, adapter_id: int, rank: int, scale: float, A=None, B
         keep += [a, b]
         a_ptrs[p] = a.ctypes.data
         b_ptrs[p] = b.ctypes.data
-    _check(lib().slora_load_adapter(pool, adapter_id, rank, float(scale), a_ptrs, b_ptrs,
-                                    _stream(stream)), "slora_load_adapter")
+    return keep, a_ptrs, b_ptrs
+
+
+def slora_adapter_image_bytes(pool, rank: int) -> int:
+    """Bytes of one adapter image of this rank (0 on a bad rank)."""
+    return int(lib().slora_adapter_image_bytes(pool, rank))
+
+
+def slora_pack_adapter(pool, rank: int, A, B, image, image_bytes: int,
+                       h_in: int = None, h_out: int = None, dtype=None) -> None:
+    """Fill the host image at `image` (an address or an object with data_ptr())."""
+    if len(A) != len(B):
+        raise ValueError("A and B need one entry per projection")
+    keep, a_ptrs, b_ptrs = _factor_ptrs(A, B, rank, h_in, h_out, dtype)
+    _check(lib().slora_pack_adapter(pool, rank, a_ptrs, b_ptrs, _ptr(image), image_bytes),
+           "slora_pack_adapter")
+    del keep
+
+
+def slora_load_adapters_async(pool, ids, ranks, scales, images, dev_stage, dev_stage_bytes: int,
+                              stream=None) -> None:
+    """Queue the fetch of adapters ids[k] from pinned packed images[k] (addresses
+    or objects with data_ptr()) through the device buffer dev_stage."""
+    n = len(ids)
+    if not (len(ranks) == len(scales) == len(images) == n):
+        raise ValueError("ids, ranks, scales and images need one entry per adapter")
+    ids_a = np.ascontiguousarray(ids, dtype=np.int32)
+    ranks_a = np.ascontiguousarray(ranks, dtype=np.int32)
+    scales_a = np.ascontiguousarray(scales, dtype=np.float32)
+    img = (c_void_p * max(n, 1))(*[_ptr(m) for m in images])
+    _check(lib().slora_load_adapters_async(pool, n, _i32p(ids_a), _i32p(ranks_a),
+                                           scales_a.ctypes.data_as(POINTER(c_float)), img,
+                                           _ptr(dev_stage), dev_stage_bytes, _stream(stream)),
+           "slora_load_adapters_async")
 
 
 def slora_unload_adapter(pool, adapter_id: int) -> None:

@@ -414,3 +414,73 @@ def test_no_mfma_under_partial_exec_mask(tmp_path):
     with open(asm) as f:
         assert sum(1 for line in f if line.strip().startswith("v_mfma")) > 0
     assert build.masked_mfma_lines(asm) == []
+
+
+@pytest.mark.parametrize("kw", [dict(dtype="f32", rank_set=(4, 8)),
+                                dict(dtype="f16", h_out=384, two_classes=True, n_proj=2,
+                                     proj_x=(0, 0), rank_set=(1, 8, 16))])
+def test_adapter_image_matches_oracle_pages(kw):
+    """Each row of a packed image equals the oracle's pool row of the page the
+    allocator gives it (A^T row j = column j of A; B row j = row j of B)."""
+    w = generate(small_spec("image", **kw), seed=3)
+    st = orc.build_from_workload(w)
+    pool, _ = make_pool(w)
+    spec, e = w.spec, np.dtype(w.np_dtype).itemsize
+    uint = np.uint16 if e == 2 else np.uint32
+    try:
+        for a in range(spec.n_adapters):
+            r = int(w.ranks[a])
+            nb = S.slora_adapter_image_bytes(pool, r)
+            rows = spec.n_proj * r
+            used = rows * (spec.h_in + spec.h_out) * e + 2 * rows * 4
+            assert nb == (used + 255) // 256 * 256
+            img = np.zeros(nb, np.uint8)
+            A = [w.weights(a, p)[0] for p in range(spec.n_proj)]
+            B = [w.weights(a, p)[1] for p in range(spec.n_proj)]
+            S.slora_pack_adapter(pool, r, A, B, img.ctypes.data, nb)
+            a_bytes = rows * spec.h_in * e
+            ent = st.alloc.table[a]
+            for p in range(spec.n_proj):
+                for j in range(r):
+                    off = ((p * r) + j) * spec.h_in * e
+                    got = img[off:off + spec.h_in * e].view(uint)
+                    assert np.array_equal(got, st.image.row(0, ent.a_pages[p][j]).view(uint)), (a, p, j)
+                    off = a_bytes + ((p * r) + j) * spec.h_out * e
+                    got = img[off:off + spec.h_out * e].view(uint)
+                    want = st.image.row(st.alloc.b_class(), ent.b_pages[p][j]).view(uint)
+                    assert np.array_equal(got, want), (a, p, j)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
+def test_async_load_argument_errors_leave_pool_unchanged():
+    """Every batch-level check of slora_load_adapters_async runs before any
+    device call, and a refused batch takes no page."""
+    pool = small_pool(n_pages=10)
+    img = np.zeros(1 << 16, np.uint8)
+    im = img.ctypes.data
+    dev, big = 1 << 40, 1 << 20
+    try:
+        assert S.slora_adapter_image_bytes(pool, 0) == 0
+        assert S.slora_adapter_image_bytes(pool, 9) == 0
+        assert status_of(S.slora_pack_adapter, pool, 2, [np.zeros((16, 2), np.float16)],
+                         [np.zeros((2, 16), np.float16)], im, 64) == S.SLORA_E_INVAL
+        S.slora_load_adapter(pool, 0, 4, 1.0)                       # 2 pages stay free
+        bad = [([0], [1], [1.0], [im], dev, big, S.SLORA_E_EXIST),
+               ([1], [2], [1.0], [im], dev, big, S.SLORA_E_NOMEM),
+               ([1, 2], [1, 1], [1.0, 1.0], [im, im], dev, big, S.SLORA_E_NOMEM),
+               ([9], [1], [1.0], [im], dev, big, S.SLORA_E_INVAL),
+               ([1], [0], [1.0], [im], dev, big, S.SLORA_E_INVAL),
+               ([1], [1], [float("inf")], [im], dev, big, S.SLORA_E_INVAL),
+               ([1], [1], [1.0], [0], dev, big, S.SLORA_E_INVAL),
+               ([1], [1], [1.0], [im], 0, big, S.SLORA_E_INVAL),
+               ([1, 1], [1, 1], [1.0, 1.0], [im, im], dev, big, S.SLORA_E_INVAL),
+               ([1], [1], [1.0], [im], dev, 16, S.SLORA_E_INVAL)]
+        for ids, ranks, scales, ims, d, nb, want in bad:
+            got = status_of(S.slora_load_adapters_async, pool, ids, ranks, scales, ims, d, nb)
+            assert got == want, (ids, ranks)
+            assert S.slora_free_count(pool, 0) == 2
+        S.slora_load_adapters_async(pool, [], [], [], [], dev, 0)    # empty batch: nothing
+        assert S.slora_free_count(pool, 0) == 2
+    finally:
+        S.slora_pool_destroy(pool)
