@@ -94,6 +94,84 @@ def cpu_baseline(w, budget_s=10.0):
             "host_cpu_count": os.cpu_count()}
 
 
+class BmmPath:
+    """The ablation baseline of the summary page ("Results & figures", Figure 5
+    narrative: the custom kernels replaced by a slower BMM path), read as the
+    plain batched-matmul LoRA: the batch's adapters as dense tensors padded
+    with zeros to the largest rank (built once per batch from the pool pages,
+    not timed), then per step a per-token gather of those tensors, two torch
+    bmm calls (x A, then (x A) B) and y[t] = y[t] + s_a d[t] in fp32 with one
+    rounding.  torch only, as a comparison; it is not the product path."""
+
+    def __init__(self, dw, proj=0):
+        import numpy as np
+        import torch
+
+        from rank_gemm_page_amd import slora as S
+        w, info, dev = dw.w, dw.info, dw.device
+        ex = S.slora_segments_export(dw.seg)
+        n_seg, sum_r = info["n_segments"], info["sum_rank"]
+        ranks = ex["seg_rank"]
+        rmax = int(ranks.max()) if n_seg else 1
+        b_cls = 1 if w.spec.two_classes else 0
+        self.A = torch.zeros(max(n_seg, 1), w.spec.h_in, rmax, dtype=dw.tdtype, device=dev)
+        self.B = torch.zeros(max(n_seg, 1), rmax, w.spec.h_out, dtype=dw.tdtype, device=dev)
+        sidx = np.full(w.T, -1, np.int64)
+        for g in range(n_seg):
+            r, o = int(ranks[g]), proj * sum_r + int(ex["seg_page_off"][g])
+            ida = torch.from_numpy(ex["a_pages"][o:o + r].astype(np.int64)).to(dev)
+            idb = torch.from_numpy(ex["b_pages"][o:o + r].astype(np.int64)).to(dev)
+            self.A[g, :, :r] = dw.pages[0].index_select(0, ida).t()
+            self.B[g, :r, :] = dw.pages[b_cls].index_select(0, idb)
+            sidx[ex["perm"][ex["seg_start"][g]:ex["seg_start"][g + 1]]] = g
+        tok = np.nonzero(sidx >= 0)[0]
+        self.tok = torch.from_numpy(tok).to(dev)
+        self.sidx = torch.from_numpy(sidx[tok]).to(dev)
+        self.scale = torch.from_numpy(ex["seg_scale"][sidx[tok]].astype(np.float32)).to(dev)[:, None]
+        self.rmax = rmax
+
+    def step(self, x, y):
+        import torch
+        if self.tok.numel() == 0:
+            return
+        a_t = self.A.index_select(0, self.sidx)                    # [n, h_in, rmax]
+        b_t = self.B.index_select(0, self.sidx)                    # [n, rmax, h_out]
+        v = torch.bmm(x.index_select(0, self.tok).unsqueeze(1), a_t)
+        d = torch.bmm(v, b_t).squeeze(1)
+        y[self.tok] = (y.index_select(0, self.tok).float() + self.scale * d.float()).to(y.dtype)
+
+
+def measure_bmm_path(dw, w, steps, flush, stream, paged_ms):
+    import torch
+    paths = [BmmPath(dw, p) for p in range(w.spec.n_proj)]
+
+    def run():
+        for p, bp in enumerate(paths):
+            bp.step(dw.x[w.spec.proj_x[p]], dw.y[p])
+
+    for _ in range(2):
+        flush()
+        run()
+    ts = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush()
+        a.record(stream)
+        run()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = statistics.fmean(ts)
+    tokens = int(paths[0].tok.numel())
+    e = 2 if w.spec.dtype == "f16" else 4
+    gathered = sum(int(bp.tok.numel()) * bp.rmax * (w.spec.h_in + w.spec.h_out) * e for bp in paths)
+    return {"ms_per_step": round(ms, 5), "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s",
+            "paged_speedup": round(ms / paged_ms, 2), "padded_rank": paths[0].rmax,
+            "gathered_weight_bytes": gathered,
+            "method": "per-token gather of zero-padded dense adapters + 2 torch.bmm + fp32 scaled add; "
+                      "HIP events, cache flushed before each step"}
+
+
 def measure_prefetch(dw, w, m, steps, flush, step, stream):
     """Walkthrough step 2 of the summary page: the next batch's adapters are
     fetched into the pool while the current batch computes.  m adapters the
@@ -190,6 +268,8 @@ def main():
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",
                     help="also fetch M adapters the batch does not use from pinned host images "
                          "on a second stream, alone and while the step runs (slora_load_adapter_async)")
+    ap.add_argument("--bmm-baseline", action="store_true",
+                    help="also time the padded-BMM path (torch) on the same batch for comparison")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain copy of this size (PMC calibration runs)")
     args = ap.parse_args()
@@ -395,6 +475,9 @@ def main():
                   "last-level cache and is outside both",
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
     }
+    if args.bmm_baseline:
+        log("[bench] padded-BMM comparison path")
+        out["bmm_path"] = measure_bmm_path(dw, w, K, flush, stream, ms)
     if args.prefetch > 0:
         log(f"[bench] adapter fetch: {args.prefetch} adapters per step")
         out["prefetch"] = measure_prefetch(dw, w, args.prefetch, K, flush, step, stream)
