@@ -248,6 +248,32 @@ def test_pool_bytes_match_oracle_image():
 
 
 # ---------------------------------------------------------------------------
+# The library's maximum sizes: h_in 16384 (fp16) and 8192 (fp32), the widest
+# vector-ALU shrink geometry (8 chunks per thread), h_out 65536, rank 256 and
+# 8 projections; sampled tokens against the oracle.
+
+MAX_SPECS = [
+    small_spec("max_f16", h_in=16384, h_out=65536, two_classes=True, n_adapters=6, n_proj=2,
+               proj_x=(0, 0), rank_set=(1, 17, 128, 256), batch=("zipf", 72, 1.0)),
+    small_spec("max_f32", dtype="f32", h_in=8192, h_out=8192, n_adapters=5, n_proj=8,
+               proj_x=(0,) * 8, rank_set=(3, 64, 256), batch=("zipf", 30, 1.0)),
+]
+
+
+@pytest.mark.parametrize("spec", MAX_SPECS, ids=lambda s: s.name)
+@pytest.mark.parametrize("route", ["default", "mfma"])
+def test_maximum_sizes(spec, route):
+    w = generate(spec, 4)
+    assert int(w.ranks.max()) == 256
+    ys, info = run_gpu(w, route)
+    st = build_from_workload(w)
+    toks = sample_tokens(w, 10)
+    for p in (0, spec.n_proj - 1):
+        y_ref, sd_ref = workload_delta(st, w, p, tokens=toks)
+        check_gates(ys[p][toks], y_ref, sd_ref, w.np_dtype, f"{spec.name}/{route}/p{p}")
+
+
+# ---------------------------------------------------------------------------
 # The five benchmark shapes at full size, default routing (as bench.py runs them)
 
 
