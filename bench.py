@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--mfma-expand-cols", type=int, default=None)
     ap.add_argument("--mfma-shrink-splits", type=int, default=None)
     ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
+    ap.add_argument("--tile-order", type=int, default=None,
+                    help="0: tiles in adapter order, 1: clustered by rank, 2 (default): most bytes first")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",
@@ -301,7 +303,8 @@ def main():
                                 (S.SLORA_TUNE_GEMV_EXPAND_ELEMS, args.gemv_expand_elems),
                                 (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
                                 (S.SLORA_TUNE_MFMA_SHRINK_SPLITS, args.mfma_shrink_splits),
-                                (S.SLORA_TUNE_XCDS, args.xcds))
+                                (S.SLORA_TUNE_XCDS, args.xcds),
+                                (S.SLORA_TUNE_TILE_ORDER, args.tile_order))
               if v is not None}
     dw = DeviceWorkload(w, dev, tuning=tuning)
     spec = w.spec

@@ -107,6 +107,11 @@ void slora_pool_destroy(slora_pool* pool);
  *  SLORA_TUNE_XCDS             - n > 1: the shrink tiles of each token block
  *                                go to one of n XCDs (workgroup i runs on
  *                                XCD i mod n); 1 (default): no grouping.
+ *  SLORA_TUNE_TILE_ORDER       - 0: tiles of each stage in segment (adapter
+ *                                id) order; 1: clustered by rank, highest
+ *                                first (summary page, "Heterogeneous batching
+ *                                kernels": clustering of ranks); 2 (default):
+ *                                the tiles that move the most bytes first.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
@@ -115,7 +120,8 @@ typedef enum {
   SLORA_TUNE_MFMA_EXPAND_COLS = 2,
   SLORA_TUNE_MFMA_SHRINK_SPLITS = 3,
   SLORA_TUNE_FUSED = 4,
-  SLORA_TUNE_XCDS = 5
+  SLORA_TUNE_XCDS = 5,
+  SLORA_TUNE_TILE_ORDER = 6
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 

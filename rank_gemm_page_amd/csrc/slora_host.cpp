@@ -89,6 +89,7 @@ struct Tuning {
   int64_t mfma_shrink_splits = 0;   // K splits per MFMA shrink block (0: automatic)
   int64_t fused = 1;
   int64_t xcds = 1;             // XCD groups of the shrink placement (1: none)
+  int64_t tile_order = 2;       // 0: segment order, 1: rank-descending, 2: bytes-descending
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -487,12 +488,34 @@ void build_tiles(slora_segments* s) {
   // Producers first keeps the waiting expand tiles of a fused launch from
   // holding the workgroup slots the shrink tiles need (measured: putting each
   // token block's expand tiles right after its shrink tiles is 20-50 % slower).
+  // SLORA_TUNE_TILE_ORDER reorders tiles within a stage (segment order among
+  // equals): 1 clusters them by rank, highest first; 2 (default) puts the
+  // tiles that move the most bytes first (longest-processing-time order), so
+  // the long tiles start early and the short ones fill the end of the launch.
+  // Measured on MI355X against segment order: 3.5 % faster on the 7B prefill
+  // batch, 1 % on the 13B mixed batch, 5 % on the 70B MLP projection, and the
+  // same on the 7B decode batch, whose vector-ALU tiles all move about as
+  // much (rank order, 1, costs that batch 4 %).
   auto launch_rank = [](const TileSpec& t) {
     if (t.kind & KIND_COMBINE_BIT) return 2;
     return ((t.kind & KIND_EXPAND_BIT) ? 3 : 0) + ((t.kind & KIND_MFMA_BIT) ? 0 : 1);
   };
+  auto tile_bytes = [&](const TileSpec& t) -> int64_t {
+    const int64_t r = s->seg_rank[t.seg];
+    switch (t.kind) {
+      case KIND_SHRINK_GEMV: return (int64_t)t.len * hin;                  // page rows (x from L2)
+      case KIND_SHRINK_MFMA: return ((int64_t)t.ntok + r) * t.len;         // x and A^T over the K range
+      case KIND_COMBINE: return (int64_t)t.ntok * r * t.aux;               // partials
+      default: return (r + 2 * (int64_t)t.ntok) * t.len;                   // B rows, y read and written
+    }
+  };
+  const int64_t order = p->tune.tile_order;
   std::stable_sort(tiles.begin(), tiles.end(), [&](const TileSpec& a, const TileSpec& b) {
-    return launch_rank(a) < launch_rank(b);
+    const int ra = launch_rank(a), rb = launch_rank(b);
+    if (ra != rb) return ra < rb;
+    if (order == 1) return s->seg_rank[a.seg] > s->seg_rank[b.seg];
+    if (order == 2) return tile_bytes(a) > tile_bytes(b);
+    return false;
   });
 
   // Optional XCD-aware placement of the shrink tiles (SLORA_TUNE_XCDS > 1).
@@ -691,6 +714,10 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
     case SLORA_TUNE_XCDS:
       if (value < 1 || value > 64) return fail(SLORA_E_INVAL, "xcds must be 1..64");
       p->tune.xcds = value;
+      return SLORA_OK;
+    case SLORA_TUNE_TILE_ORDER:
+      if (value < 0 || value > 2) return fail(SLORA_E_INVAL, "tile_order must be 0, 1 or 2");
+      p->tune.tile_order = value;
       return SLORA_OK;
     case SLORA_TUNE_FUSED:
       if (value != 0 && value != 1) return fail(SLORA_E_INVAL, "fused must be 0 or 1");

@@ -125,16 +125,18 @@ def test_page_permutation_invariance_bit_exact():
 
 
 @pytest.mark.parametrize("launch", list(LAUNCH))
-def test_xcd_placement_changes_nothing(launch):
-    """Grouping the shrink tiles by XCD reorders the launch, never the
-    arithmetic of a tile: results are bit-identical to the ungrouped order."""
+def test_xcd_placement_and_rank_order_change_nothing(launch):
+    """Grouping the shrink tiles by XCD, or clustering tiles by rank, reorders
+    the launch, never the arithmetic of a tile: results are bit-identical to
+    the default order."""
     spec = small_spec("xcd", h_in=1024, h_out=768, two_classes=True, n_adapters=12,
                       batch=("zipf", 96, 1.1), pool=("occ", 1, 2))
     outs = []
-    for xcds in (1, 8, 3):
+    for xcds, order in ((1, 0), (8, 0), (3, 0), (1, 1), (8, 1), (1, 2)):
         w = generate(spec, 4)
         (y,), _ = run_gpu(w, "default", launch=launch,
-                          tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 8, S.SLORA_TUNE_XCDS: xcds})
+                          tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 8, S.SLORA_TUNE_XCDS: xcds,
+                                  S.SLORA_TUNE_TILE_ORDER: order})
         outs.append(y)
     y_ref, sd_ref = oracle(w)
     check_gates(outs[0], y_ref, sd_ref, w.np_dtype, "xcd")

@@ -224,11 +224,14 @@ def check_tiles_cover(w, pool, ids):
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode7b", "prefill7b", "mixed13b", "mlp70b"])
-@pytest.mark.parametrize("route", ["default", "all_gemv", "all_mfma", "xcd_grouped"])
+@pytest.mark.parametrize("route", ["default", "all_gemv", "all_mfma", "xcd_grouped", "rank_order",
+                                   "bytes_order"])
 def test_tiles_cover_each_output_once(name, route):
     tuning = {"default": {}, "all_gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
               "all_mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1},
-              "xcd_grouped": {S.SLORA_TUNE_XCDS: 8}}[route]
+              "xcd_grouped": {S.SLORA_TUNE_XCDS: 8},
+              "rank_order": {S.SLORA_TUNE_TILE_ORDER: 1},
+              "bytes_order": {S.SLORA_TUNE_TILE_ORDER: 2}}[route]
     w = generate(CONFIGS[name], 0)
     pool, _ = make_pool(w, tuning=tuning)
     try:
@@ -388,6 +391,8 @@ def test_tuning_validation():
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_XCDS, 65) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_XCDS, 0) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_XCDS, 8)
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_TILE_ORDER, 3) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_TILE_ORDER, 1)
         S.slora_pool_set_tuning(pool, 2, 1024)
     finally:
         S.slora_pool_destroy(pool)
