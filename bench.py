@@ -269,7 +269,7 @@ def main():
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",
                     help="also fetch M adapters the batch does not use from pinned host images "
-                         "on a second stream, alone and while the step runs (slora_load_adapter_async)")
+                         "on a second stream, alone and while the step runs (slora_load_adapters_async)")
     ap.add_argument("--bmm-baseline", action="store_true",
                     help="also time the padded-BMM path (torch) on the same batch for comparison")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

@@ -51,7 +51,7 @@ def _one(pattern: str) -> str:
 
 
 def short_name(name: str) -> str:
-    for key in ("fused_kernel", "shrink_kernel", "expand_kernel", "scatter_rows_kernel"):
+    for key in ("fused_kernel", "shrink_kernel", "combine_kernel", "expand_kernel", "scatter_pages_kernel"):
         if key in name:
             return key
     return name.split("(")[0][:60]
