@@ -49,17 +49,18 @@ def log(msg):
 
 
 def load_traffic(config, dominant):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it is current."""
+    """(HBM bytes per launch, rocprofv3 kernel-trace average us) from the committed
+    rocprofv3 summary of this workload, if it was taken of the current kernels."""
     path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         t = json.load(f)
     from rank_gemm_page_amd.profiling import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash() or dominant not in t.get("kernels", {}):
-        return None
+        return None, None
     k = t["kernels"][dominant]
-    return k["fetch_bytes"] + k["write_bytes"]
+    return k["fetch_bytes"] + k["write_bytes"], k.get("trace_avg_us")
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -424,7 +425,7 @@ def main():
         dom_ms = statistics.fmean(kern_ms) / n_proj
         dom_bytes = sb + eb
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.config, dominant)
+    traffic, profiled_us = load_traffic(args.config, dominant)
     tokens = int(info["n_routed"])
     value = tokens / (ms * 1e-3)
 
@@ -451,7 +452,8 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
-                     "avg_launch_us": round(dom_ms * 1e3, 3)},
+                     "avg_launch_us": round(dom_ms * 1e3, 3),
+                     "profiled_avg_launch_us": round(profiled_us, 3) if profiled_us else None},
         "kernels": {**({"shrink_us": round(sh_ms * 1e3 / n_proj, 3),
                         "expand_us": round(ex_ms * 1e3 / n_proj, 3),
                         "shrink_GBps": round(sb / (sh_ms / n_proj * 1e-3) / 1e9, 1),

@@ -109,6 +109,9 @@ def write_summary(config, trace_dir, fetch_dir, write_dir, command, flush_mib, o
                   algorithmic_bytes=None, event_us=None):
     stats = kernel_stats(trace_dir)
     tr = traffic(fetch_dir, write_dir, flush_mib)
+    for s in stats:            # the kernel trace's average duration beside the bytes
+        if s["short"] in tr["kernels"]:
+            tr["kernels"][s["short"]]["trace_avg_us"] = s["avg_us"]
     tr["kernel_source_hash"] = kernel_source_hash()
     tr["config"] = config
     os.makedirs(out_dir, exist_ok=True)
