@@ -173,6 +173,41 @@ def measure_bmm_path(dw, w, steps, flush, stream, paged_ms):
                       "HIP events, cache flushed before each step"}
 
 
+def measure_base_gemm(dw, w, steps, flush, stream, paged_ms):
+    """Context for the summary page's claim that the LoRA work is cheap next to
+    the base xW ("The mechanism", separate base and delta): the same step's
+    base products x W (one dense h_in x h_out fp16/fp32 weight per projection,
+    random, torch.mm on hipBLASLt) timed like the delta, flush included."""
+    import torch
+    spec = w.spec
+    wts = [torch.randn(spec.h_in, spec.h_out, device=dw.device).to(dw.tdtype) * 0.02
+           for _ in range(spec.n_proj)]
+    outs = [torch.empty(w.T, spec.h_out, dtype=dw.tdtype, device=dw.device) for _ in range(spec.n_proj)]
+
+    def run():
+        for p in range(spec.n_proj):
+            torch.mm(dw.x[spec.proj_x[p]], wts[p], out=outs[p])
+
+    for _ in range(3):
+        flush()
+        run()
+    ts = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush()
+        a.record(stream)
+        run()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = statistics.fmean(ts)
+    flops = 2.0 * w.T * spec.h_in * spec.h_out * spec.n_proj
+    return {"ms_per_step": round(ms, 5), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "delta_over_base": round(paged_ms / ms, 4),
+            "y_round_trip_bytes": 2 * w.T * spec.h_out * spec.n_proj * (2 if spec.dtype == "f16" else 4),
+            "method": "torch.mm(x, W) per projection, random W, HIP events, cache flushed before each step"}
+
+
 def measure_prefetch(dw, w, m, steps, flush, step, stream):
     """Walkthrough step 2 of the summary page: the next batch's adapters are
     fetched into the pool while the current batch computes.  m adapters the
@@ -271,6 +306,8 @@ def main():
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",
                     help="also fetch M adapters the batch does not use from pinned host images "
                          "on a second stream, alone and while the step runs (slora_load_adapters_async)")
+    ap.add_argument("--base-gemm", action="store_true",
+                    help="also time the base products x W of the same step (torch.mm) for context")
     ap.add_argument("--bmm-baseline", action="store_true",
                     help="also time the padded-BMM path (torch) on the same batch for comparison")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -480,6 +517,9 @@ def main():
                   "last-level cache and is outside both",
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
     }
+    if args.base_gemm:
+        log("[bench] base x W products")
+        out["base_gemm"] = measure_base_gemm(dw, w, K, flush, stream, ms)
     if args.bmm_baseline:
         log("[bench] padded-BMM comparison path")
         out["bmm_path"] = measure_bmm_path(dw, w, K, flush, stream, ms)
