@@ -30,6 +30,10 @@ Pieces, each written from its definition with no blocking or reordering:
   * ``lora_delta``: walks tokens in batch order, follows the block table to
     the page rows, converts them to float64 exactly and returns
     y_in + s * ((x A) B) unrounded, with s * (x A) B beside it.
+  * ``lora_forward``: the base output plus the adapter output,
+    x W + s * ((x A) B), unrounded (summary page, "How to read the paper"
+    item 2, h = xW + xAB; blog page, section 2: the batched forward returns
+    base_out + adapter_out); x W is NumPy's dense float64 product.
 
 Parity: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, brute force, invariants and hand-worked fixtures); none is
@@ -217,6 +221,26 @@ def lora_delta(alloc: AllocatorModel, image: PoolImage, ids: Sequence[int], x: n
     return y_ref, sd_ref
 
 
+def lora_forward(alloc: AllocatorModel, image: PoolImage, ids: Sequence[int], x: np.ndarray,
+                 W: np.ndarray, proj: int = 0, tokens: Optional[Sequence[int]] = None):
+    """Return (h_ref, sd_ref) in float64 for the tokens listed (all by default).
+
+    h_ref[t] = x[t] W + s * (x[t] A) B: the base output of the dense weight W
+    (d_in x d_out) plus the adapter output of token t's adapter; a token with
+    a negative id gets x[t] W alone.  sd_ref is the adapter part, as in
+    ``lora_delta``.  Both unrounded.
+    """
+    ids = np.asarray(ids)
+    if tokens is None:
+        tokens = range(ids.shape[0])
+    tokens = list(tokens)
+    base = x[tokens].astype(np.float64) @ W.astype(np.float64)
+    # lora_delta over a base output of zeros gives the adapter output alone
+    zeros = np.zeros((ids.shape[0], W.shape[1]), dtype=np.float64)
+    _, sd_ref = lora_delta(alloc, image, ids, x, zeros, proj=proj, tokens=tokens)
+    return base + sd_ref, sd_ref
+
+
 def round_to(y: np.ndarray, dtype) -> np.ndarray:
     """One round-to-nearest-even of a float64 result to the output dtype."""
     return np.asarray(y, dtype=np.float64).astype(dtype)
@@ -259,3 +283,10 @@ def workload_delta(state: OracleState, w, proj: int = 0, tokens=None):
     """Oracle (y_ref, sd_ref) of projection ``proj`` of a synthetic workload."""
     x = w.x[w.spec.proj_x[proj]]
     return lora_delta(state.alloc, state.image, w.ids, x, w.y[proj], proj=proj, tokens=tokens)
+
+
+def workload_forward(state: OracleState, w, proj: int = 0, tokens=None):
+    """Oracle (h_ref, sd_ref) of the base-plus-delta product of projection ``proj``."""
+    x = w.x[w.spec.proj_x[proj]]
+    return lora_forward(state.alloc, state.image, w.ids, x, w.base_weight(proj), proj=proj,
+                        tokens=tokens)

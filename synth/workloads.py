@@ -34,7 +34,9 @@ Seeding: every stream comes from ``SeedSequence([cfg_idx, seed, stream])``
 (streams: 0 ranks, 1 token ids / lengths, 2 x, 3 y, 4 pool free order,
 6 scales); the weights of adapter ``a`` for projection ``p`` come from
 ``SeedSequence([cfg_idx, seed, 5, a, p])`` so one adapter can be regenerated
-alone.
+alone, and the dense base weight W (h_in x h_out) of projection ``p``, for the
+base-plus-delta product, from ``SeedSequence([cfg_idx, seed, 7, p])`` with the
+adapters' distribution.
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 STREAM_RANKS, STREAM_IDS, STREAM_X, STREAM_Y, STREAM_POOL, STREAM_W, STREAM_SCALE = 0, 1, 2, 3, 4, 5, 6
+STREAM_BASE = 7
 
 NP_DTYPE = {"f32": np.float32, "f16": np.float16}
 
@@ -137,6 +140,15 @@ class Workload:
         key = (a, p)
         if key not in self._wcache:
             self._wcache[key] = _draw_weights(self.spec, self.seed, a, p, int(self.ranks[a]))
+        return self._wcache[key]
+
+    def base_weight(self, p: int = 0) -> np.ndarray:
+        """Dense base weight W [h_in, h_out] of projection ``p`` (storage dtype)."""
+        key = ("base", p)
+        if key not in self._wcache:
+            rng = _rng(self.spec, self.seed, STREAM_BASE, p)
+            self._wcache[key] = _draw(rng, (self.spec.h_in, self.spec.h_out), self.spec.weight_std,
+                                      self.spec.values, NP_DTYPE[self.spec.dtype])
         return self._wcache[key]
 
     def drop_weight_cache(self):

@@ -381,3 +381,109 @@ def test_pins_catch_planted_mistakes(kind, spec_i):
         spec = replace(spec, pool=("fixed", 4096))
     with np.errstate(invalid="ignore"):
         assert not closed_form_check(_mutant(kind), spec)
+
+
+# ---------------------------------------------------------------------------
+# The base-plus-delta product (lora_forward)
+
+
+def test_forward_hand_fixture():
+    g = _load("hand_example.json")
+    f = _load("hand_forward.json")
+    alloc = orc.AllocatorModel([len(o) for o in g["free_order"]], g["free_order"], n_proj=1,
+                               two_classes=True)
+    alloc.load(0, g["rank"], g["scale"])
+    img = orc.PoolImage([g["h_in"], g["h_out"]], np.float32)
+    img.write_adapter(alloc, 0, 0, np.array(g["A"], np.float32), np.array(g["B"], np.float32))
+    h, sd = orc.lora_forward(alloc, img, g["ids"], np.array(g["x"], np.float32),
+                             np.array(f["W"], np.float32))
+    np.testing.assert_array_equal(h, np.array(f["expected_h"], np.float64))
+    np.testing.assert_array_equal(sd[1], [0.0, 0.0])
+
+
+@pytest.mark.parametrize("dtype,h_in,h_out,rank_set", [("f32", 256, 128, (1, 4, 8)),
+                                                       ("f16", 64, 128, (1, 2, 4))])
+def test_forward_integer_brute_force(dtype, h_in, h_out, rank_set):
+    """{-1, 0, 1} inputs: x W + 2 (x A) B is an integer computed exactly in int64."""
+    spec = small_spec("fint", dtype=dtype, h_in=h_in, h_out=h_out, two_classes=True, n_adapters=5,
+                      rank_set=rank_set, values="ternary", scale=2.0, batch=("uniform", 12))
+    w = generate(spec, 3)
+    st = orc.build_from_workload(w)
+    h, _ = orc.workload_forward(st, w)
+    xi = w.x[0].astype(np.int64)
+    Wi = w.base_weight(0).astype(np.int64)
+    assert np.abs(Wi).max() == 1
+    for t in range(w.T):
+        A, B = (m.astype(np.int64) for m in w.weights(int(w.ids[t])))
+        exact = xi[t] @ Wi + 2 * ((xi[t] @ A) @ B)
+        assert np.array_equal(h[t], exact.astype(np.float64))
+
+
+@pytest.mark.parametrize("shape", [(64, 64, 1), (48, 80, 2), (96, 32, 3)])
+def test_forward_closed_form_combined_weight(shape):
+    """Each token's output equals x (W + s A B): one dense product with the
+    merged weight, the form the pages contrast with keeping the delta apart."""
+    h_in, h_out, n_proj = shape
+    spec = small_spec("fcf", h_in=h_in, h_out=h_out, two_classes=h_in != h_out, n_proj=n_proj,
+                      proj_x=tuple(range(n_proj)), n_adapters=4, rank_set=(1, 3, 8),
+                      scale_set=(0.5, 2.0, -1.5), batch=("uniform", 10))
+    w = generate(spec, 1)
+    st = orc.build_from_workload(w)
+    for p in range(n_proj):
+        h, _ = orc.workload_forward(st, w, proj=p)
+        x = w.x[p].astype(np.float64)
+        W = w.base_weight(p).astype(np.float64)
+        for t in range(w.T):
+            a = int(w.ids[t])
+            A, B = _dense(w, a, p)
+            merged = W + np.float64(w.scales[a]) * (A @ B)
+            ref = x[t] @ merged
+            np.testing.assert_allclose(h[t], ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
+
+def test_forward_zero_base_is_the_delta():
+    """With W = 0 the forward output is the adapter output of lora_delta over a
+    zero base y, token for token; a negative id gives x W."""
+    spec = small_spec("fz", h_in=64, h_out=64, n_adapters=3, rank_set=(2, 5), batch=("uniform", 9))
+    w = generate(spec, 2)
+    st = orc.build_from_workload(w)
+    ids = w.ids.copy()
+    ids[4] = -1
+    x = w.x[0]
+    zero_w = np.zeros((64, 64), np.float16)
+    h, sd = orc.lora_forward(st.alloc, st.image, ids, x, zero_w)
+    y0 = np.zeros((w.T, 64), np.float16)
+    y_d, sd_d = orc.lora_delta(st.alloc, st.image, ids, x, y0)
+    np.testing.assert_array_equal(h, y_d)
+    np.testing.assert_array_equal(sd, sd_d)
+    assert not h[4].any()
+
+
+def _forward_mutant(kind):
+    def f(alloc, image, ids, x, W, proj=0, tokens=None):
+        if kind == "dropped_base":
+            return orc.lora_forward(alloc, image, ids, x, np.zeros_like(W), proj, tokens)
+        if kind == "transposed_base":
+            return orc.lora_forward(alloc, image, ids, x, W.T.copy(), proj, tokens)
+        if kind == "base_twice":
+            h, sd = orc.lora_forward(alloc, image, ids, x, W, proj, tokens)
+            return 2 * h - sd, sd
+        raise ValueError(kind)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["dropped_base", "transposed_base", "base_twice"])
+def test_forward_pins_catch_planted_mistakes(kind):
+    spec = small_spec("fm", h_in=64, h_out=64, n_adapters=4, rank_set=(1, 3, 8), batch=("uniform", 10))
+    w = generate(spec, 1)
+    st = orc.build_from_workload(w)
+    h, _ = _forward_mutant(kind)(st.alloc, st.image, w.ids, w.x[0], w.base_weight(0))
+    x = w.x[0].astype(np.float64)
+    W = w.base_weight(0).astype(np.float64)
+    bad = False
+    for t in range(w.T):
+        a = int(w.ids[t])
+        A, B = _dense(w, a)
+        ref = x[t] @ (W + np.float64(w.scales[a]) * (A @ B))
+        bad |= not np.allclose(h[t], ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+    assert bad, f"the closed form did not catch {kind}"
