@@ -316,6 +316,38 @@ slora_status slora_lora_shrink(slora_pool* pool, const slora_segments* seg, int3
 slora_status slora_lora_expand(slora_pool* pool, const slora_segments* seg, int32_t proj, void* y,
                                const void* workspace, size_t workspace_bytes, void* stream);
 
+/* The base projection with the delta in the same pass (summary page, "How to
+ * read the paper" item 2: h = xW + xAB; blog page, section 2: the batched
+ * forward returns the base output plus the adapter output):
+ *   y[t, o] = round( sum_k x[t, k] W[k, o] + s_a * sum_j v[t, j] B_a[j, o] ),
+ *   v[t, :] = x[t, :] A_a,
+ * one fp32 sum per output element and one rounding to fp16; a token with no
+ * adapter (negative id) gets y[t] = round(x[t] W).  y is WRITTEN (not
+ * accumulated): the delta costs no extra read and write of y.  w is device
+ * memory holding the base weight of projection `proj`, h_in x h_out fp16
+ * row-major (W[k, o] at w[k * h_out + o]), caller-owned and only read;
+ * x (n_tokens x h_in) and y (n_tokens x h_out) are device memory in batch
+ * order, as for slora_lora_delta; workspace as for slora_lora_delta.  All
+ * four 16-byte aligned.  fp16 pools only, with h_in a multiple of 64 and
+ * h_out a multiple of 128 (SLORA_E_INVAL otherwise).  Launches the shrink
+ * kernels (v into the workspace) and then one matrix-core kernel over tiles
+ * of 128 tokens (in segment order) x 128 columns on `stream`, and returns
+ * without waiting; launch errors return SLORA_E_HIP, device faults surface
+ * at the caller's next synchronisation.  Requires a prior
+ * slora_segments_upload; returns SLORA_E_STALE like slora_lora_delta.  With
+ * n_tokens == 0 it launches nothing. */
+slora_status slora_lora_forward(slora_pool* pool, const slora_segments* seg, int32_t proj,
+                                const void* x, const void* w, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* slora_lora_forward with the caller's HIP events recorded by the dispatches
+ * themselves (start when the first kernel begins, stop when the last ends),
+ * as for slora_lora_delta_timed. */
+slora_status slora_lora_forward_timed(slora_pool* pool, const slora_segments* seg, int32_t proj,
+                                      const void* x, const void* w, void* y, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* start_event,
+                                      void* stop_event);
+
 /* Message for the calling thread's last failed call ("" if none). */
 const char* slora_last_error(void);
 

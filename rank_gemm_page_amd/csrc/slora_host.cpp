@@ -150,6 +150,13 @@ struct slora_segments {
   int32_t stride = 0, tokcap = 0, pagecap = 0;
   int64_t shrink_idx_off_words = 0, expand_idx_off_words = 0;
   int64_t records_words = 0;       // records and index lists (the uploaded part)
+  // Base-plus-delta table (uploaded after the index lists): batch order of
+  // the sorted positions, segment of each routed position, per-segment
+  // start, rank, scale and v offset, per row block its LoRA stages, and the
+  // LoRA stage entries of every projection.
+  int64_t fw_order_off = 0, fw_pos_seg_off = 0, fw_seg_start_off = 0, fw_seg_rank_off = 0;
+  int64_t fw_seg_scale_off = 0, fw_seg_v_off = 0, fw_rb_info_off = 0, fw_stages_off = 0;
+  int32_t fw_n_rb = 0, fw_n_stages = 0;
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -569,9 +576,66 @@ void build_tiles(slora_segments* s) {
   s->shrink_idx_off_words = (int64_t)s->n_tiles * s->stride;
   s->expand_idx_off_words = s->shrink_idx_off_words + s->n_shrink;
   s->records_words = (s->expand_idx_off_words + s->n_expand + 3) & ~(int64_t)3;
-  s->error_off_words = s->records_words;            // records end 16-byte aligned
+
+  // Base-plus-delta table.  Row block rb holds sorted positions
+  // rb * kFwdBM .. +kFwdBM; its LoRA stages are, for every segment that owns
+  // one of those positions, one stage per kFwdLoraRows rank rows.
+  const int32_t T = s->n_tokens, routed = (int32_t)s->perm.size();
+  s->fw_n_rb = (T + kFwdBM - 1) / kFwdBM;
+  std::vector<int32_t> pos_seg(routed);
+  for (int32_t g = 0; g < S; ++g)
+    for (int32_t i = s->seg_start[g]; i < s->seg_start[g + 1]; ++i) pos_seg[i] = g;
+  std::vector<int32_t> rb_info(2 * (size_t)s->fw_n_rb, 0);
+  std::vector<std::pair<int32_t, int32_t>> fw_stages;   // (segment, first rank row)
+  for (int32_t rb = 0; rb < s->fw_n_rb; ++rb) {
+    const int32_t p0 = rb * kFwdBM, p1 = std::min(p0 + kFwdBM, routed);
+    rb_info[2 * rb] = (int32_t)fw_stages.size();
+    if (p0 < p1)
+      for (int32_t g = pos_seg[p0]; g <= pos_seg[p1 - 1]; ++g)
+        for (int32_t j0 = 0; j0 < s->seg_rank[g]; j0 += kFwdLoraRows) fw_stages.emplace_back(g, j0);
+    rb_info[2 * rb + 1] = (int32_t)fw_stages.size() - rb_info[2 * rb];
+  }
+  s->fw_n_stages = (int32_t)fw_stages.size();
+  auto take = [](int64_t& cur, int64_t words) { const int64_t at = cur; cur = (cur + words + 3) & ~(int64_t)3; return at; };
+  int64_t cur = s->records_words;
+  s->fw_order_off = take(cur, T);
+  s->fw_pos_seg_off = take(cur, routed);
+  s->fw_seg_start_off = take(cur, S + 1);
+  s->fw_seg_rank_off = take(cur, S);
+  s->fw_seg_scale_off = take(cur, S);
+  s->fw_seg_v_off = take(cur, S);
+  s->fw_rb_info_off = take(cur, 2 * (int64_t)s->fw_n_rb);
+  s->fw_stages_off = take(cur, (int64_t)np * s->fw_n_stages * kFwdStageWords);
+
+  s->error_off_words = cur;                         // 16-byte aligned
   s->vtag_off_words = s->error_off_words + 4;       // 8-byte pairs, 16-byte aligned
-  s->blob.assign((size_t)s->records_words, 0);
+  s->blob.assign((size_t)cur, 0);
+  {
+    int32_t* b = s->blob.data();
+    std::memcpy(b + s->fw_order_off, s->perm.data(), (size_t)routed * 4);
+    // then the tokens with no adapter, in batch order
+    std::vector<uint8_t> is_routed(T, 0);
+    for (int32_t t : s->perm) is_routed[t] = 1;
+    int32_t k = routed;
+    for (int32_t t = 0; t < T; ++t)
+      if (!is_routed[t]) b[s->fw_order_off + k++] = t;
+    std::memcpy(b + s->fw_pos_seg_off, pos_seg.data(), (size_t)routed * 4);
+    std::memcpy(b + s->fw_seg_start_off, s->seg_start.data(), (size_t)(S + 1) * 4);
+    std::memcpy(b + s->fw_seg_rank_off, s->seg_rank.data(), (size_t)S * 4);
+    std::memcpy(b + s->fw_seg_scale_off, s->seg_scale.data(), (size_t)S * 4);
+    for (int32_t g = 0; g < S; ++g) b[s->fw_seg_v_off + g] = (int32_t)s->seg_v_off[g];
+    std::memcpy(b + s->fw_rb_info_off, rb_info.data(), rb_info.size() * 4);
+    for (int pr = 0; pr < np; ++pr)
+      for (int32_t e = 0; e < s->fw_n_stages; ++e) {
+        const int32_t g = fw_stages[e].first, j0 = fw_stages[e].second, r = s->seg_rank[g];
+        int32_t* ent = b + s->fw_stages_off + ((int64_t)pr * s->fw_n_stages + e) * kFwdStageWords;
+        const int32_t* src = s->b_pages.data() + (size_t)pr * s->sum_r + s->seg_page_off[g];
+        for (int32_t i = 0; i < kFwdLoraRows; ++i) ent[i] = src[std::min(j0 + i, r - 1)];
+        ent[FWS_SEG] = g;
+        ent[FWS_J0] = j0;
+        ent[FWS_RANK] = r;
+      }
+  }
 
   int32_t* shrink_idx = s->blob.data() + s->shrink_idx_off_words;
   int32_t* expand_idx = s->blob.data() + s->expand_idx_off_words;
@@ -1107,32 +1171,9 @@ slora_status slora_segments_read_error(const slora_segments* s, void* stream, in
 
 namespace {
 
-slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_segments* s,
-                        int32_t proj, const void* x, void* y, const void* workspace,
-                        size_t workspace_bytes, void* stream, void* ev_start = nullptr,
-                        void* ev_stop = nullptr) {
-  const std::string f(fn);
-  if (!p || !s) return fail(SLORA_E_INVAL, f + ": NULL pool or segments");
-  if (s->pool != p) return fail(SLORA_E_INVAL, f + ": segments belong to another pool");
-  if (proj < 0 || proj >= p->d.n_proj) return fail(SLORA_E_INVAL, f + ": proj out of range");
-  const int32_t S = (int32_t)s->seg_adapter.size();
-  for (int32_t g = 0; g < S; ++g) {
-    const AdapterRec& rec = p->adapters[s->seg_adapter[g]];
-    if (!rec.loaded || rec.gen != s->seg_gen[g])
-      return fail(SLORA_E_STALE, f + ": adapter " + std::to_string(s->seg_adapter[g]) +
-                                     " changed since the segments were built");
-  }
-  if (s->perm.empty()) return SLORA_OK;
-  if (((stages & STAGE_SHRINK) && !x) || ((stages & STAGE_EXPAND) && !y) || !workspace)
-    return fail(SLORA_E_INVAL, f + ": NULL x, y or workspace");
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
-       reinterpret_cast<uintptr_t>(workspace)) & 15)
-    return fail(SLORA_E_INVAL, f + ": x, y and workspace must be 16-byte aligned");
-  if (workspace_bytes < (size_t)s->n_splits * s->sum_rt * sizeof(float))
-    return fail(SLORA_E_NOMEM, f + ": workspace smaller than workspace_bytes");
-  if (!s->dev_meta) return fail(SLORA_E_INVAL, f + ": segments not uploaded (call slora_segments_upload)");
-  slora_status st = set_device(p);
-  if (st != SLORA_OK) return st;
+// The launch description of one projection of a batch (no checks).
+DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int32_t proj,
+                              const void* x, void* y, const void* workspace) {
   DeltaLaunch L{};
   L.pool.base_a = static_cast<const char*>(p->d.class_base[0]);
   L.pool.base_b = static_cast<const char*>(p->d.class_base[p->b_class()]);
@@ -1161,6 +1202,44 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   L.y_bytes = (uint32_t)std::min<int64_t>((int64_t)s->n_tokens * p->d.h_out * elem_bytes(p->d.dtype), kMaxBufferBytes);
   L.sum_rt = (int32_t)s->sum_rt;
   L.n_combine = s->n_combine;
+  return L;
+}
+
+// Checks shared by every compute entry point: pool and segments match, the
+// projection exists, and no adapter of the batch changed since the build.
+slora_status check_batch(const std::string& f, const slora_pool* p, const slora_segments* s, int32_t proj) {
+  if (!p || !s) return fail(SLORA_E_INVAL, f + ": NULL pool or segments");
+  if (s->pool != p) return fail(SLORA_E_INVAL, f + ": segments belong to another pool");
+  if (proj < 0 || proj >= p->d.n_proj) return fail(SLORA_E_INVAL, f + ": proj out of range");
+  const int32_t S = (int32_t)s->seg_adapter.size();
+  for (int32_t g = 0; g < S; ++g) {
+    const AdapterRec& rec = p->adapters[s->seg_adapter[g]];
+    if (!rec.loaded || rec.gen != s->seg_gen[g])
+      return fail(SLORA_E_STALE, f + ": adapter " + std::to_string(s->seg_adapter[g]) +
+                                     " changed since the segments were built");
+  }
+  return SLORA_OK;
+}
+
+slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_segments* s,
+                        int32_t proj, const void* x, void* y, const void* workspace,
+                        size_t workspace_bytes, void* stream, void* ev_start = nullptr,
+                        void* ev_stop = nullptr) {
+  const std::string f(fn);
+  slora_status chk = check_batch(f, p, s, proj);
+  if (chk != SLORA_OK) return chk;
+  if (s->perm.empty()) return SLORA_OK;
+  if (((stages & STAGE_SHRINK) && !x) || ((stages & STAGE_EXPAND) && !y) || !workspace)
+    return fail(SLORA_E_INVAL, f + ": NULL x, y or workspace");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(SLORA_E_INVAL, f + ": x, y and workspace must be 16-byte aligned");
+  if (workspace_bytes < (size_t)s->n_splits * s->sum_rt * sizeof(float))
+    return fail(SLORA_E_NOMEM, f + ": workspace smaller than workspace_bytes");
+  if (!s->dev_meta) return fail(SLORA_E_INVAL, f + ": segments not uploaded (call slora_segments_upload)");
+  slora_status st = set_device(p);
+  if (st != SLORA_OK) return st;
+  DeltaLaunch L = make_delta_launch(p, s, proj, x, y, workspace);
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
     stages = STAGE_FUSED;
     // Epochs run 1 .. 2^31 - 1 (partial sums of K-split shrink tiles carry the
@@ -1176,6 +1255,66 @@ slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_s
   }
   hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream),
                               static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop));
+  if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
+  return SLORA_OK;
+}
+
+
+// Base product plus delta: the shrink stage (v = x A into the workspace), then
+// one launch of the base-plus-delta kernel over every token of the batch.
+slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s, int32_t proj,
+                         const void* x, const void* w, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream, void* ev_start, void* ev_stop) {
+  const std::string f(fn);
+  slora_status chk = check_batch(f, p, s, proj);
+  if (chk != SLORA_OK) return chk;
+  if (p->d.dtype != SLORA_F16) return fail(SLORA_E_INVAL, f + ": fp16 pools only");
+  if (p->d.h_in % kFwdBK != 0 || p->d.h_out % kFwdBN != 0)
+    return fail(SLORA_E_INVAL, f + ": needs h_in a multiple of " + std::to_string(kFwdBK) +
+                                   " and h_out a multiple of " + std::to_string(kFwdBN));
+  if (s->n_tokens == 0) return SLORA_OK;
+  const bool routed = !s->perm.empty();
+  if (!x || !w || !y || (routed && !workspace)) return fail(SLORA_E_INVAL, f + ": NULL x, w, y or workspace");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(y) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(SLORA_E_INVAL, f + ": x, w, y and workspace must be 16-byte aligned");
+  if (routed && workspace_bytes < (size_t)s->n_splits * s->sum_rt * sizeof(float))
+    return fail(SLORA_E_NOMEM, f + ": workspace smaller than workspace_bytes");
+  if (!s->dev_meta) return fail(SLORA_E_INVAL, f + ": segments not uploaded (call slora_segments_upload)");
+  slora_status st = set_device(p);
+  if (st != SLORA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (routed) {
+    const DeltaLaunch L = make_delta_launch(p, s, proj, x, nullptr, workspace);
+    hipError_t e = launch_delta(L, STAGE_SHRINK, hs, static_cast<hipEvent_t>(ev_start), nullptr);
+    if (e != hipSuccess) return hip_fail(e, (f + " shrink launch").c_str());
+  }
+  const int32_t* m = s->dev_meta;
+  ForwardLaunch F{};
+  F.base_b = static_cast<const char*>(p->d.class_base[p->b_class()]);
+  F.page_bytes_b = p->page_bytes[p->b_class()];
+  F.h_in = p->d.h_in;
+  F.h_out = p->d.h_out;
+  F.n_tokens = s->n_tokens;
+  F.n_routed = (int32_t)s->perm.size();
+  F.x = x;
+  F.w = w;
+  F.y = y;
+  F.v = static_cast<const float*>(workspace);
+  F.order = m + s->fw_order_off;
+  F.pos_seg = m + s->fw_pos_seg_off;
+  F.seg_start = m + s->fw_seg_start_off;
+  F.seg_rank = m + s->fw_seg_rank_off;
+  F.seg_scale = m + s->fw_seg_scale_off;
+  F.seg_v_off = m + s->fw_seg_v_off;
+  F.rb_info = m + s->fw_rb_info_off;
+  F.stages = m + s->fw_stages_off + (int64_t)proj * s->fw_n_stages * kFwdStageWords;
+  F.n_rb = s->fw_n_rb;
+  F.n_cb = p->d.h_out / kFwdBN;
+  F.n_tiles = F.n_rb * F.n_cb;
+  F.per_xcd = (F.n_tiles + 7) / 8;
+  hipError_t e = launch_forward(F, hs, routed ? nullptr : static_cast<hipEvent_t>(ev_start),
+                                static_cast<hipEvent_t>(ev_stop));
   if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
   return SLORA_OK;
 }
@@ -1207,6 +1346,21 @@ slora_status slora_lora_expand(slora_pool* p, const slora_segments* s, int32_t p
                                const void* workspace, size_t workspace_bytes, void* stream) {
   return run_stages("slora_lora_expand", STAGE_EXPAND, p, s, proj, nullptr, y, workspace,
                     workspace_bytes, stream);
+}
+
+slora_status slora_lora_forward(slora_pool* p, const slora_segments* s, int32_t proj, const void* x,
+                                const void* w, void* y, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return run_forward("slora_lora_forward", p, s, proj, x, w, y, workspace, workspace_bytes, stream,
+                     nullptr, nullptr);
+}
+
+slora_status slora_lora_forward_timed(slora_pool* p, const slora_segments* s, int32_t proj,
+                                      const void* x, const void* w, void* y, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* ev_start,
+                                      void* ev_stop) {
+  return run_forward("slora_lora_forward_timed", p, s, proj, x, w, y, workspace, workspace_bytes,
+                     stream, ev_start, ev_stop);
 }
 
 }  // extern "C"

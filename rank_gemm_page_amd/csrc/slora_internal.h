@@ -105,6 +105,48 @@ enum : int { STAGE_SHRINK = 1, STAGE_EXPAND = 2, STAGE_FUSED = 4 };
 hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
+// Base product with the LoRA delta folded into its tiles (fp16 only):
+//   y[t, o] = round( sum_k x[t, k] W[k, o]  +  s_a sum_j v[t, j] B_j[o] )
+// over the batch in segment order (routed tokens sorted by adapter, then the
+// tokens with no adapter), in tiles of kFwdBM sorted positions x kFwdBN
+// columns.  Each tile first runs one LoRA stage per 32 rank rows of every
+// segment its positions touch (the B page rows against s v, split into fp16
+// high and low parts), then the x W stages of kFwdBK rows of W, and writes y
+// once.  v = x A comes from the shrink kernels (workspace).
+constexpr int kFwdBM = 128;
+constexpr int kFwdBN = 128;
+constexpr int kFwdBK = 64;
+constexpr int kFwdLoraRows = 32;   // B page rows per LoRA stage
+// LoRA stage table entry (int32 words): the stage's 32 B page ids (rows past
+// the rank repeat the last row's page), then segment, first rank row, rank.
+constexpr int kFwdStageWords = 40;
+enum : int32_t { FWS_SEG = 32, FWS_J0 = 33, FWS_RANK = 34 };
+
+struct ForwardLaunch {
+  const char* base_b;        // class of the B pages
+  int64_t page_bytes_b;
+  int32_t h_in, h_out;
+  int32_t n_tokens, n_routed;
+  const void* x;             // n_tokens x h_in, batch order
+  const void* w;             // h_in x h_out, row-major
+  void* y;                   // n_tokens x h_out, batch order (written)
+  const float* v;            // x A of the routed tokens (segment order)
+  const int32_t* order;      // [n_tokens] batch index of sorted position i
+  const int32_t* pos_seg;    // [n_routed] segment of routed position i
+  const int32_t* seg_start;  // [S + 1]
+  const int32_t* seg_rank;   // [S]
+  const int32_t* seg_scale;  // [S] float bits
+  const int32_t* seg_v_off;  // [S] workspace offset of the segment's first v row
+  const int32_t* rb_info;    // [n_rb][2]: first LoRA stage entry, LoRA stages
+  const int32_t* stages;     // LoRA stage table of this projection
+  int32_t n_rb, n_cb, n_tiles, per_xcd;
+};
+
+// Launch the base-plus-delta kernel (one launch, n_tiles workgroups placed
+// XCD by XCD); start/stop events as for launch_delta.
+hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
+
 // Zero n_words 32-bit words at p (a fill kernel; no memset node in the stream).
 hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t stream);
 

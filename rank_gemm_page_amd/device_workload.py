@@ -141,6 +141,31 @@ class DeviceWorkload:
         S.slora_lora_delta_timed(self.pool, self.seg, proj, x, self.y[proj], self.workspace,
                                  self.info["workspace_bytes"], stream, start_event, stop_event)
 
+    def base_weight(self, proj=0):
+        """The workload's dense base weight W of projection ``proj`` on the device."""
+        if not hasattr(self, "_w_dev"):
+            self._w_dev = {}
+        if proj not in self._w_dev:
+            self._w_dev[proj] = self.torch.from_numpy(self.w.base_weight(proj)).to(self.device)
+        return self._w_dev[proj]
+
+    def forward(self, proj=0, out=None, stream=None):
+        """out = x W + s (x A) B (slora_lora_forward); returns out."""
+        torch = self.torch
+        stream = stream or torch.cuda.current_stream(self.device)
+        if out is None:
+            out = torch.empty((self.w.T, self.w.spec.h_out), dtype=self.tdtype, device=self.device)
+        S.slora_lora_forward(self.pool, self.seg, proj, self.x[self.w.spec.proj_x[proj]],
+                             self.base_weight(proj), out, self.workspace,
+                             self.info["workspace_bytes"], stream)
+        return out
+
+    def forward_timed(self, proj, out, start_event, stop_event, stream=None):
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        S.slora_lora_forward_timed(self.pool, self.seg, proj, self.x[self.w.spec.proj_x[proj]],
+                                   self.base_weight(proj), out, self.workspace,
+                                   self.info["workspace_bytes"], stream, start_event, stop_event)
+
     def shrink(self, proj=0, stream=None):
         stream = stream or self.torch.cuda.current_stream(self.device)
         S.slora_lora_shrink(self.pool, self.seg, proj, self.x[self.w.spec.proj_x[proj]],

@@ -35,7 +35,7 @@ EXPORTED = [
     "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
     "slora_segments_upload", "slora_segments_read_error",
     "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
-    "slora_last_error",
+    "slora_lora_forward", "slora_lora_forward_timed", "slora_last_error",
 ]
 
 
@@ -98,6 +98,8 @@ def lib():
             "slora_lora_delta_timed": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P, P, P]),
             "slora_lora_shrink": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_lora_expand": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
+            "slora_lora_forward": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P]),
+            "slora_lora_forward_timed": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P, P, P]),
             "slora_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -346,3 +348,18 @@ def slora_lora_shrink(pool, seg, proj: int, x, workspace, workspace_bytes: int, 
 def slora_lora_expand(pool, seg, proj: int, y, workspace, workspace_bytes: int, stream=None) -> None:
     _check(lib().slora_lora_expand(pool, seg, proj, _ptr(y), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream)), "slora_lora_expand")
+
+
+def slora_lora_forward(pool, seg, proj: int, x, w, y, workspace, workspace_bytes: int,
+                       stream=None) -> None:
+    """y = x W + s (x A) B, written (base weight w: h_in x h_out fp16, row-major)."""
+    _check(lib().slora_lora_forward(pool, seg, proj, _ptr(x), _ptr(w), _ptr(y), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream)), "slora_lora_forward")
+
+
+def slora_lora_forward_timed(pool, seg, proj: int, x, w, y, workspace, workspace_bytes: int, stream,
+                             start_event: int, stop_event: int) -> None:
+    """start_event / stop_event: raw hipEvent_t handles (ints)."""
+    _check(lib().slora_lora_forward_timed(pool, seg, proj, _ptr(x), _ptr(w), _ptr(y),
+                                          _ptr(workspace), int(workspace_bytes), _stream(stream),
+                                          start_event, stop_event), "slora_lora_forward_timed")

@@ -28,3 +28,28 @@ def check_gates(y_gpu, y_ref, sd_ref, dtype, label=""):
     assert not bad.any(), (f"{label}: G2 failed at {int(bad.sum())} elements, worst excess "
                            f"{(err - g2).max():.3e}")
     return float(err.max())
+
+
+def check_forward_gates(y_gpu, h_ref, sd_ref, base_abs, k, dtype, label=""):
+    """Gates of the base-plus-delta product h = x W + s d.
+
+    Unlike the delta, whose base y is an exact input, the base part x W is
+    computed here: k fp16 products (exact in fp32) summed in fp32 in some
+    order.  Any order of n additions errs by at most gamma_n * sum |terms|,
+    gamma_n = n u / (1 - n u) with u = 2^-24, so G2 gains that term per element
+    (base_abs = |x| |W|, elementwise, computed in fp64):
+        |y_gpu - h_ref| <= 1e-2 * max |s d_ref| + 0.5 ulp_out(h_ref) + gamma_k * base_abs
+    G1 is unchanged.
+    """
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    assert np.isfinite(y_gpu).all(), f"{label}: non-finite output (a page outside the batch was read?)"
+    err = np.abs(y_gpu - h_ref)
+    g1 = 1e-2 * np.abs(h_ref).max()
+    assert err.max() <= g1, f"{label}: G1 failed, max err {err.max():.3e} > {g1:.3e}"
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    g2 = 1e-2 * np.abs(sd_ref).max() + half_ulp(h_ref, dtype) + gamma * np.asarray(base_abs, np.float64)
+    bad = err > g2
+    assert not bad.any(), (f"{label}: G2 failed at {int(bad.sum())} elements, worst excess "
+                           f"{(err - g2).max():.3e}")
+    return float(err.max())

@@ -1,0 +1,175 @@
+"""Base product plus delta (slora_lora_forward) against the fp64 oracle, on an MI355X.
+
+Each case puts a seeded synthetic workload on the GPU (NaN in every page that
+is not an adapter row of the batch, NaN in the output buffer), runs
+slora_lora_forward with the workload's dense base weight W, and compares
+y = x W + s (x A) B with the oracle's lora_forward: gates G1 and G2 of
+tests/gates.py, with the base product's fp32 summation bound added to G2
+(check_forward_gates), or bit for bit where the arithmetic is exact.  The kernel's
+tiles hold 128 positions of the batch in segment order, so the shapes put
+segment boundaries inside and across tiles, and add tokens with no adapter.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import build_from_workload, lora_forward, round_to  # noqa: E402
+from rank_gemm_page_amd import slora as S  # noqa: E402
+from rank_gemm_page_amd.device_workload import DeviceWorkload  # noqa: E402
+from synth import CONFIGS, generate, small_spec  # noqa: E402
+from tests.gates import check_forward_gates  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ROUTES = {"gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
+          "mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1},
+          "default": {}}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def run_forward(w, projs=(0,), route="default", repeat=1):
+    print(f"[gpu] forward {w.spec.name} seed={w.seed} route={route} T={w.T} "
+          f"h={w.spec.h_in}x{w.spec.h_out}", flush=True)
+    dw = DeviceWorkload(w, "cuda:0", tuning=ROUTES[route])
+    try:
+        outs = []
+        for p in projs:
+            runs = []
+            for _ in range(repeat):
+                out = torch.full((w.T, w.spec.h_out), float("nan"), dtype=torch.float16, device="cuda:0")
+                dw.forward(p, out)
+                runs.append(out)
+            torch.cuda.synchronize()
+            outs.append([o.cpu().numpy() for o in runs])
+        return outs, dw.info
+    finally:
+        dw.close()
+
+
+def oracle_forward(w, proj=0, tokens=None, state=None):
+    st = state or build_from_workload(w)
+    return lora_forward(st.alloc, st.image, w.ids, w.x[w.spec.proj_x[proj]], w.base_weight(proj),
+                        proj=proj, tokens=tokens)
+
+
+def check(w, y, h_ref, sd_ref, proj=0, tokens=None, label=""):
+    x = w.x[w.spec.proj_x[proj]]
+    xs = x if tokens is None else x[tokens]
+    base_abs = np.abs(xs.astype(np.float64)) @ np.abs(w.base_weight(proj).astype(np.float64))
+    return check_forward_gates(y, h_ref, sd_ref, base_abs, w.spec.h_in, np.float16, label)
+
+
+def drop_some(w, every):
+    """Give every `every`-th token no adapter (id -1)."""
+    if every:
+        w.ids = w.ids.copy()
+        w.ids[::every] = -1
+    return w
+
+
+SMALL = {
+    # one class, tokens spread over six adapters, two row blocks
+    "sq128": dict(h_in=128, h_out=128, n_adapters=6, batch=("uniform", 200)),
+    # prefill-like requests: segments of 20..150 tokens crossing row blocks
+    "requests": dict(h_in=192, h_out=256, two_classes=True, n_adapters=7, rank_set=(1, 5, 33, 64),
+                     batch=("requests", 5, 20, 150)),
+    # decode-like: many one-token segments in each row block
+    "decode": dict(h_in=256, h_out=384, two_classes=True, n_adapters=60, batch=("zipf", 300, 1.1)),
+    # ranks past 64 (several LoRA stages per segment) up to the pool's 256
+    "highrank": dict(h_in=128, h_out=128, n_adapters=4, fixed_ranks=(100, 256, 129, 31),
+                     batch=("uniform", 70)),
+    # one token
+    "one": dict(h_in=64, h_out=128, two_classes=True, n_adapters=3, batch=("uniform", 1)),
+}
+
+
+@pytest.mark.parametrize("route", ["default", "gemv", "mfma"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small_shapes(name, route):
+    spec = small_spec(f"fw_{name}", scale_set=(0.5, 2.0, -1.5, 4.0), **SMALL[name])
+    w = drop_some(generate(spec, 11), 7 if name != "one" else 0)
+    (ys,), _ = run_forward(w, route=route)
+    h_ref, sd_ref = oracle_forward(w)
+    check(w, ys[0], h_ref, sd_ref, label=f"forward {name}/{route}")
+
+
+def test_forward_every_projection():
+    spec = small_spec("fw_proj", h_in=128, h_out=128, n_proj=3, proj_x=(0, 1, 2), n_adapters=5,
+                      batch=("requests", 3, 30, 110))
+    w = drop_some(generate(spec, 5), 9)
+    ys, _ = run_forward(w, projs=(0, 1, 2))
+    st = build_from_workload(w)
+    for p in range(3):
+        h_ref, sd_ref = oracle_forward(w, p, state=st)
+        check(w, ys[p][0], h_ref, sd_ref, proj=p, label=f"forward proj {p}")
+
+
+def test_forward_integer_bit_exact():
+    """{-1, 0, 1} inputs, s = 2: every partial sum is an integer below 2^11, so
+    the result is exact whatever the summation order and must equal the
+    oracle's bit for bit."""
+    spec = small_spec("fw_int", h_in=64, h_out=128, two_classes=True, n_adapters=6,
+                      rank_set=(1, 2, 4), values="ternary", scale=2.0, batch=("requests", 6, 10, 60))
+    w = drop_some(generate(spec, 4), 5)
+    for route in ("gemv", "mfma"):
+        (ys,), _ = run_forward(w, route=route)
+        h_ref, _ = oracle_forward(w)
+        assert np.abs(h_ref).max() < 2048
+        np.testing.assert_array_equal(ys[0], round_to(h_ref, np.float16))
+
+
+def test_forward_no_adapter_tokens_and_repeat():
+    """A batch with no routed token is the base product alone; repeated calls
+    give bit-identical outputs."""
+    spec = small_spec("fw_none", h_in=128, h_out=256, two_classes=True, n_adapters=3,
+                      batch=("uniform", 150))
+    w = generate(spec, 2)
+    w.ids = np.full_like(w.ids, -1)
+    (ys,), info = run_forward(w, repeat=2)
+    assert info["n_routed"] == 0
+    h_ref, sd_ref = oracle_forward(w)
+    assert not sd_ref.any()
+    check(w, ys[0], h_ref, sd_ref, label="forward, no adapters")
+    np.testing.assert_array_equal(ys[0], ys[1])
+    w2 = drop_some(generate(small_spec("fw_rep", h_in=128, h_out=128, batch=("uniform", 130)), 3), 4)
+    (ys2,), _ = run_forward(w2, repeat=3)
+    np.testing.assert_array_equal(ys2[0], ys2[1])
+    np.testing.assert_array_equal(ys2[0], ys2[2])
+
+
+def sample_positions(w, n, seed=0):
+    """Tokens at sorted positions on both sides of every 128-position tile
+    boundary, the first and last positions, and random tokens."""
+    ids = w.ids
+    routed = np.flatnonzero(ids >= 0)
+    order = np.concatenate([routed[np.argsort(ids[routed], kind="stable")], np.flatnonzero(ids < 0)])
+    picks = {int(order[0]), int(order[-1])}
+    for b in range(128, w.T, 128):
+        picks |= {int(order[b - 1]), int(order[b])}
+    rng = np.random.default_rng(seed)
+    picks |= set(rng.choice(w.T, size=min(n, w.T), replace=False).tolist())
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name,projs,n_sample", [("decode7b", (0,), None), ("prefill7b", (0,), 24),
+                                                 ("mixed13b", (0, 3), 24), ("mlp70b", (0,), 24)])
+def test_forward_full_size(name, projs, n_sample):
+    w = generate(CONFIGS[name], 0)
+    ys, info = run_forward(w, projs=projs)
+    print(f"[gpu] {name}: segments={info['n_segments']} tokens={w.T}", flush=True)
+    st = build_from_workload(w)
+    toks = None if n_sample is None else sample_positions(w, n_sample)
+    for p, runs in zip(projs, ys):
+        y = runs[0]
+        assert np.isfinite(y).all(), f"{name}/p{p}: a row was not written or a NaN page was read"
+        h_ref, sd_ref = oracle_forward(w, p, tokens=toks, state=st)
+        check(w, y if toks is None else y[toks], h_ref, sd_ref, proj=p, tokens=toks,
+              label=f"forward {name}/p{p}")
+    w.drop_weight_cache()

@@ -489,3 +489,44 @@ def test_async_load_argument_errors_leave_pool_unchanged():
         assert S.slora_free_count(pool, 0) == 2
     finally:
         S.slora_pool_destroy(pool)
+
+
+def test_forward_argument_errors():
+    """slora_lora_forward refuses what its kernel cannot do before any device work."""
+    fake = 1 << 42
+    # fp32 pools and shapes off the 64 / 128 grid
+    p32 = S.slora_pool_create(S.SLORA_F32, 64, 128, 1, 4, 8, FAKE_BASE, [16, 16], None)
+    p16_bad = S.slora_pool_create(S.SLORA_F16, 64, 64 + 8, 1, 4, 8, FAKE_BASE, [16, 16], None)
+    p16 = S.slora_pool_create(S.SLORA_F16, 64, 128, 1, 4, 8, FAKE_BASE, [16, 16], None)
+    try:
+        for pool in (p32, p16_bad, p16):
+            S.slora_load_adapter(pool, 0, 3, 1.0)
+        for pool in (p32, p16_bad):
+            seg = S.slora_build_segments(pool, [0, -1])
+            try:
+                assert status_of(S.slora_lora_forward, pool, seg, 0, fake, fake, fake, fake, 1 << 20) == S.SLORA_E_INVAL
+            finally:
+                S.slora_segments_destroy(seg)
+        seg = S.slora_build_segments(p16, [0, -1, 0])
+        try:
+            args = dict(x=fake, w=fake, y=fake, workspace=fake, workspace_bytes=1 << 20)
+            call = lambda **kw: status_of(S.slora_lora_forward, p16, seg, kw.pop("proj", 0),
+                                          **{**args, **kw})
+            assert call() == S.SLORA_E_INVAL                      # not uploaded
+            assert call(proj=1) == S.SLORA_E_INVAL                # no such projection
+            assert call(w=0) == S.SLORA_E_INVAL                   # NULL weight
+            assert call(y=fake + 4) == S.SLORA_E_INVAL            # unaligned output
+            assert call(workspace_bytes=4) == S.SLORA_E_NOMEM     # workspace too small
+            S.slora_unload_adapter(p16, 0)
+            assert call() == S.SLORA_E_STALE
+        finally:
+            S.slora_segments_destroy(seg)
+        # an empty batch launches nothing and touches no pointer
+        seg = S.slora_build_segments(p16, [])
+        try:
+            S.slora_lora_forward(p16, seg, 0, 0, 0, 0, 0, 0)
+        finally:
+            S.slora_segments_destroy(seg)
+    finally:
+        for pool in (p32, p16_bad, p16):
+            S.slora_pool_destroy(pool)
