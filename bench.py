@@ -283,6 +283,74 @@ def measure_prefetch(dw, w, m, steps, flush, step, stream):
                       "before each"}
 
 
+def measure_forward(dw, w, steps, flush, stream):
+    """The base product with the delta in the same tiles (slora_lora_forward:
+    shrink, then one matrix-core kernel writing y = x W + s (x A) B) against
+    the unfused alternative, the base product on hipBLASLt (torch.mm) followed
+    by slora_lora_delta into its output; both with the workload's seeded dense
+    base weight per projection, timed like the delta (flush before each step,
+    HIP events on the launch stream), plus a dispatch-timed pass of the fused
+    call (its kernels' own duration)."""
+    import torch
+    from rank_gemm_page_amd.hip_events import HipEvent
+    spec = w.spec
+    n_proj = spec.n_proj
+    wts = [dw.base_weight(p) for p in range(n_proj)]
+    w.drop_weight_cache()
+    outs = [torch.empty(w.T, spec.h_out, dtype=dw.tdtype, device=dw.device) for _ in range(n_proj)]
+
+    def fused():
+        for p in range(n_proj):
+            dw.forward(p, outs[p], stream=stream)
+
+    def unfused():
+        for p in range(n_proj):
+            torch.mm(dw.x[spec.proj_x[p]], wts[p], out=outs[p])
+            dw.delta(p, y=outs[p], stream=stream)
+
+    def timed(run):
+        for _ in range(3):
+            flush()
+            run()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush()
+            a.record(stream)
+            run()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.fmean(ts)
+
+    fused_ms = timed(fused)
+    unfused_ms = timed(unfused)
+    kev = [[(HipEvent(), HipEvent()) for _ in range(n_proj)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        flush()
+        for p in range(n_proj):
+            dw.forward_timed(p, outs[p], kev[k][p][0].handle, kev[k][p][1].handle, stream=stream)
+    torch.cuda.synchronize()
+    kern_ms = statistics.fmean(sum(kev[k][p][0].elapsed_ms(kev[k][p][1]) for p in range(n_proj))
+                               for k in range(steps))
+    sf, ef = dw.algorithmic_flops()
+    base_flops = 2.0 * w.T * spec.h_in * spec.h_out
+    flops = n_proj * (base_flops + sf + ef)
+    e = 2 if spec.dtype == "f16" else 4
+    return {"ms_per_step": round(fused_ms, 5), "unfused_ms_per_step": round(unfused_ms, 5),
+            "speedup_vs_unfused": round(unfused_ms / fused_ms, 3),
+            "kernels_us_per_projection": round(kern_ms * 1e3 / n_proj, 3),
+            "TFLOPs": round(flops / (kern_ms * 1e-3) / 1e12, 1),
+            "mfma_frac_f16_peak": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "flops_per_step": flops,
+            "y_round_trip_saved_bytes": 2 * w.T * spec.h_out * n_proj * e,
+            "method": "slora_lora_forward per projection vs torch.mm(x, W) + slora_lora_delta into "
+                      "its output; seeded dense W; HIP events on the launch stream, cache flushed "
+                      "before each step; kernels_us from dispatch-recorded events around the "
+                      "shrink and the base-plus-delta kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +369,10 @@ def main():
     ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
     ap.add_argument("--tile-order", type=int, default=None,
                     help="0: tiles in adapter order, 1: clustered by rank, 2 (default): most bytes first")
+    ap.add_argument("--fwd-group", type=int, default=None,
+                    help="row blocks per group of the base-plus-delta tile order (0: automatic)")
+    ap.add_argument("--fwd-tile", type=int, default=None, choices=[0, 128, 256],
+                    help="base-plus-delta tile (0: automatic)")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",
@@ -308,6 +380,9 @@ def main():
                          "on a second stream, alone and while the step runs (slora_load_adapters_async)")
     ap.add_argument("--base-gemm", action="store_true",
                     help="also time the base products x W of the same step (torch.mm) for context")
+    ap.add_argument("--forward", action="store_true",
+                    help="also time the base product with the delta in the same tiles "
+                         "(slora_lora_forward) against torch.mm + slora_lora_delta")
     ap.add_argument("--bmm-baseline", action="store_true",
                     help="also time the padded-BMM path (torch) on the same batch for comparison")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -342,7 +417,9 @@ def main():
                                 (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
                                 (S.SLORA_TUNE_MFMA_SHRINK_SPLITS, args.mfma_shrink_splits),
                                 (S.SLORA_TUNE_XCDS, args.xcds),
-                                (S.SLORA_TUNE_TILE_ORDER, args.tile_order))
+                                (S.SLORA_TUNE_TILE_ORDER, args.tile_order),
+                                (S.SLORA_TUNE_FWD_GROUP, args.fwd_group),
+                                (S.SLORA_TUNE_FWD_TILE, args.fwd_tile))
               if v is not None}
     dw = DeviceWorkload(w, dev, tuning=tuning)
     spec = w.spec
@@ -520,6 +597,9 @@ def main():
     if args.base_gemm:
         log("[bench] base x W products")
         out["base_gemm"] = measure_base_gemm(dw, w, K, flush, stream, ms)
+    if args.forward:
+        log("[bench] base product with the delta in the same tiles")
+        out["forward"] = measure_forward(dw, w, K, flush, stream)
     if args.bmm_baseline:
         log("[bench] padded-BMM comparison path")
         out["bmm_path"] = measure_bmm_path(dw, w, K, flush, stream, ms)

@@ -112,6 +112,17 @@ void slora_pool_destroy(slora_pool* pool);
  *                                first (summary page, "Heterogeneous batching
  *                                kernels": clustering of ranks); 2 (default):
  *                                the tiles that move the most bytes first.
+ *  SLORA_TUNE_FWD_GROUP        - slora_lora_forward's tile order: tiles
+ *                                go row block by row block in groups of n
+ *                                row blocks, column by column inside a
+ *                                group (1: row-block major); 0 (default):
+ *                                automatic.
+ *  SLORA_TUNE_FWD_TILE         - slora_lora_forward's tile: 128 (128 x 128
+ *                                everywhere), 256 (256 x 256 everywhere, when
+ *                                h_out is a multiple of 256) or 0 (default):
+ *                                256 x 256 for the leading positions that
+ *                                fill whole rounds of 256 such tiles, 128 x
+ *                                128 for the rest.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
@@ -121,7 +132,9 @@ typedef enum {
   SLORA_TUNE_MFMA_SHRINK_SPLITS = 3,
   SLORA_TUNE_FUSED = 4,
   SLORA_TUNE_XCDS = 5,
-  SLORA_TUNE_TILE_ORDER = 6
+  SLORA_TUNE_TILE_ORDER = 6,
+  SLORA_TUNE_FWD_GROUP = 7,
+  SLORA_TUNE_FWD_TILE = 8
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 
@@ -331,7 +344,8 @@ slora_status slora_lora_expand(slora_pool* pool, const slora_segments* seg, int3
  * four 16-byte aligned.  fp16 pools only, with h_in a multiple of 64 and
  * h_out a multiple of 128 (SLORA_E_INVAL otherwise).  Launches the shrink
  * kernels (v into the workspace) and then one matrix-core kernel over tiles
- * of 128 tokens (in segment order) x 128 columns on `stream`, and returns
+ * of 128 or 256 tokens (in segment order) x as many columns on `stream`
+ * (SLORA_TUNE_FWD_TILE), and returns
  * without waiting; launch errors return SLORA_E_HIP, device faults surface
  * at the caller's next synchronisation.  Requires a prior
  * slora_segments_upload; returns SLORA_E_STALE like slora_lora_delta.  With

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libslora.so")
-SOURCES = ["slora_host.cpp", "slora_kernels.hip"]
+SOURCES = ["slora_host.cpp", "slora_kernels.hip", "slora_forward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU ops are switched off for the device code: plain float code
@@ -38,16 +38,17 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
-def device_assembly(workdir: str) -> str:
-    """Compile the kernels for gfx950 keeping the assembly; return its path."""
-    src = os.path.join(CSRC, "slora_kernels.hip")
+def device_assembly(workdir: str, source: str = "slora_kernels.hip") -> str:
+    """Compile one HIP source for gfx950 keeping the assembly; return its path."""
+    src = os.path.join(CSRC, source)
+    stem = os.path.splitext(source)[0]
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-c",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", INCLUDE, "-I", CSRC, "--save-temps", "-o", os.path.join(workdir, "k.o"), src]
+           "-I", INCLUDE, "-I", CSRC, "--save-temps", "-o", os.path.join(workdir, stem + ".o"), src]
     res = subprocess.run(cmd, capture_output=True, text=True, cwd=workdir)
     if res.returncode != 0:
         raise RuntimeError(res.stderr)
-    return os.path.join(workdir, "slora_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")
+    return os.path.join(workdir, f"{stem}-hip-amdgcn-amd-amdhsa-gfx950.s")
 
 
 def masked_mfma_lines(asm_path: str):

@@ -1,0 +1,332 @@
+// Base product with the LoRA delta folded into its tiles, for MI355X (gfx950).
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "slora_device.h"
+
+namespace slora {
+
+// Base product with the LoRA delta in the same tiles: the summary page's
+// "How to read the paper" item 2 (h = xW + xAB) evaluated as one fp32 sum per
+// output element, and the blog page's section-2 interface (base output plus
+// adapter output in one call).  y is written once, so the delta costs no
+// extra pass over y.
+//
+// One workgroup per tile of BM sorted positions x BN columns, 2 x (BN / 64)
+// waves, each BM / 2 positions x 64 columns (blocks of
+// v_mfma_f32_16x16x32_f16).  Two shapes: 128 x 128 (four waves of 64 x 64)
+// and 256 x 256 (eight waves of 128 x 64).  The larger tile reads x and W
+// half as often per flop: x is read once per column block and W once per row
+// block, and at 128 x 128 that traffic, not the matrix cores, bounds the
+// kernel on large batches.  Per step the tile stages in LDS (two buffers, one
+// barrier per step):
+//   A  BM rows x 64 k of fp16 (16-byte chunks XOR-swizzled by row)
+//   B  64 rows x BN columns, as BN / 128 slices of 128 columns (the
+//      expand's slice layout, read with the transposing ds_read_b64_tr_b16)
+// An x W step holds the positions' x rows (k0 .. k0+63) in A and W rows
+// k0 .. k0+63 in B; its two 32-k halves are two MFMA sub-steps.  A LoRA step
+// of segment g and rank rows j0 .. j0+31 holds the B page rows j0 .. j0+31 of
+// g in B rows 0..31 and, in A, s v[t, j] 2^-e_t for the positions t of g
+// (zero for the others) split into an fp16 high part (k 0..31) and the
+// rounding remainder (k 32..63); both sub-steps multiply the same B rows, so
+// the matrix cores see s v with about 22 significant bits.  e_t puts the
+// position's largest |s v| in [2^14, 2^15); the accumulators are scaled back
+// by 2^e_t (exact) after the LoRA steps, before the x W steps.
+
+template <int BM, int BN>
+struct FwdTile {
+  static constexpr int WN = BN / 64;                 // waves along the columns
+  static constexpr int NT = 128 * WN;                // threads (2 x WN waves)
+  static constexpr int RW = BM / 2;                  // positions per wave
+  static constexpr int RB = RW / 16;                 // 16-row MFMA blocks per wave
+  static constexpr int NSL = BN / 128;               // 128-column B slices
+  static constexpr int CH = BN / 8;                  // 16-byte chunks per B row
+  static constexpr int ADw = BM * (kFwdBK / 2);
+  static constexpr int SliceDw = kFwdBK * kSliceRowDw;
+  static constexpr int StageDw = ADw + NSL * SliceDw;
+  static constexpr int EpiPitchDw = BN / 2 + 4;      // one fp16 output row, padded
+  static constexpr int LdsDw = 2 * StageDw + 5 * BM;
+  static_assert(BM == NT / 2, "two threads per position in the prologue and the LoRA staging");
+  static_assert(128 * EpiPitchDw <= 2 * StageDw, "an epilogue pass of 128 rows reuses the stage buffers");
+  static_assert(RW <= 128 && 128 % RW == 0, "epilogue passes hold whole waves");
+  static_assert(kShrinkKc == kFwdBK && kFwdLoraRows == 32, "stage layouts");
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__(128 * (BN / 64)) __attribute__((amdgpu_waves_per_eu(2)))
+void forward_kernel(ForwardLaunch F) {
+  using C = FwdTile<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[C::LdsDw];
+  // Workgroup b runs on XCD b mod 8; XCD x takes tiles x * per_xcd .. +per_xcd
+  // in the tile order below, so the tiles resident on one XCD at a time share
+  // x rows and W columns through its L2.
+  const int b = blockIdx.x;
+  const int tile = uni((b & 7) * F.per_xcd + (b >> 3));
+  if (tile >= F.n_tiles) return;
+  // groups of group_m row blocks, column by column inside a group
+  const int gsize = F.group_m * F.n_cb;
+  const int grp = tile / gsize, within = tile - grp * gsize;
+  const int gm = min(F.group_m, F.n_rb - grp * F.group_m);
+  const int rb = grp * F.group_m + within % gm;
+  const int r0 = F.pos0 + rb * BM, c0 = (within / gm) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  int32_t* tok_l = reinterpret_cast<int32_t*>(lds + 2 * C::StageDw);
+  int32_t* seg_l = tok_l + BM;
+  int32_t* voff_l = seg_l + BM;
+  float* mul_l = reinterpret_cast<float*>(voff_l + BM);
+  float* up_l = mul_l + BM;
+
+  // Per position of the tile: batch index, segment (-1: no adapter), v row
+  // offset, s 2^-e and 2^e.  Positions past the batch take the last token's
+  // row (loaded, never stored).  Two threads per position scan its v row for
+  // the largest |v|, eight independent loads at a time.
+  {
+    const int row = tid >> 1, half = tid & 1;
+    const int p = r0 + row;
+    int seg = -1, voff = 0, rank = 0;
+    float scale = 0.f;
+    if (p < F.n_routed) {
+      seg = F.pos_seg[p];
+      rank = F.seg_rank[seg];
+      scale = __int_as_float(F.seg_scale[seg]);
+      voff = F.seg_v_off[seg] + (p - F.seg_start[seg]) * rank;
+    }
+    float amax = 0.f;
+    for (int j0 = half; j0 < rank; j0 += 16) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + 2 * u;
+        t[u] = F.v[j < rank ? voff + j : voff];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) amax = fmaxf(amax, fabsf(t[u]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64)) * fabsf(scale);
+    int ex = 0;
+    if (amax > 0.f) {
+      (void)frexpf(amax, &ex);
+      ex = max(ex - 15, -100);
+    }
+    if (half == 0) {
+      tok_l[row] = F.order[min(p, F.n_tokens - 1)];
+      seg_l[row] = seg;
+      voff_l[row] = voff;
+      mul_l[row] = seg >= 0 ? scale * ldexpf(1.f, -ex) : 0.f;
+      up_l[row] = seg >= 0 ? ldexpf(1.f, ex) : 1.f;
+    }
+  }
+  __syncthreads();
+
+  // Thread maps.  LoRA staging: A row ar = tid / 2, rank rows 16ah .. 16ah+15
+  // (ah = tid % 2).  B rows (W or pages): rows brow + 16h, one 16-byte chunk
+  // bch of the BN columns (slice bch / 16).  x rows: chunk xch of rows
+  // xrow + (NT / 8) i, so one wave instruction reads 8 whole 128-byte row
+  // segments.
+  const int ar = tid >> 1, ah = tid & 1;
+  const int brow = tid / C::CH, bch = tid % C::CH;
+  const int bsl = bch >> 4, bquad = 2 * (bch & 15);
+  const int xrow = tid >> 3, xch = tid & 7;
+  const _Float16* xb = static_cast<const _Float16*>(F.x);
+  const _Float16* wb = static_cast<const _Float16*>(F.w);
+  const int n_w = F.h_in / kFwdBK;
+
+  float4v acc[C::RB][4];
+#pragma unroll
+  for (int i = 0; i < C::RB; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[i][c] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // One MFMA sub-step: A chunks 4h .. 4h+3 against B rows brow0 .. brow0+31.
+  auto mfma_step = [&](const uint32_t* S, int h, int brow0) {
+    const uint32_t* A = S;
+    const uint32_t* B = S + C::ADw + (wn >> 1) * C::SliceDw;
+    half8 bf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int q = 16 * (wn & 1) + 4 * c + (m & 3);
+      const short4v r0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4v*)(B + quad_dw(brow0 + 8 * g + (m >> 2), q)));
+      const short4v r1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4v*)(B + quad_dw(brow0 + 8 * g + 4 + (m >> 2), q)));
+      bf[c] = __builtin_bit_cast(half8, __builtin_shufflevector(r0v, r1v, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int i = 0; i < C::RB; ++i) {
+      const half8 af = __builtin_bit_cast(
+          half8, *reinterpret_cast<const uint4*>(A + chunk_dw(C::RW * wm + 16 * i + m, 4 * h + g)));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[c], acc[i][c], 0, 0, 0);
+    }
+  };
+
+  // x W steps: every load unconditional (a step past the end reloads the last).
+  auto w_load = [&](int s, uint4 (&aq)[4], uint4 (&bq)[4]) {
+    s = s < n_w ? s : n_w - 1;
+    const int k0 = s * kFwdBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      aq[i] = ld16(xb + (int64_t)tok_l[xrow + (C::NT / 8) * i] * F.h_in + k0 + 8 * xch);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) bq[h] = ld16(wb + (int64_t)(k0 + brow + 16 * h) * F.h_out + c0 + 8 * bch);
+  };
+  auto w_store = [&](uint32_t* S, const uint4 (&aq)[4], const uint4 (&bq)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(S + chunk_dw(xrow + (C::NT / 8) * i, xch)) = aq[i];
+    uint32_t* B = S + C::ADw + bsl * C::SliceDw;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) *reinterpret_cast<uint4*>(B + quad_dw(brow + 16 * h, bquad)) = bq[h];
+  };
+
+  const int n_lora = uni(F.rb_info[2 * rb + 1]);
+  if (n_lora > 0) {
+    const int32_t* tab = F.stages + (int64_t)uni(F.rb_info[2 * rb]) * kFwdStageWords;
+    // Stage table entry of LoRA step q (clamped): this thread's two B page
+    // ids and the step's segment, first rank row and rank.
+    struct Tab { int id0, id1, seg, j0, rank; };
+    auto tab_load = [&](int q, Tab& t) {
+      q = q < n_lora ? q : n_lora - 1;
+      const int32_t* e = tab + (int64_t)q * kFwdStageWords;
+      t.id0 = e[brow];
+      t.id1 = e[16 + brow];
+      const int4 hd = *reinterpret_cast<const int4*>(e + FWS_SEG);
+      t.seg = hd.x;
+      t.j0 = hd.y;
+      t.rank = hd.z;
+    };
+    auto lora_load = [&](const Tab& t, uint4 (&lb)[2], float (&vv)[16]) {
+      const int64_t col = (int64_t)(c0 + 8 * bch) * 2;
+      lb[0] = ld16(F.base_b + (int64_t)t.id0 * F.page_bytes_b + col);
+      lb[1] = ld16(F.base_b + (int64_t)t.id1 * F.page_bytes_b + col);
+      const bool in = seg_l[ar] == t.seg;
+      const int voff = voff_l[ar];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = t.j0 + 16 * ah + i;
+        vv[i] = F.v[(in && j < t.rank) ? voff + j : 0];
+      }
+    };
+    auto lora_store = [&](uint32_t* S, const Tab& t, const uint4 (&lb)[2], const float (&vv)[16]) {
+      uint32_t* B = S + C::ADw + bsl * C::SliceDw;
+      *reinterpret_cast<uint4*>(B + quad_dw(brow, bquad)) = lb[0];
+      *reinterpret_cast<uint4*>(B + quad_dw(16 + brow, bquad)) = lb[1];
+      const bool in = seg_l[ar] == t.seg;
+      const float mul = mul_l[ar];
+      half8 hi[2], lo[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = t.j0 + 16 * ah + i;
+        const float f = (in && j < t.rank) ? vv[i] * mul : 0.f;
+        const _Float16 hv = (_Float16)f;
+        hi[i >> 3][i & 7] = hv;
+        lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 2 * ah + c)) = __builtin_bit_cast(uint4, hi[c]);
+        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + 2 * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
+      }
+    };
+    Tab tc, tn;
+    uint4 lb[2];
+    float vv[16];
+    tab_load(0, tc);
+    lora_load(tc, lb, vv);
+    tab_load(1, tn);
+    for (int q = 0; q < n_lora; ++q) {
+      uint32_t* S = lds + (q & 1) * C::StageDw;
+      lora_store(S, tc, lb, vv);
+      lds_barrier();
+      tc = tn;
+      lora_load(tc, lb, vv);
+      tab_load(q + 2, tn);
+      mfma_step(S, 0, 0);
+      mfma_step(S, 1, 0);
+    }
+    lds_barrier();   // the x W steps reuse both buffers
+#pragma unroll
+    for (int i = 0; i < C::RB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = up_l[C::RW * wm + 16 * i + 4 * g + e];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][c][e] *= u;
+      }
+  }
+
+  // The first two x W steps (issued after the LoRA steps, whose registers
+  // they would otherwise compete with).
+  uint4 wa0[4], wb0[4], wa1[4], wb1[4];
+  w_load(0, wa0, wb0);
+  w_load(1, wa1, wb1);
+
+  // x W steps, unrolled by two so that each register set and LDS buffer is
+  // static: step s stores set s & 1 into buffer s & 1, then refills the set
+  // with step s + 2.  A buffer is written again only after every wave has
+  // passed the barrier of the step that followed its last read.
+  for (int s = 0;; s += 2) {
+    w_store(lds, wa0, wb0);
+    lds_barrier();
+    w_load(s + 2, wa0, wb0);
+    mfma_step(lds, 0, 0);
+    mfma_step(lds, 1, 32);
+    if (s + 1 >= n_w) break;
+    w_store(lds + C::StageDw, wa1, wb1);
+    lds_barrier();
+    w_load(s + 3, wa1, wb1);
+    mfma_step(lds + C::StageDw, 0, 0);
+    mfma_step(lds + C::StageDw, 1, 32);
+    if (s + 2 >= n_w) break;
+  }
+
+  // Epilogue, 128 rows at a time: fp16 results through LDS, then whole
+  // 16-byte chunks of y rows.
+  _Float16* E = reinterpret_cast<_Float16*>(lds);
+  _Float16* yb = static_cast<_Float16*>(F.y);
+#pragma unroll
+  for (int pass = 0; pass < BM / 128; ++pass) {
+    lds_barrier();   // every wave is done with the stage buffers / the previous pass
+    if (C::RW * wm / 128 == pass) {
+      const int rbase = C::RW * wm - 128 * pass;
+#pragma unroll
+      for (int i = 0; i < C::RB; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            E[(rbase + 16 * i + 4 * g + e) * (2 * C::EpiPitchDw) + 64 * wn + 16 * c + m] = (_Float16)acc[i][c][e];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < 128 * C::CH / C::NT; ++k) {
+      const int row = brow + (C::NT / C::CH) * k;
+      const uint4 val = *reinterpret_cast<const uint4*>(lds + row * C::EpiPitchDw + 4 * bch);
+      const int p = 128 * pass + row;
+      if (r0 + p < F.n_tokens) st16(yb + (int64_t)tok_l[p] * F.h_out + c0 + 8 * bch, val);
+    }
+  }
+}
+
+hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (F.n_tiles <= 0) return hipSuccess;
+  void* args[] = {const_cast<ForwardLaunch*>(&F)};
+  const void* k;
+  int nt;
+  if (F.bm == 256 && F.bn == 256) {
+    k = reinterpret_cast<const void*>(&forward_kernel<256, 256>);
+    nt = FwdTile<256, 256>::NT;
+  } else if (F.bm == 128 && F.bn == 128) {
+    k = reinterpret_cast<const void*>(&forward_kernel<128, 128>);
+    nt = FwdTile<128, 128>::NT;
+  } else {
+    return hipErrorInvalidValue;
+  }
+  const dim3 grid((unsigned)(8 * F.per_xcd));
+  if (!start && !stop) return hipLaunchKernel(k, grid, dim3(nt), args, 0, stream);
+  return hipExtLaunchKernel(k, grid, dim3(nt), args, 0, stream, start, stop, 0);
+}
+
+}  // namespace slora

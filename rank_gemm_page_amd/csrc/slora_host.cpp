@@ -90,6 +90,8 @@ struct Tuning {
   int64_t fused = 1;
   int64_t xcds = 1;             // XCD groups of the shrink placement (1: none)
   int64_t tile_order = 2;       // 0: segment order, 1: rank-descending, 2: bytes-descending
+  int64_t fwd_group = 0;        // row blocks per group of the base-plus-delta tile order (0: automatic)
+  int64_t fwd_tile = 0;         // base-plus-delta tile: 128, 256, or 0 (automatic)
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -157,6 +159,9 @@ struct slora_segments {
   int64_t fw_order_off = 0, fw_pos_seg_off = 0, fw_seg_start_off = 0, fw_seg_rank_off = 0;
   int64_t fw_seg_scale_off = 0, fw_seg_v_off = 0, fw_rb_info_off = 0, fw_stages_off = 0;
   int32_t fw_n_rb = 0, fw_n_stages = 0;
+  // Sorted positions 0 .. fw_big_rows go in 256 x 256 tiles (fw_n_rb_big row
+  // blocks), the rest in 128 x 128 tiles; fw_n_rb counts both kinds.
+  int32_t fw_big_rows = 0, fw_n_rb_big = 0;
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -577,18 +582,40 @@ void build_tiles(slora_segments* s) {
   s->expand_idx_off_words = s->shrink_idx_off_words + s->n_shrink;
   s->records_words = (s->expand_idx_off_words + s->n_expand + 3) & ~(int64_t)3;
 
-  // Base-plus-delta table.  Row block rb holds sorted positions
-  // rb * kFwdBM .. +kFwdBM; its LoRA stages are, for every segment that owns
-  // one of those positions, one stage per kFwdLoraRows rank rows.
+  // Base-plus-delta table.  A 256 x 256 tile reads x and W half as often
+  // per flop as a 128 x 128 one but holds a whole CU (one workgroup per CU,
+  // 256 CUs), so big tiles are used only in whole rounds of 256: the leading
+  // row blocks that fill complete rounds take big tiles, the remaining
+  // positions 128 x 128 tiles, which spread a partial round over the chip
+  // (for the 7B prefill batch: 512 big tiles and 320 small ones instead of
+  // 592 big tiles in three rounds, the last a third full).  Batches too small
+  // for one round use small tiles only.  Row block rb holds sorted positions
+  // start(rb) .. +tile; its LoRA stages are, for every segment that owns one
+  // of those positions, one stage per kFwdLoraRows rank rows.
   const int32_t T = s->n_tokens, routed = (int32_t)s->perm.size();
-  s->fw_n_rb = (T + kFwdBM - 1) / kFwdBM;
+  const bool big_ok = hout % kFwdBig == 0;
+  const int64_t cb_big = hout / kFwdBig;
+  const int64_t rb_big_all = (T + kFwdBig - 1) / kFwdBig;
+  int32_t n_rb_big = 0;
+  if (big_ok && p->tune.fwd_tile == kFwdBig) {
+    n_rb_big = (int32_t)rb_big_all;
+  } else if (big_ok && p->tune.fwd_tile == 0 && rb_big_all * cb_big >= 256) {
+    const int64_t rounds = rb_big_all * cb_big / 256;
+    n_rb_big = (int32_t)std::min<int64_t>(rb_big_all, rounds * 256 / cb_big);
+  }
+  s->fw_n_rb_big = n_rb_big;
+  s->fw_big_rows = std::min<int32_t>(T, n_rb_big * kFwdBig);
+  const int32_t n_rb_small = (T - s->fw_big_rows + kFwdBM - 1) / kFwdBM;
+  s->fw_n_rb = n_rb_big + n_rb_small;
   std::vector<int32_t> pos_seg(routed);
   for (int32_t g = 0; g < S; ++g)
     for (int32_t i = s->seg_start[g]; i < s->seg_start[g + 1]; ++i) pos_seg[i] = g;
   std::vector<int32_t> rb_info(2 * (size_t)s->fw_n_rb, 0);
   std::vector<std::pair<int32_t, int32_t>> fw_stages;   // (segment, first rank row)
   for (int32_t rb = 0; rb < s->fw_n_rb; ++rb) {
-    const int32_t p0 = rb * kFwdBM, p1 = std::min(p0 + kFwdBM, routed);
+    const bool big = rb < n_rb_big;
+    const int32_t p0 = big ? rb * kFwdBig : s->fw_big_rows + (rb - n_rb_big) * kFwdBM;
+    const int32_t p1 = std::min(p0 + (big ? kFwdBig : kFwdBM), routed);
     rb_info[2 * rb] = (int32_t)fw_stages.size();
     if (p0 < p1)
       for (int32_t g = pos_seg[p0]; g <= pos_seg[p1 - 1]; ++g)
@@ -786,6 +813,15 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
     case SLORA_TUNE_FUSED:
       if (value != 0 && value != 1) return fail(SLORA_E_INVAL, "fused must be 0 or 1");
       p->tune.fused = value;
+      return SLORA_OK;
+    case SLORA_TUNE_FWD_GROUP:
+      if (value < 0 || value > 65536) return fail(SLORA_E_INVAL, "fwd_group must be 0..65536 (0: automatic)");
+      p->tune.fwd_group = value;
+      return SLORA_OK;
+    case SLORA_TUNE_FWD_TILE:
+      if (value != 0 && value != kFwdBM && value != kFwdBig)
+        return fail(SLORA_E_INVAL, "fwd_tile must be 0 (automatic), 128 or 256");
+      p->tune.fwd_tile = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_SHRINK_SPLITS:
       if (value < 0 || value > kMaxSplits) return fail(SLORA_E_INVAL, "mfma_shrink_splits must be 0..4 (0: automatic)");
@@ -1307,14 +1343,27 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
   F.seg_rank = m + s->fw_seg_rank_off;
   F.seg_scale = m + s->fw_seg_scale_off;
   F.seg_v_off = m + s->fw_seg_v_off;
-  F.rb_info = m + s->fw_rb_info_off;
   F.stages = m + s->fw_stages_off + (int64_t)proj * s->fw_n_stages * kFwdStageWords;
-  F.n_rb = s->fw_n_rb;
-  F.n_cb = p->d.h_out / kFwdBN;
-  F.n_tiles = F.n_rb * F.n_cb;
-  F.per_xcd = (F.n_tiles + 7) / 8;
-  hipError_t e = launch_forward(F, hs, routed ? nullptr : static_cast<hipEvent_t>(ev_start),
-                                static_cast<hipEvent_t>(ev_stop));
+  // Big tiles over the leading positions, then small tiles over the rest; the
+  // start event goes with the first launch, the stop event with the last.
+  const int32_t n_small = s->fw_n_rb - s->fw_n_rb_big;
+  hipError_t e = hipSuccess;
+  for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+    const int32_t n_rb = part == 0 ? s->fw_n_rb_big : n_small;
+    if (n_rb == 0) continue;
+    F.bm = F.bn = part == 0 ? kFwdBig : kFwdBM;
+    F.pos0 = part == 0 ? 0 : s->fw_big_rows;
+    F.rb_info = m + s->fw_rb_info_off + (part == 0 ? 0 : 2 * (int64_t)s->fw_n_rb_big);
+    F.n_rb = n_rb;
+    F.n_cb = p->d.h_out / F.bn;
+    F.n_tiles = F.n_rb * F.n_cb;
+    F.per_xcd = (F.n_tiles + 7) / 8;
+    F.group_m = (int32_t)std::min<int64_t>(p->tune.fwd_group > 0 ? p->tune.fwd_group : 1, F.n_rb);
+    const bool first = part == 0 || s->fw_n_rb_big == 0;
+    const bool last = part == 1 || n_small == 0;
+    e = launch_forward(F, hs, (first && !routed) ? static_cast<hipEvent_t>(ev_start) : nullptr,
+                       last ? static_cast<hipEvent_t>(ev_stop) : nullptr);
+  }
   if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
   return SLORA_OK;
 }

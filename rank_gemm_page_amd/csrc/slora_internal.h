@@ -109,12 +109,14 @@ hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
 //   y[t, o] = round( sum_k x[t, k] W[k, o]  +  s_a sum_j v[t, j] B_j[o] )
 // over the batch in segment order (routed tokens sorted by adapter, then the
 // tokens with no adapter), in tiles of kFwdBM sorted positions x kFwdBN
-// columns.  Each tile first runs one LoRA stage per 32 rank rows of every
+// columns (kFwdBM x kFwdBN, or twice that on large batches).  Each tile
+// first runs one LoRA stage per 32 rank rows of every
 // segment its positions touch (the B page rows against s v, split into fp16
 // high and low parts), then the x W stages of kFwdBK rows of W, and writes y
 // once.  v = x A comes from the shrink kernels (workspace).
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 128;
+constexpr int kFwdBig = 256;       // the large tile's rows and columns
 constexpr int kFwdBK = 64;
 constexpr int kFwdLoraRows = 32;   // B page rows per LoRA stage
 // LoRA stage table entry (int32 words): the stage's 32 B page ids (rows past
@@ -137,9 +139,12 @@ struct ForwardLaunch {
   const int32_t* seg_rank;   // [S]
   const int32_t* seg_scale;  // [S] float bits
   const int32_t* seg_v_off;  // [S] workspace offset of the segment's first v row
-  const int32_t* rb_info;    // [n_rb][2]: first LoRA stage entry, LoRA stages
+  const int32_t* rb_info;    // [n_rb][2] of this launch: first LoRA stage entry, LoRA stages
   const int32_t* stages;     // LoRA stage table of this projection
   int32_t n_rb, n_cb, n_tiles, per_xcd;
+  int32_t group_m;           // tile order: groups of group_m row blocks, column-major inside a group
+  int32_t bm, bn;            // tile shape: 128 x 128 or 256 x 256
+  int32_t pos0;              // first sorted position of row block 0 of this launch
 };
 
 // Launch the base-plus-delta kernel (one launch, n_tiles workgroups placed

@@ -32,22 +32,16 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
-#include "slora_internal.h"
+#include "slora_device.h"
 
 namespace slora {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
 
 template <typename T> struct VecN;
 template <> struct VecN<_Float16> { static constexpr int N = 8; };
 template <> struct VecN<float> { static constexpr int N = 4; };
 
-__device__ __forceinline__ uint4 ld16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Streaming (non-temporal) 16-byte load and store, for data read once per
 // launch: page rows of the vector-ALU tiles, x rows of the MFMA shrink (each
@@ -159,21 +153,7 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&p)[N], int lane) {
 }
 
 
-// Values every lane of a wavefront holds alike (tile header fields, the wave
-// index) are moved to scalar registers.  Control flow on them then branches
-// instead of masking lanes, which matters for MFMA: a matrix instruction runs
-// on the whole wavefront whatever the EXEC mask says, so it must never sit
-// behind a lane mask to be skipped.
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
-// orders global memory, which makes every wave wait for all of its global
-// loads still in flight (prefetches included) before the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Copy the part of a tile record this launch needs (header, tokens and the
 // page list of projection `proj`) into LDS with one batch of independent
@@ -353,7 +333,6 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 constexpr int kShrinkStageDw = 2 * kMfmaExpandTok * (kShrinkKc / 2);   // x and A^T rows of one chunk
 constexpr int kShrinkLdsFloats = 2 * kShrinkStageDw;                   // two chunks (32 KB)
 
-__device__ __forceinline__ int chunk_dw(int row, int c) { return row * (kShrinkKc / 2) + 4 * (c ^ (row & 7)); }
 
 template <bool FUSED>
 __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
@@ -642,19 +621,10 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 // accumulators leave through LDS, so y is read and written in whole
 // 128-byte lines.
 
-constexpr int kSliceRowDw = kMfmaPass / 2;      // dwords per 128-column row
 constexpr int kSliceDw = 32 * kSliceRowDw;      // one staged 32-row slice (8 KB)
 constexpr int kEpiPitch = kMfmaPass + 4;        // floats per epilogue row
 constexpr int kMfmaExpandLds = 2 * kSliceDw + kMfmaExpandTok * kEpiPitch + kMfmaExpandTok;
 
-// Dword offset of column quad q (4 columns) of row r of a staged slice.  The
-// quads are XOR-swizzled by row so that the 8 rows the two lane groups of a
-// half-wave read together (8g + t, t = 0..3) land in distinct banks.
-__device__ __forceinline__ int quad_dw(int r, int q) {
-  return r * kSliceRowDw + 2 * (q ^ (4 * ((r & 3) + 4 * ((r >> 3) & 1))));
-}
-
-typedef short short4v __attribute__((ext_vector_type(4)));
 constexpr int kBufferFormat = 0x00020000;   // descriptor word 3: raw 32-bit buffer
 
 template <bool FUSED, int KS>   // KS: 32-row k slices of the rank (1 or 2), fixed per instantiation
@@ -1021,272 +991,5 @@ hipError_t launch_scatter_pages(const ScatterLaunch& S, hipStream_t stream) {
   return hipGetLastError();
 }
 
-
-// ---------------------------------------------------------------------------
-// Base product with the LoRA delta in the same tiles: the summary page's
-// "How to read the paper" item 2 (h = xW + xAB) evaluated as one fp32 sum per
-// output element, and the blog page's section-2 interface (base output plus
-// adapter output in one call).  y is written once, so the delta costs no
-// extra pass over y.
-//
-// One workgroup per tile of kFwdBM sorted positions x kFwdBN columns; four
-// waves in a 2 x 2 grid, each 64 positions x 64 columns (4 x 4 blocks of
-// v_mfma_f32_16x16x32_f16).  Per step the tile stages in LDS (two buffers,
-// one barrier per step):
-//   A  kFwdBM rows x 64 k of fp16 (16-byte chunks XOR-swizzled by row)
-//   B  64 rows x kFwdBN columns (the expand's slice layout, read with the
-//      transposing ds_read_b64_tr_b16)
-// An x W step holds the positions' x rows (k0 .. k0+63) in A and W rows
-// k0 .. k0+63 in B; its two 32-k halves are two MFMA sub-steps.  A LoRA step
-// of segment g and rank rows j0 .. j0+31 holds the B page rows j0 .. j0+31 of
-// g in B rows 0..31 and, in A, s v[t, j] 2^-e_t for the positions t of g
-// (zero for the others) split into an fp16 high part (k 0..31) and the
-// rounding remainder (k 32..63); both sub-steps multiply the same B rows, so
-// the matrix cores see s v with about 22 significant bits.  e_t puts the
-// position's largest |s v| in [2^14, 2^15); the accumulators are scaled back
-// by 2^e_t (exact) after the LoRA steps, before the x W steps.
-
-constexpr int kFwdADw = kFwdBM * (kFwdBK / 2);
-constexpr int kFwdBDw = kFwdBK * kSliceRowDw;
-constexpr int kFwdStageDw = kFwdADw + kFwdBDw;
-constexpr int kFwdEpiPitchDw = kFwdBN / 2 + 4;         // one fp16 output row, padded
-constexpr int kFwdLdsDw = 2 * kFwdStageDw + 5 * kFwdBM;
-static_assert(kShrinkKc == kFwdBK && 2 * kSliceRowDw == kFwdBN, "the A and B stage layouts are the shrink's and the expand's");
-static_assert(kFwdBM * kFwdEpiPitchDw <= 2 * kFwdStageDw, "the epilogue reuses the stage buffers");
-static_assert(kFwdLoraRows == 32 && kThreads == 256, "thread maps below");
-
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void forward_kernel(ForwardLaunch F) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kFwdLdsDw];
-  // Workgroup b runs on XCD b mod 8; XCD x takes tiles x * per_xcd .. +per_xcd,
-  // row-block major, so the tiles resident on one XCD share x rows and walk
-  // the W columns together through its L2.
-  const int b = blockIdx.x;
-  const int tile = uni((b & 7) * F.per_xcd + (b >> 3));
-  if (tile >= F.n_tiles) return;
-  const int rb = tile / F.n_cb;
-  const int r0 = rb * kFwdBM, c0 = (tile - rb * F.n_cb) * kFwdBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
-  const int m = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  int32_t* tok_l = reinterpret_cast<int32_t*>(lds + 2 * kFwdStageDw);
-  int32_t* seg_l = tok_l + kFwdBM;
-  int32_t* voff_l = seg_l + kFwdBM;
-  float* mul_l = reinterpret_cast<float*>(voff_l + kFwdBM);
-  float* up_l = mul_l + kFwdBM;
-
-  // Per position of the tile: batch index, segment (-1: no adapter), v row
-  // offset, s 2^-e and 2^e.  Positions past the batch take the last token's
-  // row (loaded, never stored).
-  if (tid < kFwdBM) {
-    const int p = r0 + tid;
-    tok_l[tid] = F.order[min(p, F.n_tokens - 1)];
-    int seg = -1, voff = 0;
-    float mul = 0.f, up = 1.f;
-    if (p < F.n_routed) {
-      seg = F.pos_seg[p];
-      const int rank = F.seg_rank[seg];
-      const float scale = __int_as_float(F.seg_scale[seg]);
-      voff = F.seg_v_off[seg] + (p - F.seg_start[seg]) * rank;
-      float amax = 0.f;
-      for (int j = 0; j < rank; ++j) amax = fmaxf(amax, fabsf(F.v[voff + j]));
-      amax *= fabsf(scale);
-      int ex = 0;
-      if (amax > 0.f) {
-        (void)frexpf(amax, &ex);
-        ex = max(ex - 15, -100);
-      }
-      mul = scale * ldexpf(1.f, -ex);
-      up = ldexpf(1.f, ex);
-    }
-    seg_l[tid] = seg;
-    voff_l[tid] = voff;
-    mul_l[tid] = mul;
-    up_l[tid] = up;
-  }
-  __syncthreads();
-
-  // Thread maps.  Staging: A row ar = tid / 2, half ah = tid % 2 (x: chunks
-  // 4ah .. 4ah+3; LoRA: rank rows 16ah .. 16ah+15); B rows lrow + 16h, one
-  // 16-byte column chunk lch.
-  const int ar = tid >> 1, ah = tid & 1;
-  const int lrow = tid >> 4, lch = tid & 15;
-  const _Float16* xb = static_cast<const _Float16*>(F.x);
-  const _Float16* wb = static_cast<const _Float16*>(F.w);
-  const int n_w = F.h_in / kFwdBK;
-
-  float4v acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[i][c] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  // One MFMA sub-step: A chunks 4h .. 4h+3 against B rows brow0 .. brow0+31.
-  auto mfma_step = [&](const uint32_t* S, int h, int brow0) {
-    const uint32_t* A = S;
-    const uint32_t* B = S + kFwdADw;
-    half8 af[4], bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(A + chunk_dw(64 * wm + 16 * i + m, 4 * h + g)));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int q = 16 * wn + 4 * c + (m & 3);
-      const short4v r0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4v*)(B + quad_dw(brow0 + 8 * g + (m >> 2), q)));
-      const short4v r1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4v*)(B + quad_dw(brow0 + 8 * g + 4 + (m >> 2), q)));
-      bf[c] = __builtin_bit_cast(half8, __builtin_shufflevector(r0v, r1v, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[c], acc[i][c], 0, 0, 0);
-  };
-
-  // x W steps: every load unconditional (a step past the end reloads the last).
-  auto w_load = [&](int s, uint4 (&aq)[4], uint4 (&bq)[4]) {
-    s = s < n_w ? s : n_w - 1;
-    const int k0 = s * kFwdBK;
-    const _Float16* xr = xb + (int64_t)tok_l[ar] * F.h_in + k0 + 32 * ah;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aq[i] = ld16(xr + 8 * i);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) bq[h] = ld16(wb + (int64_t)(k0 + lrow + 16 * h) * F.h_out + c0 + 8 * lch);
-  };
-  auto w_store = [&](uint32_t* S, const uint4 (&aq)[4], const uint4 (&bq)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 * ah + i)) = aq[i];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) *reinterpret_cast<uint4*>(S + kFwdADw + quad_dw(lrow + 16 * h, 2 * lch)) = bq[h];
-  };
-
-  // The first two x W steps are in flight while the LoRA steps run.
-  uint4 wa0[4], wb0[4], wa1[4], wb1[4];
-  w_load(0, wa0, wb0);
-  w_load(1, wa1, wb1);
-
-  const int n_lora = uni(F.rb_info[2 * rb + 1]);
-  if (n_lora > 0) {
-    const int32_t* tab = F.stages + (int64_t)uni(F.rb_info[2 * rb]) * kFwdStageWords;
-    // Stage table entry of LoRA step q (clamped): this thread's two B page
-    // ids and the step's segment, first rank row and rank.
-    struct Tab { int id0, id1, seg, j0, rank; };
-    auto tab_load = [&](int q, Tab& t) {
-      q = q < n_lora ? q : n_lora - 1;
-      const int32_t* e = tab + (int64_t)q * kFwdStageWords;
-      t.id0 = e[lrow];
-      t.id1 = e[16 + lrow];
-      const int4 h = *reinterpret_cast<const int4*>(e + FWS_SEG);
-      t.seg = h.x;
-      t.j0 = h.y;
-      t.rank = h.z;
-    };
-    auto lora_load = [&](const Tab& t, uint4 (&bq)[2], float (&vv)[16]) {
-      const int64_t col = (int64_t)(c0 + 8 * lch) * 2;
-      bq[0] = ld16(F.base_b + (int64_t)t.id0 * F.page_bytes_b + col);
-      bq[1] = ld16(F.base_b + (int64_t)t.id1 * F.page_bytes_b + col);
-      const bool in = seg_l[ar] == t.seg;
-      const int voff = voff_l[ar];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = t.j0 + 16 * ah + i;
-        vv[i] = F.v[(in && j < t.rank) ? voff + j : 0];
-      }
-    };
-    auto lora_store = [&](uint32_t* S, const Tab& t, const uint4 (&bq)[2], const float (&vv)[16]) {
-      *reinterpret_cast<uint4*>(S + kFwdADw + quad_dw(lrow, 2 * lch)) = bq[0];
-      *reinterpret_cast<uint4*>(S + kFwdADw + quad_dw(16 + lrow, 2 * lch)) = bq[1];
-      const bool in = seg_l[ar] == t.seg;
-      const float mul = mul_l[ar];
-      half8 hi[2], lo[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = t.j0 + 16 * ah + i;
-        const float f = (in && j < t.rank) ? vv[i] * mul : 0.f;
-        const _Float16 hv = (_Float16)f;
-        hi[i >> 3][i & 7] = hv;
-        lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 2 * ah + c)) = __builtin_bit_cast(uint4, hi[c]);
-        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + 2 * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
-      }
-    };
-    Tab tc, tn;
-    uint4 lb[2];
-    float vv[16];
-    tab_load(0, tc);
-    lora_load(tc, lb, vv);
-    tab_load(1, tn);
-    for (int q = 0; q < n_lora; ++q) {
-      uint32_t* S = lds + (q & 1) * kFwdStageDw;
-      lora_store(S, tc, lb, vv);
-      lds_barrier();
-      tc = tn;
-      lora_load(tc, lb, vv);
-      tab_load(q + 2, tn);
-      mfma_step(S, 0, 0);
-      mfma_step(S, 1, 0);
-    }
-    lds_barrier();   // the x W steps reuse both buffers
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float u = up_l[64 * wm + 16 * i + 4 * g + e];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[i][c][e] *= u;
-      }
-  }
-
-  // x W steps, unrolled by two so that each register set and LDS buffer is
-  // static: step s stores set s & 1 into buffer s & 1, then refills the set
-  // with step s + 2.  A buffer is written again only after every wave has
-  // passed the barrier of the step that followed its last read.
-  for (int s = 0;; s += 2) {
-    w_store(lds, wa0, wb0);
-    lds_barrier();
-    w_load(s + 2, wa0, wb0);
-    mfma_step(lds, 0, 0);
-    mfma_step(lds, 1, 32);
-    if (s + 1 >= n_w) break;
-    w_store(lds + kFwdStageDw, wa1, wb1);
-    lds_barrier();
-    w_load(s + 3, wa1, wb1);
-    mfma_step(lds + kFwdStageDw, 0, 0);
-    mfma_step(lds + kFwdStageDw, 1, 32);
-    if (s + 2 >= n_w) break;
-  }
-
-  // Epilogue: fp16 results through LDS, then whole 16-byte chunks of y rows.
-  lds_barrier();
-  _Float16* E = reinterpret_cast<_Float16*>(lds);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        E[(64 * wm + 16 * i + 4 * g + e) * (2 * kFwdEpiPitchDw) + 64 * wn + 16 * c + m] = (_Float16)acc[i][c][e];
-  lds_barrier();
-  _Float16* yb = static_cast<_Float16*>(F.y);
-#pragma unroll
-  for (int k = 0; k < kFwdBM / 16; ++k) {
-    const int row = lrow + 16 * k;
-    const uint4 val = *reinterpret_cast<const uint4*>(lds + row * kFwdEpiPitchDw + 4 * lch);
-    if (r0 + row < F.n_tokens) st16(yb + (int64_t)tok_l[row] * F.h_out + c0 + 8 * lch, val);
-  }
-}
-
-hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (F.n_tiles <= 0) return hipSuccess;
-  void* args[] = {const_cast<ForwardLaunch*>(&F)};
-  const void* k = reinterpret_cast<const void*>(&forward_kernel);
-  const dim3 grid((unsigned)(8 * F.per_xcd));
-  if (!start && !stop) return hipLaunchKernel(k, grid, dim3(kThreads), args, 0, stream);
-  return hipExtLaunchKernel(k, grid, dim3(kThreads), args, 0, stream, start, stop, 0);
-}
 
 }  // namespace slora

@@ -32,12 +32,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str = "fused") -> str:
+    """Hash of the sources the measured kernel depends on: every host and
+    device source, except that the delta's kernels ("fused") do not include
+    the base-plus-delta kernel's own file."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_gemm_page_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if not name.endswith((".hip", ".cpp", ".h")):
             continue            # build by-products are not sources
+        if kind == "fused" and name == "slora_forward.hip":
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -51,7 +56,8 @@ def _one(pattern: str) -> str:
 
 
 def short_name(name: str) -> str:
-    for key in ("fused_kernel", "shrink_kernel", "combine_kernel", "expand_kernel", "scatter_pages_kernel"):
+    for key in ("fused_kernel", "shrink_kernel", "combine_kernel", "expand_kernel", "scatter_pages_kernel",
+                "forward_kernel"):
         if key in name:
             return key
     return name.split("(")[0][:60]
@@ -106,16 +112,21 @@ def traffic(fetch_dir: str, write_dir: str, flush_mib: int):
 
 
 def write_summary(config, trace_dir, fetch_dir, write_dir, command, flush_mib, out_dir,
-                  algorithmic_bytes=None, event_us=None):
+                  algorithmic_bytes=None, event_us=None, kind="fused"):
+    """kind "fused": the delta's fused kernel (profiles/fused_kernel_<config>.txt,
+    traffic_<config>.json); "forward": the base-plus-delta kernel
+    (forward_kernel_<config>.txt, traffic_forward_<config>.json)."""
+    dom = f"{kind}_kernel"
+    tname = f"traffic_{config}.json" if kind == "fused" else f"traffic_{kind}_{config}.json"
     stats = kernel_stats(trace_dir)
     tr = traffic(fetch_dir, write_dir, flush_mib)
     for s in stats:            # the kernel trace's average duration beside the bytes
         if s["short"] in tr["kernels"]:
             tr["kernels"][s["short"]]["trace_avg_us"] = s["avg_us"]
-    tr["kernel_source_hash"] = kernel_source_hash()
+    tr["kernel_source_hash"] = kernel_source_hash(kind)
     tr["config"] = config
     os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, f"traffic_{config}.json"), "w") as f:
+    with open(os.path.join(out_dir, tname), "w") as f:
         json.dump(tr, f, indent=1)
     lines = [f"# rocprofv3 summary: slora kernels, workload {config}", "",
              "Commands (run from the repository root on one MI355X, TMPDIR=/tmp):"]
@@ -133,14 +144,14 @@ def write_summary(config, trace_dir, fetch_dir, write_dir, command, flush_mib, o
         lines.append(f"  {k}: fetch {v['fetch_kib_raw']:.1f} KiB raw -> {v['fetch_bytes'] / 1e6:.2f} MB, "
                      f"write {v['write_kib_raw']:.1f} KiB raw -> {v['write_bytes'] / 1e6:.2f} MB "
                      f"({v['dispatches']} dispatches)")
-        if algorithmic_bytes and k == "fused_kernel":
+        if algorithmic_bytes and k == dom:
             tot = v["fetch_bytes"] + v["write_bytes"]
             lines.append(f"    traffic / algorithmic bytes = {tot / 1e6:.2f} / "
                          f"{algorithmic_bytes / 1e6:.2f} MB = {tot / algorithmic_bytes:.3f}")
     if event_us is not None:
         lines += ["", f"bench.py dispatch-event average for the same kernel: {event_us:.3f} us"]
     lines.append(f"kernel source hash: {tr['kernel_source_hash']}")
-    path = os.path.join(out_dir, f"fused_kernel_{config}.txt")
+    path = os.path.join(out_dir, f"{dom}_{config}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return path
@@ -157,9 +168,10 @@ def main():
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--algorithmic-bytes", type=float, default=None)
     ap.add_argument("--event-us", type=float, default=None)
+    ap.add_argument("--kind", choices=["fused", "forward"], default="fused")
     a = ap.parse_args()
     print(write_summary(a.config, a.trace, a.fetch, a.write, a.command, a.flush_mib, a.out,
-                        a.algorithmic_bytes, a.event_us))
+                        a.algorithmic_bytes, a.event_us, a.kind))
 
 
 if __name__ == "__main__":

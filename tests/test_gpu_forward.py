@@ -34,10 +34,10 @@ def _gpu():
     S.lib()
 
 
-def run_forward(w, projs=(0,), route="default", repeat=1):
+def run_forward(w, projs=(0,), route="default", repeat=1, tile=0):
     print(f"[gpu] forward {w.spec.name} seed={w.seed} route={route} T={w.T} "
-          f"h={w.spec.h_in}x{w.spec.h_out}", flush=True)
-    dw = DeviceWorkload(w, "cuda:0", tuning=ROUTES[route])
+          f"h={w.spec.h_in}x{w.spec.h_out} tile={tile}", flush=True)
+    dw = DeviceWorkload(w, "cuda:0", tuning={**ROUTES[route], S.SLORA_TUNE_FWD_TILE: tile})
     try:
         outs = []
         for p in projs:
@@ -98,6 +98,64 @@ def test_forward_small_shapes(name, route):
     (ys,), _ = run_forward(w, route=route)
     h_ref, sd_ref = oracle_forward(w)
     check(w, ys[0], h_ref, sd_ref, label=f"forward {name}/{route}")
+
+
+BIG = {
+    # 256 x 256 tiles: ragged last row block, segments across row blocks
+    "big_requests": dict(h_in=192, h_out=512, two_classes=True, n_adapters=7, rank_set=(1, 5, 33, 64),
+                         batch=("requests", 6, 40, 200)),
+    # many one-token segments in one 256-position row block
+    "big_decode": dict(h_in=128, h_out=256, two_classes=True, n_adapters=80, batch=("zipf", 250, 1.1)),
+    # high ranks, one token past a row block
+    "big_highrank": dict(h_in=256, h_out=256, n_adapters=4, fixed_ranks=(100, 256, 129, 31),
+                         batch=("uniform", 257)),
+}
+
+
+@pytest.mark.parametrize("name", list(BIG))
+def test_forward_big_tiles(name):
+    spec = small_spec(f"fw_{name}", scale_set=(0.5, 2.0, -1.5, 4.0), **BIG[name])
+    w = drop_some(generate(spec, 13), 6)
+    (ys,), info = run_forward(w, tile=256)
+    h_ref, sd_ref = oracle_forward(w)
+    check(w, ys[0], h_ref, sd_ref, label=f"forward {name}/256")
+
+
+def test_forward_big_tiles_integer_bit_exact_and_same_as_small():
+    spec = small_spec("fw_bigint", h_in=64, h_out=256, two_classes=True, n_adapters=6,
+                      rank_set=(1, 2, 4), values="ternary", scale=2.0, batch=("requests", 6, 20, 90))
+    w = drop_some(generate(spec, 4), 5)
+    h_ref, _ = oracle_forward(w)
+    assert np.abs(h_ref).max() < 2048
+    outs = {}
+    for tile in (128, 256):
+        (ys,), _ = run_forward(w, route="mfma", tile=tile)
+        np.testing.assert_array_equal(ys[0], round_to(h_ref, np.float16))
+        outs[tile] = ys[0]
+    np.testing.assert_array_equal(outs[128], outs[256])
+
+
+def test_forward_big_and_small_tiles_split():
+    """Automatic tiles on a batch large enough for one whole round of 256
+    big tiles: the leading 8192 positions go in 256 x 256 tiles, the rest in
+    128 x 128 tiles of a second launch; every position around the boundary,
+    the first and last rows and random ones are checked."""
+    spec = small_spec("fw_split", h_in=64, h_out=2048, two_classes=True, n_adapters=12,
+                      rank_set=(8, 16, 32, 64), batch=("requests", 40, 190, 230))
+    w = drop_some(generate(spec, 21), 11)
+    assert w.T > 8192 + 128 and -(-w.T // 256) * 8 >= 256
+    (ys,), _ = run_forward(w)
+    y = ys[0]
+    assert np.isfinite(y).all()
+    ids = w.ids
+    routed = np.flatnonzero(ids >= 0)
+    order = np.concatenate([routed[np.argsort(ids[routed], kind="stable")], np.flatnonzero(ids < 0)])
+    rng = np.random.default_rng(0)
+    pos = set(range(8192 - 300, min(w.T, 8192 + 300))) | {0, 1, w.T - 1}
+    pos |= set(rng.choice(w.T, 200, replace=False).tolist())
+    toks = sorted(int(order[p]) for p in pos)
+    h_ref, sd_ref = oracle_forward(w, tokens=toks)
+    check(w, y[toks], h_ref, sd_ref, tokens=toks, label="forward split 256/128")
 
 
 def test_forward_every_projection():

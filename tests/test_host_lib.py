@@ -387,12 +387,17 @@ def test_tuning_validation():
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_GEMV_EXPAND_ELEMS, 0)
         assert status_of(S.slora_pool_set_tuning, pool, 2, 300) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, 9, 1) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, 99, 1) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FUSED, 2) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_XCDS, 65) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_XCDS, 0) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_XCDS, 8)
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_TILE_ORDER, 3) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_TILE_ORDER, 1)
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_TILE, 64) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_GROUP, -1) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_FWD_TILE, 256)
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_FWD_GROUP, 4)
         S.slora_pool_set_tuning(pool, 2, 1024)
     finally:
         S.slora_pool_destroy(pool)
@@ -415,10 +420,11 @@ def test_unload_reload_lands_on_other_pages():
 def test_no_mfma_under_partial_exec_mask(tmp_path):
     """Every matrix instruction sits in wave-uniform control flow (see build.masked_mfma_lines)."""
     from rank_gemm_page_amd import build
-    asm = build.device_assembly(str(tmp_path))
-    with open(asm) as f:
-        assert sum(1 for line in f if line.strip().startswith("v_mfma")) > 0
-    assert build.masked_mfma_lines(asm) == []
+    for src in ("slora_kernels.hip", "slora_forward.hip"):
+        asm = build.device_assembly(str(tmp_path), src)
+        with open(asm) as f:
+            assert sum(1 for line in f if line.strip().startswith("v_mfma")) > 0, src
+        assert build.masked_mfma_lines(asm) == [], src
 
 
 @pytest.mark.parametrize("kw", [dict(dtype="f32", rank_set=(4, 8)),
