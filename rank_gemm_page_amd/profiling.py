@@ -25,6 +25,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 from collections import defaultdict
 
@@ -56,8 +57,10 @@ def _one(pattern: str) -> str:
 
 
 def short_name(name: str) -> str:
-    for key in ("fused_kernel", "shrink_kernel", "combine_kernel", "expand_kernel", "scatter_pages_kernel",
-                "forward_kernel"):
+    if "forward_kernel" in name:       # one entry per tile shape
+        m = re.search(r"forward_kernel<(\d+), ?(\d+)>", name) or re.search(r"forward_kernelILi(\d+)ELi(\d+)E", name)
+        return f"forward_kernel<{m.group(1)},{m.group(2)}>" if m else "forward_kernel"
+    for key in ("fused_kernel", "shrink_kernel", "combine_kernel", "expand_kernel", "scatter_pages_kernel"):
         if key in name:
             return key
     return name.split("(")[0][:60]
@@ -144,10 +147,12 @@ def write_summary(config, trace_dir, fetch_dir, write_dir, command, flush_mib, o
         lines.append(f"  {k}: fetch {v['fetch_kib_raw']:.1f} KiB raw -> {v['fetch_bytes'] / 1e6:.2f} MB, "
                      f"write {v['write_kib_raw']:.1f} KiB raw -> {v['write_bytes'] / 1e6:.2f} MB "
                      f"({v['dispatches']} dispatches)")
-        if algorithmic_bytes and k == dom:
-            tot = v["fetch_bytes"] + v["write_bytes"]
-            lines.append(f"    traffic / algorithmic bytes = {tot / 1e6:.2f} / "
-                         f"{algorithmic_bytes / 1e6:.2f} MB = {tot / algorithmic_bytes:.3f}")
+    mine = [v for k, v in tr["kernels"].items() if k.startswith(dom)]
+    if algorithmic_bytes and mine:
+        # per call: one dispatch of each of the measured kernel's launches
+        tot = sum(v["fetch_bytes"] + v["write_bytes"] for v in mine)
+        lines.append(f"  {dom} per call: traffic / algorithmic bytes = {tot / 1e6:.2f} / "
+                     f"{algorithmic_bytes / 1e6:.2f} MB = {tot / algorithmic_bytes:.3f}")
     if event_us is not None:
         lines += ["", f"bench.py dispatch-event average for the same kernel: {event_us:.3f} us"]
     lines.append(f"kernel source hash: {tr['kernel_source_hash']}")
