@@ -48,19 +48,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def load_traffic(config, dominant):
+def load_traffic(config, dominant, kind="fused"):
     """(HBM bytes per launch, rocprofv3 kernel-trace average us) from the committed
-    rocprofv3 summary of this workload, if it was taken of the current kernels."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    rocprofv3 summary of this workload, if it was taken of the current kernels.
+    kind "forward": the base-plus-delta launches of one call, summed."""
+    name = f"traffic_{config}.json" if kind == "fused" else f"traffic_{kind}_{config}.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         t = json.load(f)
     from rank_gemm_page_amd.profiling import kernel_source_hash
-    if t.get("kernel_source_hash") != kernel_source_hash() or dominant not in t.get("kernels", {}):
+    if t.get("kernel_source_hash") != kernel_source_hash(kind):
         return None, None
-    k = t["kernels"][dominant]
-    return k["fetch_bytes"] + k["write_bytes"], k.get("trace_avg_us")
+    ks = [v for k, v in t.get("kernels", {}).items() if k == dominant or (kind != "fused" and k.startswith(dominant))]
+    if not ks:
+        return None, None
+    avg = [k.get("trace_avg_us") for k in ks]
+    return (sum(k["fetch_bytes"] + k["write_bytes"] for k in ks),
+            sum(avg) if all(a is not None for a in avg) else None)
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -338,7 +344,17 @@ def measure_forward(dw, w, steps, flush, stream):
     base_flops = 2.0 * w.T * spec.h_in * spec.h_out
     flops = n_proj * (base_flops + sf + ef)
     e = 2 if spec.dtype == "f16" else 4
-    return {"ms_per_step": round(fused_ms, 5), "unfused_ms_per_step": round(unfused_ms, 5),
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    # algorithmic bytes of one call's base-plus-delta launches: x rows, W, the
+    # batch's B pages, y written once
+    fwd_bytes = e * (w.T * spec.h_in + spec.h_in * spec.h_out + int(dw.info["sum_rank"]) * spec.h_out
+                     + w.T * spec.h_out)
+    traffic, prof_us = load_traffic(spec.name, "forward_kernel", kind="forward")
+    return {"roofline": {"bound": "mfma", "kernel": "shrink + forward_kernel", "achieved": round(tflops, 1),
+                         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+                         "algorithmic_bytes": fwd_bytes, "profiled_forward_kernels_us": prof_us},
+            "ms_per_step": round(fused_ms, 5), "unfused_ms_per_step": round(unfused_ms, 5),
             "speedup_vs_unfused": round(unfused_ms / fused_ms, 3),
             "kernels_us_per_projection": round(kern_ms * 1e3 / n_proj, 3),
             "TFLOPs": round(flops / (kern_ms * 1e-3) / 1e12, 1),
