@@ -14,8 +14,10 @@ namespace slora {
 //
 // One workgroup per tile of BM sorted positions x BN columns, 2 x (BN / 64)
 // waves, each BM / 2 positions x 64 columns (blocks of
-// v_mfma_f32_16x16x32_f16).  Two shapes: 128 x 128 (four waves of 64 x 64)
-// and 256 x 256 (eight waves of 128 x 64).  The larger tile reads x and W
+// v_mfma_f32_16x16x32_f16).  Three shapes: 128 x 128 (four waves of
+// 64 x 64), 256 x 256 (eight waves of 128 x 64) and 128 x 256 (eight waves
+// of 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles).
+// The larger tiles read x and W
 // half as often per flop: x is read once per column block and W once per row
 // block, and at 128 x 128 that traffic, not the matrix cores, bounds the
 // kernel on large batches.  Per step the tile stages in LDS (two buffers, one
@@ -46,7 +48,10 @@ struct FwdTile {
   static constexpr int StageDw = ADw + NSL * SliceDw;
   static constexpr int EpiPitchDw = BN / 2 + 4;      // one fp16 output row, padded
   static constexpr int LdsDw = 2 * StageDw + 5 * BM;
-  static_assert(BM == NT / 2, "two threads per position in the prologue and the LoRA staging");
+  static constexpr int TPR = NT / BM;                // threads per position (prologue, LoRA staging)
+  static constexpr int KL = kFwdLoraRows / TPR;      // rank rows of a LoRA step per thread
+  static constexpr int XL = BM * 8 / NT;             // 16-byte x loads per thread per step
+  static_assert(TPR == 2 || TPR == 4, "two or four threads per position");
   static_assert(128 * EpiPitchDw <= 2 * StageDw, "an epilogue pass of 128 rows reuses the stage buffers");
   static_assert(RW <= 128 && 128 % RW == 0, "epilogue passes hold whole waves");
   static_assert(kShrinkKc == kFwdBK && kFwdLoraRows == 32, "stage layouts");
@@ -81,10 +86,10 @@ void forward_kernel(ForwardLaunch F) {
 
   // Per position of the tile: batch index, segment (-1: no adapter), v row
   // offset, s 2^-e and 2^e.  Positions past the batch take the last token's
-  // row (loaded, never stored).  Two threads per position scan its v row for
-  // the largest |v|, eight independent loads at a time.
+  // row (loaded, never stored).  TPR threads per position scan its v row for
+  // the largest |v|, eight independent loads each at a time.
   {
-    const int row = tid >> 1, half = tid & 1;
+    const int row = tid / C::TPR, part = tid % C::TPR;
     const int p = r0 + row;
     int seg = -1, voff = 0, rank = 0;
     float scale = 0.f;
@@ -95,23 +100,25 @@ void forward_kernel(ForwardLaunch F) {
       voff = F.seg_v_off[seg] + (p - F.seg_start[seg]) * rank;
     }
     float amax = 0.f;
-    for (int j0 = half; j0 < rank; j0 += 16) {
+    for (int j0 = part; j0 < rank; j0 += 8 * C::TPR) {
       float t[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int j = j0 + 2 * u;
+        const int j = j0 + C::TPR * u;
         t[u] = F.v[j < rank ? voff + j : voff];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) amax = fmaxf(amax, fabsf(t[u]));
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64)) * fabsf(scale);
+#pragma unroll
+    for (int o = 1; o < C::TPR; o *= 2) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax *= fabsf(scale);
     int ex = 0;
     if (amax > 0.f) {
       (void)frexpf(amax, &ex);
       ex = max(ex - 15, -100);
     }
-    if (half == 0) {
+    if (part == 0) {
       tok_l[row] = F.order[min(p, F.n_tokens - 1)];
       seg_l[row] = seg;
       voff_l[row] = voff;
@@ -121,12 +128,12 @@ void forward_kernel(ForwardLaunch F) {
   }
   __syncthreads();
 
-  // Thread maps.  LoRA staging: A row ar = tid / 2, rank rows 16ah .. 16ah+15
-  // (ah = tid % 2).  B rows (W or pages): rows brow + 16h, one 16-byte chunk
+  // Thread maps.  LoRA staging: A row ar = tid / TPR, rank rows
+  // KL ah .. KL ah + KL - 1 (ah = tid % TPR).  B rows (W or pages): rows brow + 16h, one 16-byte chunk
   // bch of the BN columns (slice bch / 16).  x rows: chunk xch of rows
   // xrow + (NT / 8) i, so one wave instruction reads 8 whole 128-byte row
   // segments.
-  const int ar = tid >> 1, ah = tid & 1;
+  const int ar = tid / C::TPR, ah = tid % C::TPR;
   const int brow = tid / C::CH, bch = tid % C::CH;
   const int bsl = bch >> 4, bquad = 2 * (bch & 15);
   const int xrow = tid >> 3, xch = tid & 7;
@@ -164,18 +171,18 @@ void forward_kernel(ForwardLaunch F) {
   };
 
   // x W steps: every load unconditional (a step past the end reloads the last).
-  auto w_load = [&](int s, uint4 (&aq)[4], uint4 (&bq)[4]) {
+  auto w_load = [&](int s, uint4 (&aq)[C::XL], uint4 (&bq)[4]) {
     s = s < n_w ? s : n_w - 1;
     const int k0 = s * kFwdBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::XL; ++i)
       aq[i] = ld16(xb + (int64_t)tok_l[xrow + (C::NT / 8) * i] * F.h_in + k0 + 8 * xch);
 #pragma unroll
     for (int h = 0; h < 4; ++h) bq[h] = ld16(wb + (int64_t)(k0 + brow + 16 * h) * F.h_out + c0 + 8 * bch);
   };
-  auto w_store = [&](uint32_t* S, const uint4 (&aq)[4], const uint4 (&bq)[4]) {
+  auto w_store = [&](uint32_t* S, const uint4 (&aq)[C::XL], const uint4 (&bq)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(S + chunk_dw(xrow + (C::NT / 8) * i, xch)) = aq[i];
+    for (int i = 0; i < C::XL; ++i) *reinterpret_cast<uint4*>(S + chunk_dw(xrow + (C::NT / 8) * i, xch)) = aq[i];
     uint32_t* B = S + C::ADw + bsl * C::SliceDw;
 #pragma unroll
     for (int h = 0; h < 4; ++h) *reinterpret_cast<uint4*>(B + quad_dw(brow + 16 * h, bquad)) = bq[h];
@@ -197,42 +204,43 @@ void forward_kernel(ForwardLaunch F) {
       t.j0 = hd.y;
       t.rank = hd.z;
     };
-    auto lora_load = [&](const Tab& t, uint4 (&lb)[2], float (&vv)[16]) {
+    auto lora_load = [&](const Tab& t, uint4 (&lb)[2], float (&vv)[C::KL]) {
       const int64_t col = (int64_t)(c0 + 8 * bch) * 2;
       lb[0] = ld16(F.base_b + (int64_t)t.id0 * F.page_bytes_b + col);
       lb[1] = ld16(F.base_b + (int64_t)t.id1 * F.page_bytes_b + col);
       const bool in = seg_l[ar] == t.seg;
       const int voff = voff_l[ar];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = t.j0 + 16 * ah + i;
+      for (int i = 0; i < C::KL; ++i) {
+        const int j = t.j0 + C::KL * ah + i;
         vv[i] = F.v[(in && j < t.rank) ? voff + j : 0];
       }
     };
-    auto lora_store = [&](uint32_t* S, const Tab& t, const uint4 (&lb)[2], const float (&vv)[16]) {
+    auto lora_store = [&](uint32_t* S, const Tab& t, const uint4 (&lb)[2], const float (&vv)[C::KL]) {
       uint32_t* B = S + C::ADw + bsl * C::SliceDw;
       *reinterpret_cast<uint4*>(B + quad_dw(brow, bquad)) = lb[0];
       *reinterpret_cast<uint4*>(B + quad_dw(16 + brow, bquad)) = lb[1];
       const bool in = seg_l[ar] == t.seg;
       const float mul = mul_l[ar];
-      half8 hi[2], lo[2];
+      constexpr int NC = C::KL / 8;           // 16-byte chunks of this thread's rank rows
+      half8 hi[NC], lo[NC];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = t.j0 + 16 * ah + i;
+      for (int i = 0; i < C::KL; ++i) {
+        const int j = t.j0 + C::KL * ah + i;
         const float f = (in && j < t.rank) ? vv[i] * mul : 0.f;
         const _Float16 hv = (_Float16)f;
         hi[i >> 3][i & 7] = hv;
         lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
       }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 2 * ah + c)) = __builtin_bit_cast(uint4, hi[c]);
-        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + 2 * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
+      for (int c = 0; c < NC; ++c) {
+        *reinterpret_cast<uint4*>(S + chunk_dw(ar, NC * ah + c)) = __builtin_bit_cast(uint4, hi[c]);
+        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + NC * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
       }
     };
     Tab tc, tn;
     uint4 lb[2];
-    float vv[16];
+    float vv[C::KL];
     tab_load(0, tc);
     lora_load(tc, lb, vv);
     tab_load(1, tn);
@@ -259,7 +267,7 @@ void forward_kernel(ForwardLaunch F) {
 
   // The first two x W steps (issued after the LoRA steps, whose registers
   // they would otherwise compete with).
-  uint4 wa0[4], wb0[4], wa1[4], wb1[4];
+  uint4 wa0[C::XL], wb0[4], wa1[C::XL], wb1[4];
   w_load(0, wa0, wb0);
   w_load(1, wa1, wb1);
 
@@ -318,6 +326,9 @@ hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t
   if (F.bm == 256 && F.bn == 256) {
     k = reinterpret_cast<const void*>(&forward_kernel<256, 256>);
     nt = FwdTile<256, 256>::NT;
+  } else if (F.bm == 128 && F.bn == 256) {
+    k = reinterpret_cast<const void*>(&forward_kernel<128, 256>);
+    nt = FwdTile<128, 256>::NT;
   } else if (F.bm == 128 && F.bn == 128) {
     k = reinterpret_cast<const void*>(&forward_kernel<128, 128>);
     nt = FwdTile<128, 128>::NT;

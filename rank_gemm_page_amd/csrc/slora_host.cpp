@@ -586,10 +586,10 @@ void build_tiles(slora_segments* s) {
   // per flop as a 128 x 128 one but holds a whole CU (one workgroup per CU,
   // 256 CUs), so big tiles are used only in whole rounds of 256: the leading
   // row blocks that fill complete rounds take big tiles, the remaining
-  // positions 128 x 128 tiles, which spread a partial round over the chip
-  // (for the 7B prefill batch: 512 big tiles and 320 small ones instead of
-  // 592 big tiles in three rounds, the last a third full).  Batches too small
-  // for one round use small tiles only.  Row block rb holds sorted positions
+  // positions 128 x 256 tiles (half the work of a big tile), which spread a
+  // partial round over the chip (for the 7B prefill batch: 512 big tiles and
+  // 160 half tiles instead of 592 big tiles in three rounds, the last a third
+  // full).  Batches too small for one round use 128 x 128 tiles only.  Row block rb holds sorted positions
   // start(rb) .. +tile; its LoRA stages are, for every segment that owns one
   // of those positions, one stage per kFwdLoraRows rank rows.
   const int32_t T = s->n_tokens, routed = (int32_t)s->perm.size();
@@ -1351,7 +1351,10 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
   for (int part = 0; part < 2 && e == hipSuccess; ++part) {
     const int32_t n_rb = part == 0 ? s->fw_n_rb_big : n_small;
     if (n_rb == 0) continue;
-    F.bm = F.bn = part == 0 ? kFwdBig : kFwdBM;
+    // the remainder of a batch whose bulk takes big tiles: 128 positions x
+    // 256 columns (half a big tile's work, one round over the CUs)
+    F.bm = part == 0 ? kFwdBig : kFwdBM;
+    F.bn = (part == 0 || s->fw_n_rb_big > 0) ? kFwdBig : kFwdBN;
     F.pos0 = part == 0 ? 0 : s->fw_big_rows;
     F.rb_info = m + s->fw_rb_info_off + (part == 0 ? 0 : 2 * (int64_t)s->fw_n_rb_big);
     F.n_rb = n_rb;

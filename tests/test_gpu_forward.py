@@ -135,13 +135,16 @@ def test_forward_big_tiles_integer_bit_exact_and_same_as_small():
     np.testing.assert_array_equal(outs[128], outs[256])
 
 
-def test_forward_big_and_small_tiles_split():
+@pytest.mark.parametrize("batch,n_adapters", [(("requests", 40, 190, 230), 12),
+                                               (("mixed", 32, 256, 400), 60)])
+def test_forward_big_and_small_tiles_split(batch, n_adapters):
     """Automatic tiles on a batch large enough for one whole round of 256
     big tiles: the leading 8192 positions go in 256 x 256 tiles, the rest in
-    128 x 128 tiles of a second launch; every position around the boundary,
-    the first and last rows and random ones are checked."""
-    spec = small_spec("fw_split", h_in=64, h_out=2048, two_classes=True, n_adapters=12,
-                      rank_set=(8, 16, 32, 64), batch=("requests", 40, 190, 230))
+    128 x 256 tiles of a second launch (with the mixed batch, many one-token
+    segments there); every position around the boundary, the first and last
+    rows and random ones are checked."""
+    spec = small_spec("fw_split", h_in=64, h_out=2048, two_classes=True, n_adapters=n_adapters,
+                      rank_set=(8, 16, 32, 64), batch=batch)
     w = drop_some(generate(spec, 21), 11)
     assert w.T > 8192 + 128 and -(-w.T // 256) * 8 >= 256
     (ys,), _ = run_forward(w)
