@@ -52,6 +52,10 @@ struct FwdTile {
   static constexpr int KL = kFwdLoraRows / TPR;      // rank rows of a LoRA step per thread
   static constexpr int XL = BM * 8 / NT;             // 16-byte x loads per thread per step
   static_assert(TPR == 2 || TPR == 4, "two or four threads per position");
+  // LoRA steps with page rows two steps ahead (three register sets of stage
+  // tables, two of rows and v) where the registers allow; the 256 x 256 tile
+  // keeps one step ahead.
+  static constexpr bool DEEP = BM * BN <= 128 * 256;
   static_assert(128 * EpiPitchDw <= 2 * StageDw, "an epilogue pass of 128 rows reuses the stage buffers");
   static_assert(RW <= 128 && 128 % RW == 0, "epilogue passes hold whole waves");
   static_assert(kShrinkKc == kFwdBK && kFwdLoraRows == 32, "stage layouts");
@@ -238,21 +242,57 @@ void forward_kernel(ForwardLaunch F) {
         *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + NC * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
       }
     };
-    Tab tc, tn;
-    uint4 lb[2];
-    float vv[C::KL];
-    tab_load(0, tc);
-    lora_load(tc, lb, vv);
-    tab_load(1, tn);
-    for (int q = 0; q < n_lora; ++q) {
-      uint32_t* S = lds + (q & 1) * C::StageDw;
-      lora_store(S, tc, lb, vv);
-      lds_barrier();
-      tc = tn;
+    if constexpr (C::DEEP) {
+      // Step q: store its rows, then issue the table of step q + 3 before
+      // waiting for that of step q + 2 (issued a step earlier, ahead of step
+      // q + 1's rows, so the wait does not cover them), then issue step
+      // q + 2's rows into the freed register set.  Unrolled by two so that
+      // the register sets and LDS buffers are static.
+      Tab t0, t1, tn, tx;
+      uint4 lb0[2], lb1[2];
+      float vv0[C::KL], vv1[C::KL];
+      tab_load(0, t0);
+      tab_load(1, t1);
+      tab_load(2, tn);
+      lora_load(t0, lb0, vv0);
+      lora_load(t1, lb1, vv1);
+      for (int q = 0;; q += 2) {
+        lora_store(lds, t0, lb0, vv0);
+        lds_barrier();
+        tab_load(q + 3, tx);
+        lora_load(tn, lb0, vv0);
+        t0 = tn;
+        tn = tx;
+        mfma_step(lds, 0, 0);
+        mfma_step(lds, 1, 0);
+        if (q + 1 >= n_lora) break;
+        lora_store(lds + C::StageDw, t1, lb1, vv1);
+        lds_barrier();
+        tab_load(q + 4, tx);
+        lora_load(tn, lb1, vv1);
+        t1 = tn;
+        tn = tx;
+        mfma_step(lds + C::StageDw, 0, 0);
+        mfma_step(lds + C::StageDw, 1, 0);
+        if (q + 2 >= n_lora) break;
+      }
+    } else {
+      Tab tc, tn;
+      uint4 lb[2];
+      float vv[C::KL];
+      tab_load(0, tc);
       lora_load(tc, lb, vv);
-      tab_load(q + 2, tn);
-      mfma_step(S, 0, 0);
-      mfma_step(S, 1, 0);
+      tab_load(1, tn);
+      for (int q = 0; q < n_lora; ++q) {
+        uint32_t* S = lds + (q & 1) * C::StageDw;
+        lora_store(S, tc, lb, vv);
+        lds_barrier();
+        tc = tn;
+        lora_load(tc, lb, vv);
+        tab_load(q + 2, tn);
+        mfma_step(S, 0, 0);
+        mfma_step(S, 1, 0);
+      }
     }
     lds_barrier();   // the x W steps reuse both buffers
 #pragma unroll
