@@ -161,6 +161,35 @@ def test_forward_big_and_small_tiles_split(batch, n_adapters):
     check(w, y[toks], h_ref, sd_ref, tokens=toks, label="forward split 256/128")
 
 
+# The library's extremes, one dimension at a time (a 16384 x 65536 W would be
+# 2 GiB, and its fp64 copy for the oracle 8 GiB on the host): the longest K
+# loop (h_in 16384, 256 x W steps per tile) and the widest output (h_out
+# 65536: 512 column tiles of 128 or 256 of 256, 128 KB B pages), with rank
+# 256 adapters (eight LoRA steps a segment) and a second projection, in both
+# tile sizes.
+MAX_FWD = [
+    small_spec("fw_max_k", h_in=16384, h_out=512, two_classes=True, n_adapters=6, n_proj=2,
+               proj_x=(0, 0), rank_set=(1, 17, 128, 256), batch=("zipf", 150, 1.0)),
+    small_spec("fw_max_n", h_in=64, h_out=65536, two_classes=True, n_adapters=6, n_proj=2,
+               proj_x=(0, 0), rank_set=(1, 17, 128, 256), batch=("zipf", 150, 1.0)),
+]
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("spec", MAX_FWD, ids=lambda s: s.name)
+def test_forward_maximum_sizes(spec, tile):
+    w = generate(spec, 4)
+    assert int(w.ranks.max()) == 256
+    ys, _ = run_forward(w, projs=(0, 1), tile=tile)
+    st = build_from_workload(w)
+    toks = sample_positions(w, 20)
+    for p, runs in zip((0, 1), ys):
+        assert np.isfinite(runs[0]).all()
+        h_ref, sd_ref = oracle_forward(w, p, tokens=toks, state=st)
+        check(w, runs[0][toks], h_ref, sd_ref, proj=p, tokens=toks, label=f"{spec.name}/{tile}/p{p}")
+    w.drop_weight_cache()
+
+
 def test_forward_every_projection():
     spec = small_spec("fw_proj", h_in=128, h_out=128, n_proj=3, proj_x=(0, 1, 2), n_adapters=5,
                       batch=("requests", 3, 30, 110))
