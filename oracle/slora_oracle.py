@@ -11,7 +11,8 @@ What it computes, with its sources (S-LoRA pages):
     "What this paper explains" and "How to read the paper" item 2; "The
     mechanism", "Separate base and delta").
   * Per-token delta with a scaling factor: each token of the batch names its
-    own adapter and gets (x[t] @ A @ B) * scaling added to its base output
+    own adapter and gets its product with A and B, times the adapter's
+    scaling factor, added to its base output
     (blog page, section 2 pseudocode, "Batched S-LoRA Vector Matrix Addition").
   * Adapter factors live as non-contiguous pages of one pool shared with KV
     blocks, found through a block table (summary page, "Unified Paging";
