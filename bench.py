@@ -88,17 +88,31 @@ def cpu_baseline(w, budget_s=10.0):
     # repeat until about budget_s of CPU work is done.
     n = int(min(w.T, max(1, budget_s / per_tok)))
     toks = np.linspace(0, w.T - 1, n).astype(int).tolist()
-    passes, elapsed = 0, 0.0
-    while elapsed < budget_s or passes < 2:
-        t = time.perf_counter()
-        for p in range(n_proj):
-            workload_delta(st, w, proj=p, tokens=toks)
-        elapsed += time.perf_counter() - t
-        passes += 1
-    return {"value": passes * n / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {w.T} tokens of the same batch through all {n_proj} projection(s), "
-                      f"{passes} passes in {elapsed:.1f} s, fp64 NumPy, page-table walk per token",
-            "host_cpu_count": os.cpu_count()}
+
+    def rate(budget):
+        passes, elapsed = 0, 0.0
+        while elapsed < budget or passes < 2:
+            t = time.perf_counter()
+            for p in range(n_proj):
+                workload_delta(st, w, proj=p, tokens=toks)
+            elapsed += time.perf_counter() - t
+            passes += 1
+        return passes, elapsed
+
+    passes, elapsed = rate(budget_s)
+    out = {"value": passes * n / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} of {w.T} tokens of the same batch through all {n_proj} projection(s), "
+                     f"{passes} passes in {elapsed:.1f} s, fp64 NumPy, page-table walk per token",
+           "host_cpu_count": os.cpu_count()}
+    # the same sample with the BLAS pool held to one thread, a shorter run
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            p1, e1 = rate(budget_s / 3)
+        out["value_1_thread"] = p1 * n / e1
+    except Exception:
+        out["value_1_thread"] = None
+    return out
 
 
 class BmmPath:
