@@ -61,7 +61,9 @@ struct FwdTile {
   static_assert(kShrinkKc == kFwdBK && kFwdLoraRows == 32, "stage layouts");
 };
 
-template <int BM, int BN>
+// V4: every rank of the batch is a multiple of 4, so v rows start on 16-byte
+// boundaries and a LoRA step reads a thread's v values four at a time.
+template <int BM, int BN, bool V4>
 __global__ __launch_bounds__(128 * (BN / 64)) __attribute__((amdgpu_waves_per_eu(2)))
 void forward_kernel(ForwardLaunch F) {
   using C = FwdTile<BM, BN>;
@@ -209,15 +211,33 @@ void forward_kernel(ForwardLaunch F) {
       t.rank = hd.z;
     };
     auto lora_load = [&](const Tab& t, uint4 (&lb)[2], float (&vv)[C::KL]) {
+      // Page ids are never negative: zero-extending them (unlike a sign
+      // extension) needs no instruction on the loaded value, so the compiler
+      // does not place one right behind the id loads of a later step, where
+      // its wait would drain every load in flight.
       const int64_t col = (int64_t)(c0 + 8 * bch) * 2;
-      lb[0] = ld16(F.base_b + (int64_t)t.id0 * F.page_bytes_b + col);
-      lb[1] = ld16(F.base_b + (int64_t)t.id1 * F.page_bytes_b + col);
+      lb[0] = ld16(F.base_b + (uint64_t)(uint32_t)t.id0 * (uint64_t)F.page_bytes_b + col);
+      lb[1] = ld16(F.base_b + (uint64_t)(uint32_t)t.id1 * (uint64_t)F.page_bytes_b + col);
       const bool in = seg_l[ar] == t.seg;
       const int voff = voff_l[ar];
+      if constexpr (V4) {
+        // a chunk of 4 values lies wholly inside the row or wholly past its
+        // rank (rank % 4 == 0); one past it reads v[0 .. 3] instead
 #pragma unroll
-      for (int i = 0; i < C::KL; ++i) {
-        const int j = t.j0 + C::KL * ah + i;
-        vv[i] = F.v[(in && j < t.rank) ? voff + j : 0];
+        for (int c = 0; c < C::KL / 4; ++c) {
+          const int j = t.j0 + C::KL * ah + 4 * c;
+          const uint4 q = ld16(F.v + ((in && j < t.rank) ? voff + j : 0));
+          vv[4 * c] = __uint_as_float(q.x);
+          vv[4 * c + 1] = __uint_as_float(q.y);
+          vv[4 * c + 2] = __uint_as_float(q.z);
+          vv[4 * c + 3] = __uint_as_float(q.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::KL; ++i) {
+          const int j = t.j0 + C::KL * ah + i;
+          vv[i] = F.v[(in && j < t.rank) ? voff + j : 0];
+        }
       }
     };
     auto lora_store = [&](uint32_t* S, const Tab& t, const uint4 (&lb)[2], const float (&vv)[C::KL]) {
@@ -260,6 +280,7 @@ void forward_kernel(ForwardLaunch F) {
         lora_store(lds, t0, lb0, vv0);
         lds_barrier();
         tab_load(q + 3, tx);
+        __builtin_amdgcn_sched_barrier(0);   // keep the table loads ahead of the rows
         lora_load(tn, lb0, vv0);
         t0 = tn;
         tn = tx;
@@ -269,6 +290,7 @@ void forward_kernel(ForwardLaunch F) {
         lora_store(lds + C::StageDw, t1, lb1, vv1);
         lds_barrier();
         tab_load(q + 4, tx);
+        __builtin_amdgcn_sched_barrier(0);
         lora_load(tn, lb1, vv1);
         t1 = tn;
         tn = tx;
@@ -364,13 +386,16 @@ hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t
   const void* k;
   int nt;
   if (F.bm == 256 && F.bn == 256) {
-    k = reinterpret_cast<const void*>(&forward_kernel<256, 256>);
+    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<256, 256, true>)
+             : reinterpret_cast<const void*>(&forward_kernel<256, 256, false>);
     nt = FwdTile<256, 256>::NT;
   } else if (F.bm == 128 && F.bn == 256) {
-    k = reinterpret_cast<const void*>(&forward_kernel<128, 256>);
+    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 256, true>)
+             : reinterpret_cast<const void*>(&forward_kernel<128, 256, false>);
     nt = FwdTile<128, 256>::NT;
   } else if (F.bm == 128 && F.bn == 128) {
-    k = reinterpret_cast<const void*>(&forward_kernel<128, 128>);
+    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 128, true>)
+             : reinterpret_cast<const void*>(&forward_kernel<128, 128, false>);
     nt = FwdTile<128, 128>::NT;
   } else {
     return hipErrorInvalidValue;

@@ -1344,6 +1344,7 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
   F.seg_scale = m + s->fw_seg_scale_off;
   F.seg_v_off = m + s->fw_seg_v_off;
   F.stages = m + s->fw_stages_off + (int64_t)proj * s->fw_n_stages * kFwdStageWords;
+  F.v4 = std::all_of(s->seg_rank.begin(), s->seg_rank.end(), [](int32_t r) { return r % 4 == 0; }) ? 1 : 0;
   // Big tiles over the leading positions, then small tiles over the rest; the
   // start event goes with the first launch, the stop event with the last.
   const int32_t n_small = s->fw_n_rb - s->fw_n_rb_big;

@@ -145,6 +145,7 @@ struct ForwardLaunch {
   int32_t group_m;           // tile order: groups of group_m row blocks, column-major inside a group
   int32_t bm, bn;            // tile shape: 128 x 128 or 256 x 256
   int32_t pos0;              // first sorted position of row block 0 of this launch
+  int32_t v4;                // every segment's rank is a multiple of 4 (v rows 16-byte aligned)
 };
 
 // Launch the base-plus-delta kernel (one launch, n_tiles workgroups placed
