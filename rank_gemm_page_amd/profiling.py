@@ -58,7 +58,7 @@ def _one(pattern: str) -> str:
 
 def short_name(name: str) -> str:
     if "forward_kernel" in name:       # one entry per tile shape
-        m = re.search(r"forward_kernel<(\d+), ?(\d+)>", name) or re.search(r"forward_kernelILi(\d+)ELi(\d+)E", name)
+        m = re.search(r"forward_kernel<(\d+), ?(\d+)", name) or re.search(r"forward_kernelILi(\d+)ELi(\d+)E", name)
         return f"forward_kernel<{m.group(1)},{m.group(2)}>" if m else "forward_kernel"
     for key in ("fused_kernel", "shrink_kernel", "combine_kernel", "expand_kernel", "scatter_pages_kernel"):
         if key in name:
