@@ -198,18 +198,26 @@ void forward_kernel(ForwardLaunch F) {
   if (n_lora > 0) {
     const int32_t* tab = F.stages + (int64_t)uni(F.rb_info[2 * rb]) * kFwdStageWords;
     // Stage table entry of LoRA step q (clamped): this thread's two B page
-    // ids and the step's segment, first rank row and rank.
-    struct Tab { int id0, id1, seg, j0, rank; };
+    // ids and one word of the step's header (segment, first rank row, rank
+    // in lanes 0, 1, 2 of each wave).  The header is read with vector loads
+    // on purpose: as a scalar load it would share the counter of the LDS
+    // reads, and scalar loads complete out of order, so every LDS wait of the
+    // step (the MFMA operands included) would wait for it as well.
+    struct Tab { int id0, id1, hw; };
+    const int hlane = lane & 3;
     auto tab_load = [&](int q, Tab& t) {
       q = q < n_lora ? q : n_lora - 1;
       const int32_t* e = tab + (int64_t)q * kFwdStageWords;
       t.id0 = e[brow];
       t.id1 = e[16 + brow];
-      const int4 hd = *reinterpret_cast<const int4*>(e + FWS_SEG);
-      t.seg = hd.x;
-      t.j0 = hd.y;
-      t.rank = hd.z;
+      t.hw = e[FWS_SEG + hlane];
     };
+    auto t_seg = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw, 0); };
+    auto t_j0 = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw, 1); };
+    auto t_rank = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw, 2); };
+    // this thread's position: fixed for the tile, kept in registers
+    const int my_seg = seg_l[ar], my_voff = voff_l[ar];
+    const float my_mul = mul_l[ar];
     auto lora_load = [&](const Tab& t, uint4 (&lb)[2], float (&vv)[C::KL]) {
       // Page ids are never negative: zero-extending them (unlike a sign
       // extension) needs no instruction on the loaded value, so the compiler
@@ -218,15 +226,16 @@ void forward_kernel(ForwardLaunch F) {
       const int64_t col = (int64_t)(c0 + 8 * bch) * 2;
       lb[0] = ld16(F.base_b + (uint64_t)(uint32_t)t.id0 * (uint64_t)F.page_bytes_b + col);
       lb[1] = ld16(F.base_b + (uint64_t)(uint32_t)t.id1 * (uint64_t)F.page_bytes_b + col);
-      const bool in = seg_l[ar] == t.seg;
-      const int voff = voff_l[ar];
+      const int seg = t_seg(t), j0 = t_j0(t), rank = t_rank(t);
+      const bool in = my_seg == seg;
+      const int voff = my_voff;
       if constexpr (V4) {
         // a chunk of 4 values lies wholly inside the row or wholly past its
         // rank (rank % 4 == 0); one past it reads v[0 .. 3] instead
 #pragma unroll
         for (int c = 0; c < C::KL / 4; ++c) {
-          const int j = t.j0 + C::KL * ah + 4 * c;
-          const uint4 q = ld16(F.v + ((in && j < t.rank) ? voff + j : 0));
+          const int j = j0 + C::KL * ah + 4 * c;
+          const uint4 q = ld16(F.v + ((in && j < rank) ? voff + j : 0));
           vv[4 * c] = __uint_as_float(q.x);
           vv[4 * c + 1] = __uint_as_float(q.y);
           vv[4 * c + 2] = __uint_as_float(q.z);
@@ -235,8 +244,8 @@ void forward_kernel(ForwardLaunch F) {
       } else {
 #pragma unroll
         for (int i = 0; i < C::KL; ++i) {
-          const int j = t.j0 + C::KL * ah + i;
-          vv[i] = F.v[(in && j < t.rank) ? voff + j : 0];
+          const int j = j0 + C::KL * ah + i;
+          vv[i] = F.v[(in && j < rank) ? voff + j : 0];
         }
       }
     };
@@ -244,14 +253,15 @@ void forward_kernel(ForwardLaunch F) {
       uint32_t* B = S + C::ADw + bsl * C::SliceDw;
       *reinterpret_cast<uint4*>(B + quad_dw(brow, bquad)) = lb[0];
       *reinterpret_cast<uint4*>(B + quad_dw(16 + brow, bquad)) = lb[1];
-      const bool in = seg_l[ar] == t.seg;
-      const float mul = mul_l[ar];
+      const int seg = t_seg(t), j0 = t_j0(t), rank = t_rank(t);
+      const bool in = my_seg == seg;
+      const float mul = my_mul;
       constexpr int NC = C::KL / 8;           // 16-byte chunks of this thread's rank rows
       half8 hi[NC], lo[NC];
 #pragma unroll
       for (int i = 0; i < C::KL; ++i) {
-        const int j = t.j0 + C::KL * ah + i;
-        const float f = (in && j < t.rank) ? vv[i] * mul : 0.f;
+        const int j = j0 + C::KL * ah + i;
+        const float f = (in && j < rank) ? vv[i] * mul : 0.f;
         const _Float16 hv = (_Float16)f;
         hi[i >> 3][i & 7] = hv;
         lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
@@ -263,37 +273,41 @@ void forward_kernel(ForwardLaunch F) {
       }
     };
     if constexpr (C::DEEP) {
-      // Step q: store its rows, then issue the table of step q + 3 before
-      // waiting for that of step q + 2 (issued a step earlier, ahead of step
-      // q + 1's rows, so the wait does not cover them), then issue step
-      // q + 2's rows into the freed register set.  Unrolled by two so that
-      // the register sets and LDS buffers are static.
-      Tab t0, t1, tn, tx;
+      // Step q: store its rows, issue the table of step q + 4, then issue
+      // step q + 2's rows into the freed register set.  Step q + 2's table
+      // was issued two steps earlier, ahead of the rows of steps q and q + 1,
+      // so waiting for it neither drains rows still in flight nor waits a
+      // full load latency.  Unrolled by two so that the register sets and
+      // LDS buffers are static.
+      Tab t0, t1, ta, tb, tx;
       uint4 lb0[2], lb1[2];
       float vv0[C::KL], vv1[C::KL];
       tab_load(0, t0);
       tab_load(1, t1);
-      tab_load(2, tn);
+      tab_load(2, ta);
+      tab_load(3, tb);
       lora_load(t0, lb0, vv0);
       lora_load(t1, lb1, vv1);
       for (int q = 0;; q += 2) {
         lora_store(lds, t0, lb0, vv0);
         lds_barrier();
-        tab_load(q + 3, tx);
+        tab_load(q + 4, tx);
         __builtin_amdgcn_sched_barrier(0);   // keep the table loads ahead of the rows
-        lora_load(tn, lb0, vv0);
-        t0 = tn;
-        tn = tx;
+        lora_load(ta, lb0, vv0);
+        t0 = ta;
+        ta = tb;
+        tb = tx;
         mfma_step(lds, 0, 0);
         mfma_step(lds, 1, 0);
         if (q + 1 >= n_lora) break;
         lora_store(lds + C::StageDw, t1, lb1, vv1);
         lds_barrier();
-        tab_load(q + 4, tx);
+        tab_load(q + 5, tx);
         __builtin_amdgcn_sched_barrier(0);
-        lora_load(tn, lb1, vv1);
-        t1 = tn;
-        tn = tx;
+        lora_load(ta, lb1, vv1);
+        t1 = ta;
+        ta = tb;
+        tb = tx;
         mfma_step(lds + C::StageDw, 0, 0);
         mfma_step(lds + C::StageDw, 1, 0);
         if (q + 2 >= n_lora) break;
