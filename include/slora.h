@@ -117,13 +117,15 @@ void slora_pool_destroy(slora_pool* pool);
  *                                row blocks, column by column inside a
  *                                group (1: row-block major); 0 (default):
  *                                automatic.
- *  SLORA_TUNE_FWD_TILE         - slora_lora_forward's tile: 128 (128 x 128
- *                                everywhere), 256 (256 x 256 everywhere, when
- *                                h_out is a multiple of 256) or 0 (default):
- *                                256 x 256 for the leading positions that
- *                                fill whole rounds of 256 such tiles and
- *                                128 x 256 for the rest; 128 x 128 when the
- *                                batch is too small for one round.
+ *  SLORA_TUNE_FWD_TILE         - slora_lora_forward's tile: 64 (64 x 128
+ *                                everywhere), 128 (128 x 128 everywhere), 256
+ *                                (256 x 256 everywhere, when h_out is a
+ *                                multiple of 256) or 0 (default): 256 x 256
+ *                                for the leading positions that fill whole
+ *                                rounds of 256 such tiles and 128 x 256 for
+ *                                the rest; 128 x 128 when the batch is too
+ *                                small for one round, 64 x 128 when it is too
+ *                                small for 256 tiles of 128 x 128.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
@@ -345,7 +347,7 @@ slora_status slora_lora_expand(slora_pool* pool, const slora_segments* seg, int3
  * four 16-byte aligned.  fp16 pools only, with h_in a multiple of 64 and
  * h_out a multiple of 128 (SLORA_E_INVAL otherwise).  Launches the shrink
  * kernels (v into the workspace) and then one matrix-core kernel over tiles
- * of 128 or 256 tokens (in segment order) x 128 or 256 columns on `stream`
+ * of 64, 128 or 256 tokens (in segment order) x 128 or 256 columns on `stream`
  * (SLORA_TUNE_FWD_TILE), and returns
  * without waiting; launch errors return SLORA_E_HIP, device faults surface
  * at the caller's next synchronisation.  Requires a prior

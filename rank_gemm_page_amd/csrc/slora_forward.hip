@@ -14,9 +14,11 @@ namespace slora {
 //
 // One workgroup per tile of BM sorted positions x BN columns, 2 x (BN / 64)
 // waves, each BM / 2 positions x 64 columns (blocks of
-// v_mfma_f32_16x16x32_f16).  Three shapes: 128 x 128 (four waves of
-// 64 x 64), 256 x 256 (eight waves of 128 x 64) and 128 x 256 (eight waves
-// of 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles).
+// v_mfma_f32_16x16x32_f16).  Four shapes: 128 x 128 (four waves of
+// 64 x 64), 256 x 256 (eight waves of 128 x 64), 128 x 256 (eight waves of
+// 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles) and
+// 64 x 128 (four waves of 32 x 64, batches too small to give every CU a
+// 128 x 128 tile).
 // The larger tiles read x and W
 // half as often per flop: x is read once per column block and W once per row
 // block, and at 128 x 128 that traffic, not the matrix cores, bounds the
@@ -56,8 +58,9 @@ struct FwdTile {
   // tables, two of rows and v) where the registers allow; the 256 x 256 tile
   // keeps one step ahead.
   static constexpr bool DEEP = BM * BN <= 128 * 256;
-  static_assert(128 * EpiPitchDw <= 2 * StageDw, "an epilogue pass of 128 rows reuses the stage buffers");
-  static_assert(RW <= 128 && 128 % RW == 0, "epilogue passes hold whole waves");
+  static constexpr int EP = BM < 128 ? BM : 128;    // rows per epilogue pass
+  static_assert(EP * EpiPitchDw <= 2 * StageDw, "an epilogue pass reuses the stage buffers");
+  static_assert(RW <= EP && EP % RW == 0, "epilogue passes hold whole waves");
   static_assert(kShrinkKc == kFwdBK && kFwdLoraRows == 32, "stage layouts");
 };
 
@@ -366,15 +369,15 @@ void forward_kernel(ForwardLaunch F) {
     if (s + 2 >= n_w) break;
   }
 
-  // Epilogue, 128 rows at a time: fp16 results through LDS, then whole
+  // Epilogue, EP rows at a time: fp16 results through LDS, then whole
   // 16-byte chunks of y rows.
   _Float16* E = reinterpret_cast<_Float16*>(lds);
   _Float16* yb = static_cast<_Float16*>(F.y);
 #pragma unroll
-  for (int pass = 0; pass < BM / 128; ++pass) {
+  for (int pass = 0; pass < BM / C::EP; ++pass) {
     lds_barrier();   // every wave is done with the stage buffers / the previous pass
-    if (C::RW * wm / 128 == pass) {
-      const int rbase = C::RW * wm - 128 * pass;
+    if (C::RW * wm / C::EP == pass) {
+      const int rbase = C::RW * wm - C::EP * pass;
 #pragma unroll
       for (int i = 0; i < C::RB; ++i)
 #pragma unroll
@@ -385,10 +388,10 @@ void forward_kernel(ForwardLaunch F) {
     }
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k < 128 * C::CH / C::NT; ++k) {
+    for (int k = 0; k < C::EP * C::CH / C::NT; ++k) {
       const int row = brow + (C::NT / C::CH) * k;
       const uint4 val = *reinterpret_cast<const uint4*>(lds + row * C::EpiPitchDw + 4 * bch);
-      const int p = 128 * pass + row;
+      const int p = C::EP * pass + row;
       if (r0 + p < F.n_tokens) st16(yb + (int64_t)tok_l[p] * F.h_out + c0 + 8 * bch, val);
     }
   }
@@ -407,6 +410,10 @@ hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t
     k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 256, true>)
              : reinterpret_cast<const void*>(&forward_kernel<128, 256, false>);
     nt = FwdTile<128, 256>::NT;
+  } else if (F.bm == 64 && F.bn == 128) {
+    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<64, 128, true>)
+             : reinterpret_cast<const void*>(&forward_kernel<64, 128, false>);
+    nt = FwdTile<64, 128>::NT;
   } else if (F.bm == 128 && F.bn == 128) {
     k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 128, true>)
              : reinterpret_cast<const void*>(&forward_kernel<128, 128, false>);

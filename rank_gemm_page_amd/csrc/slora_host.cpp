@@ -162,6 +162,7 @@ struct slora_segments {
   // Sorted positions 0 .. fw_big_rows go in 256 x 256 tiles (fw_n_rb_big row
   // blocks), the rest in 128 x 128 tiles; fw_n_rb counts both kinds.
   int32_t fw_big_rows = 0, fw_n_rb_big = 0;
+  int32_t fw_small_bm = kFwdBM;    // rows of the small tiles (128, or 64 for batches below one tile per CU)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -605,7 +606,15 @@ void build_tiles(slora_segments* s) {
   }
   s->fw_n_rb_big = n_rb_big;
   s->fw_big_rows = std::min<int32_t>(T, n_rb_big * kFwdBig);
-  const int32_t n_rb_small = (T - s->fw_big_rows + kFwdBM - 1) / kFwdBM;
+  // Without big tiles, a batch that gives fewer than 256 tiles of 128 x 128
+  // (one per CU) takes 64 x 128 tiles: twice the workgroups, half the LoRA
+  // steps each (the 7B decode batch: 128 tiles instead of 64).
+  const int64_t small128 = (int64_t)((T + kFwdBM - 1) / kFwdBM) * (hout / kFwdBN);
+  s->fw_small_bm = kFwdBM;
+  if (n_rb_big == 0 && (p->tune.fwd_tile == kFwdSmall || (p->tune.fwd_tile == 0 && small128 < 256)))
+    s->fw_small_bm = kFwdSmall;
+  const int32_t SBM = s->fw_small_bm;
+  const int32_t n_rb_small = (T - s->fw_big_rows + SBM - 1) / SBM;
   s->fw_n_rb = n_rb_big + n_rb_small;
   std::vector<int32_t> pos_seg(routed);
   for (int32_t g = 0; g < S; ++g)
@@ -614,8 +623,8 @@ void build_tiles(slora_segments* s) {
   std::vector<std::pair<int32_t, int32_t>> fw_stages;   // (segment, first rank row)
   for (int32_t rb = 0; rb < s->fw_n_rb; ++rb) {
     const bool big = rb < n_rb_big;
-    const int32_t p0 = big ? rb * kFwdBig : s->fw_big_rows + (rb - n_rb_big) * kFwdBM;
-    const int32_t p1 = std::min(p0 + (big ? kFwdBig : kFwdBM), routed);
+    const int32_t p0 = big ? rb * kFwdBig : s->fw_big_rows + (rb - n_rb_big) * SBM;
+    const int32_t p1 = std::min(p0 + (big ? kFwdBig : SBM), routed);
     rb_info[2 * rb] = (int32_t)fw_stages.size();
     if (p0 < p1)
       for (int32_t g = pos_seg[p0]; g <= pos_seg[p1 - 1]; ++g)
@@ -819,8 +828,8 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       p->tune.fwd_group = value;
       return SLORA_OK;
     case SLORA_TUNE_FWD_TILE:
-      if (value != 0 && value != kFwdBM && value != kFwdBig)
-        return fail(SLORA_E_INVAL, "fwd_tile must be 0 (automatic), 128 or 256");
+      if (value != 0 && value != kFwdSmall && value != kFwdBM && value != kFwdBig)
+        return fail(SLORA_E_INVAL, "fwd_tile must be 0 (automatic), 64, 128 or 256");
       p->tune.fwd_tile = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_SHRINK_SPLITS:
@@ -1354,7 +1363,7 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
     if (n_rb == 0) continue;
     // the remainder of a batch whose bulk takes big tiles: 128 positions x
     // 256 columns (half a big tile's work, one round over the CUs)
-    F.bm = part == 0 ? kFwdBig : kFwdBM;
+    F.bm = part == 0 ? kFwdBig : s->fw_small_bm;
     F.bn = (part == 0 || s->fw_n_rb_big > 0) ? kFwdBig : kFwdBN;
     F.pos0 = part == 0 ? 0 : s->fw_big_rows;
     F.rb_info = m + s->fw_rb_info_off + (part == 0 ? 0 : 2 * (int64_t)s->fw_n_rb_big);

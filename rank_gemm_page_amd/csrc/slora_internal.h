@@ -117,6 +117,7 @@ hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 128;
 constexpr int kFwdBig = 256;       // the large tile's rows and columns
+constexpr int kFwdSmall = 64;      // rows of the tile for batches below one 128 x 128 tile per CU
 constexpr int kFwdBK = 64;
 constexpr int kFwdLoraRows = 32;   // B page rows per LoRA stage
 // LoRA stage table entry (int32 words): the stage's 32 B page ids (rows past
