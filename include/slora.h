@@ -125,7 +125,8 @@ void slora_pool_destroy(slora_pool* pool);
  *                                rounds of 256 such tiles and 128 x 256 for
  *                                the rest; 128 x 128 when the batch is too
  *                                small for one round, 64 x 128 when it is too
- *                                small for 256 tiles of 128 x 128.
+ *                                small for 256 tiles of 128 x 128 or its LoRA
+ *                                steps outnumber a tile's x W steps.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
