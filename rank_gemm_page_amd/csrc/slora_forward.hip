@@ -17,9 +17,8 @@ namespace slora {
 // v_mfma_f32_16x16x32_f16).  Four shapes: 128 x 128 (four waves of
 // 64 x 64), 256 x 256 (eight waves of 128 x 64), 128 x 256 (eight waves of
 // 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles) and
-// 64 x 128 (four waves of 32 x 64, batches too small to give every CU a
-// 128 x 128 tile).
-// The larger tiles read x and W
+// 64 x 128 (four waves of 32 x 64, for batches too small to give every CU a
+// 128 x 128 tile or heavy in LoRA steps).  The larger tiles read x and W
 // half as often per flop: x is read once per column block and W once per row
 // block, and at 128 x 128 that traffic, not the matrix cores, bounds the
 // kernel on large batches.  Per step the tile stages in LDS (two buffers, one
@@ -54,9 +53,8 @@ struct FwdTile {
   static constexpr int KL = kFwdLoraRows / TPR;      // rank rows of a LoRA step per thread
   static constexpr int XL = BM * 8 / NT;             // 16-byte x loads per thread per step
   static_assert(TPR == 2 || TPR == 4, "two or four threads per position");
-  // LoRA steps with page rows two steps ahead (three register sets of stage
-  // tables, two of rows and v) where the registers allow; the 256 x 256 tile
-  // keeps one step ahead.
+  // LoRA steps with page rows two steps ahead and stage tables four ahead
+  // where the registers allow; the 256 x 256 tile keeps one step ahead.
   static constexpr bool DEEP = BM * BN <= 128 * 256;
   static constexpr int EP = BM < 128 ? BM : 128;    // rows per epilogue pass
   static_assert(EP * EpiPitchDw <= 2 * StageDw, "an epilogue pass reuses the stage buffers");
@@ -138,10 +136,10 @@ void forward_kernel(ForwardLaunch F) {
   __syncthreads();
 
   // Thread maps.  LoRA staging: A row ar = tid / TPR, rank rows
-  // KL ah .. KL ah + KL - 1 (ah = tid % TPR).  B rows (W or pages): rows brow + 16h, one 16-byte chunk
-  // bch of the BN columns (slice bch / 16).  x rows: chunk xch of rows
-  // xrow + (NT / 8) i, so one wave instruction reads 8 whole 128-byte row
-  // segments.
+  // KL ah .. KL ah + KL - 1 (ah = tid % TPR).  B rows (W or pages): rows
+  // brow + 16h, one 16-byte chunk bch of the BN columns (slice bch / 16).
+  // x rows: chunk xch of rows xrow + (NT / 8) i, so one wave instruction
+  // reads 8 whole 128-byte row segments.
   const int ar = tid / C::TPR, ah = tid % C::TPR;
   const int brow = tid / C::CH, bch = tid % C::CH;
   const int bsl = bch >> 4, bquad = 2 * (bch & 15);
