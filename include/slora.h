@@ -96,7 +96,8 @@ void slora_pool_destroy(slora_pool* pool);
  *                                batch (16K to 128K, growing with the
  *                                batch's vector-ALU expand work).
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
- *                                of 128; default 1024.
+ *                                of 128; 0 (default): 512 when every segment
+ *                                of the batch takes the MFMA tiles, else 1024.
  *  SLORA_TUNE_MFMA_SHRINK_SPLITS - K splits of each 64-token MFMA shrink
  *                                block, 1..4; 0 (default): enough for about
  *                                512 shrink tiles.

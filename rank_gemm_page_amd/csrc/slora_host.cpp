@@ -85,7 +85,7 @@ struct AdapterRec {
 struct Tuning {
   int64_t mfma_min_tokens = 64;
   int64_t gemv_expand_elems = 0;   // 0: sized from the batch (auto_expand_elems)
-  int64_t mfma_expand_cols = 1024;
+  int64_t mfma_expand_cols = 0;    // 0: 512 when every segment takes the MFMA tiles, else 1024
   int64_t mfma_shrink_splits = 0;   // K splits per MFMA shrink block (0: automatic)
   int64_t fused = 1;
   int64_t xcds = 1;             // XCD groups of the shrink placement (1: none)
@@ -455,6 +455,21 @@ void build_tiles(slora_segments* s) {
     while (expand_elems < 131072 && expand_elems * 2 <= work / 1024) expand_elems *= 2;
   }
 
+  // MFMA expand width.  Measured on MI355X: a batch whose segments all take
+  // the MFMA tiles (the 7B prefill batch) runs 3 % faster with 512 columns
+  // (twice the expand tiles: the chip holds them all at once), while a batch
+  // whose vector-ALU tiles already fill the chip (the 13B mixed batch) runs
+  // 5 % faster with 1024 (each staged B slice serves twice the columns).
+  int64_t mfma_cols = p->tune.mfma_expand_cols;
+  if (mfma_cols == 0) {
+    bool all_mfma = mfma_ok;
+    for (int32_t g = 0; g < S && all_mfma; ++g) {
+      const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
+      all_mfma = c >= p->tune.mfma_min_tokens && s->seg_rank[g] <= kMaxRankMfma;
+    }
+    mfma_cols = all_mfma ? 512 : 1024;
+  }
+
   std::vector<TileSpec> tiles;
   std::vector<std::pair<int32_t, int32_t>> eblocks;   // token blocks of a segment
   int32_t max_rank = 1;
@@ -471,7 +486,7 @@ void build_tiles(slora_segments* s) {
     // vector-ALU expand width: largest of vec*{256,128,64,32} with rank x width within budget
     int32_t width = vec * 256;
     while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
-    const int32_t cols = mfma ? (int32_t)p->tune.mfma_expand_cols : width;
+    const int32_t cols = mfma ? (int32_t)mfma_cols : width;
     for (size_t b = 0; b < eblocks.size(); ++b) {
       const auto& tb = eblocks[b];
       const int32_t grp = n_groups + (int32_t)b;
@@ -814,8 +829,8 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       p->tune.gemv_expand_elems = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_EXPAND_COLS:
-      if (value < kMfmaPass || value % kMfmaPass || value > 65536)
-        return fail(SLORA_E_INVAL, "mfma_expand_cols must be a multiple of 128, at most 65536");
+      if (value < 0 || value % kMfmaPass || value > 65536)
+        return fail(SLORA_E_INVAL, "mfma_expand_cols must be 0 (automatic) or a multiple of 128, at most 65536");
       p->tune.mfma_expand_cols = value;
       return SLORA_OK;
     case SLORA_TUNE_XCDS:

@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 ROUTES = {"gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
           "mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1},
+          "mfma_cols_1024": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1, S.SLORA_TUNE_MFMA_EXPAND_COLS: 1024},
           "default": {}}
 LAUNCH = {"fused": {S.SLORA_TUNE_FUSED: 1}, "two": {S.SLORA_TUNE_FUSED: 0}}
 
@@ -87,7 +88,7 @@ SMALL = [
 def test_small_shapes(spec, route, launch):
     w = generate(spec, 1)
     ys, info = run_gpu(w, route, launch=launch)
-    if route == "mfma" and spec.dtype == "f16" and spec.h_in % 32 == 0:
+    if route.startswith("mfma") and spec.dtype == "f16" and spec.h_in % 32 == 0:
         assert info["n_mfma_segments"] == info["n_segments"]
     for p, y in enumerate(ys):
         y_ref, sd_ref = oracle(w, p)

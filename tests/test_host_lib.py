@@ -225,13 +225,15 @@ def check_tiles_cover(w, pool, ids):
 
 @pytest.mark.parametrize("name", ["tiny", "decode7b", "prefill7b", "mixed13b", "mlp70b"])
 @pytest.mark.parametrize("route", ["default", "all_gemv", "all_mfma", "xcd_grouped", "rank_order",
-                                   "bytes_order"])
+                                   "bytes_order", "mfma_cols_1024", "mfma_cols_384"])
 def test_tiles_cover_each_output_once(name, route):
     tuning = {"default": {}, "all_gemv": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1 << 30},
               "all_mfma": {S.SLORA_TUNE_MFMA_MIN_TOKENS: 1},
               "xcd_grouped": {S.SLORA_TUNE_XCDS: 8},
               "rank_order": {S.SLORA_TUNE_TILE_ORDER: 1},
-              "bytes_order": {S.SLORA_TUNE_TILE_ORDER: 2}}[route]
+              "bytes_order": {S.SLORA_TUNE_TILE_ORDER: 2},
+              "mfma_cols_1024": {S.SLORA_TUNE_MFMA_EXPAND_COLS: 1024},
+              "mfma_cols_384": {S.SLORA_TUNE_MFMA_EXPAND_COLS: 384}}[route]
     w = generate(CONFIGS[name], 0)
     pool, _ = make_pool(w, tuning=tuning)
     try:
@@ -386,6 +388,10 @@ def test_tuning_validation():
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_GEMV_EXPAND_ELEMS, -1) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_GEMV_EXPAND_ELEMS, 0)
         assert status_of(S.slora_pool_set_tuning, pool, 2, 300) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, -128) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 65536 + 128) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 512)
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 0)
         assert status_of(S.slora_pool_set_tuning, pool, 9, 1) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, 99, 1) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FUSED, 2) == S.SLORA_E_INVAL
