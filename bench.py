@@ -401,7 +401,7 @@ def main():
                     help="0: tiles in adapter order, 1: clustered by rank, 2 (default): most bytes first")
     ap.add_argument("--fwd-group", type=int, default=None,
                     help="row blocks per group of the base-plus-delta tile order (0: automatic)")
-    ap.add_argument("--fwd-tile", type=int, default=None, choices=[0, 64, 128, 256],
+    ap.add_argument("--fwd-tile", type=int, default=None, choices=[0, 32, 64, 128, 256],
                     help="base-plus-delta tile (0: automatic)")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")

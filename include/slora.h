@@ -118,8 +118,9 @@ void slora_pool_destroy(slora_pool* pool);
  *                                row blocks, column by column inside a
  *                                group (1: row-block major); 0 (default):
  *                                automatic.
- *  SLORA_TUNE_FWD_TILE         - slora_lora_forward's tile: 64 (64 x 128
- *                                everywhere), 128 (128 x 128 everywhere), 256
+ *  SLORA_TUNE_FWD_TILE         - slora_lora_forward's tile: 32 (32 x 128
+ *                                everywhere), 64 (64 x 128 everywhere),
+ *                                128 (128 x 128 everywhere), 256
  *                                (256 x 256 everywhere, when h_out is a
  *                                multiple of 256) or 0 (default): 256 x 256
  *                                for the leading positions that fill whole
@@ -127,7 +128,9 @@ void slora_pool_destroy(slora_pool* pool);
  *                                the rest; 128 x 128 when the batch is too
  *                                small for one round, 64 x 128 when it is too
  *                                small for 256 tiles of 128 x 128 or its LoRA
- *                                steps outnumber a tile's x W steps.
+ *                                steps outnumber a tile's x W steps, 32 x 128
+ *                                when it is too small for 256 tiles of
+ *                                64 x 128.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {

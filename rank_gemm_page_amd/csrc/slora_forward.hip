@@ -14,11 +14,12 @@ namespace slora {
 //
 // One workgroup per tile of BM sorted positions x BN columns, 2 x (BN / 64)
 // waves, each BM / 2 positions x 64 columns (blocks of
-// v_mfma_f32_16x16x32_f16).  Four shapes: 128 x 128 (four waves of
+// v_mfma_f32_16x16x32_f16).  Five shapes: 128 x 128 (four waves of
 // 64 x 64), 256 x 256 (eight waves of 128 x 64), 128 x 256 (eight waves of
-// 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles) and
+// 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles),
 // 64 x 128 (four waves of 32 x 64, for batches too small to give every CU a
-// 128 x 128 tile or heavy in LoRA steps).  The larger tiles read x and W
+// 128 x 128 tile or heavy in LoRA steps) and 32 x 128 (four waves of
+// 16 x 64, for batches too small to give every CU a 64 x 128 tile).  The larger tiles read x and W
 // half as often per flop: x is read once per column block and W once per row
 // block, and at 128 x 128 that traffic, not the matrix cores, bounds the
 // kernel on large batches.  Per step the tile stages in LDS (two buffers, one
@@ -52,7 +53,7 @@ struct FwdTile {
   static constexpr int TPR = NT / BM;                // threads per position (prologue, LoRA staging)
   static constexpr int KL = kFwdLoraRows / TPR;      // rank rows of a LoRA step per thread
   static constexpr int XL = BM * 8 / NT;             // 16-byte x loads per thread per step
-  static_assert(TPR == 2 || TPR == 4, "two or four threads per position");
+  static_assert(TPR == 2 || TPR == 4 || TPR == 8, "two, four or eight threads per position");
   // LoRA steps with page rows two steps ahead and stage tables four ahead
   // where the registers allow; the 256 x 256 tile keeps one step ahead.
   static constexpr bool DEEP = BM * BN <= 128 * 256;
@@ -257,20 +258,37 @@ void forward_kernel(ForwardLaunch F) {
       const int seg = t_seg(t), j0 = t_j0(t), rank = t_rank(t);
       const bool in = my_seg == seg;
       const float mul = my_mul;
-      constexpr int NC = C::KL / 8;           // 16-byte chunks of this thread's rank rows
-      half8 hi[NC], lo[NC];
+      if constexpr (C::KL >= 8) {
+        constexpr int NC = C::KL / 8;           // 16-byte chunks of this thread's rank rows
+        half8 hi[NC], lo[NC];
 #pragma unroll
-      for (int i = 0; i < C::KL; ++i) {
-        const int j = j0 + C::KL * ah + i;
-        const float f = (in && j < rank) ? vv[i] * mul : 0.f;
-        const _Float16 hv = (_Float16)f;
-        hi[i >> 3][i & 7] = hv;
-        lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
-      }
+        for (int i = 0; i < C::KL; ++i) {
+          const int j = j0 + C::KL * ah + i;
+          const float f = (in && j < rank) ? vv[i] * mul : 0.f;
+          const _Float16 hv = (_Float16)f;
+          hi[i >> 3][i & 7] = hv;
+          lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
+        }
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        *reinterpret_cast<uint4*>(S + chunk_dw(ar, NC * ah + c)) = __builtin_bit_cast(uint4, hi[c]);
-        *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + NC * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
+        for (int c = 0; c < NC; ++c) {
+          *reinterpret_cast<uint4*>(S + chunk_dw(ar, NC * ah + c)) = __builtin_bit_cast(uint4, hi[c]);
+          *reinterpret_cast<uint4*>(S + chunk_dw(ar, 4 + NC * ah + c)) = __builtin_bit_cast(uint4, lo[c]);
+        }
+      } else {
+        // four rank rows per thread: half of a 16-byte chunk (dwords 0-1 or 2-3)
+        static_assert(C::KL == 4, "four rank rows per thread");
+        short4v hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * ah + i;
+          const float f = (in && j < rank) ? vv[i] * mul : 0.f;
+          const _Float16 hv = (_Float16)f;
+          hi[i] = __builtin_bit_cast(short, hv);
+          lo[i] = __builtin_bit_cast(short, (_Float16)(f - (float)hv));
+        }
+        const int half = 2 * (ah & 1);
+        *reinterpret_cast<uint2*>(S + chunk_dw(ar, ah >> 1) + half) = __builtin_bit_cast(uint2, hi);
+        *reinterpret_cast<uint2*>(S + chunk_dw(ar, 4 + (ah >> 1)) + half) = __builtin_bit_cast(uint2, lo);
       }
     };
     if constexpr (C::DEEP) {
@@ -412,6 +430,10 @@ hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t
     k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<64, 128, true>)
              : reinterpret_cast<const void*>(&forward_kernel<64, 128, false>);
     nt = FwdTile<64, 128>::NT;
+  } else if (F.bm == 32 && F.bn == 128) {
+    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<32, 128, true>)
+             : reinterpret_cast<const void*>(&forward_kernel<32, 128, false>);
+    nt = FwdTile<32, 128>::NT;
   } else if (F.bm == 128 && F.bn == 128) {
     k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 128, true>)
              : reinterpret_cast<const void*>(&forward_kernel<128, 128, false>);

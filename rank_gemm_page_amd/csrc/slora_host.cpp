@@ -91,7 +91,7 @@ struct Tuning {
   int64_t xcds = 1;             // XCD groups of the shrink placement (1: none)
   int64_t tile_order = 2;       // 0: segment order, 1: rank-descending, 2: bytes-descending
   int64_t fwd_group = 0;        // row blocks per group of the base-plus-delta tile order (0: automatic)
-  int64_t fwd_tile = 0;         // base-plus-delta tile: 128, 256, or 0 (automatic)
+  int64_t fwd_tile = 0;         // base-plus-delta tile rows: 32, 64, 128, 256, or 0 (automatic)
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -162,7 +162,7 @@ struct slora_segments {
   // Sorted positions 0 .. fw_big_rows go in 256 x 256 tiles (fw_n_rb_big row
   // blocks), the rest in 128 x 128 tiles; fw_n_rb counts both kinds.
   int32_t fw_big_rows = 0, fw_n_rb_big = 0;
-  int32_t fw_small_bm = kFwdBM;    // rows of the small tiles (128, or 64 for batches below one tile per CU)
+  int32_t fw_small_bm = kFwdBM;    // rows of the small tiles (128, or 64 / 32 for batches below one tile per CU)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -626,15 +626,21 @@ void build_tiles(slora_segments* s) {
   // CU; the 7B decode batch: 128 tiles instead of 64), or when its LoRA steps
   // per 128-position block would outnumber the x W steps of a tile (the 70B
   // MLP batch: about 160 against 128, 6 % faster; the 13B mixed batch, about
-  // 24 against 80, is 7 % slower with them).
+  // 24 against 80, is 7 % slower with them); 32 x 128 tiles when even the
+  // 64 x 128 tiles number fewer than 256 (the 7B decode batch: 256 tiles
+  // instead of 128, each with about half the LoRA steps).
   const int64_t small128 = (int64_t)((T + kFwdBM - 1) / kFwdBM) * (hout / kFwdBN);
   int64_t lora_steps = 0;
   for (int32_t g = 0; g < S; ++g) lora_steps += (s->seg_rank[g] + kFwdLoraRows - 1) / kFwdLoraRows;
   const int64_t blocks128 = std::max<int64_t>(1, (T + kFwdBM - 1) / kFwdBM);
   const bool lora_heavy = lora_steps > (int64_t)(hin / kFwdBK) * blocks128;
   s->fw_small_bm = kFwdBM;
-  if (n_rb_big == 0 && (p->tune.fwd_tile == kFwdSmall || (p->tune.fwd_tile == 0 && (small128 < 256 || lora_heavy))))
-    s->fw_small_bm = kFwdSmall;
+  if (n_rb_big == 0) {
+    if (p->tune.fwd_tile == kFwdTiny || (p->tune.fwd_tile == 0 && 2 * small128 < 256))
+      s->fw_small_bm = kFwdTiny;
+    else if (p->tune.fwd_tile == kFwdSmall || (p->tune.fwd_tile == 0 && (small128 < 256 || lora_heavy)))
+      s->fw_small_bm = kFwdSmall;
+  }
   const int32_t SBM = s->fw_small_bm;
   const int32_t n_rb_small = (T - s->fw_big_rows + SBM - 1) / SBM;
   s->fw_n_rb = n_rb_big + n_rb_small;
@@ -850,8 +856,8 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       p->tune.fwd_group = value;
       return SLORA_OK;
     case SLORA_TUNE_FWD_TILE:
-      if (value != 0 && value != kFwdSmall && value != kFwdBM && value != kFwdBig)
-        return fail(SLORA_E_INVAL, "fwd_tile must be 0 (automatic), 64, 128 or 256");
+      if (value != 0 && value != kFwdTiny && value != kFwdSmall && value != kFwdBM && value != kFwdBig)
+        return fail(SLORA_E_INVAL, "fwd_tile must be 0 (automatic), 32, 64, 128 or 256");
       p->tune.fwd_tile = value;
       return SLORA_OK;
     case SLORA_TUNE_MFMA_SHRINK_SPLITS:

@@ -118,6 +118,7 @@ constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 128;
 constexpr int kFwdBig = 256;       // the large tile's rows and columns
 constexpr int kFwdSmall = 64;      // rows of the tile for batches below one 128 x 128 tile per CU
+constexpr int kFwdTiny = 32;       // rows of the tile for batches below one 64 x 128 tile per CU
 constexpr int kFwdBK = 64;
 constexpr int kFwdLoraRows = 32;   // B page rows per LoRA stage
 // LoRA stage table entry (int32 words): the stage's 32 B page ids (rows past
@@ -144,7 +145,7 @@ struct ForwardLaunch {
   const int32_t* stages;     // LoRA stage table of this projection
   int32_t n_rb, n_cb, n_tiles, per_xcd;
   int32_t group_m;           // tile order: groups of group_m row blocks, column-major inside a group
-  int32_t bm, bn;            // tile shape: 128 x 128 or 256 x 256
+  int32_t bm, bn;            // tile shape: 256 x 256, 128 x 256, 128 x 128, 64 x 128 or 32 x 128
   int32_t pos0;              // first sorted position of row block 0 of this launch
   int32_t v4;                // every segment's rank is a multiple of 4 (v rows 16-byte aligned)
 };

@@ -90,7 +90,7 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("tile", [0, 64, 128])
+@pytest.mark.parametrize("tile", [0, 32, 64, 128])
 @pytest.mark.parametrize("route", ["default", "gemv", "mfma"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_small_shapes(name, route, tile):
@@ -129,12 +129,13 @@ def test_forward_big_tiles_integer_bit_exact_and_same_as_small():
     h_ref, _ = oracle_forward(w)
     assert np.abs(h_ref).max() < 2048
     outs = {}
-    for tile in (64, 128, 256):
+    for tile in (32, 64, 128, 256):
         (ys,), _ = run_forward(w, route="mfma", tile=tile)
         np.testing.assert_array_equal(ys[0], round_to(h_ref, np.float16))
         outs[tile] = ys[0]
     np.testing.assert_array_equal(outs[128], outs[256])
     np.testing.assert_array_equal(outs[64], outs[128])
+    np.testing.assert_array_equal(outs[32], outs[64])
 
 
 @pytest.mark.parametrize("batch,n_adapters", [(("requests", 40, 190, 230), 12),
@@ -177,7 +178,7 @@ MAX_FWD = [
 ]
 
 
-@pytest.mark.parametrize("tile", [64, 128, 256])
+@pytest.mark.parametrize("tile", [32, 64, 128, 256])
 @pytest.mark.parametrize("spec", MAX_FWD, ids=lambda s: s.name)
 def test_forward_maximum_sizes(spec, tile):
     w = generate(spec, 4)

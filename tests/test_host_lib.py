@@ -400,7 +400,9 @@ def test_tuning_validation():
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_XCDS, 8)
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_TILE_ORDER, 3) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_TILE_ORDER, 1)
-        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_TILE, 32) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_TILE, 48) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_TILE, 16) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_FWD_TILE, 32)
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_FWD_TILE, 64)
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_GROUP, -1) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_FWD_TILE, 256)
