@@ -34,10 +34,11 @@ def _gpu():
     S.lib()
 
 
-def run_forward(w, projs=(0,), route="default", repeat=1, tile=0):
+def run_forward(w, projs=(0,), route="default", repeat=1, tile=0, group=0):
     print(f"[gpu] forward {w.spec.name} seed={w.seed} route={route} T={w.T} "
-          f"h={w.spec.h_in}x{w.spec.h_out} tile={tile}", flush=True)
-    dw = DeviceWorkload(w, "cuda:0", tuning={**ROUTES[route], S.SLORA_TUNE_FWD_TILE: tile})
+          f"h={w.spec.h_in}x{w.spec.h_out} tile={tile} group={group}", flush=True)
+    dw = DeviceWorkload(w, "cuda:0", tuning={**ROUTES[route], S.SLORA_TUNE_FWD_TILE: tile,
+                                             S.SLORA_TUNE_FWD_GROUP: group})
     try:
         outs = []
         for p in projs:
@@ -136,6 +137,24 @@ def test_forward_big_tiles_integer_bit_exact_and_same_as_small():
     np.testing.assert_array_equal(outs[128], outs[256])
     np.testing.assert_array_equal(outs[64], outs[128])
     np.testing.assert_array_equal(outs[32], outs[64])
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_forward_tile_order_changes_nothing(tile):
+    """The order in which tiles walk the chip (groups of 1, 3, 8 and all row
+    blocks, ragged last group) places work, never changes it: bit-identical
+    outputs, all within the gates."""
+    spec = small_spec("fw_order", h_in=192, h_out=1024, two_classes=True, n_adapters=40,
+                      rank_set=(4, 8, 16, 64), batch=("zipf", 700, 1.1))
+    w = drop_some(generate(spec, 21), 7)
+    h_ref, sd_ref = oracle_forward(w)
+    outs = {}
+    for group in (0, 1, 3, 8, 64):
+        (ys,), _ = run_forward(w, tile=tile, group=group)
+        outs[group] = ys[0]
+    check(w, outs[0], h_ref, sd_ref, label=f"forward order {tile}")
+    for group in (1, 3, 8, 64):
+        np.testing.assert_array_equal(outs[group], outs[0])
 
 
 @pytest.mark.parametrize("batch,n_adapters", [(("requests", 40, 190, 230), 12),
