@@ -19,10 +19,10 @@ namespace slora {
 // 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles),
 // 64 x 128 (four waves of 32 x 64, for batches too small to give every CU a
 // 128 x 128 tile or heavy in LoRA steps) and 32 x 128 (four waves of
-// 16 x 64, for batches too small to give every CU a 64 x 128 tile).  The larger tiles read x and W
-// half as often per flop: x is read once per column block and W once per row
-// block, and at 128 x 128 that traffic, not the matrix cores, bounds the
-// kernel on large batches.  Per step the tile stages in LDS (two buffers, one
+// 16 x 64, for batches too small to give every CU a 64 x 128 tile).  The
+// larger tiles read x and W half as often per flop: x is read once per column
+// block and W once per row block, and at 128 x 128 that traffic, not the
+// matrix cores, bounds the kernel on large batches.  Per step the tile stages in LDS (two buffers, one
 // barrier per step):
 //   A  BM rows x 64 k of fp16 (16-byte chunks XOR-swizzled by row)
 //   B  64 rows x BN columns, as BN / 128 slices of 128 columns (the

@@ -108,12 +108,12 @@ hipError_t launch_delta(const DeltaLaunch& L, int stages, hipStream_t stream,
 // Base product with the LoRA delta folded into its tiles (fp16 only):
 //   y[t, o] = round( sum_k x[t, k] W[k, o]  +  s_a sum_j v[t, j] B_j[o] )
 // over the batch in segment order (routed tokens sorted by adapter, then the
-// tokens with no adapter), in tiles of kFwdBM sorted positions x kFwdBN
-// columns (kFwdBM x kFwdBN, or twice that on large batches).  Each tile
-// first runs one LoRA stage per 32 rank rows of every
-// segment its positions touch (the B page rows against s v, split into fp16
-// high and low parts), then the x W stages of kFwdBK rows of W, and writes y
-// once.  v = x A comes from the shrink kernels (workspace).
+// tokens with no adapter), in tiles of sorted positions x columns: 128 x 128
+// (kFwdBM x kFwdBN), 256 x 256 and 128 x 256 on large batches, 64 x 128 and
+// 32 x 128 on small ones.  Each tile first runs one LoRA stage per 32 rank
+// rows of every segment its positions touch (the B page rows against s v,
+// split into fp16 high and low parts), then the x W stages of kFwdBK rows of
+// W, and writes y once.  v = x A comes from the shrink kernels (workspace).
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 128;
 constexpr int kFwdBig = 256;       // the large tile's rows and columns
