@@ -247,6 +247,27 @@ def test_tiles_cover_each_output_once(name, route):
         S.slora_pool_destroy(pool)
 
 
+@pytest.mark.parametrize("name,tuning,want", [
+    ("prefill7b", {}, 512),                                  # every segment on the MFMA tiles
+    ("mixed13b", {}, 1024),                                  # vector-ALU segments beside them
+    ("prefill7b", {S.SLORA_TUNE_MFMA_EXPAND_COLS: 1024}, 1024),   # an explicit width wins
+    ("mixed13b", {S.SLORA_TUNE_MFMA_EXPAND_COLS: 384}, 384)])
+def test_mfma_expand_width_follows_the_batch(name, tuning, want):
+    w = generate(CONFIGS[name], 0)
+    pool, _ = make_pool(w, tuning=tuning)
+    try:
+        seg = S.slora_build_segments(pool, w.ids)
+        try:
+            _, recs = S.slora_segments_tiles(seg)
+            widths = [int(rec[4]) for rec in recs if int(rec[0]) == 3]   # MFMA expand: columns handled
+            assert widths and max(widths) == want
+            assert all(c == want for c in widths if c != w.spec.h_out % want)
+        finally:
+            S.slora_segments_destroy(seg)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
 def test_tiles_with_ragged_shapes_and_no_adapter_tokens():
     spec = small_spec("ragged", h_in=136, h_out=200, two_classes=True, n_adapters=7,
                       rank_set=(1, 3, 13, 40, 100), batch=("zipf", 60, 1.0))
