@@ -33,7 +33,10 @@ namespace slora {
 // g in B rows 0..31 and, in A, s v[t, j] 2^-e_t for the positions t of g
 // (zero for the others) split into an fp16 high part (k 0..31) and the
 // rounding remainder (k 32..63); both sub-steps multiply the same B rows, so
-// the matrix cores see s v with about 22 significant bits.  e_t puts the
+// the matrix cores see s v with about 22 significant bits.  The 32- and
+// 64-row tiles pack their steps: B rows 4u .. 4u+3 hold up to 4 rank rows of
+// any of the tile's segments (group u), and the A column of such a row is
+// nonzero only for the positions of that row's segment.  e_t puts the
 // position's largest |s v| in [2^14, 2^15); the accumulators are scaled back
 // by 2^e_t (exact) after the LoRA steps, before the x W steps.
 
@@ -57,6 +60,9 @@ struct FwdTile {
   // LoRA steps with page rows two steps ahead and stage tables four ahead
   // where the registers allow; the 256 x 256 tile keeps one step ahead.
   static constexpr bool DEEP = BM * BN <= 128 * 256;
+  // The 32- and 64-row tiles read the packed stage table (groups of 4 rank
+  // rows of any segment); the others one segment per stage.
+  static constexpr bool PACK = BM <= kFwdSmall;
   static constexpr int EP = BM < 128 ? BM : 128;    // rows per epilogue pass
   static_assert(EP * EpiPitchDw <= 2 * StageDw, "an epilogue pass reuses the stage buffers");
   static_assert(RW <= EP && EP % RW == 0, "epilogue passes hold whole waves");
@@ -205,21 +211,52 @@ void forward_kernel(ForwardLaunch F) {
     // on purpose: as a scalar load it would share the counter of the LDS
     // reads, and scalar loads complete out of order, so every LDS wait of the
     // step (the MFMA operands included) would wait for it as well.
-    struct Tab { int id0, id1, hw; };
+    // Packed: this thread's rank rows KL ah .. KL ah + KL - 1 are groups
+    // NG ah .. NG ah + NG - 1, one table word each.
+    constexpr int NG = C::PACK ? C::KL / 4 : 1;
+    struct Tab { int id0, id1, hw[NG]; };
     const int hlane = lane & 3;
     auto tab_load = [&](int q, Tab& t) {
       q = q < n_lora ? q : n_lora - 1;
       const int32_t* e = tab + (int64_t)q * kFwdStageWords;
       t.id0 = e[brow];
       t.id1 = e[16 + brow];
-      t.hw = e[FWS_SEG + hlane];
+      if constexpr (C::PACK) {
+#pragma unroll
+        for (int u = 0; u < NG; ++u) t.hw[u] = e[FWS_GROUP + NG * ah + u];
+      } else {
+        t.hw[0] = e[FWS_SEG + hlane];
+      }
     };
-    auto t_seg = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw, 0); };
-    auto t_j0 = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw, 1); };
-    auto t_rank = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw, 2); };
+    auto t_seg = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw[0], 0); };
+    auto t_j0 = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw[0], 1); };
+    auto t_rank = [](const Tab& t) { return __builtin_amdgcn_readlane(t.hw[0], 2); };
     // this thread's position: fixed for the tile, kept in registers
     const int my_seg = seg_l[ar], my_voff = voff_l[ar];
     const float my_mul = mul_l[ar];
+    // A step's header as this thread needs it: the packed group words, or
+    // (one segment per step) whether the step's segment is this thread's,
+    // its first rank row of this thread and the rank, read once per step.
+    struct View { bool in; int j, rank; };
+    auto view_of = [&](const Tab& t) -> View {
+      if constexpr (C::PACK) {
+        return View{false, 0, 0};
+      } else {
+        return View{my_seg == t_seg(t), t_j0(t) + C::KL * ah, t_rank(t)};
+      }
+    };
+    // Rank row KL ah + i of a step: whether it is a row of this thread's
+    // segment, and the index of its v value.
+    struct Row { bool ok; int at; };
+    auto row_of = [&](const Tab& t, const View& vw, int i) -> Row {
+      if constexpr (C::PACK) {
+        const uint32_t w = (uint32_t)t.hw[i >> 2];
+        const int k = i & 3;
+        return Row{(int)(w & 7u) > k && (int)(w >> 9) == my_seg, my_voff + 4 * (int)((w >> 3) & 63u) + k};
+      } else {
+        return Row{vw.in && vw.j + i < vw.rank, my_voff + vw.j + i};
+      }
+    };
     auto lora_load = [&](const Tab& t, uint4 (&lb)[2], float (&vv)[C::KL]) {
       // Page ids are never negative: zero-extending them (unlike a sign
       // extension) needs no instruction on the loaded value, so the compiler
@@ -228,16 +265,14 @@ void forward_kernel(ForwardLaunch F) {
       const int64_t col = (int64_t)(c0 + 8 * bch) * 2;
       lb[0] = ld16(F.base_b + (uint64_t)(uint32_t)t.id0 * (uint64_t)F.page_bytes_b + col);
       lb[1] = ld16(F.base_b + (uint64_t)(uint32_t)t.id1 * (uint64_t)F.page_bytes_b + col);
-      const int seg = t_seg(t), j0 = t_j0(t), rank = t_rank(t);
-      const bool in = my_seg == seg;
-      const int voff = my_voff;
+      const View vw = view_of(t);
       if constexpr (V4) {
         // a chunk of 4 values lies wholly inside the row or wholly past its
         // rank (rank % 4 == 0); one past it reads v[0 .. 3] instead
 #pragma unroll
         for (int c = 0; c < C::KL / 4; ++c) {
-          const int j = j0 + C::KL * ah + 4 * c;
-          const uint4 q = ld16(F.v + ((in && j < rank) ? voff + j : 0));
+          const Row r = row_of(t, vw, 4 * c);
+          const uint4 q = ld16(F.v + (r.ok ? r.at : 0));
           vv[4 * c] = __uint_as_float(q.x);
           vv[4 * c + 1] = __uint_as_float(q.y);
           vv[4 * c + 2] = __uint_as_float(q.z);
@@ -246,8 +281,8 @@ void forward_kernel(ForwardLaunch F) {
       } else {
 #pragma unroll
         for (int i = 0; i < C::KL; ++i) {
-          const int j = j0 + C::KL * ah + i;
-          vv[i] = F.v[(in && j < rank) ? voff + j : 0];
+          const Row r = row_of(t, vw, i);
+          vv[i] = F.v[r.ok ? r.at : 0];
         }
       }
     };
@@ -255,16 +290,14 @@ void forward_kernel(ForwardLaunch F) {
       uint32_t* B = S + C::ADw + bsl * C::SliceDw;
       *reinterpret_cast<uint4*>(B + quad_dw(brow, bquad)) = lb[0];
       *reinterpret_cast<uint4*>(B + quad_dw(16 + brow, bquad)) = lb[1];
-      const int seg = t_seg(t), j0 = t_j0(t), rank = t_rank(t);
-      const bool in = my_seg == seg;
       const float mul = my_mul;
+      const View vw = view_of(t);
       if constexpr (C::KL >= 8) {
         constexpr int NC = C::KL / 8;           // 16-byte chunks of this thread's rank rows
         half8 hi[NC], lo[NC];
 #pragma unroll
         for (int i = 0; i < C::KL; ++i) {
-          const int j = j0 + C::KL * ah + i;
-          const float f = (in && j < rank) ? vv[i] * mul : 0.f;
+          const float f = row_of(t, vw, i).ok ? vv[i] * mul : 0.f;
           const _Float16 hv = (_Float16)f;
           hi[i >> 3][i & 7] = hv;
           lo[i >> 3][i & 7] = (_Float16)(f - (float)hv);
@@ -280,8 +313,7 @@ void forward_kernel(ForwardLaunch F) {
         short4v hi, lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 4 * ah + i;
-          const float f = (in && j < rank) ? vv[i] * mul : 0.f;
+          const float f = row_of(t, vw, i).ok ? vv[i] * mul : 0.f;
           const _Float16 hv = (_Float16)f;
           hi[i] = __builtin_bit_cast(short, hv);
           lo[i] = __builtin_bit_cast(short, (_Float16)(f - (float)hv));

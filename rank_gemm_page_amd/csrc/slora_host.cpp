@@ -17,6 +17,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -163,6 +164,7 @@ struct slora_segments {
   // blocks), the rest in 128 x 128 tiles; fw_n_rb counts both kinds.
   int32_t fw_big_rows = 0, fw_n_rb_big = 0;
   int32_t fw_small_bm = kFwdBM;    // rows of the small tiles (128, or 64 / 32 for batches below one tile per CU)
+  bool fw_packed = false;          // LoRA stages in the packed layout (the 32- and 64-row tiles)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -648,15 +650,42 @@ void build_tiles(slora_segments* s) {
   for (int32_t g = 0; g < S; ++g)
     for (int32_t i = s->seg_start[g]; i < s->seg_start[g + 1]; ++i) pos_seg[i] = g;
   std::vector<int32_t> rb_info(2 * (size_t)s->fw_n_rb, 0);
-  std::vector<std::pair<int32_t, int32_t>> fw_stages;   // (segment, first rank row)
+  // LoRA stages as 8 groups of 4 rank rows (segment, first row, rows).  The
+  // 128- and 256-row tiles take one segment per stage (32 rank rows of it,
+  // groups past its rank empty); the 32- and 64-row tiles pack the groups of
+  // all their segments 8 to a stage, so ranks of 8 or 16 no longer leave
+  // most of a stage empty (the 7B decode batch: 116 stages instead of 150).
+  const bool pack = n_rb_big == 0 && SBM <= kFwdSmall;
+  s->fw_packed = pack;
+  struct Group { int32_t g = 0, j0 = 0, n = 0; };
+  using Stage = std::array<Group, kFwdLoraRows / 4>;
+  std::vector<Stage> fw_stages;
   for (int32_t rb = 0; rb < s->fw_n_rb; ++rb) {
     const bool big = rb < n_rb_big;
     const int32_t p0 = big ? rb * kFwdBig : s->fw_big_rows + (rb - n_rb_big) * SBM;
     const int32_t p1 = std::min(p0 + (big ? kFwdBig : SBM), routed);
     rb_info[2 * rb] = (int32_t)fw_stages.size();
-    if (p0 < p1)
-      for (int32_t g = pos_seg[p0]; g <= pos_seg[p1 - 1]; ++g)
-        for (int32_t j0 = 0; j0 < s->seg_rank[g]; j0 += kFwdLoraRows) fw_stages.emplace_back(g, j0);
+    if (p0 < p1) {
+      size_t u = Stage().size();
+      for (int32_t g = pos_seg[p0]; g <= pos_seg[p1 - 1]; ++g) {
+        const int32_t r = s->seg_rank[g];
+        if (pack) {
+          for (int32_t j0 = 0; j0 < r; j0 += 4) {
+            if (u == Stage().size()) fw_stages.emplace_back(), u = 0;
+            fw_stages.back()[u++] = Group{g, j0, std::min(4, r - j0)};
+          }
+        } else {
+          for (int32_t j0 = 0; j0 < r; j0 += kFwdLoraRows) {
+            Stage st;
+            for (size_t v = 0; v < st.size(); ++v) {
+              const int32_t jg = j0 + 4 * (int32_t)v;
+              st[v] = Group{g, jg, std::max(0, std::min(4, r - jg))};
+            }
+            fw_stages.push_back(st);
+          }
+        }
+      }
+    }
     rb_info[2 * rb + 1] = (int32_t)fw_stages.size() - rb_info[2 * rb];
   }
   s->fw_n_stages = (int32_t)fw_stages.size();
@@ -691,13 +720,28 @@ void build_tiles(slora_segments* s) {
     std::memcpy(b + s->fw_rb_info_off, rb_info.data(), rb_info.size() * 4);
     for (int pr = 0; pr < np; ++pr)
       for (int32_t e = 0; e < s->fw_n_stages; ++e) {
-        const int32_t g = fw_stages[e].first, j0 = fw_stages[e].second, r = s->seg_rank[g];
+        const Stage& st = fw_stages[e];
         int32_t* ent = b + s->fw_stages_off + ((int64_t)pr * s->fw_n_stages + e) * kFwdStageWords;
-        const int32_t* src = s->b_pages.data() + (size_t)pr * s->sum_r + s->seg_page_off[g];
-        for (int32_t i = 0; i < kFwdLoraRows; ++i) ent[i] = src[std::min(j0 + i, r - 1)];
-        ent[FWS_SEG] = g;
-        ent[FWS_J0] = j0;
-        ent[FWS_RANK] = r;
+        const int32_t* bp = s->b_pages.data() + (size_t)pr * s->sum_r;
+        // Rows with no rank row of their own (past a group's rows, or in an
+        // empty group) repeat the page of the last row before them; their
+        // A column is zero.  Group 0 always holds rows.
+        int32_t last = bp[s->seg_page_off[st[0].g] + st[0].j0];
+        for (size_t v = 0; v < st.size(); ++v) {
+          const Group& q = st[v];
+          for (int32_t k = 0; k < 4; ++k) {
+            if (k < q.n) last = bp[s->seg_page_off[q.g] + q.j0 + k];
+            ent[4 * v + k] = last;
+          }
+          if (pack)
+            ent[FWS_GROUP + v] = q.n > 0 ? (int32_t)(((uint32_t)q.g << 9) | ((uint32_t)(q.j0 >> 2) << 3) | (uint32_t)q.n)
+                                         : 0;
+        }
+        if (!pack) {
+          ent[FWS_SEG] = st[0].g;
+          ent[FWS_J0] = st[0].j0;
+          ent[FWS_RANK] = s->seg_rank[st[0].g];
+        }
       }
   }
 
@@ -1346,6 +1390,8 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
     return fail(SLORA_E_INVAL, f + ": needs h_in a multiple of " + std::to_string(kFwdBK) +
                                    " and h_out a multiple of " + std::to_string(kFwdBN));
   if (s->n_tokens == 0) return SLORA_OK;
+  if (s->fw_packed && s->seg_adapter.size() >= ((size_t)1 << 23))
+    return fail(SLORA_E_INVAL, f + ": more than 2^23 - 1 segments on the 32- and 64-row tiles");
   const bool routed = !s->perm.empty();
   if (!x || !w || !y || (routed && !workspace)) return fail(SLORA_E_INVAL, f + ": NULL x, w, y or workspace");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(y) |
