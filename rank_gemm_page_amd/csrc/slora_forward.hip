@@ -33,10 +33,10 @@ namespace slora {
 // g in B rows 0..31 and, in A, s v[t, j] 2^-e_t for the positions t of g
 // (zero for the others) split into an fp16 high part (k 0..31) and the
 // rounding remainder (k 32..63); both sub-steps multiply the same B rows, so
-// the matrix cores see s v with about 22 significant bits.  The 32- and
-// 64-row tiles pack their steps: B rows 4u .. 4u+3 hold up to 4 rank rows of
-// any of the tile's segments (group u), and the A column of such a row is
-// nonzero only for the positions of that row's segment.  e_t puts the
+// the matrix cores see s v with about 22 significant bits.  The 128-column
+// tiles pack their steps: B rows 4u .. 4u+3 hold up to 4 rank rows of any of
+// the tile's segments (group u), and the A column of such a row is nonzero
+// only for the positions of that row's segment.  e_t puts the
 // position's largest |s v| in [2^14, 2^15); the accumulators are scaled back
 // by 2^e_t (exact) after the LoRA steps, before the x W steps.
 
@@ -60,9 +60,10 @@ struct FwdTile {
   // LoRA steps with page rows two steps ahead and stage tables four ahead
   // where the registers allow; the 256 x 256 tile keeps one step ahead.
   static constexpr bool DEEP = BM * BN <= 128 * 256;
-  // The 32- and 64-row tiles read the packed stage table (groups of 4 rank
-  // rows of any segment); the others one segment per stage.
-  static constexpr bool PACK = BM <= kFwdSmall;
+  // The 128-column tiles (32, 64 and 128 rows: batches without 256-row
+  // tiles) read the packed stage table (groups of 4 rank rows of any
+  // segment); the 256-column tiles one segment per stage.
+  static constexpr bool PACK = BN == kFwdBN;
   static constexpr int EP = BM < 128 ? BM : 128;    // rows per epilogue pass
   static_assert(EP * EpiPitchDw <= 2 * StageDw, "an epilogue pass reuses the stage buffers");
   static_assert(RW <= EP && EP % RW == 0, "epilogue passes hold whole waves");

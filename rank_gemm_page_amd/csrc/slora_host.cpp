@@ -164,7 +164,7 @@ struct slora_segments {
   // blocks), the rest in 128 x 128 tiles; fw_n_rb counts both kinds.
   int32_t fw_big_rows = 0, fw_n_rb_big = 0;
   int32_t fw_small_bm = kFwdBM;    // rows of the small tiles (128, or 64 / 32 for batches below one tile per CU)
-  bool fw_packed = false;          // LoRA stages in the packed layout (the 32- and 64-row tiles)
+  bool fw_packed = false;          // LoRA stages in the packed layout (batches without 256-row tiles)
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
@@ -650,12 +650,13 @@ void build_tiles(slora_segments* s) {
   for (int32_t g = 0; g < S; ++g)
     for (int32_t i = s->seg_start[g]; i < s->seg_start[g + 1]; ++i) pos_seg[i] = g;
   std::vector<int32_t> rb_info(2 * (size_t)s->fw_n_rb, 0);
-  // LoRA stages as 8 groups of 4 rank rows (segment, first row, rows).  The
-  // 128- and 256-row tiles take one segment per stage (32 rank rows of it,
-  // groups past its rank empty); the 32- and 64-row tiles pack the groups of
-  // all their segments 8 to a stage, so ranks of 8 or 16 no longer leave
-  // most of a stage empty (the 7B decode batch: 116 stages instead of 150).
-  const bool pack = n_rb_big == 0 && SBM <= kFwdSmall;
+  // LoRA stages as 8 groups of 4 rank rows (segment, first row, rows).  On
+  // batches with 256-row tiles every tile takes one segment per stage (32
+  // rank rows of it, groups past its rank empty); the 128-column tiles of
+  // the other batches pack the groups of all their segments 8 to a stage, so
+  // ranks of 8 or 16 no longer leave most of a stage empty (the 7B decode
+  // batch: 116 stages instead of 150).
+  const bool pack = n_rb_big == 0;
   s->fw_packed = pack;
   struct Group { int32_t g = 0, j0 = 0, n = 0; };
   using Stage = std::array<Group, kFwdLoraRows / 4>;
@@ -1391,7 +1392,7 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
                                    " and h_out a multiple of " + std::to_string(kFwdBN));
   if (s->n_tokens == 0) return SLORA_OK;
   if (s->fw_packed && s->seg_adapter.size() >= ((size_t)1 << 23))
-    return fail(SLORA_E_INVAL, f + ": more than 2^23 - 1 segments on the 32- and 64-row tiles");
+    return fail(SLORA_E_INVAL, f + ": more than 2^23 - 1 segments in a batch without 256-row tiles");
   const bool routed = !s->perm.empty();
   if (!x || !w || !y || (routed && !workspace)) return fail(SLORA_E_INVAL, f + ": NULL x, w, y or workspace");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(y) |

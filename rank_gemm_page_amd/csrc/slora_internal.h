@@ -122,10 +122,10 @@ constexpr int kFwdTiny = 32;       // rows of the tile for batches below one 64 
 constexpr int kFwdBK = 64;
 constexpr int kFwdLoraRows = 32;   // B page rows per LoRA stage
 // LoRA stage table entry (int32 words): the stage's 32 B page ids (rows with
-// no rank row of their own repeat the page of the row before), then, for the
-// 128- and 256-row tiles (one segment per stage), segment, first rank row and
-// rank; for the 32- and 64-row tiles (packed: rows 4u .. 4u+3 hold group u,
-// up to 4 rank rows of any segment of the row block), one word per group,
+// no rank row of their own repeat the page of the row before), then, on
+// batches with 256-row tiles (one segment per stage), segment, first rank row
+// and rank; otherwise (packed: rows 4u .. 4u+3 hold group u, up to 4 rank
+// rows of any segment of the row block), one word per group,
 // segment << 9 | first rank row / 4 << 3 | rows (0: an empty group).
 constexpr int kFwdStageWords = 40;
 enum : int32_t { FWS_SEG = 32, FWS_J0 = 33, FWS_RANK = 34, FWS_GROUP = 32 };
