@@ -69,7 +69,7 @@ def load_traffic(config, dominant, kind="fused"):
             sum(avg) if all(a is not None for a in avg) else None)
 
 
-def cpu_baseline(w, budget_s=10.0):
+def cpu_baseline(w, budget_s=10.0, one_thread=True):
     """The fp64 oracle on the host cores over a bounded sample of the batch."""
     import numpy as np
 
@@ -105,6 +105,8 @@ def cpu_baseline(w, budget_s=10.0):
                      f"{passes} passes in {elapsed:.1f} s, fp64 NumPy, page-table walk per token",
            "host_cpu_count": os.cpu_count()}
     # the same sample with the BLAS pool held to one thread, a shorter run
+    if not one_thread:
+        return out
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
@@ -381,82 +383,112 @@ def measure_forward(dw, w, steps, flush, stream):
                       "shrink and the base-plus-delta kernel"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="decode7b",
-                    choices=["tiny", "decode7b", "prefill7b", "mixed13b", "mlp70b"])
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--flush-mib", type=int, default=1024,
-                    help="device copy between steps that evicts the last-level cache (0: none)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mfma-min-tokens", type=int, default=None)
-    ap.add_argument("--gemv-expand-elems", type=int, default=None)
-    ap.add_argument("--mfma-expand-cols", type=int, default=None)
-    ap.add_argument("--mfma-shrink-splits", type=int, default=None)
-    ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
-    ap.add_argument("--tile-order", type=int, default=None,
-                    help="0: tiles in adapter order, 1: clustered by rank, 2 (default): most bytes first")
-    ap.add_argument("--fwd-group", type=int, default=None,
-                    help="row blocks per group of the base-plus-delta tile order (0: automatic)")
-    ap.add_argument("--fwd-tile", type=int, default=None, choices=[0, 32, 64, 128, 256],
-                    help="base-plus-delta tile (0: automatic)")
-    ap.add_argument("--staged", action="store_true",
-                    help="time the two stages as separate launches (slora_lora_shrink / _expand)")
-    ap.add_argument("--prefetch", type=int, default=0, metavar="M",
-                    help="also fetch M adapters the batch does not use from pinned host images "
-                         "on a second stream, alone and while the step runs (slora_load_adapters_async)")
-    ap.add_argument("--base-gemm", action="store_true",
-                    help="also time the base products x W of the same step (torch.mm) for context")
-    ap.add_argument("--forward", action="store_true",
-                    help="also time the base product with the delta in the same tiles "
-                         "(slora_lora_forward) against torch.mm + slora_lora_delta")
-    ap.add_argument("--bmm-baseline", action="store_true",
-                    help="also time the padded-BMM path (torch) on the same batch for comparison")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run a plain copy of this size (PMC calibration runs)")
-    args = ap.parse_args()
+def host_cpu_model():
+    """The host CPU's model name (lscpu's "Model name", else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported; the delta shards by tokens or columns with no exchange, and this "
-              "build measures one GPU's share.", file=sys.stderr, flush=True)
-        sys.exit(3)
 
+def measure_achievable(dw, w, launch_bytes, flush, stream, reps=5):
+    """What the GPU delivers for one launch of the delta's size, cold, timed
+    with dispatch-recorded events like the delta kernel: a contiguous streaming
+    read of the launch's algorithmic bytes, and a gather (streaming hint) of as
+    many whole page rows of the same pool as the launch reads adapter rows
+    (random page ids of the same classes, so the same row sizes and the same
+    scatter over the pool).  Each probe is the best of a few load depths."""
     import numpy as np
     import torch
 
+    from rank_gemm_page_amd import slora as S
+    from rank_gemm_page_amd.hip_events import HipEvent
+    dev = dw.device
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    nbytes = (int(launch_bytes) + 15) // 16 * 16
+    src = torch.ones(nbytes // 2, dtype=torch.int16, device=dev)
+
+    def timed(launch):
+        ms = []
+        for _ in range(reps + 1):
+            a, b = HipEvent(), HipEvent()
+            flush()
+            launch(a.handle, b.handle)
+            b.synchronize()
+            ms.append(a.elapsed_ms(b))
+        return statistics.fmean(ms[1:])
+
+    read = {}
+    for items in (4, 8, 16):
+        for nt in (False, True):
+            read[(items, nt)] = timed(lambda a, b: S.slora_probe_read(src, nbytes, items, nt, sink, stream, a, b))
+    (ri, rnt), rms = min(read.items(), key=lambda kv: kv[1])
+    del src
+    # the launch's adapter rows: sum_rank rows of A^T (class 0) and of B (the B class)
+    r_u = int(dw.info["sum_rank"])
+    rng = np.random.default_rng(1234)
+    b_cls = 1 if w.spec.two_classes else 0
+    e = 2 if w.spec.dtype == "f16" else 4
+    arrays, gbytes, keep = [], 0, []
+    for cls, n in ((0, r_u), (b_cls, r_u)):
+        P = int(w.n_pages[cls])
+        rows = torch.from_numpy(rng.choice(P, size=min(n, P), replace=False).astype(np.int32)).to(dev)
+        keep.append(rows)
+        rb = w.page_elems(cls) * e
+        arrays.append((dw.pages[cls], rb, rb, rows, rows.numel()))
+        gbytes += rows.numel() * rb
+    gather = {}
+    for items in (4, 8, 16):
+        gather[items] = timed(lambda a, b: S.slora_probe_gather(arrays, items, sink, stream, a, b))
+    gi, gms = min(gather.items(), key=lambda kv: kv[1])
+    return {"stream_read_GBps": round(nbytes / (rms * 1e-3) / 1e9, 1), "stream_read_bytes": nbytes,
+            "stream_read_us": round(rms * 1e3, 3), "stream_read_loads_in_flight": ri,
+            "stream_read_nontemporal": rnt,
+            "row_gather_GBps": round(gbytes / (gms * 1e-3) / 1e9, 1), "row_gather_bytes": gbytes,
+            "row_gather_us": round(gms * 1e3, 3), "row_gather_loads_in_flight": gi,
+            "method": "slora_probe_read / slora_probe_gather (one launch each, cache flushed "
+                      "before each, dispatch-recorded HIP events, mean of "
+                      f"{reps} after one untimed); best over 16-byte loads in flight per thread "
+                      "{4, 8, 16} (and the streaming hint on or off for the read)"}
+
+
+CONFIG_ORDER = ["decode7b", "tiny", "prefill7b", "mixed13b", "mlp70b"]
+
+
+def measure_config(name, args, tuning, dev, headline):
+    """One workload: the timed steps, the kernel's own duration, the roofline
+    against 8 TB/s and against the achievable probes, and the CPU oracle."""
+    import numpy as np
+    import torch
+
+    from rank_gemm_page_amd import slora as S
     from rank_gemm_page_amd.device_workload import DeviceWorkload
+    from rank_gemm_page_amd.hip_events import HipEvent
     from synth import CONFIGS, generate
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    log(f"[bench] generating {args.config} seed={args.seed}")
-    w = generate(CONFIGS[args.config], args.seed)
-    log("[bench] loading pool")
-    from rank_gemm_page_amd import slora as S
-    tuning = {k: v for k, v in ((S.SLORA_TUNE_MFMA_MIN_TOKENS, args.mfma_min_tokens),
-                                (S.SLORA_TUNE_GEMV_EXPAND_ELEMS, args.gemv_expand_elems),
-                                (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
-                                (S.SLORA_TUNE_MFMA_SHRINK_SPLITS, args.mfma_shrink_splits),
-                                (S.SLORA_TUNE_XCDS, args.xcds),
-                                (S.SLORA_TUNE_TILE_ORDER, args.tile_order),
-                                (S.SLORA_TUNE_FWD_GROUP, args.fwd_group),
-                                (S.SLORA_TUNE_FWD_TILE, args.fwd_tile))
-              if v is not None}
+    t_cfg = time.perf_counter()
+    log(f"[bench] generating {name} seed={args.seed}")
+    w = generate(CONFIGS[name], args.seed)
+    log(f"[bench] {name}: loading pool")
     dw = DeviceWorkload(w, dev, tuning=tuning)
     spec = w.spec
     n_proj = spec.n_proj
     info = dw.info
-    log(f"[bench] T={w.T} segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
-        f"shrink_tiles={info['n_shrink_tiles']} expand_tiles={info['n_expand_tiles']}")
+    log(f"[bench] {name}: T={w.T} segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
+        f"shrink_tiles={info['n_shrink_tiles']} expand_tiles={info['n_expand_tiles']} "
+        f"(set up in {time.perf_counter() - t_cfg:.1f} s)")
 
     stream = torch.cuda.current_stream(dev)
     half = args.flush_mib * (1 << 20) // 2
@@ -500,7 +532,7 @@ def main():
         step(ev[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"[bench] {K} timed steps done in {wall * 1e3:.1f} ms wall (flushes included)")
+    log(f"[bench] {name}: {K} timed steps done in {wall * 1e3:.1f} ms wall (flushes included)")
 
     step_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][2]) for p in range(n_proj)) for k in range(K)]
     ms = statistics.fmean(step_ms)
@@ -513,7 +545,6 @@ def main():
         # Second timed pass over the same steps: events recorded by the dispatch
         # itself give the fused kernel's own duration (what rocprofv3 reports);
         # recording them costs launch time, so this pass does not feed ms_per_step.
-        from rank_gemm_page_amd.hip_events import HipEvent
         kev = [[(HipEvent(), HipEvent()) for _ in range(n_proj)] for _ in range(K)]
         torch.cuda.synchronize()
         for k in range(K):
@@ -524,15 +555,14 @@ def main():
             row[-1][1].synchronize()
         kern_ms = [sum(kev[k][p][0].elapsed_ms(kev[k][p][1]) for p in range(n_proj))
                    for k in range(K)]
-        log(f"[bench] {K} dispatch-timed steps done")
+        log(f"[bench] {name}: {K} dispatch-timed steps done")
     assert S.slora_segments_read_error(dw.seg, stream) == 0, "a fused launch gave up waiting"
 
     # Host segment build and metadata upload, timed apart (PCIe-inclusive figures).
-    ids = w.ids
     builds = []
     for _ in range(20):
         t = time.perf_counter()
-        seg = S.slora_build_segments(dw.pool, ids)
+        seg = S.slora_build_segments(dw.pool, w.ids)
         builds.append(time.perf_counter() - t)
         S.slora_segments_destroy(seg)
     up_ms = []
@@ -554,50 +584,63 @@ def main():
             flush()
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
+    e = 2 if spec.dtype == "f16" else 4
     sb, eb = dw.algorithmic_bytes()
     sf, ef = dw.algorithmic_flops()
-    # per step: each projection moves its own pages and y; x counted once per launch
-    bytes_shrink, bytes_expand = n_proj * sb, n_proj * eb
+    launch_bytes = sb + eb        # one projection: its adapters' pages, x once, y read and written
+    # One step's algorithmic bytes: every projection's pages and y, each distinct x once
+    n_x = len(set(spec.proj_x))
+    routed = int(info["n_routed"])
+    step_bytes = n_proj * launch_bytes - (n_proj - n_x) * routed * spec.h_in * e
     flops = n_proj * (sf + ef)
     if args.staged:
         dominant = "shrink_kernel" if sh_ms >= ex_ms else "expand_kernel"
         dom_ms = max(sh_ms, ex_ms) / n_proj
         dom_bytes = sb if dominant == "shrink_kernel" else eb
+        step_kern_ms = sh_ms + ex_ms
     else:
         dominant = "fused_kernel"
-        dom_ms = statistics.fmean(kern_ms) / n_proj
-        dom_bytes = sb + eb
+        step_kern_ms = statistics.fmean(kern_ms)
+        dom_ms = step_kern_ms / n_proj
+        dom_bytes = launch_bytes
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic, profiled_us = load_traffic(args.config, dominant)
-    tokens = int(info["n_routed"])
-    value = tokens / (ms * 1e-3)
+    traffic, profiled_us = load_traffic(name, dominant)
+    value = routed / (ms * 1e-3)
+    step_achieved = step_bytes / (step_kern_ms * 1e-3) / 1e9
+
+    achievable = None
+    if not args.no_probe and name != "tiny":
+        log(f"[bench] {name}: achievable-bandwidth probes")
+        achievable = measure_achievable(dw, w, launch_bytes, flush, stream)
+    best = max(achievable["stream_read_GBps"], achievable["row_gather_GBps"]) if achievable else None
 
     out = {
-        "metric": METRIC,
+        "ms_per_step": round(ms, 5),
         "value": round(value, 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": spec.dtype,
-        "data": "synthetic",
-        "config": {"workload": args.config, "description": WORKLOAD_NOTES[args.config],
-                   "tokens": tokens, "h_in": spec.h_in, "h_out": spec.h_out,
-                   "projections": n_proj, "adapters": spec.n_adapters,
+        "config": {"workload": name, "description": WORKLOAD_NOTES[name],
+                   "tokens": routed, "h_in": spec.h_in, "h_out": spec.h_out,
+                   "projections": n_proj, "distinct_x": n_x, "adapters": spec.n_adapters,
                    "segments": info["n_segments"], "mfma_segments": info["n_mfma_segments"],
-                   "seed": args.seed, "parallelism": "single GPU",
+                   "sum_rank": int(info["sum_rank"]), "seed": args.seed, "parallelism": "single GPU",
                    "tuning": {str(k): v for k, v in tuning.items()}},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3),
-                     "profiled_avg_launch_us": round(profiled_us, 3) if profiled_us else None},
+                     "profiled_avg_launch_us": round(profiled_us, 3) if profiled_us else None,
+                     "achievable": achievable,
+                     "frac_of_achievable": round(achieved / best, 4) if best else None},
+        "step_roofline": {"algorithmic_bytes": step_bytes, "kernel_us": round(step_kern_ms * 1e3, 3),
+                          "achieved": round(step_achieved, 1), "unit": "GB/s",
+                          "frac": round(step_achieved / HBM_PEAK_GBPS, 4),
+                          "frac_of_achievable": round(step_achieved / best, 4) if best else None,
+                          "bytes": "per step: each projection's distinct adapter pages once, each "
+                                   "distinct x once, every projection's y read and written"},
         "kernels": {**({"shrink_us": round(sh_ms * 1e3 / n_proj, 3),
                         "expand_us": round(ex_ms * 1e3 / n_proj, 3),
                         "shrink_GBps": round(sb / (sh_ms / n_proj * 1e-3) / 1e9, 1),
@@ -605,16 +648,139 @@ def main():
                        if args.staged else {"launch": "fused (one kernel per projection)",
                                             "fused_kernel_us": round(dom_ms * 1e3, 3),
                                             "fused_step_us": round(ms * 1e3 / n_proj, 3)}),
-                    "step_GBps": round((bytes_shrink + bytes_expand) / (ms * 1e-3) / 1e9, 1),
-                    "step_frac_hbm_peak": round((bytes_shrink + bytes_expand) / (ms * 1e-3) / 1e9
-                                                / HBM_PEAK_GBPS, 4),
-                    "mfma_frac_f16_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 5),
+                    "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                    "step_frac_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                     "step_us_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 3),
                     "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 3),
                     "shrink_tiles": info["n_shrink_tiles"], "expand_tiles": info["n_expand_tiles"]},
         "host_build_us": round(build_us, 1),
         "metadata_upload_us": round(upload_us, 2),
         "metadata_bytes": int(info["meta_bytes"]),
+        "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
+    }
+    # Matrix-core use: flops over the kernels' own time against the fp16 dense
+    # peak, and against the attainable roofline min(peak, AI x 8 TB/s) at this
+    # batch's arithmetic intensity.
+    tflops = flops / (step_kern_ms * 1e-3) / 1e12
+    ai = flops / step_bytes
+    attainable = min(MFMA_F16_PEAK_TFLOPS, ai * HBM_PEAK_GBPS / 1e3)
+    out["mfma"] = {"achieved_TFLOPs": round(tflops, 2), "peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
+                   "frac_of_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 5),
+                   "flops_per_step": flops, "arithmetic_intensity": round(ai, 3),
+                   "attainable_TFLOPs": round(attainable, 2),
+                   "frac_of_attainable": round(tflops / attainable, 4),
+                   "note": "fp16 flops of the matrix-core and vector-ALU tiles together "
+                           "(2 sum_t r_t (h_in + h_out) per projection)"}
+    if headline:
+        if args.base_gemm:
+            log("[bench] base x W products")
+            out["base_gemm"] = measure_base_gemm(dw, w, K, flush, stream, ms)
+        if args.forward:
+            log("[bench] base product with the delta in the same tiles")
+            out["forward"] = measure_forward(dw, w, K, flush, stream)
+        if args.bmm_baseline:
+            log("[bench] padded-BMM comparison path")
+            out["bmm_path"] = measure_bmm_path(dw, w, K, flush, stream, ms)
+        if args.prefetch > 0:
+            log(f"[bench] adapter fetch: {args.prefetch} adapters per step")
+            out["prefetch"] = measure_prefetch(dw, w, args.prefetch, K, flush, step, stream)
+    dw.close()
+    del dw, flush_src, flush_dst
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log(f"[bench] {name}: timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(w, budget_s=10.0 if headline else 3.0, one_thread=headline)
+        out["cpu_baseline"]["host_cpu_model"] = host_cpu_model()
+    log(f"[bench] {name}: done in {time.perf_counter() - t_cfg:.1f} s")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="all", choices=["all"] + CONFIG_ORDER,
+                    help="all (default): decode7b as the headline, the other four under per_config")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="device copy between steps that evicts the last-level cache (0: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the achievable-bandwidth probes")
+    ap.add_argument("--mfma-min-tokens", type=int, default=None)
+    ap.add_argument("--gemv-expand-elems", type=int, default=None)
+    ap.add_argument("--mfma-expand-cols", type=int, default=None)
+    ap.add_argument("--mfma-shrink-splits", type=int, default=None)
+    ap.add_argument("--xcds", type=int, default=None, help="XCD groups of the tile placement (1: none)")
+    ap.add_argument("--tile-order", type=int, default=None,
+                    help="0: tiles in adapter order, 1: clustered by rank, 2 (default): most bytes first")
+    ap.add_argument("--fwd-group", type=int, default=None,
+                    help="row blocks per group of the base-plus-delta tile order (0: automatic)")
+    ap.add_argument("--fwd-tile", type=int, default=None, choices=[0, 32, 64, 128, 256],
+                    help="base-plus-delta tile (0: automatic)")
+    ap.add_argument("--staged", action="store_true",
+                    help="time the two stages as separate launches (slora_lora_shrink / _expand)")
+    ap.add_argument("--prefetch", type=int, default=0, metavar="M",
+                    help="also fetch M adapters the batch does not use from pinned host images "
+                         "on a second stream, alone and while the step runs (slora_load_adapters_async)")
+    ap.add_argument("--base-gemm", action="store_true",
+                    help="also time the base products x W of the same step (torch.mm) for context")
+    ap.add_argument("--forward", action="store_true",
+                    help="also time the base product with the delta in the same tiles "
+                         "(slora_lora_forward) against torch.mm + slora_lora_delta")
+    ap.add_argument("--bmm-baseline", action="store_true",
+                    help="also time the padded-BMM path (torch) on the same batch for comparison")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain copy of this size (PMC calibration runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; the delta shards by tokens or columns with no exchange, and this "
+              "build measures one GPU's share.", file=sys.stderr, flush=True)
+        sys.exit(3)
+
+    import torch
+
+    from rank_gemm_page_amd import slora as S
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tuning = {k: v for k, v in ((S.SLORA_TUNE_MFMA_MIN_TOKENS, args.mfma_min_tokens),
+                                (S.SLORA_TUNE_GEMV_EXPAND_ELEMS, args.gemv_expand_elems),
+                                (S.SLORA_TUNE_MFMA_EXPAND_COLS, args.mfma_expand_cols),
+                                (S.SLORA_TUNE_MFMA_SHRINK_SPLITS, args.mfma_shrink_splits),
+                                (S.SLORA_TUNE_XCDS, args.xcds),
+                                (S.SLORA_TUNE_TILE_ORDER, args.tile_order),
+                                (S.SLORA_TUNE_FWD_GROUP, args.fwd_group),
+                                (S.SLORA_TUNE_FWD_TILE, args.fwd_tile))
+              if v is not None}
+    names = CONFIG_ORDER if args.config == "all" else [args.config]
+    t_all = time.perf_counter()
+    results = {n: measure_config(n, args, tuning, dev, headline=(i == 0)) for i, n in enumerate(names)}
+    head = results[names[0]]
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        **{k: v for k, v in head.items() if k not in ("value", "unit", "ms_per_step", "dtype", "config",
+                                                     "roofline")},
         "timing": "ms_per_step: HIP events recorded on the launch stream around each step's "
                   "delta launch(es); roofline.avg_launch_us: a second pass over as many steps "
                   "with HIP events recorded by the kernel dispatch itself "
@@ -622,24 +788,10 @@ def main():
                   "it; means over the timed steps; a "
                   f"{args.flush_mib} MiB device copy before every step evicts the 256 MB "
                   "last-level cache and is outside both",
-        "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
     }
-    if args.base_gemm:
-        log("[bench] base x W products")
-        out["base_gemm"] = measure_base_gemm(dw, w, K, flush, stream, ms)
-    if args.forward:
-        log("[bench] base product with the delta in the same tiles")
-        out["forward"] = measure_forward(dw, w, K, flush, stream)
-    if args.bmm_baseline:
-        log("[bench] padded-BMM comparison path")
-        out["bmm_path"] = measure_bmm_path(dw, w, K, flush, stream, ms)
-    if args.prefetch > 0:
-        log(f"[bench] adapter fetch: {args.prefetch} adapters per step")
-        out["prefetch"] = measure_prefetch(dw, w, args.prefetch, K, flush, step, stream)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(w)
-    dw.close()
+    if len(names) > 1:
+        out["per_config"] = {n: results[n] for n in names[1:]}
+    out["bench_wall_s"] = round(time.perf_counter() - t_all, 1)
     print(json.dumps(out), flush=True)
 
 

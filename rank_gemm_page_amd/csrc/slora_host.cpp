@@ -107,6 +107,8 @@ int shrink_nck(int32_t dtype, int32_t h_in) {
 
 }  // namespace
 
+void slora::set_last_error(const char* msg) { g_last_error = msg; }
+
 struct slora_pool {
   slora_pool_desc d{};
   int elem = 2;

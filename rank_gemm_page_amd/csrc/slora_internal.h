@@ -10,6 +10,10 @@
 
 namespace slora {
 
+// Record the calling thread's message for slora_last_error() (for sources
+// other than the host runtime's C ABI).
+void set_last_error(const char* msg);
+
 // A tile record is a run of int32 words:
 //   [0] kind        KIND_{SHRINK,EXPAND}_{GEMV,MFMA}: bit 0 set for the
 //                   matrix-core (MFMA) tiles, bit 1 set for expand tiles

@@ -38,6 +38,8 @@ EXPORTED = [
     "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
     "slora_lora_forward", "slora_lora_forward_timed", "slora_last_error",
 ]
+# include/slora_probe.h: bandwidth probes (measurement only)
+EXPORTED_PROBE = ["slora_probe_read", "slora_probe_gather"]
 
 
 class SloraError(RuntimeError):
@@ -102,6 +104,9 @@ def lib():
             "slora_lora_forward": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P]),
             "slora_lora_forward_timed": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P, P, P]),
             "slora_last_error": (ctypes.c_char_p, []),
+            "slora_probe_read": (c_int32, [P, c_int64, c_int32, c_int32, P, P, P, P]),
+            "slora_probe_gather": (c_int32, [P, c_int64, c_int64, P, c_int64, P, c_int64, c_int64, P,
+                                             c_int64, c_int32, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -364,3 +369,19 @@ def slora_lora_forward_timed(pool, seg, proj: int, x, w, y, workspace, workspace
     _check(lib().slora_lora_forward_timed(pool, seg, proj, _ptr(x), _ptr(w), _ptr(y),
                                           _ptr(workspace), int(workspace_bytes), _stream(stream),
                                           start_event, stop_event), "slora_lora_forward_timed")
+
+
+def slora_probe_read(src, nbytes: int, items: int, nontemporal: bool, sink, stream=None,
+                     start_event=None, stop_event=None) -> None:
+    _check(lib().slora_probe_read(_ptr(src), int(nbytes), int(items), int(bool(nontemporal)), _ptr(sink),
+                                  _stream(stream), start_event, stop_event), "slora_probe_read")
+
+
+def slora_probe_gather(arrays, items: int, sink, stream=None, start_event=None, stop_event=None) -> None:
+    """arrays: one or two (base, stride_bytes, row_bytes, rows_device_int32, n_rows) tuples."""
+    a0 = arrays[0]
+    a1 = arrays[1] if len(arrays) > 1 else (0, 0, 0, 0, 0)
+    _check(lib().slora_probe_gather(_ptr(a0[0]), int(a0[1]), int(a0[2]), _ptr(a0[3]), int(a0[4]),
+                                    _ptr(a1[0]), int(a1[1]), int(a1[2]), _ptr(a1[3]), int(a1[4]),
+                                    int(items), _ptr(sink), _stream(stream), start_event, stop_event),
+           "slora_probe_gather")

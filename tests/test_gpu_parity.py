@@ -290,18 +290,15 @@ def sample_tokens(w, n, seed=0):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,n_sample", [("decode7b", None), ("prefill7b", 48),
-                                           ("mixed13b", 40), ("mlp70b", 40)])
-def test_full_size_config(name, n_sample):
+@pytest.mark.parametrize("name", ["decode7b", "prefill7b", "mixed13b", "mlp70b"])
+def test_full_size_config(name):
+    """Every token of every projection of the benchmark batches against the oracle."""
     w = generate(CONFIGS[name], 0)
     ys, info = run_gpu(w, "default")
     print(f"[gpu] {name}: segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
           f"shrink_tiles={info['n_shrink_tiles']} expand_tiles={info['n_expand_tiles']}", flush=True)
     st = build_from_workload(w)
-    toks = None if n_sample is None else sample_tokens(w, n_sample)
     for p, y in enumerate(ys):
-        y_ref, sd_ref = workload_delta(st, w, proj=p, tokens=toks)
-        got = y if toks is None else y[toks]
-        check_gates(got, y_ref, sd_ref, np.float16, f"{name}/p{p}")
-        # rows of tokens outside the sample are still finite (no NaN page was read)
-        assert np.isfinite(y).all()
+        y_ref, sd_ref = workload_delta(st, w, proj=p)
+        check_gates(y, y_ref, sd_ref, np.float16, f"{name}/p{p}")
+        print(f"[gpu] {name}/p{p}: all {w.T} tokens within the gates", flush=True)

@@ -33,13 +33,19 @@ def make_pool(w, base=FAKE_BASE, tuning=None):
     return pool, kv
 
 
-def test_library_exports_every_declared_symbol():
-    header = open(os.path.join(ROOT, "include", "slora.h")).read()
-    declared = set(re.findall(r"\b(slora_[a-z_]+)\s*\(", header))
-    assert declared == set(S.EXPORTED)
+@pytest.mark.parametrize("header,names", [("slora.h", S.EXPORTED), ("slora_probe.h", S.EXPORTED_PROBE)])
+def test_library_exports_every_declared_symbol(header, names):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)        # declarations only, not comments
+    declared = set(re.findall(r"\b(slora_[a-z_]+)\s*\(", text))
+    assert declared == set(names)
     lib = S.lib()
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["slora.h", "slora_probe.h"]
 
 
 @pytest.mark.parametrize("case", ["single_class", "two_class_two_proj"])

@@ -162,6 +162,80 @@ def test_integer_brute_force(dtype, h, rank_set):
 
 
 # ---------------------------------------------------------------------------
+# The one rounding of the result to the output type (reading 6: round to
+# nearest, ties to even, straight from the exact value).  Each fixture value is
+# a tie or sits next to one, worked out by hand from the IEEE binary16 and
+# binary32 formats: in [2048, 4096) binary16 values are 2 apart and in
+# [4096, 8192) 4 apart, binary32 values in [2^24, 2^25) are 2 apart, and at a
+# tie the result is the neighbour whose last significand bit is 0.
+
+ROUND_PINS = {
+    np.float16: [
+        (2049.0, 2048.0),             # tie between 2048 (even) and 2050
+        (2051.0, 2052.0),             # tie between 2050 and 2052 (even)
+        (-2051.0, -2052.0),           # the same, negative
+        (4097.0, 4096.0),             # a quarter of the way: nearest, not a tie
+        (4098.0, 4096.0),             # tie between 4096 (even) and 4100
+        (4102.0, 4104.0),             # tie between 4100 and 4104 (even)
+        (4103.0, 4104.0),             # three quarters of the way
+        (2049.0 + 2.0 ** -30, 2050.0),  # just above a tie: no detour through binary32
+        (2.0 ** -25, 0.0),            # tie between 0 (even) and the least subnormal
+        (3 * 2.0 ** -25, 2.0 ** -23), # tie between 2^-24 and 2^-23 (even)
+        (65519.0, 65504.0),           # below the tie with 65536: the largest finite value
+        (65520.0, np.inf),            # the tie rounds to even, past the largest finite value
+    ],
+    np.float32: [
+        (16777217.0, 16777216.0),     # 2^24 + 1: tie between 2^24 (even) and 2^24 + 2
+        (16777219.0, 16777220.0),     # tie between 2^24 + 2 and 2^24 + 4 (even)
+        (-16777217.0, -16777216.0),
+        (16777217.0 + 2.0 ** -20, 16777218.0),   # just above a tie
+        (1.0 + 2.0 ** -24, 1.0),      # half an ulp above 1: tie, to 1 (even)
+        (1.0 + 3 * 2.0 ** -24, 1.0 + 2.0 ** -22),  # tie between 1 + 2^-23 and 1 + 2^-22 (even)
+    ],
+}
+
+
+def _round_pin_failures(fn):
+    bad = []
+    for dt, cases in ROUND_PINS.items():
+        got = fn(np.array([c[0] for c in cases], np.float64), dt)
+        for (val, want), g in zip(cases, np.asarray(got)):
+            if not (g == want and np.asarray(g).dtype == np.dtype(dt)):
+                bad.append((dt.__name__, val, want, float(g)))
+    return bad
+
+
+def test_round_to_ties_to_even():
+    with np.errstate(over="ignore"):
+        assert _round_pin_failures(orc.round_to) == []
+
+
+def _truncate(y, dt):
+    r = np.asarray(y, np.float64).astype(dt)
+    return np.where(np.abs(r.astype(np.float64)) > np.abs(y), np.nextafter(r, dt(0)), r).astype(dt)
+
+
+def _half_away(y, dt):
+    r = np.asarray(y, np.float64).astype(dt)
+    lo = np.where(r.astype(np.float64) > y, np.nextafter(r, dt(-np.inf)), r)
+    hi = np.where(r.astype(np.float64) < y, np.nextafter(r, dt(np.inf)), r)
+    dlo, dhi = y - lo.astype(np.float64), hi.astype(np.float64) - y
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (y > 0))
+    return np.where(pick_hi, hi, lo).astype(dt)
+
+
+def _via_f32(y, dt):
+    return np.asarray(y, np.float64).astype(np.float32).astype(dt)
+
+
+@pytest.mark.parametrize("planted", [_truncate, _half_away, _via_f32],
+                         ids=["truncate", "ties_away", "double_rounding"])
+def test_round_pins_catch_planted_roundings(planted):
+    with np.errstate(over="ignore", invalid="ignore"):
+        assert _round_pin_failures(planted), f"{planted.__name__} passed every rounding pin"
+
+
+# ---------------------------------------------------------------------------
 # Invariants
 
 
