@@ -170,6 +170,7 @@ struct slora_segments {
   int64_t error_off_words = 0;     // one error word (zeroed on device at upload), padding
   int64_t vtag_off_words = 0;      // fused-launch v pairs (zeroed on device at upload)
   int32_t gemv_rows = 0;
+  bool pipe_expand = false;        // a vector-ALU expand thread holds more than kExpandRowSet B rows
   const int32_t* dev_meta = nullptr;
   mutable uint32_t epoch = 0;      // fused launches since the last upload
 };
@@ -414,8 +415,6 @@ void build_tiles(slora_segments* s) {
   const bool f16 = p->d.dtype == SLORA_F16;
   const int vec = f16 ? 8 : 4;
   const int nck = shrink_nck(p->d.dtype, hin);
-  const int gemv_rows = kShrinkRowBudget / nck;
-  s->gemv_rows = gemv_rows;
 
   // Matrix-core tiles need fp16, h_in a multiple of 64 and a y that the
   // expand can address through one buffer descriptor.
@@ -446,6 +445,8 @@ void build_tiles(slora_segments* s) {
   }
   if (mfma_blocks == 0) splits = 1;
   s->n_splits = splits;
+  const int gemv_rows = kShrinkRowBudget / nck;
+  s->gemv_rows = gemv_rows;
 
   int64_t expand_elems = p->tune.gemv_expand_elems;
   if (expand_elems == 0) {
@@ -491,6 +492,10 @@ void build_tiles(slora_segments* s) {
     int32_t width = vec * 256;
     while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
     const int32_t cols = mfma ? (int32_t)mfma_cols : width;
+    if (!mfma) {
+      const int32_t groups = kThreads / (width / vec);
+      if ((r + groups - 1) / groups > kExpandRowSet) s->pipe_expand = true;
+    }
     for (size_t b = 0; b < eblocks.size(); ++b) {
       const auto& tb = eblocks[b];
       const int32_t grp = n_groups + (int32_t)b;
@@ -1322,6 +1327,7 @@ DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int3
   L.y_bytes = (uint32_t)std::min<int64_t>((int64_t)s->n_tokens * p->d.h_out * elem_bytes(p->d.dtype), kMaxBufferBytes);
   L.sum_rt = (int32_t)s->sum_rt;
   L.n_combine = s->n_combine;
+  L.pipe_expand = s->pipe_expand ? 1 : 0;
   return L;
 }
 

@@ -64,6 +64,7 @@ constexpr int kMfmaPass = 128;          // columns per MFMA expand pass
 constexpr int64_t kMaxBufferBytes = 0xFFFFFF00LL;
 constexpr int kGemvMaxTok = 4;          // tokens per vector-ALU tile
 constexpr int kShrinkRowBudget = 16;    // rows x 16-byte chunks per thread (GEMV shrink)
+constexpr int kExpandRowSet = 8;        // B rows a vector-ALU expand thread loads at once
 static_assert(kTokCap >= kGemvMaxTok && kTokCap >= kMfmaExpandTok && kTokCap >= kCombineTok, "token slots");
 static_assert(kMaxRankMfma <= 64, "the MFMA shrink holds at most four 16-row blocks of A^T");
 
@@ -98,6 +99,7 @@ struct DeltaLaunch {
   int32_t n_combine;      // combine tiles (records n_shrink .. n_shrink + n_combine)
   uint32_t y_bytes;       // extent of y (n_tokens x h_out x element), < kMaxBufferBytes when has_mfma
   uint32_t epoch;
+  int32_t pipe_expand;    // some vector-ALU expand thread holds more B rows than one register set
 };
 
 // Launch the shrink kernel (stages & 1) then the expand kernel (stages & 2) on

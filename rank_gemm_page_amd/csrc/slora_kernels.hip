@@ -495,11 +495,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DeltaLaunch L) {
 // G = 256 / (width/VEC) groups of them split the r rows; the groups' partial
 // sums meet in LDS and group 0 applies y += s * d with one rounding.
 
-template <typename T, bool FUSED>
+template <typename T, bool FUSED, bool PIPE>
 __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
   constexpr int VEC = VecN<T>::N;
   constexpr int TB = kGemvMaxTok;
-  constexpr int RCH = 8;  // B rows per thread issued together
+  constexpr int RCH = kExpandRowSet;  // B rows per thread issued together
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
   const int o0 = uni(srec[REC_POS]);
@@ -520,15 +520,28 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 
   // Issue everything the tile reads before waiting on any of it: the first
   // RCH B rows of this thread, (group 0) the y chunks of the epilogue, and v
-  // (in a fused launch, once the segment's shrink tiles are done).
+  // (in a fused launch, once the segment's shrink tiles are done).  With PIPE
+  // (batches whose threads hold more than RCH B rows) the rows are
+  // software-pipelined: the next RCH rows are in flight while the current
+  // ones are used, every B load issued unconditionally at a clamped row (rows
+  // past this thread's last one re-read it, threads with no row read row 0 at
+  // column o0) so that the compiler's wait counts cover exactly the rows in
+  // use.  Without PIPE (at most RCH rows a thread, the decode batches) the
+  // second register set is not needed and more workgroups stay resident.
   const bool active = ct * VEC < ncol;
   const int nrt = (active && g < rank) ? (rank - g + G - 1) / G : 0;   // rows of this thread
-  const int64_t col_byte = (int64_t)(o0 + ct * VEC) * sizeof(T);
+  const bool has = nrt > 0;
+  const int64_t col_byte = (int64_t)(o0 + (has ? ct * VEC : 0)) * sizeof(T);
+  auto brow = [&](int i) -> const char* {
+    const int slot = has ? g + min(i, nrt - 1) * G : 0;
+    return L.pool.base_b + (int64_t)pages[slot] * L.pool.page_bytes_b + col_byte;
+  };
   uint4 bq[RCH];
 #pragma unroll
-  for (int i = 0; i < RCH; ++i)
-    bq[i] = i < nrt ? ldsel<SLORA_NT_B>(L.pool.base_b + (int64_t)pages[g + i * G] * L.pool.page_bytes_b + col_byte)
-                    : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < RCH; ++i) {
+    if constexpr (PIPE) bq[i] = ldsel<SLORA_NT_B>(brow(i));
+    else bq[i] = i < nrt ? ldsel<SLORA_NT_B>(brow(i)) : make_uint4(0, 0, 0, 0);
+  }
   uint4 yv[TB];
 #pragma unroll
   for (int k = 0; k < TB; ++k)
@@ -545,13 +558,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   for (int k = 0; k < TB; ++k)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[k][e] = 0.f;
-  for (int i0 = 0; i0 < nrt; i0 += RCH) {
-    if (i0 > 0) {
-#pragma unroll
-      for (int i = 0; i < RCH; ++i)
-        bq[i] = i0 + i < nrt ? ldsel<SLORA_NT_B>(L.pool.base_b + (int64_t)pages[g + (i0 + i) * G] * L.pool.page_bytes_b + col_byte)
-                             : make_uint4(0, 0, 0, 0);
-    }
+  auto use_rows = [&](int i0) {
 #pragma unroll
     for (int i = 0; i < RCH; ++i) {
       if (i0 + i < nrt) {
@@ -567,6 +574,31 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
           }
         }
       }
+    }
+  };
+  if constexpr (PIPE) {
+    const int nrt_u = (rank + G - 1) / G;   // rows of group 0, the most any thread has
+    for (int i0 = 0; i0 < nrt_u; i0 += RCH) {
+      uint4 nq[RCH];
+      const bool more = i0 + RCH < nrt_u;
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < RCH; ++i) nq[i] = ldsel<SLORA_NT_B>(brow(i0 + RCH + i));
+      }
+      use_rows(i0);
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < RCH; ++i) bq[i] = nq[i];
+      }
+    }
+  } else {
+    for (int i0 = 0; i0 < nrt; i0 += RCH) {
+      if (i0 > 0) {
+#pragma unroll
+        for (int i = 0; i < RCH; ++i)
+          bq[i] = i0 + i < nrt ? ldsel<SLORA_NT_B>(brow(i0 + i)) : make_uint4(0, 0, 0, 0);
+      }
+      use_rows(i0);
     }
   }
   if (G > 1) {
@@ -811,7 +843,7 @@ constexpr int kGemvLdsFloats = kGemvMaxTok * 256 + 7 * kGemvMaxTok * 256;
 constexpr int kExpandLdsFloats = kMfmaExpandLds > kGemvLdsFloats ? kMfmaExpandLds : kGemvLdsFloats;
 static_assert(kShrinkLdsFloats <= kExpandLdsFloats, "the fused kernel's LDS holds the MFMA shrink stages");
 
-template <typename T>
+template <typename T, bool PIPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void expand_kernel(DeltaLaunch L) {
   __shared__ float lds[sizeof(T) == 2 ? kExpandLdsFloats : kGemvLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
@@ -823,7 +855,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       return;
     }
   }
-  expand_gemv_tile<T, false>(L, srec, lds);
+  expand_gemv_tile<T, false, PIPE>(L, srec, lds);
 }
 
 // Both stages in one launch over the records in launch order: shrink tiles
@@ -834,7 +866,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 // Three workgroups per CU fit the matrix-core tiles' registers without
 // spilling (fewer would leave slots empty); the widest vector-ALU shrink
 // (h_in above 8192) needs more registers and runs two.
-template <typename T, int NCK, bool MFMA>
+template <typename T, int NCK, bool MFMA, bool PIPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCK == 8 ? 2 : 3)))
 void fused_kernel(DeltaLaunch L) {
   __shared__ float lds[sizeof(T) == 2 && MFMA ? kExpandLdsFloats : kGemvLdsFloats];
@@ -861,7 +893,7 @@ void fused_kernel(DeltaLaunch L) {
       return;
     }
   }
-  expand_gemv_tile<T, true>(L, srec, lds);
+  expand_gemv_tile<T, true, PIPE>(L, srec, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -895,15 +927,21 @@ static const void* shrink_fn(int nck) {
   }
 }
 
-template <typename T, bool MFMA>
+template <typename T, bool MFMA, bool PIPE>
 static const void* fused_fn(int nck) {
   switch (nck) {
-    case 1: return reinterpret_cast<const void*>(&fused_kernel<T, 1, MFMA>);
-    case 2: return reinterpret_cast<const void*>(&fused_kernel<T, 2, MFMA>);
-    case 4: return reinterpret_cast<const void*>(&fused_kernel<T, 4, MFMA>);
-    case 8: return reinterpret_cast<const void*>(&fused_kernel<T, 8, MFMA>);
+    case 1: return reinterpret_cast<const void*>(&fused_kernel<T, 1, MFMA, PIPE>);
+    case 2: return reinterpret_cast<const void*>(&fused_kernel<T, 2, MFMA, PIPE>);
+    case 4: return reinterpret_cast<const void*>(&fused_kernel<T, 4, MFMA, PIPE>);
+    case 8: return reinterpret_cast<const void*>(&fused_kernel<T, 8, MFMA, PIPE>);
     default: return nullptr;
   }
+}
+
+template <typename T>
+static const void* fused_pick(int nck, bool mfma, bool pipe) {
+  if (mfma) return pipe ? fused_fn<T, true, true>(nck) : fused_fn<T, true, false>(nck);
+  return pipe ? fused_fn<T, false, true>(nck) : fused_fn<T, false, false>(nck);
 }
 
 template <typename T>
@@ -913,7 +951,7 @@ static hipError_t launch_delta_t(const DeltaLaunch& L, int stages, hipStream_t s
   if (stages & STAGE_FUSED) {
     const int blocks = L.n_tiles;
     if (blocks == 0) return hipSuccess;
-    const void* k = (sizeof(T) == 2 && L.has_mfma) ? fused_fn<T, true>(nck) : fused_fn<T, false>(nck);
+    const void* k = fused_pick<T>(nck, sizeof(T) == 2 && L.has_mfma, L.pipe_expand != 0);
     if (!k) return hipErrorInvalidValue;
     return launch_one(k, blocks, L, stream, start, stop);
   }
@@ -934,7 +972,8 @@ static hipError_t launch_delta_t(const DeltaLaunch& L, int stages, hipStream_t s
     if (e != hipSuccess) return e;
   }
   if (ex) {
-    const void* k = reinterpret_cast<const void*>(&expand_kernel<T>);
+    const void* k = L.pipe_expand ? reinterpret_cast<const void*>(&expand_kernel<T, true>)
+                                  : reinterpret_cast<const void*>(&expand_kernel<T, false>);
     return launch_one(k, L.n_expand, L, stream, (sh || co) ? nullptr : start, stop);
   }
   return hipSuccess;
