@@ -719,6 +719,8 @@ def main():
                     help="row blocks per group of the base-plus-delta tile order (0: automatic)")
     ap.add_argument("--fwd-tile", type=int, default=None, choices=[0, 32, 64, 128, 256],
                     help="base-plus-delta tile (0: automatic)")
+    ap.add_argument("--shrink-rows", type=int, default=None,
+                    help="rank rows per vector-ALU shrink tile (0: as many as fit)")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",
@@ -758,7 +760,8 @@ def main():
                                 (S.SLORA_TUNE_XCDS, args.xcds),
                                 (S.SLORA_TUNE_TILE_ORDER, args.tile_order),
                                 (S.SLORA_TUNE_FWD_GROUP, args.fwd_group),
-                                (S.SLORA_TUNE_FWD_TILE, args.fwd_tile))
+                                (S.SLORA_TUNE_FWD_TILE, args.fwd_tile),
+                                (S.SLORA_TUNE_SHRINK_ROWS, args.shrink_rows))
               if v is not None}
     names = CONFIG_ORDER if args.config == "all" else [args.config]
     t_all = time.perf_counter()

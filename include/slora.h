@@ -132,6 +132,9 @@ void slora_pool_destroy(slora_pool* pool);
  *                                steps outnumber a tile's x W steps, 32 x 128
  *                                when it is too small for 256 tiles of
  *                                64 x 128.
+ *  SLORA_TUNE_SHRINK_ROWS      - rank rows of one vector-ALU shrink tile, at
+ *                                most 16 / (16-byte chunks of an x row per
+ *                                thread); 0 (default): that maximum.
  * They change how the work is cut, never what is computed. */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
@@ -143,7 +146,8 @@ typedef enum {
   SLORA_TUNE_XCDS = 5,
   SLORA_TUNE_TILE_ORDER = 6,
   SLORA_TUNE_FWD_GROUP = 7,
-  SLORA_TUNE_FWD_TILE = 8
+  SLORA_TUNE_FWD_TILE = 8,
+  SLORA_TUNE_SHRINK_ROWS = 9
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 

@@ -93,6 +93,7 @@ struct Tuning {
   int64_t tile_order = 2;       // 0: segment order, 1: rank-descending, 2: bytes-descending
   int64_t fwd_group = 0;        // row blocks per group of the base-plus-delta tile order (0: automatic)
   int64_t fwd_tile = 0;         // base-plus-delta tile rows: 32, 64, 128, 256, or 0 (automatic)
+  int64_t shrink_rows = 0;      // rank rows per vector-ALU shrink tile (0: as many as fit)
 };
 
 // GEMV shrink geometry: chunks of 16 bytes per thread per row, as a power of
@@ -445,7 +446,8 @@ void build_tiles(slora_segments* s) {
   }
   if (mfma_blocks == 0) splits = 1;
   s->n_splits = splits;
-  const int gemv_rows = kShrinkRowBudget / nck;
+  const int gemv_rows = p->tune.shrink_rows > 0 ? (int)std::min<int64_t>(p->tune.shrink_rows, kShrinkRowBudget / nck)
+                                                : kShrinkRowBudget / nck;
   s->gemv_rows = gemv_rows;
 
   int64_t expand_elems = p->tune.gemv_expand_elems;
@@ -915,6 +917,10 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
     case SLORA_TUNE_MFMA_SHRINK_SPLITS:
       if (value < 0 || value > kMaxSplits) return fail(SLORA_E_INVAL, "mfma_shrink_splits must be 0..4 (0: automatic)");
       p->tune.mfma_shrink_splits = value;
+      return SLORA_OK;
+    case SLORA_TUNE_SHRINK_ROWS:
+      if (value < 0 || value > kShrinkRowBudget) return fail(SLORA_E_INVAL, "shrink_rows must be 0..16 (0: automatic)");
+      p->tune.shrink_rows = value;
       return SLORA_OK;
     default:
       return fail(SLORA_E_INVAL, "slora_pool_set_tuning: unknown key");

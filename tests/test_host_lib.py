@@ -419,7 +419,9 @@ def test_tuning_validation():
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 65536 + 128) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 512)
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 0)
-        assert status_of(S.slora_pool_set_tuning, pool, 9, 1) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, 10, 1) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_SHRINK_ROWS, 17) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_SHRINK_ROWS, 2)
         assert status_of(S.slora_pool_set_tuning, pool, 99, 1) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FUSED, 2) == S.SLORA_E_INVAL
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_XCDS, 65) == S.SLORA_E_INVAL
