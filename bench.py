@@ -500,7 +500,18 @@ def measure_config(name, args, tuning, dev, headline):
         if args.flush_mib > 0:
             flush_dst.copy_(flush_src)
 
+    # Several projections run as one launch (slora_lora_delta_multi) unless
+    # --per-projection asks for one launch each.
+    multi = n_proj > 1 and not args.staged and not args.per_projection
+
     def step(events=None, kev=None):
+        if multi:
+            if events is not None:
+                events[0][0].record(stream)
+            dw.delta_multi(stream=stream, events=None if kev is None else (kev[0][0].handle, kev[0][1].handle))
+            if events is not None:
+                events[0][2].record(stream)
+            return
         for p in range(n_proj):
             if events is not None:
                 events[p][0].record(stream)
@@ -534,7 +545,8 @@ def measure_config(name, args, tuning, dev, headline):
     wall = time.perf_counter() - t0
     log(f"[bench] {name}: {K} timed steps done in {wall * 1e3:.1f} ms wall (flushes included)")
 
-    step_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][2]) for p in range(n_proj)) for k in range(K)]
+    n_launch = 1 if multi else n_proj
+    step_ms = [sum(ev[k][p][0].elapsed_time(ev[k][p][2]) for p in range(n_launch)) for k in range(K)]
     ms = statistics.fmean(step_ms)
     if args.staged:
         sh_ms = statistics.fmean(sum(ev[k][p][0].elapsed_time(ev[k][p][1]) for p in range(n_proj))
@@ -553,7 +565,7 @@ def measure_config(name, args, tuning, dev, headline):
         torch.cuda.synchronize()
         for row in kev:
             row[-1][1].synchronize()
-        kern_ms = [sum(kev[k][p][0].elapsed_ms(kev[k][p][1]) for p in range(n_proj))
+        kern_ms = [sum(kev[k][p][0].elapsed_ms(kev[k][p][1]) for p in range(n_launch))
                    for k in range(K)]
         log(f"[bench] {name}: {K} dispatch-timed steps done")
     assert S.slora_segments_read_error(dw.seg, stream) == 0, "a fused launch gave up waiting"
@@ -600,6 +612,11 @@ def measure_config(name, args, tuning, dev, headline):
         dom_ms = max(sh_ms, ex_ms) / n_proj
         dom_bytes = sb if dominant == "shrink_kernel" else eb
         step_kern_ms = sh_ms + ex_ms
+    elif multi:
+        dominant = "fused_kernel"
+        step_kern_ms = statistics.fmean(kern_ms)
+        dom_ms = step_kern_ms            # one launch holds every projection
+        dom_bytes = step_bytes
     else:
         dominant = "fused_kernel"
         step_kern_ms = statistics.fmean(kern_ms)
@@ -645,9 +662,11 @@ def measure_config(name, args, tuning, dev, headline):
                         "expand_us": round(ex_ms * 1e3 / n_proj, 3),
                         "shrink_GBps": round(sb / (sh_ms / n_proj * 1e-3) / 1e9, 1),
                         "expand_GBps": round(eb / (ex_ms / n_proj * 1e-3) / 1e9, 1)}
-                       if args.staged else {"launch": "fused (one kernel per projection)",
+                       if args.staged else {"launch": ("fused, every projection in one launch "
+                                                       "(slora_lora_delta_multi)") if multi
+                                            else "fused (one kernel per projection)",
                                             "fused_kernel_us": round(dom_ms * 1e3, 3),
-                                            "fused_step_us": round(ms * 1e3 / n_proj, 3)}),
+                                            "fused_step_us": round(ms * 1e3 / n_launch, 3)}),
                     "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                     "step_frac_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                     "step_us_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 3),
@@ -721,6 +740,8 @@ def main():
                     help="base-plus-delta tile (0: automatic)")
     ap.add_argument("--shrink-rows", type=int, default=None,
                     help="rank rows per vector-ALU shrink tile (0: as many as fit)")
+    ap.add_argument("--per-projection", action="store_true",
+                    help="one fused launch per projection instead of one launch for all of them")
     ap.add_argument("--staged", action="store_true",
                     help="time the two stages as separate launches (slora_lora_shrink / _expand)")
     ap.add_argument("--prefetch", type=int, default=0, metavar="M",

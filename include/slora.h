@@ -324,6 +324,30 @@ slora_status slora_lora_delta_timed(slora_pool* pool, const slora_segments* seg,
                                     const void* x, void* y, void* workspace, size_t workspace_bytes,
                                     void* stream, void* start_event, void* stop_event);
 
+/* Several projections of one batch in one launch (summary page, "Algorithm /
+ * figure walkthrough" step 3: each request's adapter is applied to the
+ * layer's projections; catalog page, mechanism paragraph: custom kernels
+ * batch the LoRA products of many adapters together).  For i = 0 .. n-1,
+ * projection projs[i] (distinct, each 0 <= projs[i] < n_proj) reads xs[i] and
+ * updates ys[i] exactly as slora_lora_delta(projs[i], xs[i], ys[i]) would, to
+ * the bit: several projections may share one x (q, k and v of an attention
+ * layer) and each has its own y.  The workspace holds n areas of
+ * workspace_bytes (n x slora_segments_info.workspace_bytes in all).  With
+ * SLORA_TUNE_FUSED (the default) the n projections run as one kernel launch
+ * whose grid holds every projection's tiles, so one launch pays one ramp and
+ * one tail instead of n; otherwise the projections run one after another as
+ * staged launches.  1 <= n <= 8; errors and ordering as for
+ * slora_lora_delta. */
+slora_status slora_lora_delta_multi(slora_pool* pool, const slora_segments* seg, int32_t n,
+                                    const int32_t* projs, const void* const* xs, void* const* ys,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+/* slora_lora_delta_multi with dispatch-recorded HIP events, as for
+ * slora_lora_delta_timed. */
+slora_status slora_lora_delta_multi_timed(slora_pool* pool, const slora_segments* seg, int32_t n,
+                                          const int32_t* projs, const void* const* xs, void* const* ys,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* start_event, void* stop_event);
+
 /* Reads (synchronously, on `stream`) whether any fused launch since the last
  * upload gave up waiting for the x A values of its tokens: *flag = 1 if so,
  * which would mean its results are wrong; 0 otherwise.  A wait gives up only

@@ -180,8 +180,16 @@ namespace {
 
 // Device metadata: the tile records, an error word, then 8 bytes per
 // (token, rank row) of v pairs for the fused launch.
+// One exchange area of n_splits x sum_rt pairs per projection.
+int64_t vtag_words_of(const slora_segments* s) { return (int64_t)s->n_proj * s->n_splits * s->sum_rt * 2; }
+
+// Workspace of one projection: the x A products and their K-split partials.
+size_t workspace_bytes_of(const slora_segments* s) {
+  return std::max<size_t>(16, (size_t)s->n_splits * s->sum_rt * sizeof(float));
+}
+
 size_t meta_bytes_of(const slora_segments* s) {
-  return (size_t)(s->vtag_off_words * 4) + (size_t)s->n_splits * s->sum_rt * 8;
+  return (size_t)(s->vtag_off_words + vtag_words_of(s)) * 4;
 }
 
 slora_status set_device(slora_pool* p) {
@@ -1206,7 +1214,7 @@ slora_status slora_segments_get_info(const slora_segments* s, slora_segments_inf
   info->n_mfma_segments = s->n_mfma_segments;
   info->n_combine_tiles = s->n_combine;
   info->meta_bytes = meta_bytes_of(s);
-  info->workspace_bytes = std::max<size_t>(16, (size_t)s->n_splits * s->sum_rt * sizeof(float));
+  info->workspace_bytes = workspace_bytes_of(s);
   return SLORA_OK;
 }
 
@@ -1302,9 +1310,10 @@ slora_status slora_segments_read_error(const slora_segments* s, void* stream, in
 
 namespace {
 
-// The launch description of one projection of a batch (no checks).
-DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int32_t proj,
-                              const void* x, void* y, const void* workspace) {
+// The launch description of projections projs[0 .. n) of a batch, with
+// inputs xs[i] and outputs ys[i] (no checks).
+DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int32_t n, const int32_t* projs,
+                              const void* const* xs, void* const* ys, const void* workspace) {
   DeltaLaunch L{};
   L.pool.base_a = static_cast<const char*>(p->d.class_base[0]);
   L.pool.base_b = static_cast<const char*>(p->d.class_base[p->b_class()]);
@@ -1313,9 +1322,12 @@ DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int3
   L.dtype = p->d.dtype;
   L.h_in = p->d.h_in;
   L.h_out = p->d.h_out;
-  L.proj = proj;
-  L.x = x;
-  L.y = y;
+  L.n_slots = n;
+  for (int32_t i = 0; i < n; ++i) {
+    L.projs[i] = projs[i];
+    L.xs[i] = xs ? xs[i] : nullptr;
+    L.ys[i] = ys ? ys[i] : nullptr;
+  }
   L.v = static_cast<float*>(const_cast<void*>(workspace));
   L.rec = s->dev_meta;
   L.stride = s->stride;
@@ -1332,6 +1344,7 @@ DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int3
   L.vtag = reinterpret_cast<unsigned long long*>(const_cast<int32_t*>(s->dev_meta + s->vtag_off_words));
   L.y_bytes = (uint32_t)std::min<int64_t>((int64_t)s->n_tokens * p->d.h_out * elem_bytes(p->d.dtype), kMaxBufferBytes);
   L.sum_rt = (int32_t)s->sum_rt;
+  L.n_splits = s->n_splits;
   L.n_combine = s->n_combine;
   L.pipe_expand = s->pipe_expand ? 1 : 0;
   return L;
@@ -1353,42 +1366,72 @@ slora_status check_batch(const std::string& f, const slora_pool* p, const slora_
   return SLORA_OK;
 }
 
-slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_segments* s,
-                        int32_t proj, const void* x, void* y, const void* workspace,
-                        size_t workspace_bytes, void* stream, void* ev_start = nullptr,
-                        void* ev_stop = nullptr) {
+// Projections projs[0 .. n) of one batch: in one fused launch (slots of
+// one grid), or staged, one projection at a time.  stages: STAGE_SHRINK,
+// STAGE_EXPAND or both.
+slora_status run_delta(const char* fn, int stages, slora_pool* p, const slora_segments* s, int32_t n,
+                       const int32_t* projs, const void* const* xs, void* const* ys, const void* workspace,
+                       size_t workspace_bytes, void* stream, void* ev_start = nullptr, void* ev_stop = nullptr) {
   const std::string f(fn);
-  slora_status chk = check_batch(f, p, s, proj);
-  if (chk != SLORA_OK) return chk;
+  if (n < 1 || n > kMaxSlots || !projs) return fail(SLORA_E_INVAL, f + ": n must be 1..8 with a projs array");
+  if (p && (n > p->d.n_proj)) return fail(SLORA_E_INVAL, f + ": more projections than the pool has");
+  for (int32_t i = 0; i < n; ++i) {
+    slora_status chk = check_batch(f, p, s, projs[i]);
+    if (chk != SLORA_OK) return chk;
+    for (int32_t k = 0; k < i; ++k)
+      if (projs[k] == projs[i]) return fail(SLORA_E_INVAL, f + ": a projection is named twice");
+  }
   if (s->perm.empty()) return SLORA_OK;
-  if (((stages & STAGE_SHRINK) && !x) || ((stages & STAGE_EXPAND) && !y) || !workspace)
-    return fail(SLORA_E_INVAL, f + ": NULL x, y or workspace");
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
-       reinterpret_cast<uintptr_t>(workspace)) & 15)
-    return fail(SLORA_E_INVAL, f + ": x, y and workspace must be 16-byte aligned");
-  if (workspace_bytes < (size_t)s->n_splits * s->sum_rt * sizeof(float))
-    return fail(SLORA_E_NOMEM, f + ": workspace smaller than workspace_bytes");
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(SLORA_E_INVAL, f + ": workspace must be non-NULL and 16-byte aligned");
+  for (int32_t i = 0; i < n; ++i) {
+    const void* x = xs ? xs[i] : nullptr;
+    const void* y = ys ? ys[i] : nullptr;
+    if (((stages & STAGE_SHRINK) && !x) || ((stages & STAGE_EXPAND) && !y))
+      return fail(SLORA_E_INVAL, f + ": NULL x or y");
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15)
+      return fail(SLORA_E_INVAL, f + ": x and y must be 16-byte aligned");
+  }
+  const size_t area = (size_t)s->n_splits * s->sum_rt * sizeof(float);
+  if (workspace_bytes < (size_t)n * area)
+    return fail(SLORA_E_NOMEM, f + ": workspace smaller than " + (n > 1 ? "n x " : "") + "workspace_bytes");
   if (!s->dev_meta) return fail(SLORA_E_INVAL, f + ": segments not uploaded (call slora_segments_upload)");
   slora_status st = set_device(p);
   if (st != SLORA_OK) return st;
-  DeltaLaunch L = make_delta_launch(p, s, proj, x, y, workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   if (stages == (STAGE_SHRINK | STAGE_EXPAND) && p->tune.fused) {
-    stages = STAGE_FUSED;
+    DeltaLaunch L = make_delta_launch(p, s, n, projs, xs, ys, workspace);
     // Epochs run 1 .. 2^31 - 1 (partial sums of K-split shrink tiles carry the
     // epoch with bit 31 set); before they would wrap, clear the pairs so that
     // no stale pair can match a new epoch.
     if (s->epoch == 0x7FFFFFFFu) {
-      hipError_t z = launch_zero_words(const_cast<int32_t*>(s->dev_meta) + s->vtag_off_words,
-                                       (int64_t)s->n_splits * s->sum_rt * 2, static_cast<hipStream_t>(stream));
+      hipError_t z = launch_zero_words(const_cast<int32_t*>(s->dev_meta) + s->vtag_off_words, vtag_words_of(s), hs);
       if (z != hipSuccess) return hip_fail(z, (f + " clearing v pairs").c_str());
       s->epoch = 0;
     }
     L.epoch = ++s->epoch;
+    hipError_t e = launch_delta(L, STAGE_FUSED, hs, static_cast<hipEvent_t>(ev_start),
+                                static_cast<hipEvent_t>(ev_stop));
+    if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
+    return SLORA_OK;
   }
-  hipError_t e = launch_delta(L, stages, static_cast<hipStream_t>(stream),
-                              static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop));
-  if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
+  for (int32_t i = 0; i < n; ++i) {
+    const void* x1[1] = {xs ? xs[i] : nullptr};
+    void* y1[1] = {ys ? ys[i] : nullptr};
+    const char* ws = static_cast<const char*>(workspace) + i * area;
+    const DeltaLaunch L = make_delta_launch(p, s, 1, projs + i, x1, y1, ws);
+    hipError_t e = launch_delta(L, stages, hs, i == 0 ? static_cast<hipEvent_t>(ev_start) : nullptr,
+                                i == n - 1 ? static_cast<hipEvent_t>(ev_stop) : nullptr);
+    if (e != hipSuccess) return hip_fail(e, (f + " launch").c_str());
+  }
   return SLORA_OK;
+}
+
+slora_status run_stages(const char* fn, int stages, slora_pool* p, const slora_segments* s,
+                        int32_t proj, const void* x, void* y, const void* workspace,
+                        size_t workspace_bytes, void* stream, void* ev_start = nullptr,
+                        void* ev_stop = nullptr) {
+  return run_delta(fn, stages, p, s, 1, &proj, &x, &y, workspace, workspace_bytes, stream, ev_start, ev_stop);
 }
 
 
@@ -1419,7 +1462,7 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
   if (st != SLORA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (routed) {
-    const DeltaLaunch L = make_delta_launch(p, s, proj, x, nullptr, workspace);
+    const DeltaLaunch L = make_delta_launch(p, s, 1, &proj, &x, nullptr, workspace);
     hipError_t e = launch_delta(L, STAGE_SHRINK, hs, static_cast<hipEvent_t>(ev_start), nullptr);
     if (e != hipSuccess) return hip_fail(e, (f + " shrink launch").c_str());
   }
@@ -1494,6 +1537,21 @@ slora_status slora_lora_delta_timed(slora_pool* p, const slora_segments* s, int3
                                     void* stream, void* ev_start, void* ev_stop) {
   return run_stages("slora_lora_delta_timed", STAGE_SHRINK | STAGE_EXPAND, p, s, proj, x, y,
                     workspace, workspace_bytes, stream, ev_start, ev_stop);
+}
+
+slora_status slora_lora_delta_multi(slora_pool* p, const slora_segments* s, int32_t n, const int32_t* projs,
+                                    const void* const* xs, void* const* ys, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return run_delta("slora_lora_delta_multi", STAGE_SHRINK | STAGE_EXPAND, p, s, n, projs, xs, ys, workspace,
+                   workspace_bytes, stream);
+}
+
+slora_status slora_lora_delta_multi_timed(slora_pool* p, const slora_segments* s, int32_t n,
+                                          const int32_t* projs, const void* const* xs, void* const* ys,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* ev_start, void* ev_stop) {
+  return run_delta("slora_lora_delta_multi_timed", STAGE_SHRINK | STAGE_EXPAND, p, s, n, projs, xs, ys,
+                   workspace, workspace_bytes, stream, ev_start, ev_stop);
 }
 
 slora_status slora_lora_shrink(slora_pool* p, const slora_segments* s, int32_t proj, const void* x,

@@ -75,13 +75,22 @@ struct PoolView {
   int64_t page_bytes_b;
 };
 
+// A launch covers n_slots projections of one batch (slora_lora_delta: one;
+// slora_lora_delta_multi: up to n_proj, e.g. q, k and v with their shared x,
+// and o with its own).  Slot s is projection projs[s] with input xs[s],
+// output ys[s] and, in a staged launch, the x A products at v + s * n_splits
+// * sum_rt; a fused launch passes them through the exchange area of its
+// projection, vtag + projs[s] * n_splits * sum_rt.
+constexpr int kMaxSlots = 8;
+
 struct DeltaLaunch {
   PoolView pool;
   int32_t dtype;          // 0 fp32, 1 fp16
   int32_t h_in, h_out;
-  int32_t proj;
-  const void* x;
-  void* y;
+  int32_t n_slots;
+  int32_t projs[kMaxSlots];
+  const void* xs[kMaxSlots];
+  void* ys[kMaxSlots];
   float* v;
   const int32_t* rec;             // all tile records, launch order
   int32_t stride, tokcap, pagecap;
@@ -96,6 +105,7 @@ struct DeltaLaunch {
   unsigned long long* vtag;
   uint32_t* error_flag;
   int32_t sum_rt;         // v values of the batch (stride between the K-split partial areas)
+  int32_t n_splits;       // K splits of the MFMA shrink blocks (areas per projection)
   int32_t n_combine;      // combine tiles (records n_shrink .. n_shrink + n_combine)
   uint32_t y_bytes;       // extent of y (n_tokens x h_out x element), < kMaxBufferBytes when has_mfma
   uint32_t epoch;

@@ -169,6 +169,23 @@ __device__ __forceinline__ void record_to_lds(const int32_t* rec, int tokcap, in
   __syncthreads();
 }
 
+// The projection a workgroup works on: its x, its y, where its x A values go
+// (staged launches: the workspace; fused launches: the exchange pairs) and
+// which page list of the tile record it reads.
+struct Slot {
+  const void* x;
+  void* y;
+  float* v;
+  unsigned long long* vtag;
+  int32_t proj;
+};
+
+__device__ __forceinline__ Slot make_slot(const DeltaLaunch& L, int s) {
+  const int64_t area = (int64_t)L.n_splits * L.sum_rt;
+  const int p = L.projs[s];
+  return Slot{L.xs[s], L.ys[s], L.v + s * area, L.vtag + p * area, p};
+}
+
 // Fused launch: shrink tiles and expand tiles run in one grid, and v passes
 // from one to the other as self-validating (value, epoch) pairs.  A shrink
 // tile stores each v value together with the launch's epoch in one 64-bit
@@ -196,12 +213,12 @@ constexpr uint32_t kMaxSpins = 1u << 20;
 constexpr uint32_t kPartialTag = 0x80000000u;
 
 template <bool FUSED>
-__device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float x, uint32_t tag) {
+__device__ __forceinline__ void store_v(const Slot& S, int64_t idx, float x, uint32_t tag) {
   if constexpr (FUSED) {
     const unsigned long long pair = ((unsigned long long)tag << 32) | __float_as_uint(x);
-    __hip_atomic_store(L.vtag + idx, pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(S.vtag + idx, pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    L.v[idx] = x;
+    S.v[idx] = x;
   }
 }
 
@@ -212,7 +229,8 @@ __device__ __forceinline__ void store_v(const DeltaLaunch& L, int64_t idx, float
 // any is consumed, at index `safe` (any valid v index) for a slot with no
 // value, so they travel to memory together instead of one round trip each.
 template <bool FUSED, int N, typename Get, typename Put>
-__device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, Get get, Put put, uint32_t want) {
+__device__ __forceinline__ void load_v(const DeltaLaunch& L, const Slot& S, int nq, int safe, Get get, Put put,
+                                       uint32_t want) {
   int idx[N];
 #pragma unroll
   for (int q = 0; q < N; ++q) idx[q] = q < nq ? get(q) : -1;
@@ -220,7 +238,7 @@ __device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, G
     float val[N];
 #pragma unroll
     for (int q = 0; q < N; ++q)
-      if (q < nq) val[q] = L.v[idx[q] >= 0 ? idx[q] : safe];
+      if (q < nq) val[q] = S.v[idx[q] >= 0 ? idx[q] : safe];
 #pragma unroll
     for (int q = 0; q < N; ++q)
       if (q < nq) put(q, idx[q] >= 0 ? val[q] : 0.f);
@@ -230,7 +248,7 @@ __device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, G
 #pragma unroll
       for (int q = 0; q < N; ++q)
         if (q < nq)
-          pair[q] = __hip_atomic_load(L.vtag + (idx[q] >= 0 ? idx[q] : safe), __ATOMIC_RELAXED,
+          pair[q] = __hip_atomic_load(S.vtag + (idx[q] >= 0 ? idx[q] : safe), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
       bool ok = true;
 #pragma unroll
@@ -256,7 +274,7 @@ __device__ __forceinline__ void load_v(const DeltaLaunch& L, int nq, int safe, G
 // rows stay in registers while each token's x chunks are dotted against them.
 
 template <typename T, int NCK, bool FUSED>
-__device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* red) {
+__device__ void shrink_gemv_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* red) {
   constexpr int VEC = VecN<T>::N;
   constexpr int RB = kShrinkRowBudget / NCK;
   constexpr int TB = kGemvMaxTok;
@@ -269,7 +287,7 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int32_t* pages = srec + REC_HDR + L.tokcap;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int nchunks = L.h_in / VEC;
-  const T* x = reinterpret_cast<const T*>(L.x);
+  const T* x = reinterpret_cast<const T*>(S.x);
 
   // All row and token addresses first, then every load of the tile in one batch.
   const char* arow[RB];
@@ -314,7 +332,7 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     const int k = i / nrows, r = i - k * nrows;
     const float* q = red + (k * 4) * RB + r;
     const float sum = ((q[0] + q[RB]) + q[2 * RB]) + q[3 * RB];
-    store_v<FUSED>(L, v0 + (int64_t)k * rank + j0 + r, sum, L.epoch);
+    store_v<FUSED>(S, v0 + (int64_t)k * rank + j0 + r, sum, L.epoch);
   }
 }
 
@@ -335,7 +353,7 @@ constexpr int kShrinkLdsFloats = 2 * kShrinkStageDw;                   // two ch
 
 
 template <bool FUSED>
-__device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
+__device__ void shrink_mfma_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* lds) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
   const int k0 = uni(srec[REC_POS]);
@@ -360,7 +378,7 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int row = lr + 32 * h;
-    xr[h] = reinterpret_cast<const _Float16*>(L.x) + (int64_t)toks[min(row, ntok - 1)] * L.h_in + k0 + 8 * lc;
+    xr[h] = reinterpret_cast<const _Float16*>(S.x) + (int64_t)toks[min(row, ntok - 1)] * L.h_in + k0 + 8 * lc;
     ar[h] = L.pool.base_a + (int64_t)pages[min(row, rank - 1)] * L.pool.page_bytes_a + (int64_t)(k0 + 8 * lc) * 2;
   }
   auto load_chunk = [&](int kc, uint4 (&r)[4]) {
@@ -429,7 +447,7 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * wave + 4 * g + i, j = 16 * b + m;
-      if (b < nb && t < ntok && j < rank) store_v<FUSED>(L, area + v0 + (int64_t)t * rank + j, acc[b][i], tag);
+      if (b < nb && t < ntok && j < rank) store_v<FUSED>(S, area + v0 + (int64_t)t * rank + j, acc[b][i], tag);
     }
   }
 }
@@ -439,7 +457,7 @@ __device__ void shrink_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
 // v = sum over splits s = 0, 1, ... of the partial in area s, added in that
 // order (deterministic), written to area 0 with the plain epoch.
 template <bool FUSED>
-__device__ void combine_tile(const DeltaLaunch& L, const int32_t* srec) {
+__device__ void combine_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
   const int v0 = uni(srec[REC_V0]);
@@ -450,7 +468,7 @@ __device__ void combine_tile(const DeltaLaunch& L, const int32_t* srec) {
   // slot q * kMaxSplits + s: value tid + 256 q of split s
   float part[Q * kMaxSplits];
   load_v<FUSED, Q * kMaxSplits>(
-      L, Q * kMaxSplits, v0,
+      L, S, Q * kMaxSplits, v0,
       [&](int qs) -> int {
         const int q = qs / kMaxSplits, sp = qs % kMaxSplits, i = tid + q * kThreads;
         return (i < n && sp < nsplit) ? sp * L.sum_rt + v0 + i : -1;
@@ -463,7 +481,7 @@ __device__ void combine_tile(const DeltaLaunch& L, const int32_t* srec) {
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp)
       if (sp < nsplit) sum += part[q * kMaxSplits + sp];
-    if (i < n) store_v<FUSED>(L, v0 + i, sum, L.epoch);
+    if (i < n) store_v<FUSED>(S, v0 + i, sum, L.epoch);
   }
 }
 
@@ -471,22 +489,24 @@ template <typename T, int NCK>
 __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
   __shared__ float red[sizeof(T) == 2 ? kShrinkLdsFloats : 4 * 4 * 16];
   __shared__ int32_t srec[kMaxRecWords];
+  const Slot S = make_slot(L, 0);   // staged launches run one projection
   const int32_t* rec = L.rec + (int64_t)L.shrink_idx[blockIdx.x] * L.stride;
-  record_to_lds(rec, L.tokcap, L.pagecap, L.proj, srec);
+  record_to_lds(rec, L.tokcap, L.pagecap, S.proj, srec);
   if constexpr (sizeof(T) == 2) {
     if (uni(srec[REC_KIND]) & KIND_MFMA_BIT) {
-      shrink_mfma_tile<false>(L, srec, red);
+      shrink_mfma_tile<false>(L, S, srec, red);
       return;
     }
   }
-  shrink_gemv_tile<T, NCK, false>(L, srec, red);
+  shrink_gemv_tile<T, NCK, false>(L, S, srec, red);
 }
 
 // Staged launches: the combine tiles, records n_shrink .. n_shrink + n_combine.
 __global__ __launch_bounds__(kThreads) void combine_kernel(DeltaLaunch L) {
   __shared__ int32_t srec[kMaxRecWords];
-  record_to_lds(L.rec + (int64_t)(L.n_shrink + blockIdx.x) * L.stride, L.tokcap, L.pagecap, L.proj, srec);
-  combine_tile<false>(L, srec);
+  const Slot S = make_slot(L, 0);
+  record_to_lds(L.rec + (int64_t)(L.n_shrink + blockIdx.x) * L.stride, L.tokcap, L.pagecap, S.proj, srec);
+  combine_tile<false>(L, S, srec);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(DeltaLaunch L) {
 // sums meet in LDS and group 0 applies y += s * d with one rounding.
 
 template <typename T, bool FUSED, bool PIPE>
-__device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
+__device__ void expand_gemv_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* lds) {
   constexpr int VEC = VecN<T>::N;
   constexpr int TB = kGemvMaxTok;
   constexpr int RCH = kExpandRowSet;  // B rows per thread issued together
@@ -516,7 +536,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
 
   float* sv = lds;                   // [TB][rank] v of the tile's tokens
   float* part = lds + TB * 256;      // [G-1][TB][nct][VEC] partial sums of groups 1..G-1
-  T* y = reinterpret_cast<T*>(L.y);
+  T* y = reinterpret_cast<T*>(S.y);
 
   // Issue everything the tile reads before waiting on any of it: the first
   // RCH B rows of this thread, (group 0) the y chunks of the epilogue, and v
@@ -548,7 +568,7 @@ __device__ void expand_gemv_tile(const DeltaLaunch& L, const int32_t* srec, floa
     yv[k] = (g == 0 && active && k < ntok) ? ldsel<SLORA_NT_Y>(y + (int64_t)toks[k] * L.h_out + o0 + ct * VEC)
                                            : make_uint4(0, 0, 0, 0);
   load_v<FUSED, TB>(
-      L, (ntok * rank + kThreads - 1) / kThreads, v0,
+      L, S, (ntok * rank + kThreads - 1) / kThreads, v0,
       [&](int q) -> int { const int i = tid + q * kThreads; return i < ntok * rank ? v0 + i : -1; },
       [&](int q, float val) { const int i = tid + q * kThreads; if (i < ntok * rank) sv[i] = val; }, L.epoch);
   __syncthreads();
@@ -660,7 +680,7 @@ constexpr int kMfmaExpandLds = 2 * kSliceDw + kMfmaExpandTok * kEpiPitch + kMfma
 constexpr int kBufferFormat = 0x00020000;   // descriptor word 3: raw 32-bit buffer
 
 template <bool FUSED, int KS>   // KS: 32-row k slices of the rank (1 or 2), fixed per instantiation
-__device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, float* lds) {
+__device__ void expand_mfma_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* lds) {
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
   const int o0 = uni(srec[REC_POS]);
@@ -677,8 +697,8 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   uint32_t* slice = reinterpret_cast<uint32_t*>(lds);  // two slices, used in turn
   float* epi = lds + 2 * kSliceDw;                     // [64][kEpiPitch]
   float* up_tok = epi + kMfmaExpandTok * kEpiPitch;    // per-token scale back
-  _Float16* yb = reinterpret_cast<_Float16*>(L.y);
-  const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(L.y, 0, (int)L.y_bytes, kBufferFormat);
+  _Float16* yb = reinterpret_cast<_Float16*>(S.y);
+  const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(S.y, 0, (int)L.y_bytes, kBufferFormat);
 
   // Every global access below is issued unconditionally (loads at a clamped
   // address where they fall outside the tile), so that each wait covers only
@@ -727,7 +747,7 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
   const int tok = 16 * wave + m;
   float sv[8 * KS];
   load_v<FUSED, 8 * KS>(
-      L, 8 * ks_n, v0,
+      L, S, 8 * ks_n, v0,
       [&](int q) -> int {
         const int j = 32 * (q >> 3) + 8 * g + (q & 7);
         return (tok < ntok && j < rank) ? v0 + tok * rank + j : -1;
@@ -828,12 +848,12 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const int32_t* srec, floa
 }
 
 template <bool FUSED>
-__device__ __forceinline__ void expand_mfma_dispatch(const DeltaLaunch& L, const int32_t* srec, float* lds) {
+__device__ __forceinline__ void expand_mfma_dispatch(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* lds) {
   static_assert(kMaxRankMfma == 64, "two instantiations cover ranks 1..64");
   if (uni(srec[REC_RANK]) <= 32)
-    expand_mfma_tile<FUSED, 1>(L, srec, lds);
+    expand_mfma_tile<FUSED, 1>(L, S, srec, lds);
   else
-    expand_mfma_tile<FUSED, 2>(L, srec, lds);
+    expand_mfma_tile<FUSED, 2>(L, S, srec, lds);
 }
 
 // LDS of the expand tiles: the vector-ALU tiles need kGemvLdsFloats, the
@@ -847,19 +867,23 @@ template <typename T, bool PIPE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void expand_kernel(DeltaLaunch L) {
   __shared__ float lds[sizeof(T) == 2 ? kExpandLdsFloats : kGemvLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
+  const Slot S = make_slot(L, 0);
   const int32_t* rec = L.rec + (int64_t)L.expand_idx[blockIdx.x] * L.stride;
-  record_to_lds(rec, L.tokcap, L.pagecap, L.proj, srec);
+  record_to_lds(rec, L.tokcap, L.pagecap, S.proj, srec);
   if constexpr (sizeof(T) == 2) {
     if (uni(srec[REC_KIND]) & KIND_MFMA_BIT) {
-      expand_mfma_dispatch<false>(L, srec, lds);
+      expand_mfma_dispatch<false>(L, S, srec, lds);
       return;
     }
   }
-  expand_gemv_tile<T, false, PIPE>(L, srec, lds);
+  expand_gemv_tile<T, false, PIPE>(L, S, srec, lds);
 }
 
 // Both stages in one launch over the records in launch order: shrink tiles
 // and expand tiles that wait for their tokens' v (see store_v / load_v).
+// With several projections (slots) the grid runs every slot's shrink tiles,
+// then every slot's combine tiles, then every slot's expand tiles, so every
+// tile a workgroup waits for still has a lower block index.
 // MFMA=false leaves the matrix-core tiles out (a batch without them), which
 // keeps the register budget, and so the workgroups resident per CU, of the
 // vector-ALU tiles alone.
@@ -871,29 +895,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCK ==
 void fused_kernel(DeltaLaunch L) {
   __shared__ float lds[sizeof(T) == 2 && MFMA ? kExpandLdsFloats : kGemvLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
-  record_to_lds(L.rec + (int64_t)blockIdx.x * L.stride, L.tokcap, L.pagecap, L.proj, srec);
+  // block -> (slot, record): [slots x shrink][slots x combine][slots x expand]
+  int b = blockIdx.x, slot, rec;
+  const int ns = L.n_slots * L.n_shrink, nc = L.n_slots * L.n_combine;
+  if (b < ns) {
+    slot = b / L.n_shrink;
+    rec = b - slot * L.n_shrink;
+  } else if (b < ns + nc) {
+    b -= ns;
+    slot = b / L.n_combine;
+    rec = L.n_shrink + (b - slot * L.n_combine);
+  } else {
+    b -= ns + nc;
+    slot = b / L.n_expand;
+    rec = L.n_shrink + L.n_combine + (b - slot * L.n_expand);
+  }
+  const Slot S = make_slot(L, uni(slot));
+  record_to_lds(L.rec + (int64_t)uni(rec) * L.stride, L.tokcap, L.pagecap, S.proj, srec);
   const int kind = uni(srec[REC_KIND]);
   if (!(kind & KIND_EXPAND_BIT)) {
     if constexpr (sizeof(T) == 2 && MFMA) {
       if (kind & KIND_COMBINE_BIT) {
-        combine_tile<true>(L, srec);
+        combine_tile<true>(L, S, srec);
         return;
       }
       if (kind & KIND_MFMA_BIT) {
-        shrink_mfma_tile<true>(L, srec, lds);
+        shrink_mfma_tile<true>(L, S, srec, lds);
         return;
       }
     }
-    shrink_gemv_tile<T, NCK, true>(L, srec, lds);
+    shrink_gemv_tile<T, NCK, true>(L, S, srec, lds);
     return;
   }
   if constexpr (sizeof(T) == 2 && MFMA) {
     if (kind & KIND_MFMA_BIT) {
-      expand_mfma_dispatch<true>(L, srec, lds);
+      expand_mfma_dispatch<true>(L, S, srec, lds);
       return;
     }
   }
-  expand_gemv_tile<T, true, PIPE>(L, srec, lds);
+  expand_gemv_tile<T, true, PIPE>(L, S, srec, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -949,7 +989,7 @@ static hipError_t launch_delta_t(const DeltaLaunch& L, int stages, hipStream_t s
                                  hipEvent_t start, hipEvent_t stop) {
   const int nck = chunks_per_thread<T>(L.h_in);
   if (stages & STAGE_FUSED) {
-    const int blocks = L.n_tiles;
+    const int blocks = L.n_tiles * L.n_slots;
     if (blocks == 0) return hipSuccess;
     const void* k = fused_pick<T>(nck, sizeof(T) == 2 && L.has_mfma, L.pipe_expand != 0);
     if (!k) return hipErrorInvalidValue;

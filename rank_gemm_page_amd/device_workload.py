@@ -134,6 +134,27 @@ class DeviceWorkload:
         S.slora_lora_delta(self.pool, self.seg, proj, x, self.y[proj] if y is None else y,
                            self.workspace, self.info["workspace_bytes"], stream)
 
+    def ensure_workspace(self, n):
+        """Workspace for n projections in one launch (slora_lora_delta_multi)."""
+        need = n * self.info["workspace_bytes"]
+        if self.workspace.numel() < need:
+            self.workspace = self.torch.empty(need, dtype=self.torch.uint8, device=self.device)
+        return need
+
+    def delta_multi(self, projs=None, ys=None, stream=None, events=None):
+        """Every projection in projs (all by default) in one slora_lora_delta_multi
+        launch; events: (start, stop) raw hipEvent_t handles for the timed call."""
+        stream = stream or self.torch.cuda.current_stream(self.device)
+        projs = list(range(self.w.spec.n_proj)) if projs is None else list(projs)
+        xs = [self.x[self.w.spec.proj_x[p]] for p in projs]
+        ys = [self.y[p] for p in projs] if ys is None else list(ys)
+        nbytes = self.ensure_workspace(len(projs))
+        if events is None:
+            S.slora_lora_delta_multi(self.pool, self.seg, projs, xs, ys, self.workspace, nbytes, stream)
+        else:
+            S.slora_lora_delta_multi_timed(self.pool, self.seg, projs, xs, ys, self.workspace, nbytes, stream,
+                                           events[0], events[1])
+
     def delta_timed(self, proj, start_event, stop_event, stream=None):
         """delta() with the dispatch recording two raw hipEvent_t handles."""
         stream = stream or self.torch.cuda.current_stream(self.device)

@@ -37,6 +37,7 @@ EXPORTED = [
     "slora_segments_upload", "slora_segments_read_error",
     "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
     "slora_lora_forward", "slora_lora_forward_timed", "slora_last_error",
+    "slora_lora_delta_multi", "slora_lora_delta_multi_timed",
 ]
 # include/slora_probe.h: bandwidth probes (measurement only)
 EXPORTED_PROBE = ["slora_probe_read", "slora_probe_gather"]
@@ -99,6 +100,10 @@ def lib():
             "slora_segments_read_error": (c_int32, [P, P, POINTER(c_int32)]),
             "slora_lora_delta": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
             "slora_lora_delta_timed": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P, P, P]),
+            "slora_lora_delta_multi": (c_int32, [P, P, c_int32, POINTER(c_int32), POINTER(P), POINTER(P), P,
+                                                 c_size_t, P]),
+            "slora_lora_delta_multi_timed": (c_int32, [P, P, c_int32, POINTER(c_int32), POINTER(P), POINTER(P),
+                                                       P, c_size_t, P, P, P]),
             "slora_lora_shrink": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_lora_expand": (c_int32, [P, P, c_int32, P, P, c_size_t, P]),
             "slora_lora_forward": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P]),
@@ -344,6 +349,31 @@ def slora_lora_delta_timed(pool, seg, proj: int, x, y, workspace, workspace_byte
     _check(lib().slora_lora_delta_timed(pool, seg, proj, _ptr(x), _ptr(y), _ptr(workspace),
                                         int(workspace_bytes), _stream(stream), start_event,
                                         stop_event), "slora_lora_delta_timed")
+
+
+def _multi_args(projs, xs, ys):
+    n = len(projs)
+    if len(xs) != n or len(ys) != n:
+        raise ValueError("one x and one y per projection")
+    pj = np.ascontiguousarray(projs, dtype=np.int32)
+    xa = (c_void_p * n)(*[_ptr(x) for x in xs])
+    ya = (c_void_p * n)(*[_ptr(y) for y in ys])
+    return n, pj, xa, ya
+
+
+def slora_lora_delta_multi(pool, seg, projs, xs, ys, workspace, workspace_bytes: int, stream=None) -> None:
+    """Projections projs[i] with inputs xs[i] and outputs ys[i] in one launch."""
+    n, pj, xa, ya = _multi_args(projs, xs, ys)
+    _check(lib().slora_lora_delta_multi(pool, seg, n, _i32p(pj), xa, ya, _ptr(workspace), int(workspace_bytes),
+                                        _stream(stream)), "slora_lora_delta_multi")
+
+
+def slora_lora_delta_multi_timed(pool, seg, projs, xs, ys, workspace, workspace_bytes: int, stream,
+                                 start_event: int, stop_event: int) -> None:
+    n, pj, xa, ya = _multi_args(projs, xs, ys)
+    _check(lib().slora_lora_delta_multi_timed(pool, seg, n, _i32p(pj), xa, ya, _ptr(workspace),
+                                              int(workspace_bytes), _stream(stream), start_event, stop_event),
+           "slora_lora_delta_multi_timed")
 
 
 def slora_lora_shrink(pool, seg, proj: int, x, workspace, workspace_bytes: int, stream=None) -> None:

@@ -391,6 +391,38 @@ def test_segments_errors_and_staleness():
         S.slora_pool_destroy(pool)
 
 
+def test_multi_projection_argument_errors():
+    """slora_lora_delta_multi refuses bad projection lists, NULL or unaligned
+    buffers and a workspace smaller than n areas before any device work."""
+    pool = small_pool(n_pages=64, n_proj=3)
+    try:
+        for a in range(2):
+            S.slora_load_adapter(pool, a, 2, 1.0)
+        seg = S.slora_build_segments(pool, [1, 0, 1])
+        try:
+            ws = S.slora_segments_get_info(seg)["workspace_bytes"]
+            fake = 1 << 42
+            call = lambda projs, xs=None, ys=None, w=fake, wb=3 * ws: status_of(   # noqa: E731
+                S.slora_lora_delta_multi, pool, seg, projs, xs or [fake] * len(projs),
+                ys or [fake] * len(projs), w, wb)
+            assert call([]) == S.SLORA_E_INVAL                       # n = 0
+            assert call([0, 1, 2, 0]) == S.SLORA_E_INVAL             # more than n_proj, and a repeat
+            assert call([0, 0]) == S.SLORA_E_INVAL                   # a projection twice
+            assert call([0, 3]) == S.SLORA_E_INVAL                   # out of range
+            assert call([2, -1]) == S.SLORA_E_INVAL
+            assert call([0, 1], xs=[fake, 0]) == S.SLORA_E_INVAL     # NULL x
+            assert call([0, 1], ys=[fake + 8, fake]) == S.SLORA_E_INVAL   # unaligned y
+            assert call([0, 1], w=0) == S.SLORA_E_INVAL              # NULL workspace
+            assert call([0, 1, 2], wb=3 * ws - 1) == S.SLORA_E_NOMEM  # n areas needed
+            assert call([0, 1, 2]) == S.SLORA_E_INVAL                # not uploaded yet
+            S.slora_unload_adapter(pool, 1)
+            assert call([0, 1]) == S.SLORA_E_STALE
+        finally:
+            S.slora_segments_destroy(seg)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
 def test_empty_and_unrouted_batches_launch_nothing():
     pool = small_pool()
     try:
