@@ -399,6 +399,20 @@ slora_status slora_lora_forward_timed(slora_pool* pool, const slora_segments* se
                                       size_t workspace_bytes, void* stream, void* start_event,
                                       void* stop_event);
 
+/* slora_lora_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, arguments and checks, but the workspace
+ * (the fp32 x A products and their K-split partials) is the library's own
+ * device array of 8 MiB, one per GPU, held until the process ends.  The call
+ * allocates nothing.  A batch whose workspace_bytes exceed 8 MiB is refused
+ * with SLORA_E_NOMEM before any device work.  Every call on one GPU shares
+ * that GPU's array and leaves its contents behind (each call writes every
+ * value it reads before reading it): calls on one GPU that overlap in time
+ * (different streams, or different host threads without ordering) race and
+ * must be serialised by the caller. */
+slora_status slora_lora_forward_noalloc(slora_pool* pool, const slora_segments* seg, int32_t proj,
+                                        const void* x, const void* w, void* y, void* stream);
+
 /* Message for the calling thread's last failed call ("" if none). */
 const char* slora_last_error(void);
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libslora.so")
-SOURCES = ["slora_host.cpp", "slora_kernels.hip", "slora_forward.hip", "slora_probe.hip"]
+SOURCES = ["slora_host.cpp", "slora_kernels.hip", "slora_forward.hip", "slora_probe.hip", "slora_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU ops are switched off for the device code: plain float code

@@ -1308,6 +1308,13 @@ slora_status slora_segments_read_error(const slora_segments* s, void* stream, in
 
 }  // extern "C"
 
+slora_status slora::pool_device_current(slora_pool* p) {
+  if (!p) return fail(SLORA_E_INVAL, "NULL pool");
+  return set_device(p);
+}
+
+size_t slora::segments_workspace_bytes(const slora_segments* s) { return workspace_bytes_of(s); }
+
 namespace {
 
 // The launch description of projections projs[0 .. n) of a batch, with

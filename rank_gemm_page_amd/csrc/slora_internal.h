@@ -13,6 +13,10 @@ namespace slora {
 // Record the calling thread's message for slora_last_error() (for sources
 // other than the host runtime's C ABI).
 void set_last_error(const char* msg);
+// Make the pool's device current (the device of its first HIP call).
+slora_status pool_device_current(slora_pool* pool);
+// Workspace bytes one projection of the batch needs (slora_segments_info.workspace_bytes).
+size_t segments_workspace_bytes(const slora_segments* seg);
 
 // A tile record is a run of int32 words:
 //   [0] kind        KIND_{SHRINK,EXPAND}_{GEMV,MFMA}: bit 0 set for the

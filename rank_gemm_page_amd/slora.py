@@ -37,7 +37,7 @@ EXPORTED = [
     "slora_segments_upload", "slora_segments_read_error",
     "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
     "slora_lora_forward", "slora_lora_forward_timed", "slora_last_error",
-    "slora_lora_delta_multi", "slora_lora_delta_multi_timed",
+    "slora_lora_delta_multi", "slora_lora_delta_multi_timed", "slora_lora_forward_noalloc",
 ]
 # include/slora_probe.h: bandwidth probes (measurement only)
 EXPORTED_PROBE = ["slora_probe_read", "slora_probe_gather"]
@@ -109,6 +109,7 @@ def lib():
             "slora_lora_forward": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P]),
             "slora_lora_forward_timed": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P, P, P]),
             "slora_last_error": (ctypes.c_char_p, []),
+            "slora_lora_forward_noalloc": (c_int32, [P, P, c_int32, P, P, P, P]),
             "slora_probe_read": (c_int32, [P, c_int64, c_int32, c_int32, P, P, P, P]),
             "slora_probe_gather": (c_int32, [P, c_int64, c_int64, P, c_int64, P, c_int64, c_int64, P,
                                              c_int64, c_int32, P, P, P, P]),
@@ -415,3 +416,9 @@ def slora_probe_gather(arrays, items: int, sink, stream=None, start_event=None, 
                                     _ptr(a1[0]), int(a1[1]), int(a1[2]), _ptr(a1[3]), int(a1[4]),
                                     int(items), _ptr(sink), _stream(stream), start_event, stop_event),
            "slora_probe_gather")
+
+
+def slora_lora_forward_noalloc(pool, seg, proj: int, x, w, y, stream=None) -> None:
+    """slora_lora_forward with the library's own workspace (no caller allocation)."""
+    _check(lib().slora_lora_forward_noalloc(pool, seg, proj, _ptr(x), _ptr(w), _ptr(y), _stream(stream)),
+           "slora_lora_forward_noalloc")

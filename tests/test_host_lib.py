@@ -567,6 +567,26 @@ def test_async_load_argument_errors_leave_pool_unchanged():
         S.slora_pool_destroy(pool)
 
 
+def test_forward_noalloc_refuses_batches_beyond_its_array():
+    """The no-allocation forward's workspace is an 8 MiB device array: a batch
+    whose workspace_bytes exceed it is refused before any device work."""
+    pool = S.slora_pool_create(S.SLORA_F16, 512, 512, 1, 4, 64, FAKE_BASE[:1], [256], None)
+    try:
+        S.slora_load_adapter(pool, 0, 64, 1.0)
+        seg = S.slora_build_segments(pool, [0] * 10000)    # 64-token MFMA blocks split over K
+        try:
+            info = S.slora_segments_get_info(seg)
+            assert info["workspace_bytes"] > 8 << 20
+            fake = 1 << 42
+            assert status_of(S.slora_lora_forward_noalloc, pool, seg, 0, fake, fake, fake) == S.SLORA_E_NOMEM
+            assert "8388608" in S.slora_last_error()
+        finally:
+            S.slora_segments_destroy(seg)
+        assert status_of(S.slora_lora_forward_noalloc, None, None, 0, 0, 0, 0) == S.SLORA_E_INVAL
+    finally:
+        S.slora_pool_destroy(pool)
+
+
 def test_forward_argument_errors():
     """slora_lora_forward refuses what its kernel cannot do before any device work."""
     fake = 1 << 42
