@@ -38,6 +38,40 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+SANITIZED_LIB_PATH = os.path.join(PKG_DIR, "libslora_sanitized.so")
+
+
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime, to preload into a process that
+    loads the sanitized library."""
+    clangxx = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clangxx):
+        clangxx = "/opt/rocm/llvm/bin/clang++"
+    out = subprocess.run([clangxx, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libslora with its host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (every undefined-behaviour report is fatal);
+    the device code is built as usual.  For CPU tests of the host runtime
+    (allocator, segment builder, tile lists, argument checks): load it with
+    SLORA_LIB pointing at it and asan_runtime() preloaded."""
+    tmp = SANITIZED_LIB_PATH + ".tmp"
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-shared-libasan", "-g"]
+    cmd = [HIPCC, *FLAGS, *san, "-I", INCLUDE, "-I", CSRC, "-o", tmp,
+           *[os.path.join(CSRC, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc (sanitized) failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, SANITIZED_LIB_PATH)
+    return SANITIZED_LIB_PATH
+
+
 def device_assembly(workdir: str, source: str = "slora_kernels.hip") -> str:
     """Compile one HIP source for gfx950 keeping the assembly; return its path."""
     src = os.path.join(CSRC, source)

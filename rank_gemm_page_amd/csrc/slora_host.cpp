@@ -723,19 +723,22 @@ void build_tiles(slora_segments* s) {
   s->blob.assign((size_t)cur, 0);
   {
     int32_t* b = s->blob.data();
-    std::memcpy(b + s->fw_order_off, s->perm.data(), (size_t)routed * 4);
+    // copies of possibly empty arrays (an empty vector's data() may be NULL,
+    // which memcpy may not be given even for zero bytes)
+    auto copy_words = [](int32_t* dst, const void* src, size_t n) { if (n) std::memcpy(dst, src, n * 4); };
+    copy_words(b + s->fw_order_off, s->perm.data(), (size_t)routed);
     // then the tokens with no adapter, in batch order
     std::vector<uint8_t> is_routed(T, 0);
     for (int32_t t : s->perm) is_routed[t] = 1;
     int32_t k = routed;
     for (int32_t t = 0; t < T; ++t)
       if (!is_routed[t]) b[s->fw_order_off + k++] = t;
-    std::memcpy(b + s->fw_pos_seg_off, pos_seg.data(), (size_t)routed * 4);
-    std::memcpy(b + s->fw_seg_start_off, s->seg_start.data(), (size_t)(S + 1) * 4);
-    std::memcpy(b + s->fw_seg_rank_off, s->seg_rank.data(), (size_t)S * 4);
-    std::memcpy(b + s->fw_seg_scale_off, s->seg_scale.data(), (size_t)S * 4);
+    copy_words(b + s->fw_pos_seg_off, pos_seg.data(), (size_t)routed);
+    copy_words(b + s->fw_seg_start_off, s->seg_start.data(), (size_t)(S + 1));
+    copy_words(b + s->fw_seg_rank_off, s->seg_rank.data(), (size_t)S);
+    copy_words(b + s->fw_seg_scale_off, s->seg_scale.data(), (size_t)S);
     for (int32_t g = 0; g < S; ++g) b[s->fw_seg_v_off + g] = (int32_t)s->seg_v_off[g];
-    std::memcpy(b + s->fw_rb_info_off, rb_info.data(), rb_info.size() * 4);
+    copy_words(b + s->fw_rb_info_off, rb_info.data(), rb_info.size());
     for (int pr = 0; pr < np; ++pr)
       for (int32_t e = 0; e < s->fw_n_stages; ++e) {
         const Stage& st = fw_stages[e];

@@ -71,9 +71,11 @@ def lib():
     """The loaded libslora.so (raises if it has not been built)."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with rank_gemm_page_amd.build.build()")
-        L = ctypes.CDLL(LIB_PATH)
+        # SLORA_LIB: another build of the same library (the sanitized host build)
+        path = os.environ.get("SLORA_LIB") or LIB_PATH
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with rank_gemm_page_amd.build.build()")
+        L = ctypes.CDLL(path)
         P = c_void_p
         sig = {
             "slora_pool_create": (c_int32, [POINTER(PoolDesc), POINTER(P)]),
