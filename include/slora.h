@@ -80,8 +80,12 @@ typedef struct {
   const int32_t* free_order[2];
 } slora_pool_desc;
 
-/* Create a pool over caller-owned page memory.  Host-only: no device memory is
- * touched until the first adapter load with data. */
+/* Create a pool over caller-owned page memory: one allocator and block table
+ * for adapter factors of every rank and for KV blocks (summary page, "Unified
+ * Paging": a unified memory pool manages adapter weights and KV cache
+ * together; blog page, section 2: adapter weights sit in non-contiguous
+ * memory blocks).  Host-only: no device memory is touched until the first
+ * adapter load with data. */
 slora_status slora_pool_create(const slora_pool_desc* desc, slora_pool** out);
 void slora_pool_destroy(slora_pool* pool);
 
@@ -215,8 +219,10 @@ slora_status slora_pack_adapter(const slora_pool* pool, int32_t rank, const void
  * or wait for an event recorded there.  Likewise, unloading an adapter whose
  * pages a queued delta still reads and fetching another into them races unless
  * the fetch's stream waits for the delta.  A failed queue call returns
- * SLORA_E_HIP with every page given back; device faults surface at the
- * caller's synchronisation.  n == 0 does nothing. */
+ * SLORA_E_HIP with every page given back, after waiting on `stream` for the
+ * copies and scatters it had already queued (none of them still writes a
+ * page it gave back); device faults surface at the caller's
+ * synchronisation.  n == 0 does nothing. */
 slora_status slora_load_adapters_async(slora_pool* pool, int32_t n, const int32_t* ids,
                                        const int32_t* ranks, const float* scales, void* const* images,
                                        void* dev_stage, size_t dev_stage_bytes, void* stream);
@@ -230,7 +236,11 @@ slora_status slora_unload_adapter(slora_pool* pool, int32_t id);
 slora_status slora_adapter_pages(const slora_pool* pool, int32_t id, int32_t proj,
                                  int32_t* a_ids, int32_t* b_ids, int32_t* rank_out);
 
-/* Group a batch by adapter (host only).  ids[t] (host, n_tokens entries) is
+/* Group a batch by adapter (host only; summary page, "Heterogeneous batching
+ * kernels": a batch mixes requests of different adapters and ranks, and the
+ * kernels gather each request's adapter pages; blog page, section 3: each
+ * request's hidden state is matched with its adapter's pages through the
+ * paging table).  ids[t] (host, n_tokens entries) is
  * token t's adapter; a negative id means "no adapter" and leaves y[t]
  * untouched.  Tokens are stably sorted by adapter id into segments in
  * ascending id order, each with its rank, scale, rank prefix offset and page
@@ -257,7 +267,9 @@ typedef struct {
 
 slora_status slora_segments_get_info(const slora_segments* seg, slora_segments_info* info);
 
-/* Host copies of the segment metadata; any pointer may be NULL.  Sizes:
+/* Host copies of the segment metadata (the sorted batch and the page lists
+ * of the block table that the kernels gather from, summary page "Unified
+ * Paging"); any pointer may be NULL.  Sizes:
  * perm[n_routed] (batch index of the i-th sorted token), seg_start[S+1],
  * seg_adapter[S], seg_rank[S], seg_scale[S], seg_page_off[S+1] (prefix sum of
  * ranks), a_pages[n_proj*sum_rank] and b_pages[n_proj*sum_rank] (entry
@@ -288,7 +300,21 @@ slora_status slora_segments_export(const slora_segments* seg, int32_t* perm, int
 slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, int32_t* records,
                                   size_t records_words);
 
-/* Copy the tile metadata to caller-owned device memory dev_meta (at least
+/* Introspection of slora_lora_forward's tables (host copies): layout[8]
+ * receives {n_rb, n_rb_big, big_rows, small_bm, n_stages, packed,
+ * stage_words, n_proj}.  Sorted positions [0, big_rows) form n_rb_big row
+ * blocks of 256 and the rest row blocks of small_bm (32, 64 or 128); rb_info
+ * (2 x n_rb words) holds per row block its first LoRA stage and stage count;
+ * stages (n_proj x n_stages x stage_words words, projection-major) the LoRA
+ * stage entries: 32 B page ids, then, when packed, one word per group of 4
+ * rows, segment << 9 | (first rank row / 4) << 3 | rows (0: empty group),
+ * else the segment, first rank row and rank of the stage's one segment.
+ * Either buffer may be NULL.  For tests and tools; the layout may change. */
+slora_status slora_segments_forward_tables(const slora_segments* seg, int32_t* layout, int32_t* rb_info,
+                                           size_t rb_words, int32_t* stages, size_t stage_words);
+
+/* Copy the tile metadata (the batch's page lists and work split, summary page
+ * "Heterogeneous batching kernels") to caller-owned device memory dev_meta (at least
  * meta_bytes, 16-byte aligned) on `stream` and remember that address for
  * later deltas.  The copy is asynchronous; dev_meta must stay untouched while
  * deltas that use it are in flight.  The metadata also holds the area where
@@ -298,7 +324,12 @@ slora_status slora_segments_tiles(const slora_segments* seg, int32_t* layout, in
 slora_status slora_segments_upload(slora_segments* seg, void* dev_meta, size_t dev_meta_bytes,
                                    void* stream);
 
-/* The hot path: y[t] += s_a * (x[t] A_a) B_a for every routed token, for
+/* The hot path (summary page, "How to read the paper" item 2, h = xW + xAB,
+ * with the delta xAB kept separate from the base product; blog page, section
+ * 2: each token's product with its adapter's A and B, times the adapter's
+ * scaling factor, added to the base output; summary page, "Heterogeneous
+ * batching kernels": one launch for a batch of many adapters and ranks
+ * gathering non-contiguous pages): y[t] += s_a * (x[t] A_a) B_a for every routed token, for
  * projection `proj` (0 <= proj < n_proj).  x is device memory of
  * n_tokens x h_in and y of n_tokens x h_out, both row-major in batch order
  * and of the pool dtype; y is updated in place with one rounding of
@@ -379,10 +410,12 @@ slora_status slora_lora_expand(slora_pool* pool, const slora_segments* seg, int3
  * x (n_tokens x h_in) and y (n_tokens x h_out) are device memory in batch
  * order, as for slora_lora_delta; workspace as for slora_lora_delta.  All
  * four 16-byte aligned.  fp16 pools only, with h_in a multiple of 64 and
- * h_out a multiple of 128 (SLORA_E_INVAL otherwise).  Launches the shrink
- * kernels (v into the workspace) and then one matrix-core kernel over tiles
- * of 64, 128 or 256 tokens (in segment order) x 128 or 256 columns on `stream`
- * (SLORA_TUNE_FWD_TILE), and returns
+ * h_out a multiple of 128 (SLORA_E_INVAL otherwise).  A batch without
+ * 256-row tiles packs its LoRA stages with 23-bit segment fields, so it may
+ * hold at most 2^23 - 1 segments (SLORA_E_INVAL otherwise).  Launches the
+ * shrink kernels (v into the workspace) and then one matrix-core kernel over
+ * tiles of 32, 64, 128 or 256 tokens (in segment order) x 128 or 256 columns
+ * on `stream` (SLORA_TUNE_FWD_TILE), and returns
  * without waiting; launch errors return SLORA_E_HIP, device faults surface
  * at the caller's next synchronisation.  Requires a prior
  * slora_segments_upload; returns SLORA_E_STALE like slora_lora_delta.  With

@@ -295,8 +295,19 @@ void rollback_pages(slora_pool* p, const AdapterRec& rec) {
 // the copy of the image to dev_stage + (sum of the earlier images' sizes);
 // then queue the scatters of all rows into their pages, kMaxFetch adapters
 // per launch.  All copies go first so the copy engine runs them back to back.
+// On a failure, whatever was already queued is waited for before returning,
+// so that the caller can give the pages back (and reuse the staging) without
+// a queued copy or scatter still reading or writing them.
 slora_status enqueue_images(slora_pool* p, const std::vector<const AdapterRec*>& recs,
                             char* const* images, char* dev_stage, hipStream_t stream) {
+  bool queued = false;
+  auto failed = [&](hipError_t he, const char* what) {
+    if (queued) {
+      (void)hipStreamSynchronize(stream);
+      (void)hipGetLastError();
+    }
+    return hip_fail(he, what);
+  };
   const int np = p->d.n_proj;
   const size_t n = recs.size();
   std::vector<size_t> off(n + 1, 0);
@@ -308,7 +319,8 @@ slora_status enqueue_images(slora_pool* p, const std::vector<const AdapterRec*>&
     std::memcpy(ids, rec.a_pages.data(), (size_t)np * r * sizeof(int32_t));
     std::memcpy(ids + (size_t)np * r, rec.b_pages.data(), (size_t)np * r * sizeof(int32_t));
     hipError_t he = hipMemcpyAsync(dev_stage + off[k], images[k], L.used, hipMemcpyHostToDevice, stream);
-    if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(adapter image)");
+    if (he != hipSuccess) return failed(he, "hipMemcpyAsync(adapter image)");
+    queued = true;
     off[k + 1] = off[k] + L.total;
   }
   for (size_t k0 = 0; k0 < n; k0 += kMaxFetch) {
@@ -329,7 +341,7 @@ slora_status enqueue_images(slora_pool* p, const std::vector<const AdapterRec*>&
       S.row_start[i + 1] = S.row_start[i] + 2 * np * S.rank[i];
     }
     hipError_t he = launch_scatter_pages(S, stream);
-    if (he != hipSuccess) return hip_fail(he, "scatter adapter rows");
+    if (he != hipSuccess) return failed(he, "scatter adapter rows");
   }
   return SLORA_OK;
 }
@@ -1247,6 +1259,25 @@ slora_status slora_segments_tiles(const slora_segments* s, int32_t* layout, int3
     const size_t words = (size_t)s->n_tiles * s->stride;
     if (records_words < words) return fail(SLORA_E_NOMEM, "slora_segments_tiles: records buffer too small");
     std::memcpy(records, s->blob.data(), words * sizeof(int32_t));
+  }
+  return SLORA_OK;
+}
+
+slora_status slora_segments_forward_tables(const slora_segments* s, int32_t* layout, int32_t* rb_info,
+                                           size_t rb_words, int32_t* stages, size_t stage_words) {
+  if (!s || !layout) return fail(SLORA_E_INVAL, "slora_segments_forward_tables: NULL argument");
+  const int32_t lay[8] = {s->fw_n_rb, s->fw_n_rb_big, s->fw_big_rows, s->fw_small_bm, s->fw_n_stages,
+                          s->fw_packed ? 1 : 0, kFwdStageWords, s->n_proj};
+  std::memcpy(layout, lay, sizeof(lay));
+  const size_t rbw = 2 * (size_t)s->fw_n_rb;
+  const size_t stw = (size_t)s->n_proj * s->fw_n_stages * kFwdStageWords;
+  if (rb_info) {
+    if (rb_words < rbw) return fail(SLORA_E_NOMEM, "slora_segments_forward_tables: rb_info buffer too small");
+    if (rbw) std::memcpy(rb_info, s->blob.data() + s->fw_rb_info_off, rbw * sizeof(int32_t));
+  }
+  if (stages) {
+    if (stage_words < stw) return fail(SLORA_E_NOMEM, "slora_segments_forward_tables: stages buffer too small");
+    if (stw) std::memcpy(stages, s->blob.data() + s->fw_stages_off, stw * sizeof(int32_t));
   }
   return SLORA_OK;
 }

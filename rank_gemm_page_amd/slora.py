@@ -38,6 +38,7 @@ EXPORTED = [
     "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
     "slora_lora_forward", "slora_lora_forward_timed", "slora_last_error",
     "slora_lora_delta_multi", "slora_lora_delta_multi_timed", "slora_lora_forward_noalloc",
+    "slora_segments_forward_tables",
 ]
 # include/slora_probe.h: bandwidth probes (measurement only)
 EXPORTED_PROBE = ["slora_probe_read", "slora_probe_gather"]
@@ -112,6 +113,8 @@ def lib():
             "slora_lora_forward_timed": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P, P, P]),
             "slora_last_error": (ctypes.c_char_p, []),
             "slora_lora_forward_noalloc": (c_int32, [P, P, c_int32, P, P, P, P]),
+            "slora_segments_forward_tables": (c_int32, [P, POINTER(c_int32), POINTER(c_int32), c_size_t,
+                                                        POINTER(c_int32), c_size_t]),
             "slora_probe_read": (c_int32, [P, c_int64, c_int32, c_int32, P, P, P, P]),
             "slora_probe_gather": (c_int32, [P, c_int64, c_int64, P, c_int64, P, c_int64, c_int64, P,
                                              c_int64, c_int32, P, P, P, P]),
@@ -424,3 +427,19 @@ def slora_lora_forward_noalloc(pool, seg, proj: int, x, w, y, stream=None) -> No
     """slora_lora_forward with the library's own workspace (no caller allocation)."""
     _check(lib().slora_lora_forward_noalloc(pool, seg, proj, _ptr(x), _ptr(w), _ptr(y), _stream(stream)),
            "slora_lora_forward_noalloc")
+
+
+def slora_segments_forward_tables(seg):
+    """(layout dict, rb_info [n_rb, 2], stages [n_proj, n_stages, stage_words]) of slora_lora_forward."""
+    lay = np.zeros(8, np.int32)
+    _check(lib().slora_segments_forward_tables(seg, _i32p(lay), None, 0, None, 0),
+           "slora_segments_forward_tables")
+    keys = ["n_rb", "n_rb_big", "big_rows", "small_bm", "n_stages", "packed", "stage_words", "n_proj"]
+    L = dict(zip(keys, (int(v) for v in lay)))
+    rb = np.zeros(max(2 * L["n_rb"], 1), np.int32)
+    st = np.zeros(max(L["n_proj"] * L["n_stages"] * L["stage_words"], 1), np.int32)
+    _check(lib().slora_segments_forward_tables(seg, _i32p(lay), _i32p(rb), rb.size, _i32p(st), st.size),
+           "slora_segments_forward_tables")
+    return (L, rb[:2 * L["n_rb"]].reshape(-1, 2),
+            st[:L["n_proj"] * L["n_stages"] * L["stage_words"]].reshape(L["n_proj"], L["n_stages"],
+                                                                          L["stage_words"]))

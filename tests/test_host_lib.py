@@ -122,6 +122,96 @@ def test_metadata_bit_exact_vs_oracle(name):
         S.slora_pool_destroy(pool)
 
 
+def check_forward_tables(w, pool, ids, tuning_label=""):
+    """slora_lora_forward's LoRA stage table, decoded per row block: every
+    (segment, rank row) of the segments that own a position of the block
+    appears exactly once, with the oracle's B page id; rows with no rank row
+    of their own repeat the page before them and, packed, sit in a group whose
+    word counts only the real rows (0 for an empty group); the packed fields
+    stay within their 23-bit segment and 6-bit row-quad ranges."""
+    seg = S.slora_build_segments(pool, ids)
+    try:
+        L, rb_info, stages = S.slora_segments_forward_tables(seg)
+        _, ref = oracle_segments_of(w, ids)
+        routed = int(np.count_nonzero(np.asarray(ids) >= 0))
+        starts, ranks, page_off = ref.seg_start, ref.seg_rank, ref.seg_page_off
+        sum_r = int(page_off[-1])
+        pos_seg = np.repeat(np.arange(len(ranks)), np.diff(starts))
+        assert L["stage_words"] == 40 and L["n_proj"] == w.spec.n_proj
+        assert L["n_rb"] == L["n_rb_big"] + -(-(len(ids) - L["big_rows"]) // L["small_bm"])
+        for rb in range(L["n_rb"]):
+            big = rb < L["n_rb_big"]
+            p0 = rb * 256 if big else L["big_rows"] + (rb - L["n_rb_big"]) * L["small_bm"]
+            p1 = min(p0 + (256 if big else L["small_bm"]), routed)
+            first, count = (int(v) for v in rb_info[rb])
+            want = set()
+            if p0 < p1:
+                for g in range(int(pos_seg[p0]), int(pos_seg[p1 - 1]) + 1):
+                    want |= {(g, j) for j in range(int(ranks[g]))}
+            else:
+                assert count == 0
+            for proj in range(L["n_proj"]):
+                seen = []
+                bp = ref.b_pages[proj * sum_r:(proj + 1) * sum_r]
+                for e in range(first, first + count):
+                    ent = stages[proj, e]
+                    last = None
+                    if L["packed"]:
+                        for u in range(8):
+                            word = int(ent[32 + u])
+                            if word == 0:
+                                rows = []
+                            else:
+                                g, jq, n = word >> 9, (word >> 3) & 63, word & 7
+                                assert 1 <= n <= 4 and g < (1 << 23) and jq < 64
+                                rows = [(g, 4 * jq + k) for k in range(n)]
+                            for k in range(4):
+                                pg = int(ent[4 * u + k])
+                                if k < len(rows):
+                                    g, j = rows[k]
+                                    assert pg == bp[page_off[g] + j], (rb, e, u, k)
+                                    seen.append((g, j))
+                                    last = pg
+                                else:
+                                    assert last is not None and pg == last, (rb, e, u, k)   # filler row
+                    else:
+                        g, j0, r = int(ent[32]), int(ent[33]), int(ent[34])
+                        assert r == ranks[g] and j0 % 32 == 0
+                        for k in range(32):
+                            pg = int(ent[k])
+                            if j0 + k < r:
+                                assert pg == bp[page_off[g] + j0 + k]
+                                seen.append((g, j0 + k))
+                                last = pg
+                            else:
+                                assert pg == last
+                assert len(seen) == len(set(seen)) and set(seen) == want, (tuning_label, rb, proj)
+        return L
+    finally:
+        S.slora_segments_destroy(seg)
+
+
+def oracle_segments_of(w, ids):
+    st = orc.build_from_workload(w, load_weights=False)
+    return st, orc.segment_model(ids, st.alloc)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+@pytest.mark.parametrize("tile", [0, 32, 128, 256])
+def test_forward_tables_match_oracle_pages(name, tile):
+    w = generate(CONFIGS[name], 0)
+    if w.spec.dtype != "f16" or (tile == 256 and w.spec.h_out % 256):
+        pytest.skip("slora_lora_forward: fp16 only; 256-wide tiles need h_out a multiple of 256")
+    pool, _ = make_pool(w, tuning={S.SLORA_TUNE_FWD_TILE: tile})
+    try:
+        ids = w.ids.copy()
+        ids[::7] = -1                 # tokens with no adapter sort after the routed ones
+        L = check_forward_tables(w, pool, ids, f"{name}/tile {tile}")
+        assert L["packed"] == (L["n_rb_big"] == 0)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
 def check_tiles_cover(w, pool, ids):
     """Every (token, rank row) is shrunk once (MFMA shrink: once per K split,
     the splits' k ranges tiling [0, h_in), summed by exactly one combine tile
