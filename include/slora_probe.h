@@ -42,7 +42,10 @@ slora_status slora_probe_read(const void* src, int64_t bytes, int32_t items, int
  * row i at base0 + i * stride0) and rows rows1[0 .. n1) of the array at base1
  * (n1 may be 0), in one launch, with the streaming hint.  rows0 and rows1 are
  * device arrays of int32 row ids; the caller guarantees that every id is in
- * range.  items as for slora_probe_read. */
+ * range.  A workgroup reads whole rows, or one piece of a long row, so its
+ * row ids are uniform.  items as for slora_probe_read: rows of up to items
+ * 4 KB passes share a workgroup, longer rows take several.  n0, n1 and the
+ * 16-byte chunks of a row must each stay below 2^31. */
 slora_status slora_probe_gather(const void* base0, int64_t stride0, int64_t row_bytes0,
                                 const int32_t* rows0, int64_t n0, const void* base1, int64_t stride1,
                                 int64_t row_bytes1, const int32_t* rows1, int64_t n1, int32_t items,

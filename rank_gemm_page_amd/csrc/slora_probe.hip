@@ -15,10 +15,17 @@ namespace {
 constexpr int kProbeThreads = 256;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool NT>
-__device__ __forceinline__ u32x4 load16(const u32x4* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
+constexpr int kBufferFormat = 0x00020000;   // descriptor word 3: raw 32-bit buffer
+constexpr int kNontemporal = 2;             // cache-policy bits of a buffer load: streaming
+
+// A buffer load returns zero, without touching memory, for any offset at or
+// past the descriptor's byte count: the probes read ragged ends and skipped
+// rows with no branch, so every load of a thread stays in flight together.
+__device__ __forceinline__ u32x4 load16(const char* base, uint32_t bytes, uint32_t offset, bool nt) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, (int)bytes,
+                                                                      kBufferFormat);
+  return nt ? __builtin_amdgcn_raw_buffer_load_b128(rs, offset, 0, kNontemporal)
+            : __builtin_amdgcn_raw_buffer_load_b128(rs, offset, 0, 0);
 }
 
 // The loads feed an xor that decides whether one store runs; the store never
@@ -29,51 +36,70 @@ __device__ __forceinline__ void sink_if(u32x4 acc, u32x4* sink) {
 }
 
 // Workgroup b reads chunks [b * 256 * ITEMS, (b + 1) * 256 * ITEMS): at step k
-// thread tid reads chunk base + k * 256 + tid, so every load instruction of a
-// wave covers 1 KB of contiguous memory.  All ITEMS loads are issued before
-// any is used.
+// thread tid reads chunk k * 256 + tid of that span, so every load instruction
+// of a wave covers 1 KB of contiguous memory.  All ITEMS loads are issued
+// before any is used; the last workgroup's loads past the end return zero.
 template <int ITEMS, bool NT>
-__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* src, int64_t n_chunks,
-                                                                   u32x4* sink) {
-  const int64_t base = (int64_t)blockIdx.x * kProbeThreads * ITEMS + threadIdx.x;
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const char* src, int64_t bytes, u32x4* sink) {
+  constexpr int64_t kSpan = (int64_t)kProbeThreads * ITEMS * 16;
+  const int64_t start = (int64_t)blockIdx.x * kSpan;
+  const int64_t left = bytes - start;
+  const uint32_t span = (uint32_t)(left < kSpan ? left : kSpan);
   u32x4 v[ITEMS];
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int64_t c = base + (int64_t)k * kProbeThreads;
-    v[k] = load16<NT>(src + (c < n_chunks ? c : n_chunks - 1));
-  }
+  for (int k = 0; k < ITEMS; ++k) v[k] = load16(src + start, span, (k * kProbeThreads + threadIdx.x) * 16, NT);
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
   u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) acc ^= v[k];
   sink_if(acc, sink);
 }
 
-struct GatherArgs {
-  const char* base[2];
-  int64_t stride[2];
-  const int32_t* rows[2];
-  uint32_t cpr[2];       // 16-byte chunks per row
-  uint32_t n_chunks0;    // chunks of the first array's rows
-  uint32_t n_chunks;     // all chunks
+struct GatherArray {
+  const char* base;
+  int64_t stride;
+  const int32_t* rows;
+  uint32_t n;           // rows listed
+  uint32_t row_bytes;
+  uint32_t cpt;         // 256-thread passes per row: ceil(row_bytes / 4096)
+  uint32_t pad;
 };
 
-// The listed rows' chunks, numbered first array first, row by row; workgroup
-// b reads numbers [b * 256 * ITEMS, ...) as the read probe does, each through
-// its row id.
+struct GatherArgs {
+  GatherArray a[2];
+  uint32_t blocks0;     // workgroups of the first array
+};
+
+// Each row is cut into cpt passes of 256 16-byte chunks (the last one ragged);
+// the passes of the listed rows, row after row, are dealt ITEMS to a
+// workgroup: [0, blocks0) over the first array, the rest over the second.
+// A pass lies in one row, so the row id of every load instruction is uniform
+// (one scalar load) and the instruction covers 1 KB of that row; chunks past
+// the row's end, and passes past the last listed row, read nothing.
 template <int ITEMS>
 __global__ __launch_bounds__(kProbeThreads) void probe_gather_kernel(GatherArgs G, u32x4* sink) {
-  const uint32_t base = blockIdx.x * (uint32_t)(kProbeThreads * ITEMS) + threadIdx.x;
-  u32x4 v[ITEMS];
+  uint32_t b = blockIdx.x;
+  const bool second = b >= G.blocks0;
+  const GatherArray A = second ? G.a[1] : G.a[0];
+  if (second) b -= G.blocks0;
+  const uint32_t p0 = b * ITEMS;
+  uint32_t row = p0 / A.cpt, pc = p0 - row * A.cpt;
+  uint32_t id[ITEMS], bytes[ITEMS], off[ITEMS];
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
-    uint32_t i = base + (uint32_t)k * kProbeThreads;
-    i = i < G.n_chunks ? i : G.n_chunks - 1;
-    const int a = i < G.n_chunks0 ? 0 : 1;
-    const uint32_t j = a ? i - G.n_chunks0 : i;
-    const uint32_t row = j / G.cpr[a], c = j - row * G.cpr[a];
-    const char* p = G.base[a] + (int64_t)(uint32_t)G.rows[a][row] * G.stride[a] + (int64_t)c * 16;
-    v[k] = load16<true>(reinterpret_cast<const u32x4*>(p));
+    const bool listed = row < A.n;
+    id[k] = (uint32_t)A.rows[listed ? row : A.n - 1];
+    bytes[k] = listed ? A.row_bytes : 0u;
+    off[k] = (pc * kProbeThreads + threadIdx.x) * 16;
+    ++pc;
+    const bool wrap = pc == A.cpt;
+    row += wrap ? 1u : 0u;
+    pc = wrap ? 0u : pc;
   }
+  u32x4 v[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) v[k] = load16(A.base + (int64_t)id[k] * A.stride, bytes[k], off[k], true);
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use
   u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) acc ^= v[k];
@@ -110,7 +136,6 @@ slora_status slora_probe_read(const void* src, int64_t bytes, int32_t items, int
   if (!src || !sink || bytes <= 0 || (bytes & 15) || ((reinterpret_cast<uintptr_t>(src) |
                                                        reinterpret_cast<uintptr_t>(sink)) & 15))
     return probe_fail(SLORA_E_INVAL, "slora_probe_read: NULL, unaligned or empty buffer");
-  const int64_t n_chunks = bytes / 16;
   const void* k = nullptr;
   switch (items) {
     case 1: k = read_fn<1>(nontemporal); break;
@@ -120,17 +145,13 @@ slora_status slora_probe_read(const void* src, int64_t bytes, int32_t items, int
     case 16: k = read_fn<16>(nontemporal); break;
     default: return probe_fail(SLORA_E_INVAL, "slora_probe_read: items must be 1, 2, 4, 8 or 16");
   }
-  const int64_t per = (int64_t)kProbeThreads * items;
-  const int64_t blocks = (n_chunks + per - 1) / per;
+  const int64_t per = (int64_t)kProbeThreads * items * 16;
+  const int64_t blocks = (bytes + per - 1) / per;
   if (blocks > 0x7FFFFFFF) return probe_fail(SLORA_E_INVAL, "slora_probe_read: too many bytes");
-  const u32x4* s = static_cast<const u32x4*>(src);
+  const char* s = static_cast<const char*>(src);
   u32x4* o = static_cast<u32x4*>(sink);
-  void* args[] = {&s, const_cast<int64_t*>(&n_chunks), &o};
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = (!ev0 && !ev1)
-      ? hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kProbeThreads), args, 0, st)
-      : hipExtLaunchKernel(k, dim3((unsigned)blocks), dim3(kProbeThreads), args, 0, st,
-                           static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0);
+  void* args[] = {&s, &bytes, &o};
+  const hipError_t e = launch(k, blocks, args, stream, ev0, ev1);
   if (e != hipSuccess) return probe_fail(SLORA_E_HIP, std::string("slora_probe_read: ") + hipGetErrorString(e));
   return SLORA_OK;
 }
@@ -143,31 +164,41 @@ slora_status slora_probe_gather(const void* base0, int64_t stride0, int64_t row_
       (stride0 & 15) || !sink || n1 < 0 || (n1 > 0 && (!base1 || !rows1 || row_bytes1 <= 0 || (row_bytes1 & 15) ||
                                                        stride1 < row_bytes1 || (stride1 & 15))))
     return probe_fail(SLORA_E_INVAL, "slora_probe_gather: bad row arrays");
+  if (items != 1 && items != 2 && items != 4 && items != 8 && items != 16)
+    return probe_fail(SLORA_E_INVAL, "slora_probe_gather: items must be 1, 2, 4, 8 or 16");
+  if (n0 >= ((int64_t)1 << 31) || n1 >= ((int64_t)1 << 31) || row_bytes0 >= ((int64_t)1 << 30) ||
+      (n1 > 0 && row_bytes1 >= ((int64_t)1 << 30)))
+    return probe_fail(SLORA_E_INVAL, "slora_probe_gather: too many rows or row too long");
   GatherArgs G{};
-  G.base[0] = static_cast<const char*>(base0);
-  G.base[1] = n1 > 0 ? static_cast<const char*>(base1) : G.base[0];
-  G.stride[0] = stride0;
-  G.stride[1] = n1 > 0 ? stride1 : stride0;
-  G.rows[0] = rows0;
-  G.rows[1] = n1 > 0 ? rows1 : rows0;
-  G.cpr[0] = (uint32_t)(row_bytes0 / 16);
-  G.cpr[1] = n1 > 0 ? (uint32_t)(row_bytes1 / 16) : G.cpr[0];
-  const int64_t c0 = n0 * (row_bytes0 / 16), c1 = n1 * (n1 > 0 ? row_bytes1 / 16 : 0);
-  if (c0 + c1 >= ((int64_t)1 << 31)) return probe_fail(SLORA_E_INVAL, "slora_probe_gather: too many chunks");
-  G.n_chunks0 = (uint32_t)c0;
-  G.n_chunks = (uint32_t)(c0 + c1);
+  const void* bases[2] = {base0, base1};
+  const int64_t strides[2] = {stride0, stride1}, rbytes[2] = {row_bytes0, row_bytes1}, ns[2] = {n0, n1};
+  const int32_t* rows[2] = {rows0, rows1};
+  int64_t blocks[2] = {0, 0};
+  for (int a = 0; a < 2; ++a) {
+    const int src = ns[a] > 0 ? a : 0;  // an empty second array repeats the first's fields
+    GatherArray& A = G.a[a];
+    A.base = static_cast<const char*>(bases[src]);
+    A.stride = strides[src];
+    A.rows = rows[src];
+    A.n = (uint32_t)ns[a];
+    A.row_bytes = (uint32_t)rbytes[src];
+    A.cpt = (uint32_t)((rbytes[src] + 16 * kProbeThreads - 1) / (16 * kProbeThreads));
+    blocks[a] = (ns[a] * A.cpt + items - 1) / items;
+    if (ns[a] * A.cpt + items >= ((int64_t)1 << 32))
+      return probe_fail(SLORA_E_INVAL, "slora_probe_gather: too many rows");
+  }
+  if (blocks[0] + blocks[1] > 0x7FFFFFFF) return probe_fail(SLORA_E_INVAL, "slora_probe_gather: too many rows");
+  G.blocks0 = (uint32_t)blocks[0];
   u32x4* o = static_cast<u32x4*>(sink);
   void* args[] = {&G, &o};
-  const int64_t per = (int64_t)kProbeThreads * items;
-  const int64_t blocks = (c0 + c1 + per - 1) / per;
+  const int64_t nblocks = blocks[0] + blocks[1];
   hipError_t e;
   switch (items) {
-    case 1: e = launch(&probe_gather_kernel<1>, blocks, args, stream, ev0, ev1); break;
-    case 2: e = launch(&probe_gather_kernel<2>, blocks, args, stream, ev0, ev1); break;
-    case 4: e = launch(&probe_gather_kernel<4>, blocks, args, stream, ev0, ev1); break;
-    case 8: e = launch(&probe_gather_kernel<8>, blocks, args, stream, ev0, ev1); break;
-    case 16: e = launch(&probe_gather_kernel<16>, blocks, args, stream, ev0, ev1); break;
-    default: return probe_fail(SLORA_E_INVAL, "slora_probe_gather: items must be 1, 2, 4, 8 or 16");
+    case 1: e = launch(&probe_gather_kernel<1>, nblocks, args, stream, ev0, ev1); break;
+    case 2: e = launch(&probe_gather_kernel<2>, nblocks, args, stream, ev0, ev1); break;
+    case 4: e = launch(&probe_gather_kernel<4>, nblocks, args, stream, ev0, ev1); break;
+    case 8: e = launch(&probe_gather_kernel<8>, nblocks, args, stream, ev0, ev1); break;
+    default: e = launch(&probe_gather_kernel<16>, nblocks, args, stream, ev0, ev1); break;
   }
   if (e != hipSuccess) return probe_fail(SLORA_E_HIP, std::string("slora_probe_gather: ") + hipGetErrorString(e));
   return SLORA_OK;

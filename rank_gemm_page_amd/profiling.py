@@ -35,13 +35,16 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 def kernel_source_hash(kind: str = "fused") -> str:
     """Hash of the sources the measured kernel depends on: every host and
-    device source, except that the delta's kernels ("fused") do not include
-    the base-plus-delta kernel's own file."""
+    device source except the bandwidth probes and the no-allocation wrapper,
+    and for the delta's kernels ("fused") not the base-plus-delta kernel's
+    own file either."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_gemm_page_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if not name.endswith((".hip", ".cpp", ".h")):
             continue            # build by-products are not sources
+        if name in ("slora_probe.hip", "slora_noalloc.hip"):
+            continue            # measurement probes and a wrapper: no kernel of the delta
         if kind == "fused" and name == "slora_forward.hip":
             continue
         with open(os.path.join(csrc, name), "rb") as f:

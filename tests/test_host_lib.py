@@ -716,3 +716,24 @@ def test_forward_argument_errors():
     finally:
         for pool in (p32, p16_bad, p16):
             S.slora_pool_destroy(pool)
+
+
+def test_probe_argument_errors():
+    """The bandwidth probes refuse bad arguments before any launch."""
+    fake = 1 << 42
+    read = lambda **kw: status_of(S.slora_probe_read, **{**dict(src=fake, nbytes=4096, items=4,
+                                                                   nontemporal=True, sink=fake), **kw})
+    assert read(items=3) == S.SLORA_E_INVAL
+    assert read(nbytes=4100) == S.SLORA_E_INVAL
+    assert read(nbytes=0) == S.SLORA_E_INVAL
+    assert read(src=fake + 8) == S.SLORA_E_INVAL
+    assert read(sink=0) == S.SLORA_E_INVAL
+    row = (fake, 8192, 8192, fake, 4)
+    gather = lambda arrays, items=4, sink=fake: status_of(S.slora_probe_gather, arrays, items, sink)
+    assert gather([row], items=5) == S.SLORA_E_INVAL
+    assert gather([(fake, 8192, 8200, fake, 4)]) == S.SLORA_E_INVAL       # row longer than its stride
+    assert gather([(fake, 8192, 8184, fake, 4)]) == S.SLORA_E_INVAL       # row not whole 16-byte chunks
+    assert gather([(fake, 8192, 8192, 0, 4)]) == S.SLORA_E_INVAL          # NULL row ids
+    assert gather([(fake, 8192, 8192, fake, 0)]) == S.SLORA_E_INVAL       # no rows
+    assert gather([row, (0, 8192, 8192, fake, 2)]) == S.SLORA_E_INVAL     # NULL second array
+    assert gather([row], sink=0) == S.SLORA_E_INVAL
