@@ -740,6 +740,8 @@ def main():
                     help="base-plus-delta tile (0: automatic)")
     ap.add_argument("--shrink-rows", type=int, default=None,
                     help="rank rows per vector-ALU shrink tile (0: as many as fit)")
+    ap.add_argument("--fwd-ksplit", type=int, default=None,
+                    help="wave groups splitting a 32- or 64-row forward tile's steps (0: automatic)")
     ap.add_argument("--per-projection", action="store_true",
                     help="one fused launch per projection instead of one launch for all of them")
     ap.add_argument("--staged", action="store_true",
@@ -782,7 +784,8 @@ def main():
                                 (S.SLORA_TUNE_TILE_ORDER, args.tile_order),
                                 (S.SLORA_TUNE_FWD_GROUP, args.fwd_group),
                                 (S.SLORA_TUNE_FWD_TILE, args.fwd_tile),
-                                (S.SLORA_TUNE_SHRINK_ROWS, args.shrink_rows))
+                                (S.SLORA_TUNE_SHRINK_ROWS, args.shrink_rows),
+                                (S.SLORA_TUNE_FWD_KSPLIT, args.fwd_ksplit))
               if v is not None}
     names = CONFIG_ORDER if args.config == "all" else [args.config]
     t_all = time.perf_counter()

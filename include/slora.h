@@ -139,7 +139,15 @@ void slora_pool_destroy(slora_pool* pool);
  *  SLORA_TUNE_SHRINK_ROWS      - rank rows of one vector-ALU shrink tile, at
  *                                most 16 / (16-byte chunks of an x row per
  *                                thread); 0 (default): that maximum.
- * They change how the work is cut, never what is computed. */
+ *  SLORA_TUNE_FWD_KSPLIT       - slora_lora_forward's 32- and 64-row tiles:
+ *                                1 (one group of waves takes every step of
+ *                                a tile) or 2 (two groups take alternate
+ *                                steps into sums of their own, added before
+ *                                the output is rounded); 0 (default): 2 for
+ *                                the 32-row tiles, 1 for the 64-row ones.
+ *                                The larger tiles always take 1.
+ * They change how the work is cut, never what is computed (only, in floating
+ * point, the order in which partial sums meet). */
 #define SLORA_MFMA_MAX_RANK 64
 typedef enum {
   SLORA_TUNE_MFMA_MIN_TOKENS = 0,
@@ -151,7 +159,8 @@ typedef enum {
   SLORA_TUNE_TILE_ORDER = 6,
   SLORA_TUNE_FWD_GROUP = 7,
   SLORA_TUNE_FWD_TILE = 8,
-  SLORA_TUNE_SHRINK_ROWS = 9
+  SLORA_TUNE_SHRINK_ROWS = 9,
+  SLORA_TUNE_FWD_KSPLIT = 10
 } slora_tune_key;
 slora_status slora_pool_set_tuning(slora_pool* pool, int32_t key, int64_t value);
 

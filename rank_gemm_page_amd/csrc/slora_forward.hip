@@ -40,10 +40,11 @@ namespace slora {
 // position's largest |s v| in [2^14, 2^15); the accumulators are scaled back
 // by 2^e_t (exact) after the LoRA steps, before the x W steps.
 
-template <int BM, int BN>
+template <int BM, int BN, int KS = 1>
 struct FwdTile {
   static constexpr int WN = BN / 64;                 // waves along the columns
-  static constexpr int NT = 128 * WN;                // threads (2 x WN waves)
+  static constexpr int GT = 128 * WN;                // threads of one group (2 x WN waves)
+  static constexpr int NT = GT * KS;                 // threads: KS groups
   static constexpr int RW = BM / 2;                  // positions per wave
   static constexpr int RB = RW / 16;                 // 16-row MFMA blocks per wave
   static constexpr int NSL = BN / 128;               // 128-column B slices
@@ -52,10 +53,11 @@ struct FwdTile {
   static constexpr int SliceDw = kFwdBK * kSliceRowDw;
   static constexpr int StageDw = ADw + NSL * SliceDw;
   static constexpr int EpiPitchDw = BN / 2 + 4;      // one fp16 output row, padded
-  static constexpr int LdsDw = 2 * StageDw + 5 * BM;
-  static constexpr int TPR = NT / BM;                // threads per position (prologue, LoRA staging)
+  static constexpr int GroupDw = 2 * StageDw;        // one group's two stage buffers
+  static constexpr int LdsDw = KS * GroupDw + 5 * BM;
+  static constexpr int TPR = GT / BM;                // threads per position (prologue, LoRA staging)
   static constexpr int KL = kFwdLoraRows / TPR;      // rank rows of a LoRA step per thread
-  static constexpr int XL = BM * 8 / NT;             // 16-byte x loads per thread per step
+  static constexpr int XL = BM * 8 / GT;             // 16-byte x loads per thread per step
   static_assert(TPR == 2 || TPR == 4 || TPR == 8, "two, four or eight threads per position");
   // LoRA steps with page rows two steps ahead and stage tables four ahead
   // where the registers allow; the 256 x 256 tile keeps one step ahead.
@@ -68,14 +70,24 @@ struct FwdTile {
   static_assert(EP * EpiPitchDw <= 2 * StageDw, "an epilogue pass reuses the stage buffers");
   static_assert(RW <= EP && EP % RW == 0, "epilogue passes hold whole waves");
   static_assert(kShrinkKc == kFwdBK && kFwdLoraRows == 32, "stage layouts");
+  static_assert(KS == 1 || (KS == 2 && BM * BN <= GroupDw), "the second group's partial sums fit its buffers");
+  static_assert(EP * CH % NT == 0, "epilogue stores: whole passes of the workgroup");
 };
 
 // V4: every rank of the batch is a multiple of 4, so v rows start on 16-byte
 // boundaries and a LoRA step reads a thread's v values four at a time.
-template <int BM, int BN, bool V4>
-__global__ __launch_bounds__(128 * (BN / 64)) __attribute__((amdgpu_waves_per_eu(2)))
+// KS = 2: two groups of 2 x WN waves share the tile and split its steps, the
+// LoRA steps and the x W steps alike, group k taking steps k, k + 2, ...
+// into accumulators of its own (its own stage buffers; both groups pass the
+// same barriers, a group without a step of its own in the last round
+// staging zeros); group 1's sums join group 0's through LDS before the
+// epilogue.  For tiles with one workgroup per CU (the 32-row tiles), where
+// each step's chain of load, LDS store, barrier and MFMAs otherwise runs with
+// nothing beside it on its SIMD.
+template <int BM, int BN, bool V4, int KS>
+__global__ __launch_bounds__(128 * (BN / 64) * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void forward_kernel(ForwardLaunch F) {
-  using C = FwdTile<BM, BN>;
+  using C = FwdTile<BM, BN, KS>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[C::LdsDw];
   // Workgroup b runs on XCD b mod 8; XCD x takes tiles x * per_xcd .. +per_xcd
   // in the tile order below, so the tiles resident on one XCD at a time share
@@ -89,11 +101,13 @@ void forward_kernel(ForwardLaunch F) {
   const int gm = min(F.group_m, F.n_rb - grp * F.group_m);
   const int rb = grp * F.group_m + within % gm;
   const int r0 = F.pos0 + rb * BM, c0 = (within / gm) * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int kg = KS > 1 ? uni((int)threadIdx.x / C::GT) : 0;    // this thread's group
+  const int tid = (int)threadIdx.x - kg * C::GT, lane = tid & 63, wave = uni(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int wm = wave / C::WN, wn = wave % C::WN;
+  uint32_t* const stg = lds + kg * C::GroupDw;                   // this group's stage buffers
 
-  int32_t* tok_l = reinterpret_cast<int32_t*>(lds + 2 * C::StageDw);
+  int32_t* tok_l = reinterpret_cast<int32_t*>(lds + KS * C::GroupDw);
   int32_t* seg_l = tok_l + BM;
   int32_t* voff_l = seg_l + BM;
   float* mul_l = reinterpret_cast<float*>(voff_l + BM);
@@ -102,8 +116,8 @@ void forward_kernel(ForwardLaunch F) {
   // Per position of the tile: batch index, segment (-1: no adapter), v row
   // offset, s 2^-e and 2^e.  Positions past the batch take the last token's
   // row (loaded, never stored).  TPR threads per position scan its v row for
-  // the largest |v|, eight independent loads each at a time.
-  {
+  // the largest |v|, eight independent loads each at a time (group 0).
+  if (kg == 0) {
     const int row = tid / C::TPR, part = tid % C::TPR;
     const int p = r0 + row;
     int seg = -1, voff = 0, rank = 0;
@@ -186,24 +200,30 @@ void forward_kernel(ForwardLaunch F) {
   };
 
   // x W steps: every load unconditional (a step past the end reloads the last).
-  auto w_load = [&](int s, uint4 (&aq)[C::XL], uint4 (&bq)[4]) {
+  auto w_load = [&](int i, uint4 (&aq)[C::XL], uint4 (&bq)[4]) {
+    int s = KS * i + kg;
     s = s < n_w ? s : n_w - 1;
     const int k0 = s * kFwdBK;
 #pragma unroll
     for (int i = 0; i < C::XL; ++i)
-      aq[i] = ld16(xb + (int64_t)tok_l[xrow + (C::NT / 8) * i] * F.h_in + k0 + 8 * xch);
+      aq[i] = ld16(xb + (int64_t)tok_l[xrow + (C::GT / 8) * i] * F.h_in + k0 + 8 * xch);
 #pragma unroll
     for (int h = 0; h < 4; ++h) bq[h] = ld16(wb + (int64_t)(k0 + brow + 16 * h) * F.h_out + c0 + 8 * bch);
   };
-  auto w_store = [&](uint32_t* S, const uint4 (&aq)[C::XL], const uint4 (&bq)[4]) {
+  // Local step j of a group is step KS j + kg; past the last step (a group's
+  // share in the last round) it stages zero x rows.
+  auto w_store = [&](uint32_t* S, const uint4 (&aq)[C::XL], const uint4 (&bq)[4], int j) {
+    const bool ok = KS == 1 || KS * j + kg < n_w;
 #pragma unroll
-    for (int i = 0; i < C::XL; ++i) *reinterpret_cast<uint4*>(S + chunk_dw(xrow + (C::NT / 8) * i, xch)) = aq[i];
+    for (int i = 0; i < C::XL; ++i)
+      *reinterpret_cast<uint4*>(S + chunk_dw(xrow + (C::GT / 8) * i, xch)) = ok ? aq[i] : uint4{0u, 0u, 0u, 0u};
     uint32_t* B = S + C::ADw + bsl * C::SliceDw;
 #pragma unroll
     for (int h = 0; h < 4; ++h) *reinterpret_cast<uint4*>(B + quad_dw(brow + 16 * h, bquad)) = bq[h];
   };
 
   const int n_lora = uni(F.rb_info[2 * rb + 1]);
+  const int n_it = (n_lora + KS - 1) / KS;       // LoRA steps of each group
   if (n_lora > 0) {
     const int32_t* tab = F.stages + (int64_t)uni(F.rb_info[2 * rb]) * kFwdStageWords;
     // Stage table entry of LoRA step q (clamped): this thread's two B page
@@ -215,9 +235,12 @@ void forward_kernel(ForwardLaunch F) {
     // Packed: this thread's rank rows KL ah .. KL ah + KL - 1 are groups
     // NG ah .. NG ah + NG - 1, one table word each.
     constexpr int NG = C::PACK ? C::KL / 4 : 1;
-    struct Tab { int id0, id1, hw[NG]; };
+    struct Tab { int id0, id1, hw[NG]; bool ok; };
     const int hlane = lane & 3;
-    auto tab_load = [&](int q, Tab& t) {
+    // local step i of this group: step KS i + kg, ok = whether it exists
+    auto tab_load = [&](int i, Tab& t) {
+      int q = KS * i + kg;
+      t.ok = KS == 1 || q < n_lora;
       q = q < n_lora ? q : n_lora - 1;
       const int32_t* e = tab + (int64_t)q * kFwdStageWords;
       t.id0 = e[brow];
@@ -243,7 +266,7 @@ void forward_kernel(ForwardLaunch F) {
       if constexpr (C::PACK) {
         return View{false, 0, 0};
       } else {
-        return View{my_seg == t_seg(t), t_j0(t) + C::KL * ah, t_rank(t)};
+        return View{t.ok && my_seg == t_seg(t), t_j0(t) + C::KL * ah, t_rank(t)};
       }
     };
     // Rank row KL ah + i of a step: whether it is a row of this thread's
@@ -253,7 +276,7 @@ void forward_kernel(ForwardLaunch F) {
       if constexpr (C::PACK) {
         const uint32_t w = (uint32_t)t.hw[i >> 2];
         const int k = i & 3;
-        return Row{(int)(w & 7u) > k && (int)(w >> 9) == my_seg, my_voff + 4 * (int)((w >> 3) & 63u) + k};
+        return Row{t.ok && (int)(w & 7u) > k && (int)(w >> 9) == my_seg, my_voff + 4 * (int)((w >> 3) & 63u) + k};
       } else {
         return Row{vw.in && vw.j + i < vw.rank, my_voff + vw.j + i};
       }
@@ -341,7 +364,7 @@ void forward_kernel(ForwardLaunch F) {
       lora_load(t0, lb0, vv0);
       lora_load(t1, lb1, vv1);
       for (int q = 0;; q += 2) {
-        lora_store(lds, t0, lb0, vv0);
+        lora_store(stg, t0, lb0, vv0);
         lds_barrier();
         tab_load(q + 4, tx);
         __builtin_amdgcn_sched_barrier(0);   // keep the table loads ahead of the rows
@@ -349,10 +372,10 @@ void forward_kernel(ForwardLaunch F) {
         t0 = ta;
         ta = tb;
         tb = tx;
-        mfma_step(lds, 0, 0);
-        mfma_step(lds, 1, 0);
-        if (q + 1 >= n_lora) break;
-        lora_store(lds + C::StageDw, t1, lb1, vv1);
+        mfma_step(stg, 0, 0);
+        mfma_step(stg, 1, 0);
+        if (q + 1 >= n_it) break;
+        lora_store(stg + C::StageDw, t1, lb1, vv1);
         lds_barrier();
         tab_load(q + 5, tx);
         __builtin_amdgcn_sched_barrier(0);
@@ -360,9 +383,9 @@ void forward_kernel(ForwardLaunch F) {
         t1 = ta;
         ta = tb;
         tb = tx;
-        mfma_step(lds + C::StageDw, 0, 0);
-        mfma_step(lds + C::StageDw, 1, 0);
-        if (q + 2 >= n_lora) break;
+        mfma_step(stg + C::StageDw, 0, 0);
+        mfma_step(stg + C::StageDw, 1, 0);
+        if (q + 2 >= n_it) break;
       }
     } else {
       Tab tc, tn;
@@ -371,8 +394,8 @@ void forward_kernel(ForwardLaunch F) {
       tab_load(0, tc);
       lora_load(tc, lb, vv);
       tab_load(1, tn);
-      for (int q = 0; q < n_lora; ++q) {
-        uint32_t* S = lds + (q & 1) * C::StageDw;
+      for (int q = 0; q < n_it; ++q) {
+        uint32_t* S = stg + (q & 1) * C::StageDw;
         lora_store(S, tc, lb, vv);
         lds_barrier();
         tc = tn;
@@ -403,29 +426,50 @@ void forward_kernel(ForwardLaunch F) {
   // static: step s stores set s & 1 into buffer s & 1, then refills the set
   // with step s + 2.  A buffer is written again only after every wave has
   // passed the barrier of the step that followed its last read.
+  const int n_wit = (n_w + KS - 1) / KS;         // x W steps of each group
   for (int s = 0;; s += 2) {
-    w_store(lds, wa0, wb0);
+    w_store(stg, wa0, wb0, s);
     lds_barrier();
     w_load(s + 2, wa0, wb0);
-    mfma_step(lds, 0, 0);
-    mfma_step(lds, 1, 32);
-    if (s + 1 >= n_w) break;
-    w_store(lds + C::StageDw, wa1, wb1);
+    mfma_step(stg, 0, 0);
+    mfma_step(stg, 1, 32);
+    if (s + 1 >= n_wit) break;
+    w_store(stg + C::StageDw, wa1, wb1, s + 1);
     lds_barrier();
     w_load(s + 3, wa1, wb1);
-    mfma_step(lds + C::StageDw, 0, 0);
-    mfma_step(lds + C::StageDw, 1, 32);
-    if (s + 2 >= n_w) break;
+    mfma_step(stg + C::StageDw, 0, 0);
+    mfma_step(stg + C::StageDw, 1, 32);
+    if (s + 2 >= n_wit) break;
   }
 
-  // Epilogue, EP rows at a time: fp16 results through LDS, then whole
-  // 16-byte chunks of y rows.
+  if constexpr (KS > 1) {
+    // group 1's sums, through its own stage buffers, into group 0's
+    float4v* R = reinterpret_cast<float4v*>(lds + C::GroupDw);
+    lds_barrier();
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < C::RB; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) R[(4 * i + c) * C::GT + tid] = acc[i][c];
+    }
+    lds_barrier();
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < C::RB; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][c] += R[(4 * i + c) * C::GT + tid];
+    }
+  }
+
+  // Epilogue, EP rows at a time: fp16 results of group 0 through LDS, then
+  // whole 16-byte chunks of y rows, stored by every thread of the workgroup.
   _Float16* E = reinterpret_cast<_Float16*>(lds);
   _Float16* yb = static_cast<_Float16*>(F.y);
+  const int erow = (int)threadIdx.x / C::CH, ech = (int)threadIdx.x % C::CH;
 #pragma unroll
   for (int pass = 0; pass < BM / C::EP; ++pass) {
     lds_barrier();   // every wave is done with the stage buffers / the previous pass
-    if (C::RW * wm / C::EP == pass) {
+    if (kg == 0 && C::RW * wm / C::EP == pass) {
       const int rbase = C::RW * wm - C::EP * pass;
 #pragma unroll
       for (int i = 0; i < C::RB; ++i)
@@ -438,12 +482,19 @@ void forward_kernel(ForwardLaunch F) {
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < C::EP * C::CH / C::NT; ++k) {
-      const int row = brow + (C::NT / C::CH) * k;
-      const uint4 val = *reinterpret_cast<const uint4*>(lds + row * C::EpiPitchDw + 4 * bch);
+      const int row = erow + (C::NT / C::CH) * k;
+      const uint4 val = *reinterpret_cast<const uint4*>(lds + row * C::EpiPitchDw + 4 * ech);
       const int p = C::EP * pass + row;
-      if (r0 + p < F.n_tokens) st16(yb + (int64_t)tok_l[p] * F.h_out + c0 + 8 * bch, val);
+      if (r0 + p < F.n_tokens) st16(yb + (int64_t)tok_l[p] * F.h_out + c0 + 8 * ech, val);
     }
   }
+}
+
+template <int BM, int BN, int KS>
+static const void* forward_fn(bool v4, int& nt) {
+  nt = FwdTile<BM, BN, KS>::NT;
+  return v4 ? reinterpret_cast<const void*>(&forward_kernel<BM, BN, true, KS>)
+            : reinterpret_cast<const void*>(&forward_kernel<BM, BN, false, KS>);
 }
 
 hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -451,29 +502,15 @@ hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t
   void* args[] = {const_cast<ForwardLaunch*>(&F)};
   const void* k;
   int nt;
-  if (F.bm == 256 && F.bn == 256) {
-    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<256, 256, true>)
-             : reinterpret_cast<const void*>(&forward_kernel<256, 256, false>);
-    nt = FwdTile<256, 256>::NT;
-  } else if (F.bm == 128 && F.bn == 256) {
-    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 256, true>)
-             : reinterpret_cast<const void*>(&forward_kernel<128, 256, false>);
-    nt = FwdTile<128, 256>::NT;
-  } else if (F.bm == 64 && F.bn == 128) {
-    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<64, 128, true>)
-             : reinterpret_cast<const void*>(&forward_kernel<64, 128, false>);
-    nt = FwdTile<64, 128>::NT;
-  } else if (F.bm == 32 && F.bn == 128) {
-    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<32, 128, true>)
-             : reinterpret_cast<const void*>(&forward_kernel<32, 128, false>);
-    nt = FwdTile<32, 128>::NT;
-  } else if (F.bm == 128 && F.bn == 128) {
-    k = F.v4 ? reinterpret_cast<const void*>(&forward_kernel<128, 128, true>)
-             : reinterpret_cast<const void*>(&forward_kernel<128, 128, false>);
-    nt = FwdTile<128, 128>::NT;
-  } else {
-    return hipErrorInvalidValue;
-  }
+  const bool v4 = F.v4 != 0;
+  if (F.bm == 256 && F.bn == 256 && F.ks == 1) k = forward_fn<256, 256, 1>(v4, nt);
+  else if (F.bm == 128 && F.bn == 256 && F.ks == 1) k = forward_fn<128, 256, 1>(v4, nt);
+  else if (F.bm == 128 && F.bn == 128 && F.ks == 1) k = forward_fn<128, 128, 1>(v4, nt);
+  else if (F.bm == 64 && F.bn == 128 && F.ks == 1) k = forward_fn<64, 128, 1>(v4, nt);
+  else if (F.bm == 64 && F.bn == 128 && F.ks == 2) k = forward_fn<64, 128, 2>(v4, nt);
+  else if (F.bm == 32 && F.bn == 128 && F.ks == 1) k = forward_fn<32, 128, 1>(v4, nt);
+  else if (F.bm == 32 && F.bn == 128 && F.ks == 2) k = forward_fn<32, 128, 2>(v4, nt);
+  else return hipErrorInvalidValue;
   const dim3 grid((unsigned)(8 * F.per_xcd));
   if (!start && !stop) return hipLaunchKernel(k, grid, dim3(nt), args, 0, stream);
   return hipExtLaunchKernel(k, grid, dim3(nt), args, 0, stream, start, stop, 0);

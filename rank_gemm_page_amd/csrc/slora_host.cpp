@@ -93,6 +93,7 @@ struct Tuning {
   int64_t tile_order = 2;       // 0: segment order, 1: rank-descending, 2: bytes-descending
   int64_t fwd_group = 0;        // row blocks per group of the base-plus-delta tile order (0: automatic)
   int64_t fwd_tile = 0;         // base-plus-delta tile rows: 32, 64, 128, 256, or 0 (automatic)
+  int64_t fwd_ksplit = 0;       // wave groups splitting a base-plus-delta tile's steps: 1, 2, or 0 (automatic)
   int64_t shrink_rows = 0;      // rank rows per vector-ALU shrink tile (0: as many as fit)
 };
 
@@ -945,6 +946,10 @@ slora_status slora_pool_set_tuning(slora_pool* p, int32_t key, int64_t value) {
       if (value < 0 || value > kShrinkRowBudget) return fail(SLORA_E_INVAL, "shrink_rows must be 0..16 (0: automatic)");
       p->tune.shrink_rows = value;
       return SLORA_OK;
+    case SLORA_TUNE_FWD_KSPLIT:
+      if (value < 0 || value > 2) return fail(SLORA_E_INVAL, "fwd_ksplit must be 0 (automatic), 1 or 2");
+      p->tune.fwd_ksplit = value;
+      return SLORA_OK;
     default:
       return fail(SLORA_E_INVAL, "slora_pool_set_tuning: unknown key");
   }
@@ -1554,6 +1559,11 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
     // different segments instead of neighbouring columns of the same rows).
     const int64_t auto_group = F.bm <= kFwdSmall ? 8 : 1;
     F.group_m = (int32_t)std::min<int64_t>(p->tune.fwd_group > 0 ? p->tune.fwd_group : auto_group, F.n_rb);
+    // Two wave groups per tile, splitting its steps (automatic: the 32-row
+    // tiles, one workgroup per CU, whose step chains otherwise run alone on
+    // their SIMDs); only the 32- and 64-row tiles have the variant.
+    F.ks = (int32_t)(p->tune.fwd_ksplit > 0 ? p->tune.fwd_ksplit : (F.bm == kFwdTiny ? 2 : 1));
+    if (F.bn != kFwdBN || F.bm > kFwdSmall) F.ks = 1;
     const bool first = part == 0 || s->fw_n_rb_big == 0;
     const bool last = part == 1 || n_small == 0;
     e = launch_forward(F, hs, (first && !routed) ? static_cast<hipEvent_t>(ev_start) : nullptr,

@@ -172,6 +172,7 @@ struct ForwardLaunch {
   int32_t bm, bn;            // tile shape: 256 x 256, 128 x 256, 128 x 128, 64 x 128 or 32 x 128
   int32_t pos0;              // first sorted position of row block 0 of this launch
   int32_t v4;                // every segment's rank is a multiple of 4 (v rows 16-byte aligned)
+  int32_t ks;                // wave groups splitting each tile's steps: 1, or 2 (32- and 64-row tiles)
 };
 
 // Launch the base-plus-delta kernel (one launch, n_tiles workgroups placed

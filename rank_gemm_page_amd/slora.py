@@ -26,7 +26,7 @@ SLORA_F32, SLORA_F16 = 0, 1
 SLORA_TUNE_MFMA_MIN_TOKENS, SLORA_TUNE_GEMV_EXPAND_ELEMS, SLORA_TUNE_MFMA_EXPAND_COLS = 0, 1, 2
 SLORA_MFMA_MAX_RANK = 64          # segments of higher rank always take the vector-ALU tiles
 SLORA_TUNE_MFMA_SHRINK_SPLITS, SLORA_TUNE_FUSED, SLORA_TUNE_XCDS, SLORA_TUNE_TILE_ORDER = 3, 4, 5, 6
-SLORA_TUNE_FWD_GROUP, SLORA_TUNE_FWD_TILE, SLORA_TUNE_SHRINK_ROWS = 7, 8, 9
+SLORA_TUNE_FWD_GROUP, SLORA_TUNE_FWD_TILE, SLORA_TUNE_SHRINK_ROWS, SLORA_TUNE_FWD_KSPLIT = 7, 8, 9, 10
 
 EXPORTED = [
     "slora_pool_create", "slora_pool_destroy", "slora_pool_set_tuning", "slora_alloc_pages",

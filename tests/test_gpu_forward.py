@@ -34,11 +34,11 @@ def _gpu():
     S.lib()
 
 
-def run_forward(w, projs=(0,), route="default", repeat=1, tile=0, group=0):
+def run_forward(w, projs=(0,), route="default", repeat=1, tile=0, group=0, ks=0):
     print(f"[gpu] forward {w.spec.name} seed={w.seed} route={route} T={w.T} "
-          f"h={w.spec.h_in}x{w.spec.h_out} tile={tile} group={group}", flush=True)
+          f"h={w.spec.h_in}x{w.spec.h_out} tile={tile} group={group} ks={ks}", flush=True)
     dw = DeviceWorkload(w, "cuda:0", tuning={**ROUTES[route], S.SLORA_TUNE_FWD_TILE: tile,
-                                             S.SLORA_TUNE_FWD_GROUP: group})
+                                             S.SLORA_TUNE_FWD_GROUP: group, S.SLORA_TUNE_FWD_KSPLIT: ks})
     try:
         outs = []
         for p in projs:
@@ -102,6 +102,20 @@ def test_forward_small_shapes(name, route, tile):
     check(w, ys[0], h_ref, sd_ref, label=f"forward {name}/{route}/{tile}")
 
 
+@pytest.mark.parametrize("ks", [1, 2])
+@pytest.mark.parametrize("tile", [32, 64])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_wave_groups_split_steps(name, tile, ks):
+    """One or two groups of waves per 32- or 64-row tile.  The shapes give
+    odd and even numbers of x W steps (h_in 64, 128, 192, 256) and of LoRA
+    steps, so a group's last step is sometimes one it does not own."""
+    spec = small_spec(f"fw_{name}", scale_set=(0.5, 2.0, -1.5, 4.0), **SMALL[name])
+    w = drop_some(generate(spec, 17), 5 if name != "one" else 0)
+    (ys,), _ = run_forward(w, route="mfma", tile=tile, ks=ks)
+    h_ref, sd_ref = oracle_forward(w)
+    check(w, ys[0], h_ref, sd_ref, label=f"forward {name}/{tile}/ks{ks}")
+
+
 BIG = {
     # 256 x 256 tiles: ragged last row block, segments across row blocks
     "big_requests": dict(h_in=192, h_out=512, two_classes=True, n_adapters=7, rank_set=(1, 5, 33, 64),
@@ -130,13 +144,12 @@ def test_forward_big_tiles_integer_bit_exact_and_same_as_small():
     h_ref, _ = oracle_forward(w)
     assert np.abs(h_ref).max() < 2048
     outs = {}
-    for tile in (32, 64, 128, 256):
-        (ys,), _ = run_forward(w, route="mfma", tile=tile)
+    for tile, ks in ((32, 1), (32, 2), (64, 1), (64, 2), (128, 0), (256, 0)):
+        (ys,), _ = run_forward(w, route="mfma", tile=tile, ks=ks)
         np.testing.assert_array_equal(ys[0], round_to(h_ref, np.float16))
-        outs[tile] = ys[0]
-    np.testing.assert_array_equal(outs[128], outs[256])
-    np.testing.assert_array_equal(outs[64], outs[128])
-    np.testing.assert_array_equal(outs[32], outs[64])
+        outs[tile, ks] = ys[0]
+    for key in outs:
+        np.testing.assert_array_equal(outs[key], outs[256, 0], err_msg=str(key))
 
 
 @pytest.mark.parametrize("tile", [32, 64, 128])

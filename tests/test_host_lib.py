@@ -541,7 +541,10 @@ def test_tuning_validation():
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 65536 + 128) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 512)
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_MFMA_EXPAND_COLS, 0)
-        assert status_of(S.slora_pool_set_tuning, pool, 10, 1) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, 11, 1) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_KSPLIT, 3) == S.SLORA_E_INVAL
+        assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_FWD_KSPLIT, -1) == S.SLORA_E_INVAL
+        S.slora_pool_set_tuning(pool, S.SLORA_TUNE_FWD_KSPLIT, 2)
         assert status_of(S.slora_pool_set_tuning, pool, S.SLORA_TUNE_SHRINK_ROWS, 17) == S.SLORA_E_INVAL
         S.slora_pool_set_tuning(pool, S.SLORA_TUNE_SHRINK_ROWS, 2)
         assert status_of(S.slora_pool_set_tuning, pool, 99, 1) == S.SLORA_E_INVAL
