@@ -623,7 +623,12 @@ void build_tiles(slora_segments* s) {
 
   const int np = s->n_proj;
   s->n_tiles = (int32_t)tiles.size();
-  s->tokcap = kTokCap;
+  // Token slots of a record: the most tokens any tile of the batch holds,
+  // rounded up to 4 (4 for batches of vector-ALU tiles only, 64 with MFMA
+  // tiles), so a decode batch's records are 80 words instead of 140.
+  int32_t max_tok = 1;
+  for (const TileSpec& t : tiles) max_tok = std::max(max_tok, t.ntok);
+  s->tokcap = std::min<int32_t>(kTokCap, (max_tok + 3) & ~3);
   s->pagecap = (std::max(gemv_rows, max_rank) + 3) & ~3;   // <= kMaxPageCap
   s->stride = (REC_HDR + s->tokcap + np * s->pagecap + 3) & ~3;
   s->shrink_idx_off_words = (int64_t)s->n_tiles * s->stride;

@@ -59,7 +59,7 @@ constexpr int kCombineTok = 16;         // tokens per combine tile
 constexpr int kMaxSplits = 4;           // K splits of an MFMA shrink token block
 constexpr int kShrinkKc = 64;           // k elements per staged MFMA shrink chunk
 constexpr int kMaxRankMfma = SLORA_MFMA_MAX_RANK;   // rank limit of MFMA segments
-constexpr int kTokCap = 64;             // token slots of every record (>= every tile kind's)
+constexpr int kTokCap = 64;             // most token slots of a record (>= every tile kind's)
 constexpr int kMaxPageCap = 256;        // page slots per projection (max_rank <= 256)
 constexpr int kMfmaPass = 128;          // columns per MFMA expand pass
 // The MFMA expand addresses y through a buffer descriptor (stores past its
