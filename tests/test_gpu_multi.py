@@ -109,3 +109,26 @@ def test_multi_repeated_launches_and_full_mixed_batch():
               f"(segments={dw.info['n_segments']})", flush=True)
     finally:
         dw.close()
+
+
+@pytest.mark.parametrize("route", ["gemv", "default"])
+def test_multi_eight_projections_the_largest_launch(route):
+    """The most projections one launch takes (8), each on an x of its own or
+    shared, with ranks up to the pool's largest: every projection equals its
+    single launch bit for bit, in one launch and as two launches of four."""
+    spec = small_spec("proj8", h_in=320, h_out=448, two_classes=True, n_adapters=9, n_proj=8,
+                      proj_x=(0, 1, 1, 2, 3, 3, 3, 4), rank_set=(1, 7, 32, 64, 200),
+                      batch=("mixed", 2, 66, 30))
+    w = generate(spec, 8)
+    tuning = dict(ROUTES[route])
+    subsets = [list(range(8)), [7, 6, 5, 4], [3, 2, 1, 0]]
+    singles, multis, info = singles_and_multi(w, tuning, subsets)
+    st = build_from_workload(w)
+    for p in range(8):
+        y_ref, sd_ref = workload_delta(st, w, proj=p)
+        check_gates(singles[p], y_ref, sd_ref, w.np_dtype, f"proj8/{route}/single p{p}")
+    for projs, got in zip(subsets, multis):
+        for p in projs:
+            np.testing.assert_array_equal(got[p].view(np.uint16), singles[p].view(np.uint16),
+                                          err_msg=f"proj8/{route} projs={projs} p{p}")
+    print(f"[gpu] proj8/{route}: segments={info['n_segments']} mfma={info['n_mfma_segments']}", flush=True)
