@@ -121,8 +121,9 @@ void slora_pool_destroy(slora_pool* pool);
  *                                go row block by row block in groups of n
  *                                row blocks, column by column inside a
  *                                group (1: row-block major); 0 (default):
- *                                groups of 8 for the 32- and 64-row tiles,
- *                                row-block major for the larger ones.
+ *                                groups of 8 for the 32- and 64-row tiles
+ *                                and the 256-column ones, row-block major
+ *                                for 128 x 128.
  *  SLORA_TUNE_FWD_TILE         - slora_lora_forward's tile: 32 (32 x 128
  *                                everywhere), 64 (64 x 128 everywhere),
  *                                128 (128 x 128 everywhere), 256

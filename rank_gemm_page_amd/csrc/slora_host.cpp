@@ -1559,10 +1559,14 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
     // at once share 4 column blocks of W (and 8 blocks of x) in its L2
     // instead of each reading a column block of W of its own (measured: the
     // 7B decode batch 76.2 -> 68.4 us, the 70B MLP batch 930 -> 878 us).  The
-    // larger tiles stay row-block major: grouped, the 13B mixed batch ran
-    // 428 us against 332 us (its tiles on one XCD then read B page rows of
-    // different segments instead of neighbouring columns of the same rows).
-    const int64_t auto_group = F.bm <= kFwdSmall ? 8 : 1;
+    // 256-column tiles too: row-block major, an XCD's 32 tiles of a round
+    // span 2 row blocks and all 16 column blocks of the 7B prefill batch, so
+    // each XCD streams the whole W every round; in groups of 8 they span 4 x
+    // 8 (the prefill forward's memory reads 907 -> 549 MB, 435 -> 425 us).
+    // The 128 x 128 tiles stay row-block major: grouped, the 13B mixed batch
+    // ran 428 us against 332 us (its tiles on one XCD then read B page rows
+    // of different segments instead of neighbouring columns of the same rows).
+    const int64_t auto_group = (F.bm <= kFwdSmall || F.bn == kFwdBig) ? 8 : 1;
     F.group_m = (int32_t)std::min<int64_t>(p->tune.fwd_group > 0 ? p->tune.fwd_group : auto_group, F.n_rb);
     // Two wave groups per tile, splitting its steps (automatic: the 32-row
     // tiles, one workgroup per CU, whose step chains otherwise run alone on
