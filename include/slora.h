@@ -144,8 +144,7 @@ void slora_pool_destroy(slora_pool* pool);
  *                                1 (one group of waves takes every step of
  *                                a tile) or 2 (two groups take alternate
  *                                steps into sums of their own, added before
- *                                the output is rounded); 0 (default): 2 for
- *                                the 32-row tiles, 1 for the 64-row ones.
+ *                                the output is rounded); 0 (default): 2.
  *                                The larger tiles always take 1.
  * They change how the work is cut, never what is computed (only, in floating
  * point, the order in which partial sums meet). */

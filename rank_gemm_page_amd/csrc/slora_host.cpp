@@ -1571,10 +1571,13 @@ slora_status run_forward(const char* fn, slora_pool* p, const slora_segments* s,
     // of different segments instead of neighbouring columns of the same rows).
     const int64_t auto_group = (F.bm <= kFwdSmall || F.bn == kFwdBig) ? 8 : 1;
     F.group_m = (int32_t)std::min<int64_t>(p->tune.fwd_group > 0 ? p->tune.fwd_group : auto_group, F.n_rb);
-    // Two wave groups per tile, splitting its steps (automatic: the 32-row
-    // tiles, one workgroup per CU, whose step chains otherwise run alone on
-    // their SIMDs); only the 32- and 64-row tiles have the variant.
-    F.ks = (int32_t)(p->tune.fwd_ksplit > 0 ? p->tune.fwd_ksplit : (F.bm == kFwdTiny ? 2 : 1));
+    // Two wave groups per tile, splitting its steps (automatic for the 32-
+    // and 64-row tiles, which have the variant: the decode batch's 32-row
+    // tiles are one workgroup per CU, whose step chains otherwise run alone
+    // on their SIMDs, 63.0 -> 54.4 us; the 70B MLP's 64-row tiles 869-897 ->
+    // 826-871 us over four boxes).  On 128 x 128 tiles it was slower (the 13B
+    // mixed batch 336 against 308-316 us).
+    F.ks = (int32_t)(p->tune.fwd_ksplit > 0 ? p->tune.fwd_ksplit : (F.bm <= kFwdSmall ? 2 : 1));
     if (F.bn != kFwdBN || F.bm > kFwdSmall) F.ks = 1;
     parts[part] = F;
   }
