@@ -494,38 +494,11 @@ void forward_kernel(ForwardLaunch F) {
   forward_tile<BM, BN, V4, KS>(F, blockIdx.x, lds);
 }
 
-// A batch whose leading positions take 256 x 256 tiles and whose rest takes
-// 128 x 256 tiles, in one launch (both eight waves): the half-size tiles
-// first, so they run beside the first big tiles instead of in a round of
-// their own after the last ones.  A: the 128 x 256 part, B: the 256 x 256 part.
-template <bool V4>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void forward_pair_kernel(ForwardLaunch A, ForwardLaunch B) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds[FwdTile<256, 256, 1>::LdsDw];
-  static_assert(FwdTile<128, 256, 1>::NT == 512 && FwdTile<256, 256, 1>::NT == 512, "one block size");
-  static_assert(FwdTile<128, 256, 1>::LdsDw <= FwdTile<256, 256, 1>::LdsDw, "one LDS size");
-  const int na = 8 * A.per_xcd;   // a multiple of 8: B's blocks keep their XCD (b mod 8)
-  if ((int)blockIdx.x < na) forward_tile<128, 256, V4, 1>(A, blockIdx.x, lds);
-  else forward_tile<256, 256, V4, 1>(B, (int)blockIdx.x - na, lds);
-}
-
 template <int BM, int BN, int KS>
 static const void* forward_fn(bool v4, int& nt) {
   nt = FwdTile<BM, BN, KS>::NT;
   return v4 ? reinterpret_cast<const void*>(&forward_kernel<BM, BN, true, KS>)
             : reinterpret_cast<const void*>(&forward_kernel<BM, BN, false, KS>);
-}
-
-hipError_t launch_forward_pair(const ForwardLaunch& A, const ForwardLaunch& B, hipStream_t stream,
-                               hipEvent_t start, hipEvent_t stop) {
-  if (A.bm != 128 || A.bn != 256 || B.bm != 256 || B.bn != 256 || A.ks != 1 || B.ks != 1 || A.v4 != B.v4)
-    return hipErrorInvalidValue;
-  void* args[] = {const_cast<ForwardLaunch*>(&A), const_cast<ForwardLaunch*>(&B)};
-  const void* k = A.v4 ? reinterpret_cast<const void*>(&forward_pair_kernel<true>)
-                       : reinterpret_cast<const void*>(&forward_pair_kernel<false>);
-  const dim3 grid((unsigned)(8 * (A.per_xcd + B.per_xcd)));
-  if (!start && !stop) return hipLaunchKernel(k, grid, dim3(512), args, 0, stream);
-  return hipExtLaunchKernel(k, grid, dim3(512), args, 0, stream, start, stop, 0);
 }
 
 hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {

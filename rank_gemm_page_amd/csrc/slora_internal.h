@@ -179,10 +179,6 @@ struct ForwardLaunch {
 // XCD by XCD); start/stop events as for launch_delta.
 hipError_t launch_forward(const ForwardLaunch& F, hipStream_t stream, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);
-// The 128 x 256 part A and the 256 x 256 part B of one batch in one launch
-// (A's tiles first); start/stop events as for launch_forward.
-hipError_t launch_forward_pair(const ForwardLaunch& A, const ForwardLaunch& B, hipStream_t stream,
-                               hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Zero n_words 32-bit words at p (a fill kernel; no memset node in the stream).
 hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t stream);
