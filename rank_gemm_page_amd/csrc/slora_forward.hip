@@ -19,7 +19,9 @@ namespace slora {
 // 64 x 64, the remainder of a batch whose bulk takes 256 x 256 tiles),
 // 64 x 128 (four waves of 32 x 64, for batches too small to give every CU a
 // 128 x 128 tile or heavy in LoRA steps) and 32 x 128 (four waves of
-// 16 x 64, for batches too small to give every CU a 64 x 128 tile).  The
+// 16 x 64, for batches too small to give every CU a 64 x 128 tile); the
+// 32- and 64-row tiles run two such groups of waves that split the tile's
+// steps (KS = 2, below).  The
 // larger tiles read x and W half as often per flop: x is read once per column
 // block and W once per row block, and at 128 x 128 that traffic, not the
 // matrix cores, bounds the kernel on large batches.  Per step the tile stages in LDS (two buffers, one
