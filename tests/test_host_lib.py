@@ -740,3 +740,88 @@ def test_probe_argument_errors():
     assert gather([(fake, 8192, 8192, fake, 0)]) == S.SLORA_E_INVAL       # no rows
     assert gather([row, (0, 8192, 8192, fake, 2)]) == S.SLORA_E_INVAL     # NULL second array
     assert gather([row], sink=0) == S.SLORA_E_INVAL
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_allocator_random_operations_match_oracle(seed):
+    """Random sequences of adapter loads and unloads and KV allocations and
+    frees, one or two page classes, one to three projections: after every
+    operation the library's block table and free counts equal the oracle's
+    allocator model, failed operations leave both unchanged, and the free
+    lists drain in the same order at the end.  Every few operations a random
+    batch's segment metadata is compared with the oracle's segment model."""
+    rng = np.random.default_rng(seed)
+    two = bool(seed % 2)
+    n_proj = 1 + seed % 3
+    n_pages = [int(rng.integers(40, 160))] + ([int(rng.integers(40, 160))] if two else [])
+    orders = [rng.permutation(P).astype(np.int32) for P in n_pages]
+    n_adapters, max_rank = 12, 9
+    model = orc.AllocatorModel(n_pages, [o.tolist() for o in orders], n_proj=n_proj, two_classes=two)
+    pool = S.slora_pool_create(S.SLORA_F16, 8, 16 if two else 8, n_proj, n_adapters, max_rank,
+                               FAKE_BASE[:len(n_pages)], n_pages, orders)
+    kv = [[] for _ in n_pages]          # KV pages held, per class
+    try:
+        for step in range(160):
+            op = rng.integers(0, 5)
+            if op <= 1:                                      # load
+                a = int(rng.integers(0, n_adapters))
+                r = int(rng.integers(1, max_rank + 1))
+                s = float(rng.choice([0.5, 1.0, 2.0]))
+                if a in model.table:
+                    assert status_of(S.slora_load_adapter, pool, a, r, s) == S.SLORA_E_EXIST
+                    continue
+                try:
+                    entry = model.load(a, r, s)
+                except orc.OracleError:
+                    assert status_of(S.slora_load_adapter, pool, a, r, s) == S.SLORA_E_NOMEM
+                else:
+                    S.slora_load_adapter(pool, a, r, s)
+                    for p in range(n_proj):
+                        ga, gb = S.slora_adapter_pages(pool, a, p)
+                        assert ga.tolist() == entry.a_pages[p] and gb.tolist() == entry.b_pages[p], (seed, step)
+            elif op == 2:                                    # unload
+                a = int(rng.integers(0, n_adapters))
+                if a in model.table:
+                    model.unload(a)
+                    S.slora_unload_adapter(pool, a)
+                else:
+                    assert status_of(S.slora_unload_adapter, pool, a) == S.SLORA_E_NOENT
+            elif op == 3:                                    # KV allocation
+                c = int(rng.integers(0, len(n_pages)))
+                n = int(rng.integers(1, 12))
+                if n > len(model.free[c]):
+                    assert status_of(S.slora_alloc_pages, pool, c, n) == S.SLORA_E_NOMEM
+                else:
+                    want = model.alloc(c, n)
+                    assert S.slora_alloc_pages(pool, c, n).tolist() == want, (seed, step)
+                    kv[c].extend(want)
+            else:                                            # KV free, a random subset in random order
+                c = int(rng.integers(0, len(n_pages)))
+                if kv[c]:
+                    k = int(rng.integers(1, len(kv[c]) + 1))
+                    pick = [kv[c][i] for i in rng.permutation(len(kv[c]))[:k]]
+                    for p in pick:
+                        kv[c].remove(p)
+                    model.release(c, pick)
+                    S.slora_free_pages(pool, c, pick)
+            assert [S.slora_free_count(pool, c) for c in range(len(n_pages))] == \
+                [len(f) for f in model.free], (seed, step)
+            if step % 20 == 19 and model.table:              # a batch over the loaded adapters
+                loaded = sorted(model.table)
+                ids = rng.choice(loaded + [-1], size=int(rng.integers(1, 40))).astype(np.int32)
+                ref = orc.segment_model(ids, model)
+                seg = S.slora_build_segments(pool, ids)
+                try:
+                    ex = S.slora_segments_export(seg)
+                    np.testing.assert_array_equal(ex["perm"], ref.perm)
+                    np.testing.assert_array_equal(ex["seg_start"], ref.seg_start)
+                    np.testing.assert_array_equal(ex["seg_adapter"], ref.seg_adapter)
+                    np.testing.assert_array_equal(ex["seg_rank"], ref.seg_rank)
+                    np.testing.assert_array_equal(ex["a_pages"], ref.a_pages)
+                    np.testing.assert_array_equal(ex["b_pages"], ref.b_pages)
+                finally:
+                    S.slora_segments_destroy(seg)
+        for c in range(len(n_pages)):                        # the free lists drain in the same order
+            assert S.slora_alloc_pages(pool, c, len(model.free[c])).tolist() == list(model.free[c])
+    finally:
+        S.slora_pool_destroy(pool)
