@@ -825,3 +825,22 @@ def test_allocator_random_operations_match_oracle(seed):
             assert S.slora_alloc_pages(pool, c, len(model.free[c])).tolist() == list(model.free[c])
     finally:
         S.slora_pool_destroy(pool)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With no built library the binding raises on first use; nothing falls
+    back to a CPU computation."""
+    import subprocess
+    import sys
+    code = ("from rank_gemm_page_amd import slora as S\n"
+            "try:\n"
+            "    S.slora_pool_create(S.SLORA_F16, 8, 8, 1, 2, 2, [1 << 40], [16], None)\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    env = dict(os.environ, SLORA_LIB=str(tmp_path / "libslora_absent.so"))
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert "raised:" in res.stdout and "is missing" in res.stdout, res.stdout
