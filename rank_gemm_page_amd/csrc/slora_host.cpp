@@ -470,6 +470,10 @@ void build_tiles(slora_segments* s) {
   const int gemv_rows = p->tune.shrink_rows > 0 ? (int)std::min<int64_t>(p->tune.shrink_rows, kShrinkRowBudget / nck)
                                                 : kShrinkRowBudget / nck;
   s->gemv_rows = gemv_rows;
+  // One-token blocks at four 16-byte chunks a thread take tiles of
+  // kShrinkRowsOne rows (the kernel's one-token shape) unless the rows are
+  // set by hand.
+  const int gemv_rows_one = (nck == kShrinkOneNck && p->tune.shrink_rows == 0) ? kShrinkRowsOne : gemv_rows;
 
   int64_t expand_elems = p->tune.gemv_expand_elems;
   if (expand_elems == 0) {
@@ -532,8 +536,9 @@ void build_tiles(slora_segments* s) {
           for (int32_t k = 0; k < tb.second; k += kCombineTok, ++s->n_combine)
             tiles.push_back({KIND_COMBINE, g, tb.first + k, std::min(kCombineTok, tb.second - k), 0, r, splits, grp});
       } else {
-        for (int32_t j0 = 0; j0 < r; j0 += gemv_rows, ++s->n_shrink)
-          tiles.push_back({KIND_SHRINK_GEMV, g, tb.first, tb.second, j0, std::min(gemv_rows, r - j0), 0, grp});
+        const int32_t rows = tb.second == 1 ? gemv_rows_one : gemv_rows;
+        for (int32_t j0 = 0; j0 < r; j0 += rows, ++s->n_shrink)
+          tiles.push_back({KIND_SHRINK_GEMV, g, tb.first, tb.second, j0, std::min(rows, r - j0), 0, grp});
       }
       for (int32_t o0 = 0; o0 < hout; o0 += cols, ++s->n_expand)
         tiles.push_back({mfma ? KIND_EXPAND_MFMA : KIND_EXPAND_GEMV, g, tb.first, tb.second, o0,

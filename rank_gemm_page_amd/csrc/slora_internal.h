@@ -68,6 +68,8 @@ constexpr int kMfmaPass = 128;          // columns per MFMA expand pass
 constexpr int64_t kMaxBufferBytes = 0xFFFFFF00LL;
 constexpr int kGemvMaxTok = 4;          // tokens per vector-ALU tile
 constexpr int kShrinkRowBudget = 16;    // rows x 16-byte chunks per thread (GEMV shrink)
+constexpr int kShrinkOneNck = 4;        // chunks per thread of the one-token GEMV shrink shape
+constexpr int kShrinkRowsOne = 8;       // its rows (twice the general tile's at four chunks)
 constexpr int kExpandRowSet = 8;        // B rows a vector-ALU expand thread loads at once
 static_assert(kTokCap >= kGemvMaxTok && kTokCap >= kMfmaExpandTok && kTokCap >= kCombineTok, "token slots");
 static_assert(kMaxRankMfma <= 64, "the MFMA shrink holds at most four 16-row blocks of A^T");

@@ -269,15 +269,16 @@ __device__ __forceinline__ void load_v(const DeltaLaunch& L, const Slot& S, int 
 }
 
 // ---------------------------------------------------------------------------
-// Shrink, vector-ALU tile: up to kGemvMaxTok tokens x RB rank rows, whole h_in.
+// Shrink, vector-ALU tile: up to TB tokens x RB rank rows, whole h_in.
 // Thread tid owns the 16-byte chunks tid, tid+256, ... of every row; the A^T
 // rows stay in registers while each token's x chunks are dotted against them.
+// The general tile holds kGemvMaxTok tokens; a tile of one token needs a
+// quarter of the x registers, which with four chunks a thread pay for twice
+// the rows (kShrinkRowsOne): half the tiles, twice the bytes in flight each.
 
-template <typename T, int NCK, bool FUSED>
+template <typename T, int NCK, bool FUSED, int RB = kShrinkRowBudget / NCK, int TB = kGemvMaxTok>
 __device__ void shrink_gemv_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* red) {
   constexpr int VEC = VecN<T>::N;
-  constexpr int RB = kShrinkRowBudget / NCK;
-  constexpr int TB = kGemvMaxTok;
   const int ntok = uni(srec[REC_NTOK]);
   const int rank = uni(srec[REC_RANK]);
   const int j0 = uni(srec[REC_POS]);
@@ -334,6 +335,19 @@ __device__ void shrink_gemv_tile(const DeltaLaunch& L, const Slot& S, const int3
     const float sum = ((q[0] + q[RB]) + q[2 * RB]) + q[3 * RB];
     store_v<FUSED>(S, v0 + (int64_t)k * rank + j0 + r, sum, L.epoch);
   }
+}
+
+// The vector-ALU shrink tile a record asks for: one token with more rows than
+// the general tile holds takes the one-token shape.
+template <typename T, int NCK, bool FUSED>
+__device__ __forceinline__ void shrink_gemv_any(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* red) {
+  if constexpr (NCK == kShrinkOneNck) {
+    if (uni(srec[REC_NTOK]) == 1 && uni(srec[REC_LEN]) > kShrinkRowBudget / NCK) {
+      shrink_gemv_tile<T, NCK, FUSED, kShrinkRowsOne, 1>(L, S, srec, red);
+      return;
+    }
+  }
+  shrink_gemv_tile<T, NCK, FUSED>(L, S, srec, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void shrink_kernel(DeltaLaunch L) {
       return;
     }
   }
-  shrink_gemv_tile<T, NCK, false>(L, S, srec, red);
+  shrink_gemv_any<T, NCK, false>(L, S, srec, red);
 }
 
 // Staged launches: the combine tiles, records n_shrink .. n_shrink + n_combine.
@@ -924,7 +938,7 @@ void fused_kernel(DeltaLaunch L) {
         return;
       }
     }
-    shrink_gemv_tile<T, NCK, true>(L, S, srec, lds);
+    shrink_gemv_any<T, NCK, true>(L, S, srec, lds);
     return;
   }
   if constexpr (sizeof(T) == 2 && MFMA) {
