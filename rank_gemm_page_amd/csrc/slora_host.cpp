@@ -156,6 +156,7 @@ struct slora_segments {
   int32_t n_tiles = 0, n_shrink = 0, n_expand = 0;
   int32_t stride = 0, tokcap = 0, pagecap = 0;
   int64_t shrink_idx_off_words = 0, expand_idx_off_words = 0;
+  std::vector<int32_t> phase_rec;   // record runs of one tile kind (fused launch phases), with the end
   int64_t records_words = 0;       // records and index lists (the uploaded part)
   // Base-plus-delta table (uploaded after the index lists): batch order of
   // the sorted positions, segment of each routed position, per-segment
@@ -628,6 +629,21 @@ void build_tiles(slora_segments* s) {
 
   const int np = s->n_proj;
   s->n_tiles = (int32_t)tiles.size();
+  // Phases of a fused launch over several projections: each run of one tile
+  // kind, every projection's copies of it before the next run, so that
+  // matrix-core tiles of the last projection do not queue behind the other
+  // projections' vector-ALU tiles.  With one projection this is the record
+  // order itself.  Should the runs outnumber kMaxPhases (tiles placed by XCD)
+  // the three stages serve as phases.
+  s->phase_rec.assign(1, 0);
+  for (int32_t i = 1; i < s->n_tiles; ++i)
+    if (launch_rank(tiles[i]) != launch_rank(tiles[i - 1])) s->phase_rec.push_back(i);
+  if ((int)s->phase_rec.size() > kMaxPhases) {
+    s->phase_rec.assign(1, 0);
+    for (int32_t edge : {s->n_shrink, s->n_shrink + s->n_combine})
+      if (edge > s->phase_rec.back() && edge < s->n_tiles) s->phase_rec.push_back(edge);
+  }
+  s->phase_rec.push_back(s->n_tiles);
   // Token slots of a record: the most tokens any tile of the batch holds,
   // rounded up to 4 (4 for batches of vector-ALU tiles only, 64 with MFMA
   // tiles), so a decode batch's records are 80 words instead of 140.
@@ -1403,6 +1419,8 @@ DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int3
   L.n_splits = s->n_splits;
   L.n_combine = s->n_combine;
   L.pipe_expand = s->pipe_expand ? 1 : 0;
+  L.n_phases = (int32_t)s->phase_rec.size() - 1;
+  for (int32_t k = 0; k <= L.n_phases; ++k) L.phase_rec[k] = s->phase_rec[(size_t)k];
   return L;
 }
 

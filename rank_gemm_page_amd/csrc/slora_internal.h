@@ -88,6 +88,7 @@ struct PoolView {
 // * sum_rt; a fused launch passes them through the exchange area of its
 // projection, vtag + projs[s] * n_splits * sum_rt.
 constexpr int kMaxSlots = 8;
+constexpr int kMaxPhases = 6;    // runs of one tile kind in the launch order (at most 5 kinds)
 
 struct DeltaLaunch {
   PoolView pool;
@@ -116,6 +117,10 @@ struct DeltaLaunch {
   uint32_t y_bytes;       // extent of y (n_tokens x h_out x element), < kMaxBufferBytes when has_mfma
   uint32_t epoch;
   int32_t pipe_expand;    // some vector-ALU expand thread holds more B rows than one register set
+  // Fused launch order: phase k runs records phase_rec[k] .. phase_rec[k+1]
+  // - 1 of every slot, slot by slot; the phases cover the records in order.
+  int32_t n_phases;
+  int32_t phase_rec[kMaxPhases + 1];
 };
 
 // Launch the shrink kernel (stages & 1) then the expand kernel (stages & 2) on

@@ -895,9 +895,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 // Both stages in one launch over the records in launch order: shrink tiles
 // and expand tiles that wait for their tokens' v (see store_v / load_v).
-// With several projections (slots) the grid runs every slot's shrink tiles,
-// then every slot's combine tiles, then every slot's expand tiles, so every
-// tile a workgroup waits for still has a lower block index.
+// With several projections (slots) the grid runs the records in phases, each
+// a run of one tile kind (matrix-core shrink, vector-ALU shrink, combine,
+// matrix-core expand, vector-ALU expand), every slot's copy of a phase before
+// the next phase, so every tile a workgroup waits for still has a lower block
+// index.
 // MFMA=false leaves the matrix-core tiles out (a batch without them), which
 // keeps the register budget, and so the workgroups resident per CU, of the
 // vector-ALU tiles alone.
@@ -909,21 +911,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCK ==
 void fused_kernel(DeltaLaunch L) {
   __shared__ float lds[sizeof(T) == 2 && MFMA ? kExpandLdsFloats : kGemvLdsFloats];
   __shared__ int32_t srec[kMaxRecWords];
-  // block -> (slot, record): [slots x shrink][slots x combine][slots x expand]
-  int b = blockIdx.x, slot, rec;
-  const int ns = L.n_slots * L.n_shrink, nc = L.n_slots * L.n_combine;
-  if (b < ns) {
-    slot = b / L.n_shrink;
-    rec = b - slot * L.n_shrink;
-  } else if (b < ns + nc) {
-    b -= ns;
-    slot = b / L.n_combine;
-    rec = L.n_shrink + (b - slot * L.n_combine);
-  } else {
-    b -= ns + nc;
-    slot = b / L.n_expand;
-    rec = L.n_shrink + L.n_combine + (b - slot * L.n_expand);
-  }
+  // block -> (slot, record): phase k holds blocks n_slots * phase_rec[k] ..
+  // n_slots * phase_rec[k+1] - 1, slot-major
+  const int b = blockIdx.x;
+  int k = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxPhases; ++i)
+    if (i < L.n_phases && b >= L.n_slots * L.phase_rec[i]) k = i;
+  const int r0 = L.phase_rec[k], len = L.phase_rec[k + 1] - r0;
+  const int off = b - L.n_slots * r0;
+  const int slot = off / len;
+  const int rec = r0 + (off - slot * len);
   const Slot S = make_slot(L, uni(slot));
   record_to_lds(L.rec + (int64_t)uni(rec) * L.stride, L.tokcap, L.pagecap, S.proj, srec);
   const int kind = uni(srec[REC_KIND]);
