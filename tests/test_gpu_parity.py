@@ -79,6 +79,12 @@ SMALL = [
                batch=("requests", 5, 3, 40)),
     small_spec("f32big", dtype="f32", h_in=2048, h_out=1024, two_classes=True, n_adapters=5,
                rank_set=(4, 16, 64), batch=("zipf", 40, 1.1)),
+    # four 16-byte chunks a thread: one-token blocks take the 8-row shrink
+    # shape (rank tails of 1 to 7 rows, rows past the tile's end clamped)
+    small_spec("f32w", dtype="f32", h_in=3000, h_out=520, two_classes=True, n_adapters=40,
+               rank_set=(1, 5, 8, 12, 24), batch=("zipf", 48, 0.7)),
+    small_spec("f16w", h_in=6000, h_out=264, two_classes=True, n_adapters=40,
+               rank_set=(3, 8, 9, 16, 40), batch=("zipf", 48, 0.7)),
 ]
 
 
