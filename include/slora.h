@@ -139,7 +139,10 @@ void slora_pool_destroy(slora_pool* pool);
  *                                64 x 128.
  *  SLORA_TUNE_SHRINK_ROWS      - rank rows of one vector-ALU shrink tile, at
  *                                most 16 / (16-byte chunks of an x row per
- *                                thread); 0 (default): that maximum.
+ *                                thread); 0 (default): that maximum, and 8
+ *                                for blocks of one token at four chunks a
+ *                                thread (their x needs a quarter of the
+ *                                registers).
  *  SLORA_TUNE_FWD_KSPLIT       - slora_lora_forward's 32- and 64-row tiles:
  *                                1 (one group of waves takes every step of
  *                                a tile) or 2 (two groups take alternate

@@ -272,9 +272,10 @@ __device__ __forceinline__ void load_v(const DeltaLaunch& L, const Slot& S, int 
 // Shrink, vector-ALU tile: up to TB tokens x RB rank rows, whole h_in.
 // Thread tid owns the 16-byte chunks tid, tid+256, ... of every row; the A^T
 // rows stay in registers while each token's x chunks are dotted against them.
-// The general tile holds kGemvMaxTok tokens; a tile of one token needs a
-// quarter of the x registers, which with four chunks a thread pay for twice
-// the rows (kShrinkRowsOne): half the tiles, twice the bytes in flight each.
+// The general tile holds kGemvMaxTok tokens.  A tile of one token needs a
+// quarter of the x registers; at four chunks a thread the registers saved
+// hold twice the rows (kShrinkRowsOne): half the tiles, each with twice the
+// bytes in flight.
 
 template <typename T, int NCK, bool FUSED, int RB = kShrinkRowBudget / NCK, int TB = kGemvMaxTok>
 __device__ void shrink_gemv_tile(const DeltaLaunch& L, const Slot& S, const int32_t* srec, float* red) {
