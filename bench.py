@@ -677,6 +677,12 @@ def measure_config(name, args, tuning, dev, headline):
         "metadata_bytes": int(info["meta_bytes"]),
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
     }
+    if kern_ms is not None:
+        # the kernel's own duration per launch, spread over the timed steps
+        per_launch = [k / (1 if multi else n_proj) * 1e3 for k in kern_ms]
+        out["kernels"]["fused_kernel_us_median"] = round(statistics.median(per_launch), 3)
+        out["kernels"]["fused_kernel_us_p10"] = round(float(np.percentile(per_launch, 10)), 3)
+        out["kernels"]["fused_kernel_us_p90"] = round(float(np.percentile(per_launch, 90)), 3)
     # Matrix-core use: flops over the kernels' own time against the fp16 dense
     # peak, and against the attainable roofline min(peak, AI x 8 TB/s) at this
     # batch's arithmetic intensity.
