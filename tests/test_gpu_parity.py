@@ -299,12 +299,25 @@ def sample_tokens(w, n, seed=0):
 @pytest.mark.parametrize("name", ["decode7b", "prefill7b", "mixed13b", "mlp70b"])
 def test_full_size_config(name):
     """Every token of every projection of the benchmark batches against the oracle."""
-    w = generate(CONFIGS[name], 0)
+    full_size_parity(name, 0)
+
+
+# Other draws of the same workloads (other batches, ranks and page layouts):
+# seeds 1-4 of the two decode-shaped batches under the bandwidth gate, seed 1
+# of the others.
+@pytest.mark.parametrize("name,seed", [("decode7b", 1), ("decode7b", 2), ("decode7b", 3), ("decode7b", 4),
+                                       ("mlp70b", 1), ("mlp70b", 2), ("prefill7b", 1), ("mixed13b", 1)])
+def test_full_size_other_seeds(name, seed):
+    full_size_parity(name, seed)
+
+
+def full_size_parity(name, seed):
+    w = generate(CONFIGS[name], seed)
     ys, info = run_gpu(w, "default")
-    print(f"[gpu] {name}: segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
+    print(f"[gpu] {name}/seed{seed}: segments={info['n_segments']} mfma_segments={info['n_mfma_segments']} "
           f"shrink_tiles={info['n_shrink_tiles']} expand_tiles={info['n_expand_tiles']}", flush=True)
     st = build_from_workload(w)
     for p, y in enumerate(ys):
         y_ref, sd_ref = workload_delta(st, w, proj=p)
-        check_gates(y, y_ref, sd_ref, np.float16, f"{name}/p{p}")
-        print(f"[gpu] {name}/p{p}: all {w.T} tokens within the gates", flush=True)
+        check_gates(y, y_ref, sd_ref, np.float16, f"{name}/seed{seed}/p{p}")
+        print(f"[gpu] {name}/seed{seed}/p{p}: all {w.T} tokens within the gates", flush=True)
