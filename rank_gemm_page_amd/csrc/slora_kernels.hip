@@ -49,7 +49,8 @@ template <> struct VecN<float> { static constexpr int N = 4; };
 // on MI355X, row gathers of 60-240 MB stream 1.5-1.7x faster with the
 // non-temporal hint than with ordinary loads.  The A^T rows of the MFMA
 // shrink and the B slices of the MFMA expand, read again by every token block
-// of the segment, keep ordinary loads.
+// of the segment, keep ordinary loads, and the MFMA expand stores y with
+// ordinary stores (measured faster there).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -855,9 +856,12 @@ __device__ void expand_mfma_tile(const DeltaLaunch& L, const Slot& S, const int3
       for (int i = 0; i < 8; ++i) d[i] = e[i] * u;
       const uint4 out = add_round(yc[k], d, _Float16());
       // A row or column outside the tile stores past the descriptor's extent,
-      // which the hardware drops: no branch, no traffic.
+      // which the hardware drops: no branch, no traffic.  An ordinary store,
+      // not a streaming one (7B prefill: 68.3-69.0 against 70.1-71.1 us; the
+      // vector-ALU expand's y stores measured the same either way and keep
+      // the streaming hint).
       const uint32_t off = (row < ntok && col < ncol) ? 2u * ((uint32_t)toks[row] * L.h_out + o0 + col) : 0xFFFFFFF0u;
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{out.x, out.y, out.z, out.w}, yrsrc, off, 0, SLORA_NT_Y ? 2 : 0);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{out.x, out.y, out.z, out.w}, yrsrc, off, 0, 0);
     }
   };
   for (int pass = 0;; pass += 2) {
