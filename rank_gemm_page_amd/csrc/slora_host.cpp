@@ -1419,6 +1419,10 @@ DeltaLaunch make_delta_launch(const slora_pool* p, const slora_segments* s, int3
   L.n_splits = s->n_splits;
   L.n_combine = s->n_combine;
   L.pipe_expand = s->pipe_expand ? 1 : 0;
+  L.x_shared = 0;
+  for (int32_t i = 0; i < n && xs; ++i)
+    for (int32_t j = i + 1; j < n; ++j)
+      if (xs[i] && xs[i] == xs[j]) L.x_shared = 1;
   L.n_phases = (int32_t)s->phase_rec.size() - 1;
   for (int32_t k = 0; k <= L.n_phases; ++k) L.phase_rec[k] = s->phase_rec[(size_t)k];
   return L;

@@ -117,6 +117,7 @@ struct DeltaLaunch {
   uint32_t y_bytes;       // extent of y (n_tokens x h_out x element), < kMaxBufferBytes when has_mfma
   uint32_t epoch;
   int32_t pipe_expand;    // some vector-ALU expand thread holds more B rows than one register set
+  int32_t x_shared;       // two slots of the launch read the same x
   // Fused launch order: phase k runs records phase_rec[k] .. phase_rec[k+1]
   // - 1 of every slot, slot by slot; the phases cover the records in order.
   int32_t n_phases;
