@@ -132,3 +132,26 @@ def test_multi_eight_projections_the_largest_launch(route):
             np.testing.assert_array_equal(got[p].view(np.uint16), singles[p].view(np.uint16),
                                           err_msg=f"proj8/{route} projs={projs} p{p}")
     print(f"[gpu] proj8/{route}: segments={info['n_segments']} mfma={info['n_mfma_segments']}", flush=True)
+
+
+@pytest.mark.parametrize("xcds", [3, 8])
+def test_multi_with_xcd_placement(xcds):
+    """Shrink tiles grouped by XCD interleave the matrix-core and vector-ALU
+    shrink kinds, so a launch over several projections runs its three stages
+    as phases instead of one phase per tile kind: every projection still equals
+    its single launch bit for bit, and the single launches meet the gates."""
+    spec = SPECS[0]
+    w = generate(spec, 5)
+    tuning = dict(ROUTES["default"])
+    tuning[S.SLORA_TUNE_XCDS] = xcds
+    subsets = [list(range(spec.n_proj)), [3, 1]]
+    singles, multis, info = singles_and_multi(w, tuning, subsets)
+    assert 0 < info["n_mfma_segments"] < info["n_segments"]
+    st = build_from_workload(w)
+    for p in range(spec.n_proj):
+        y_ref, sd_ref = workload_delta(st, w, proj=p)
+        check_gates(singles[p], y_ref, sd_ref, w.np_dtype, f"xcds{xcds}/single p{p}")
+    for projs, got in zip(subsets, multis):
+        for p in projs:
+            np.testing.assert_array_equal(got[p].view(np.uint16), singles[p].view(np.uint16),
+                                          err_msg=f"xcds{xcds} projs={projs} p{p}")
