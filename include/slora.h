@@ -97,7 +97,7 @@ void slora_pool_destroy(slora_pool* pool);
  *                                tiles; default 64.
  *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
  *                                expand tile; 0 (default): chosen from the
- *                                batch (16K to 128K, growing with the
+ *                                batch (16K to 256K, growing with the
  *                                batch's vector-ALU expand work).
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
  *                                of 128; 0 (default): 512 when every segment

@@ -447,9 +447,10 @@ void build_tiles(slora_segments* s) {
   // many small tiles to keep enough loads in flight; a large one runs faster
   // with fewer, larger tiles (less per-tile setup).  Measured on MI355X the
   // best budget tracks the batch's vector-ALU expand work / 1024, rounded
-  // down to a power of two and clamped to [16K, 128K] elements: 16K for 256
-  // Llama-7B decode tokens, 32K for the 13B mixed batch, 128K for 512 tokens
-  // of the 70B MLP projection.
+  // down to a power of two and clamped to [16K, 256K] elements: 16K for 256
+  // Llama-7B decode tokens, 32K for the 13B mixed batch, 256K for 512 tokens
+  // of the 70B MLP projection (257.9-258.3 against 261.2-262.5 us at 128K;
+  // above 256K a rank-128 tile is already at its widest, 2048 columns).
   // K splits of the MFMA shrink: enough tiles to give every CU about two
   // (512), at most kMaxSplits; with more than one, a combine tile per 16
   // tokens sums the splits' partial x A in a fixed order.
@@ -485,7 +486,7 @@ void build_tiles(slora_segments* s) {
       if (!mfma_seg) work += (int64_t)((c + kGemvMaxTok - 1) / kGemvMaxTok) * s->seg_rank[g] * hout;
     }
     expand_elems = 16384;
-    while (expand_elems < 131072 && expand_elems * 2 <= work / 1024) expand_elems *= 2;
+    while (expand_elems < 262144 && expand_elems * 2 <= work / 1024) expand_elems *= 2;
   }
 
   // MFMA expand width.  Measured on MI355X: a batch whose segments all take
