@@ -98,7 +98,10 @@ void slora_pool_destroy(slora_pool* pool);
  *  SLORA_TUNE_GEMV_EXPAND_ELEMS- target rank x columns of one vector-ALU
  *                                expand tile; 0 (default): chosen from the
  *                                batch (16K to 256K, growing with the
- *                                batch's vector-ALU expand work).
+ *                                batch's vector-ALU expand work, counted
+ *                                over all projections when the batch has
+ *                                matrix-core tiles or tiles too deep for
+ *                                one register set).
  *  SLORA_TUNE_MFMA_EXPAND_COLS - columns of one MFMA expand tile, a multiple
  *                                of 128; 0 (default): 512 when every segment
  *                                of the batch takes the MFMA tiles, else 1024.

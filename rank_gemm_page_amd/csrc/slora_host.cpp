@@ -477,16 +477,50 @@ void build_tiles(slora_segments* s) {
   // set by hand.
   const int gemv_rows_one = (nck == kShrinkOneNck && p->tune.shrink_rows == 0) ? kShrinkRowsOne : gemv_rows;
 
+  // Width of a vector-ALU expand tile of rank r under a budget: the largest
+  // of vec * {256, 128, 64, 32} columns with r x width within it; a thread
+  // of it holds more than kExpandRowSet B rows (the pipelined variant) when
+  // the 256 / (width / vec) row groups leave it more rows than that.
+  auto gemv_width = [&](int32_t r, int64_t budget) {
+    int32_t width = vec * 256;
+    while (width > vec * 32 && (int64_t)r * width > budget) width /= 2;
+    return width;
+  };
+  auto gemv_pipelined = [&](int32_t r, int64_t budget) {
+    const int32_t groups = kThreads / (gemv_width(r, budget) / vec);
+    return (r + groups - 1) / groups > kExpandRowSet;
+  };
   int64_t expand_elems = p->tune.gemv_expand_elems;
   if (expand_elems == 0) {
     int64_t work = 0;
+    bool heavy = false;   // the launch runs a variant with three workgroups per CU anyway
     for (int32_t g = 0; g < S; ++g) {
       const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
       const bool mfma_seg = mfma_ok && c >= p->tune.mfma_min_tokens && s->seg_rank[g] <= kMaxRankMfma;
       if (!mfma_seg) work += (int64_t)((c + kGemvMaxTok - 1) / kGemvMaxTok) * s->seg_rank[g] * hout;
+      heavy = heavy || mfma_seg;
     }
-    expand_elems = 16384;
-    while (expand_elems < 262144 && expand_elems * 2 <= work / 1024) expand_elems *= 2;
+    auto budget_of = [](int64_t w) {
+      int64_t b = 16384;
+      while (b < 262144 && b * 2 <= w / 1024) b *= 2;
+      return b;
+    };
+    expand_elems = budget_of(work);
+    for (int32_t g = 0; g < S && !heavy; ++g) {
+      const int32_t c = s->seg_start[g + 1] - s->seg_start[g];
+      const bool mfma_seg = mfma_ok && c >= p->tune.mfma_min_tokens && s->seg_rank[g] <= kMaxRankMfma;
+      heavy = !mfma_seg && gemv_pipelined(s->seg_rank[g], expand_elems);
+    }
+    // A launch whose registers already leave three workgroups per CU (matrix-
+    // core tiles, or vector-ALU tiles deeper than one register set) loses no
+    // residency to larger expand tiles, so there the budget follows the work
+    // of a launch over all projections (slora_lora_delta_multi): the 13B
+    // mixed step 218.7-219.2 against 223.6-224.0 us at its one-projection
+    // budget of 32K (one projection per launch it is 3 % slower: each launch
+    // holds a quarter of the tiles).  A batch that would become pipelined
+    // keeps the small budget (7B decode 21.2-21.4 us at 16K against 22.4 at
+    // 32K and 26.4 at 64K).
+    if (heavy) expand_elems = budget_of(work * s->n_proj);
   }
 
   // MFMA expand width.  Measured on MI355X: a batch whose segments all take
@@ -517,14 +551,9 @@ void build_tiles(slora_segments* s) {
     const bool mfma = mfma_ok && c >= p->tune.mfma_min_tokens && r <= kMaxRankMfma;
     if (mfma) ++s->n_mfma_segments;
     split_tokens(c, mfma ? kMfmaExpandTok : kGemvMaxTok, eblocks);
-    // vector-ALU expand width: largest of vec*{256,128,64,32} with rank x width within budget
-    int32_t width = vec * 256;
-    while (width > vec * 32 && (int64_t)r * width > expand_elems) width /= 2;
+    const int32_t width = gemv_width(r, expand_elems);
     const int32_t cols = mfma ? (int32_t)mfma_cols : width;
-    if (!mfma) {
-      const int32_t groups = kThreads / (width / vec);
-      if ((r + groups - 1) / groups > kExpandRowSet) s->pipe_expand = true;
-    }
+    if (!mfma && gemv_pipelined(r, expand_elems)) s->pipe_expand = true;
     for (size_t b = 0; b < eblocks.size(); ++b) {
       const auto& tb = eblocks[b];
       const int32_t grp = n_groups + (int32_t)b;
