@@ -364,6 +364,34 @@ def test_mfma_expand_width_follows_the_batch(name, tuning, want):
         S.slora_pool_destroy(pool)
 
 
+@pytest.mark.parametrize("name,tuning,budget,pipelined", [
+    ("decode7b", {}, 16384, False),      # light launch: stays within one register set of B rows
+    ("mixed13b", {}, 131072, True),      # MFMA tiles beside: budget from all four projections' work
+    ("mlp70b", {}, 262144, True),        # deep tiles at any budget: the cap
+    ("mlp70b", {S.SLORA_TUNE_GEMV_EXPAND_ELEMS: 32768}, 32768, True)])   # an explicit budget wins
+def test_vector_alu_expand_budget_follows_the_launch(name, tuning, budget, pipelined):
+    """Vector-ALU expand tiles: rank x width within the chosen budget, and as
+    wide as it allows (up to 8 x 256 columns); whether some thread holds more
+    B rows than one register set (the pipelined kernel) follows from it."""
+    w = generate(CONFIGS[name], 0)
+    pool, _ = make_pool(w, tuning=tuning)
+    try:
+        seg = S.slora_build_segments(pool, w.ids)
+        try:
+            _, recs = S.slora_segments_tiles(seg)
+            gemv = [(int(rec[2]), int(rec[7])) for rec in recs if int(rec[0]) == 2]   # (rank, width)
+            assert gemv
+            for r, width in gemv:
+                assert r * width <= budget or width == 8 * 32
+                assert width == 8 * 256 or r * width * 2 > budget
+            deep = any(-(-r // (256 // (width // 8))) > 8 for r, width in gemv)
+            assert deep == pipelined
+        finally:
+            S.slora_segments_destroy(seg)
+    finally:
+        S.slora_pool_destroy(pool)
+
+
 def test_tiles_with_ragged_shapes_and_no_adapter_tokens():
     spec = small_spec("ragged", h_in=136, h_out=200, two_classes=True, n_adapters=7,
                       rank_set=(1, 3, 13, 40, 100), batch=("zipf", 60, 1.0))
