@@ -400,6 +400,16 @@ slora_status slora_lora_delta_multi_timed(slora_pool* pool, const slora_segments
  * after about 2^20 polls, so a healthy GPU never raises it. */
 slora_status slora_segments_read_error(const slora_segments* seg, void* stream, int32_t* flag);
 
+/* For tests of the epoch counter: fused launches tag the x A values they
+ * exchange with an epoch that counts 1, 2, ... per launch since the upload
+ * and, once it reaches 2^31 - 1, clear the exchange pairs on the stream and
+ * start again at 1.  Moves the count of fused launches since the upload
+ * forward to `launches` (from the current count up to 2^31 - 1; SLORA_E_INVAL
+ * otherwise, nothing changed), so that the next launch takes epoch
+ * launches + 1, or clears and takes 1.  Only forward: pairs left by earlier
+ * launches then carry smaller epochs and can never match a later one. */
+slora_status slora_segments_set_launch_count(slora_segments* seg, int64_t launches);
+
 /* The two stages of slora_lora_delta, for callers that schedule or time them
  * apart: slora_lora_shrink writes v = x A (fp32) for every routed token into
  * the workspace; slora_lora_expand then applies y += s v B.  Same arguments,

@@ -1387,6 +1387,15 @@ slora_status slora_segments_upload(slora_segments* s, void* dev_meta, size_t dev
   return SLORA_OK;
 }
 
+slora_status slora_segments_set_launch_count(slora_segments* s, int64_t launches) {
+  if (!s) return fail(SLORA_E_INVAL, "slora_segments_set_launch_count: NULL segments");
+  if (launches < (int64_t)s->epoch || launches > 0x7FFFFFFF)
+    return fail(SLORA_E_INVAL, "slora_segments_set_launch_count: launches must be at least the current count "
+                               "and at most 2^31 - 1");
+  s->epoch = (uint32_t)launches;
+  return SLORA_OK;
+}
+
 slora_status slora_segments_read_error(const slora_segments* s, void* stream, int32_t* flag) {
   if (!s || !flag) return fail(SLORA_E_INVAL, "slora_segments_read_error: NULL argument");
   *flag = 0;

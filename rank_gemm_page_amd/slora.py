@@ -34,7 +34,7 @@ EXPORTED = [
     "slora_adapter_image_bytes", "slora_pack_adapter", "slora_load_adapters_async",
     "slora_adapter_pages", "slora_build_segments", "slora_segments_destroy",
     "slora_segments_get_info", "slora_segments_export", "slora_segments_tiles",
-    "slora_segments_upload", "slora_segments_read_error",
+    "slora_segments_upload", "slora_segments_read_error", "slora_segments_set_launch_count",
     "slora_lora_delta", "slora_lora_delta_timed", "slora_lora_shrink", "slora_lora_expand",
     "slora_lora_forward", "slora_lora_forward_timed", "slora_last_error",
     "slora_lora_delta_multi", "slora_lora_delta_multi_timed", "slora_lora_forward_noalloc",
@@ -101,6 +101,7 @@ def lib():
             "slora_segments_tiles": (c_int32, [P, POINTER(c_int32), POINTER(c_int32), c_size_t]),
             "slora_segments_upload": (c_int32, [P, P, c_size_t, P]),
             "slora_segments_read_error": (c_int32, [P, P, POINTER(c_int32)]),
+            "slora_segments_set_launch_count": (c_int32, [P, c_int64]),
             "slora_lora_delta": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
             "slora_lora_delta_timed": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P, P, P]),
             "slora_lora_delta_multi": (c_int32, [P, P, c_int32, POINTER(c_int32), POINTER(P), POINTER(P), P,
@@ -343,6 +344,10 @@ def slora_segments_read_error(seg, stream=None) -> int:
            "slora_segments_read_error")
     return int(flag.value)
 
+
+
+def slora_segments_set_launch_count(seg, launches: int) -> None:
+    _check(lib().slora_segments_set_launch_count(seg, launches), "slora_segments_set_launch_count")
 
 def slora_lora_delta(pool, seg, proj: int, x, y, workspace, workspace_bytes: int, stream=None) -> None:
     _check(lib().slora_lora_delta(pool, seg, proj, _ptr(x), _ptr(y), _ptr(workspace),

@@ -150,6 +150,44 @@ def test_xcd_placement_and_rank_order_change_nothing(launch):
     assert all(np.array_equal(outs[0].view(np.uint16), o.view(np.uint16)) for o in outs[1:])
 
 
+def test_epoch_wrap_clears_the_pairs_and_starts_again():
+    """Fused launches across the epoch counter's end (2^31 - 1 launches since
+    the upload): the launch past it clears the exchange pairs and takes epoch 1
+    again.  K-split partials carry the epoch with bit 31 set, so the last
+    epochs tag them 0xFFFFFFFF.  Every launch gives the bits of the upload's
+    first launch, alone and with four projections in one launch, and no wait
+    gives up."""
+    spec = small_spec("wrap", h_in=1024, h_out=512, two_classes=True, n_adapters=6, n_proj=2,
+                      proj_x=(0, 0), batch=("mixed", 2, 70, 20))
+    w = generate(spec, 2)
+    dw = DeviceWorkload(w, "cuda:0", tuning={S.SLORA_TUNE_MFMA_MIN_TOKENS: 16})
+    try:
+        assert dw.info["n_mfma_segments"] > 0
+        dw.delta(0)
+        dw.delta(1)
+        torch.cuda.synchronize()
+        ref = [dw.y[p].cpu().numpy().view(np.uint16) for p in range(2)]
+        with pytest.raises(S.SloraError):
+            S.slora_segments_set_launch_count(dw.seg, 1)          # backwards: refused
+        S.slora_segments_set_launch_count(dw.seg, 0x7FFFFFFD)
+        # k = 0: epochs 2^31 - 2 and 2^31 - 1; k = 1 (both projections in one
+        # launch): the pairs cleared, epoch 1; then epochs 2 and 3, and 4
+        for k in range(4):
+            dw.reset_y()
+            if k % 2:
+                dw.delta_multi()
+            else:
+                dw.delta(0)
+                dw.delta(1)
+            torch.cuda.synchronize()
+            for p in range(2):
+                np.testing.assert_array_equal(dw.y[p].cpu().numpy().view(np.uint16), ref[p],
+                                              err_msg=f"launch {k} p{p}")
+        assert S.slora_segments_read_error(dw.seg) == 0
+    finally:
+        dw.close()
+
+
 @pytest.mark.parametrize("route", ["gemv", "mfma"])
 def test_deterministic_run_to_run(route):
     """Same result bit for bit from repeated fused launches on one upload (epochs

@@ -500,6 +500,12 @@ def test_segments_errors_and_staleness():
             assert status_of(S.slora_lora_delta, pool, seg, 0, fake, fake, fake, 1 << 20) == S.SLORA_E_STALE
             S.slora_load_adapter(pool, 0, 2, 1.0)   # reloaded: a new generation, still stale
             assert status_of(S.slora_lora_delta, pool, seg, 0, fake, fake, fake, 1 << 20) == S.SLORA_E_STALE
+            # the launch count only moves forward and stays below 2^31
+            S.slora_segments_set_launch_count(seg, 5)
+            assert status_of(S.slora_segments_set_launch_count, seg, 4) == S.SLORA_E_INVAL
+            assert status_of(S.slora_segments_set_launch_count, seg, 1 << 31) == S.SLORA_E_INVAL
+            S.slora_segments_set_launch_count(seg, 5)
+            S.slora_segments_set_launch_count(seg, (1 << 31) - 1)
         finally:
             S.slora_segments_destroy(seg)
         ex = S.slora_segments_export(seg2 := S.slora_build_segments(pool, [2, -1, 0, 2]))
