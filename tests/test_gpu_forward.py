@@ -283,13 +283,15 @@ def sample_positions(w, n, bm=128, seed=0):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,projs", [("decode7b", (0,)), ("prefill7b", (0,)),
-                                        ("mixed13b", (0, 1, 2, 3)), ("mlp70b", (0,))])
-def test_forward_full_size(name, projs):
+@pytest.mark.parametrize("name,projs,seed", [("decode7b", (0,), 0), ("prefill7b", (0,), 0),
+                                             ("mixed13b", (0, 1, 2, 3), 0), ("mlp70b", (0,), 0),
+                                             # other draws: new ranks, token ids, x, W, y and page layout
+                                             ("decode7b", (0,), 1), ("mlp70b", (0,), 1)])
+def test_forward_full_size(name, projs, seed):
     """Every row of every projection of the benchmark batches against the oracle."""
-    w = generate(CONFIGS[name], 0)
+    w = generate(CONFIGS[name], seed)
     ys, info = run_forward(w, projs=projs)
-    print(f"[gpu] {name}: segments={info['n_segments']} tokens={w.T}", flush=True)
+    print(f"[gpu] {name}/seed{seed}: segments={info['n_segments']} tokens={w.T}", flush=True)
     st = build_from_workload(w)
     for p, runs in zip(projs, ys):
         y = runs[0]

@@ -341,10 +341,10 @@ def test_full_size_config(name):
 
 
 # Other draws of the same workloads (other batches, ranks and page layouts):
-# seeds 1-4 of the two decode-shaped batches under the bandwidth gate, seed 1
-# of the others.
+# seeds 1-4 of decode, 1-2 of the others.
 @pytest.mark.parametrize("name,seed", [("decode7b", 1), ("decode7b", 2), ("decode7b", 3), ("decode7b", 4),
-                                       ("mlp70b", 1), ("mlp70b", 2), ("prefill7b", 1), ("mixed13b", 1)])
+                                       ("mlp70b", 1), ("mlp70b", 2), ("prefill7b", 1), ("prefill7b", 2),
+                                       ("mixed13b", 1), ("mixed13b", 2)])
 def test_full_size_other_seeds(name, seed):
     full_size_parity(name, seed)
 
