@@ -769,8 +769,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported; the delta shards by tokens or columns with no exchange, and this "
-              "build measures one GPU's share.", file=sys.stderr, flush=True)
+              "supported; the delta shards by tokens or columns with no exchange, and "
+              "bench.py measures one GPU's share.", file=sys.stderr, flush=True)
         sys.exit(3)
 
     import torch
