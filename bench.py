@@ -18,6 +18,7 @@ host cores (``cpu_baseline``).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -481,6 +482,12 @@ def measure_config(name, args, tuning, dev, headline):
     t_cfg = time.perf_counter()
     log(f"[bench] generating {name} seed={args.seed}")
     w = generate(CONFIGS[name], args.seed)
+    if args.rank_pad:
+        # the same batch with every adapter's rank rounded up to a multiple of
+        # rank_pad, as a layout that pads ranks to uniform tiles would store it
+        # (token ids, x and y are drawn from their own streams and stay as they were)
+        padded = tuple(min(256, -(-int(r) // args.rank_pad) * args.rank_pad) for r in w.ranks)
+        w = generate(dataclasses.replace(CONFIGS[name], fixed_ranks=padded), args.seed)
     log(f"[bench] {name}: loading pool")
     dw = DeviceWorkload(w, dev, tuning=tuning)
     spec = w.spec
@@ -642,7 +649,8 @@ def measure_config(name, args, tuning, dev, headline):
                    "tokens": routed, "h_in": spec.h_in, "h_out": spec.h_out,
                    "projections": n_proj, "distinct_x": n_x, "adapters": spec.n_adapters,
                    "segments": info["n_segments"], "mfma_segments": info["n_mfma_segments"],
-                   "sum_rank": int(info["sum_rank"]), "seed": args.seed, "parallelism": "single GPU",
+                   "sum_rank": int(info["sum_rank"]), "seed": args.seed, "rank_pad": args.rank_pad,
+                   "parallelism": "single GPU",
                    "tuning": {str(k): v for k, v in tuning.items()}},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -748,6 +756,8 @@ def main():
                     help="rank rows per vector-ALU shrink tile (0: as many as fit)")
     ap.add_argument("--fwd-ksplit", type=int, default=None,
                     help="wave groups splitting a 32- or 64-row forward tile's steps (0: automatic)")
+    ap.add_argument("--rank-pad", type=int, default=0,
+                    help="round every adapter's rank up to a multiple of this (padded-rank comparison; 0: off)")
     ap.add_argument("--per-projection", action="store_true",
                     help="one fused launch per projection instead of one launch for all of them")
     ap.add_argument("--staged", action="store_true",
