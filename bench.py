@@ -45,6 +45,20 @@ WORKLOAD_NOTES = {
 }
 
 
+def workload(name, seed, rank_pad=0):
+    """The named synthetic batch; with rank_pad > 0, the same batch with every
+    adapter's rank rounded up to a multiple of rank_pad (at most 256), as a
+    layout that pads ranks to uniform tiles would store it (token ids, x and y
+    come from their own random streams and stay as they were)."""
+    from synth import CONFIGS, generate
+
+    w = generate(CONFIGS[name], seed)
+    if rank_pad:
+        padded = tuple(min(256, -(-int(r) // rank_pad) * rank_pad) for r in w.ranks)
+        w = generate(dataclasses.replace(CONFIGS[name], fixed_ranks=padded), seed)
+    return w
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -477,17 +491,10 @@ def measure_config(name, args, tuning, dev, headline):
     from rank_gemm_page_amd import slora as S
     from rank_gemm_page_amd.device_workload import DeviceWorkload
     from rank_gemm_page_amd.hip_events import HipEvent
-    from synth import CONFIGS, generate
 
     t_cfg = time.perf_counter()
     log(f"[bench] generating {name} seed={args.seed}")
-    w = generate(CONFIGS[name], args.seed)
-    if args.rank_pad:
-        # the same batch with every adapter's rank rounded up to a multiple of
-        # rank_pad, as a layout that pads ranks to uniform tiles would store it
-        # (token ids, x and y are drawn from their own streams and stay as they were)
-        padded = tuple(min(256, -(-int(r) // args.rank_pad) * args.rank_pad) for r in w.ranks)
-        w = generate(dataclasses.replace(CONFIGS[name], fixed_ranks=padded), args.seed)
+    w = workload(name, args.seed, args.rank_pad)
     log(f"[bench] {name}: loading pool")
     dw = DeviceWorkload(w, dev, tuning=tuning)
     spec = w.spec

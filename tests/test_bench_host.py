@@ -51,3 +51,18 @@ def test_committed_profiles_match_the_sources():
     for cfg in ("decode7b", "prefill7b", "mixed13b", "mlp70b"):
         b, us = bench.load_traffic(cfg, "forward_kernel", kind="forward")
         assert b is not None and us is not None, cfg
+
+
+@pytest.mark.parametrize("pad", [16, 32, 64, 128])
+def test_rank_padding_keeps_the_batch(pad):
+    """bench.py --rank-pad: ranks rounded up to a multiple of pad (at most 256),
+    the tokens, their adapters, x and y unchanged."""
+    import numpy as np
+
+    w0, w1 = bench.workload("decode7b", 0), bench.workload("decode7b", 0, pad)
+    assert np.array_equal(w0.ids, w1.ids)
+    assert all(np.array_equal(a, b) for a, b in zip(w0.x, w1.x))
+    assert all(np.array_equal(a, b) for a, b in zip(w0.y, w1.y))
+    want = np.minimum(256, -(-w0.ranks // pad) * pad)
+    assert np.array_equal(w1.ranks, want) and (w1.ranks % pad == 0).all()
+    assert (w1.ranks >= w0.ranks).all()
