@@ -84,6 +84,23 @@ def load_traffic(config, dominant, kind="fused"):
             sum(avg) if all(a is not None for a in avg) else None)
 
 
+def load_mfma_util(config):
+    """Matrix-core busy share and issued fp16 MFMA flops of the fused kernel
+    from the committed rocprofv3 counter run of this workload, if it was taken
+    of the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    from rank_gemm_page_amd.profiling import kernel_source_hash
+    if t.get("kernel_source_hash") != kernel_source_hash("fused"):
+        return None
+    return {"mfma_util_percent": t["mfma_util_percent"],
+            "mfma_flops_f16_per_launch": t["mfma_flops_f16_per_launch"],
+            "source": f"profiles/mfma_{config}.json ({t['counters']})"}
+
+
 def cpu_baseline(w, budget_s=10.0, one_thread=True):
     """The fp64 oracle on the host cores over a bounded sample of the batch."""
     import numpy as np
@@ -711,6 +728,9 @@ def measure_config(name, args, tuning, dev, headline):
                    "frac_of_attainable": round(tflops / attainable, 4),
                    "note": "fp16 flops of the matrix-core and vector-ALU tiles together "
                            "(2 sum_t r_t (h_in + h_out) per projection)"}
+    util = load_mfma_util(name)
+    if util is not None:
+        out["mfma"]["profiled"] = util
     if headline:
         if args.base_gemm:
             log("[bench] base x W products")

@@ -66,3 +66,17 @@ def test_rank_padding_keeps_the_batch(pad):
     want = np.minimum(256, -(-w0.ranks // pad) * pad)
     assert np.array_equal(w1.ranks, want) and (w1.ranks % pad == 0).all()
     assert (w1.ranks >= w0.ranks).all()
+
+
+def test_mfma_util_follows_the_kernel_sources(tmp_path, monkeypatch):
+    """The committed counter runs are read back while they match the sources."""
+    for cfg in ("prefill7b", "mixed13b"):
+        u = bench.load_mfma_util(cfg)
+        assert u is not None and 0 < u["mfma_util_percent"] < 100, cfg
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_mfma_util("prefill7b") is None
+    os.makedirs(os.path.join(str(tmp_path), "profiles"))
+    with open(os.path.join(str(tmp_path), "profiles", "mfma_prefill7b.json"), "w") as f:
+        json.dump({"kernel_source_hash": "0" * 16, "mfma_util_percent": 5.0,
+                   "mfma_flops_f16_per_launch": 1.0, "counters": "x"}, f)
+    assert bench.load_mfma_util("prefill7b") is None
